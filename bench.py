@@ -1,0 +1,301 @@
+"""Benchmark of the fused q/kv norm-rope-quant-insert operator on one MI355X.
+
+One step = one call of the operator over the whole batch (every q head and kv
+row of every token: norm, RoPE, q written back, kv quantized and inserted).
+The metric is effective HBM bandwidth: the operator's algorithmic bytes (read
++ written once) divided by the time per step, reported as GB/s, as a fraction
+of the 8 TB/s HBM3E peak and as a fraction of a warm device-to-device copy
+ceiling measured in the same process.
+
+Prints ONE JSON line.  ``value`` is the Prefill workload (32768 tokens x 64
+heads); the Long workload (131072 x 128) is reported under ``also``.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-also]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s & % of warm copy ceiling, tokens×heads 32768×64 / 131072×128"
+PEAK_HBM_GBPS = 8000.0
+KERNEL_NAME = "qkv_prep_kernel"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- copy ceiling
+
+class DeviceCopy:
+    """hipMemcpyAsync device-to-device through the HIP runtime torch loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_int, ctypes.c_void_p]
+        self.hip.hipMemcpyAsync.restype = ctypes.c_int
+
+    def __call__(self, dst, src, nbytes, stream):
+        rc = self.hip.hipMemcpyAsync(dst, src, nbytes, 3, stream)   # 3 = device to device
+        if rc != 0:
+            raise RuntimeError("hipMemcpyAsync failed: %d" % rc)
+
+
+def copy_ceiling(torch, size_bytes, reps=20, max_rounds=12):
+    """Warm D2D copy rate, counted as 2 x size / time (read + write).  Repeats
+    rounds of `reps` copies until three consecutive round medians agree within
+    0.5%, and returns the best round median."""
+    cp = DeviceCopy()
+    src = torch.empty(size_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    for _ in range(10):
+        cp(dst.data_ptr(), src.data_ptr(), size_bytes, h)
+    torch.cuda.synchronize()
+    medians = []
+    for _ in range(max_rounds):
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            cp(dst.data_ptr(), src.data_ptr(), size_bytes, h)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        medians.append(statistics.median(times))
+        if len(medians) >= 3:
+            last = medians[-3:]
+            if (max(last) - min(last)) / min(last) < 0.005:
+                break
+    del src, dst
+    return 2.0 * size_bytes / min(medians) / 1e9
+
+
+# ----------------------------------------------------------------- one workload
+
+def bench_workload(torch, W, qp, name, steps, warmup):
+    w = W.WORKLOADS[name]
+    log("bench: drawing %s inputs on the GPU" % w.label)
+    inp = W.make_inputs(w, device="cuda")
+    valid = int(((inp["slot_mapping"] >= 0) &
+                 (inp["slot_mapping"] < w.num_blocks * w.block_size)).sum())
+    nbytes = W.algorithmic_bytes(w.num_tokens, w.num_heads, valid)
+    op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
+    shape = op.launch_shape(w.num_tokens)
+    stream = torch.cuda.current_stream()
+    args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+            inp["slot_mapping"], inp["cache"])
+    log("bench: %s warmup %d" % (w.label, warmup))
+    for _ in range(warmup):
+        op(*args)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    log("bench: %s timing %d steps" % (w.label, steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in events:
+        e0.record(stream)
+        op(*args)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_s = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events]
+    res = {
+        "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
+        "bytes_per_step": nbytes,
+        "wall_s_per_step": wall / steps,
+        "kernel_s_mean": statistics.fmean(kernel_s),
+        "kernel_s_median": statistics.median(kernel_s),
+        "kernel_s_min": min(kernel_s),
+        "launch": {"sets_per_wave": shape.sets_per_wave, "waves_per_block": shape.waves_per_block,
+                   "convert": shape.convert, "grid": shape.grid},
+        "valid_slots": valid,
+    }
+    res["gbps_wall"] = nbytes / res["wall_s_per_step"] / 1e9
+    res["gbps_kernel_mean"] = nbytes / res["kernel_s_mean"] / 1e9
+    res["gbps_kernel_median"] = nbytes / res["kernel_s_median"] / 1e9
+    del inp, args
+    torch.cuda.empty_cache()
+    return w, res
+
+
+def known_answer_check(torch, W, qp):
+    """Tiny workload on the device vs the oracle, bit for bit (run before and
+    after the measurement so a device that misbehaves cannot go unnoticed)."""
+    import numpy as np
+    import oracle
+    w = W.WORKLOADS["tiny"]
+    inp = W.make_inputs(w, device="cuda")
+    q0 = W.as_u16(inp["q"])
+    cache = inp["cache"].cpu().numpy().copy()
+    qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)(
+        inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+        inp["slot_mapping"], inp["cache"])
+    torch.cuda.synchronize()
+    want_q = oracle.qkv_prep(q0, W.as_u16(inp["kv"]), W.as_u16(inp["q_w"]), W.as_u16(inp["kv_w"]),
+                             inp["positions"].cpu().numpy(), inp["cos_sin"].cpu().numpy(),
+                             inp["slot_mapping"].cpu().numpy(), cache, w.num_blocks,
+                             w.block_size, w.eps)
+    return bool(np.array_equal(W.as_u16(inp["q"]), want_q) and
+                np.array_equal(inp["cache"].cpu().numpy(), cache))
+
+
+# ----------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(torch, W, name, target_s=15.0):
+    """The oracle (plain scalar C, OpenMP over tokens) on a bounded sample of
+    the same workload: the first tokens of the batch, grown until the run
+    takes about target_s seconds.  Throughput uses the same byte formula."""
+    import numpy as np
+    import oracle
+    w = W.WORKLOADS[name]
+    nth = max(1, min(16, os.cpu_count() or 1))
+    inp = W.make_inputs(W.Workload(w.name, min(w.num_tokens, 4096), w.num_heads, w.max_position,
+                                   w.num_blocks, w.block_size, w.positions, w.slots, w.seed,
+                                   num_seqs=1, outlier_frac=w.outlier_frac), device="cuda")
+    q = W.as_u16(inp["q"])
+    kv = W.as_u16(inp["kv"])
+    qw, kvw = W.as_u16(inp["q_w"]), W.as_u16(inp["kv_w"])
+    pos = inp["positions"].cpu().numpy()
+    cs = inp["cos_sin"].cpu().numpy()
+    slots = inp["slot_mapping"].cpu().numpy()
+    cache = inp["cache"].cpu().numpy()
+    n = 64
+    while True:
+        t0 = time.perf_counter()
+        oracle.qkv_prep(q[:n], kv[:n], qw, kvw, pos[:n], cs, slots[:n], cache, w.num_blocks,
+                        w.block_size, w.eps, nth)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= q.shape[0]:
+            break
+        n = min(q.shape[0], max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)))
+    valid = int(((slots[:n] >= 0) & (slots[:n] < w.num_blocks * w.block_size)).sum())
+    nbytes = W.algorithmic_bytes(n, w.num_heads, valid)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": "first %d of %d tokens of %s %dx%d (%.1f s)" % (
+                n, w.num_tokens, w.name, w.num_tokens, w.num_heads, dt)}
+
+
+# ----------------------------------------------------------------- counters
+
+def recorded_traffic(workload_label):
+    """HBM bytes per dispatch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "qkv_prep_counters_%s.txt" % workload_label.replace(" ", "_"))
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{"):
+                rec = json.loads(line)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "fp8_kv_cache_amd", "csrc", "qkv_prep_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("kernel_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_dispatch")
+
+
+# ----------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--also", default="long")
+    ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this operator is per token and needs no collective; "
+              "run with --gpus 1 (see the design notes for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp8_kv_cache_amd import qkv_prep as qp
+    from fp8_kv_cache_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kat_before = known_answer_check(torch, W, qp)
+    ceil_before = None if args.no_ceiling else max(copy_ceiling(torch, 512 << 20),
+                                                   copy_ceiling(torch, 2 << 30))
+    log("bench: copy ceiling before = %s GB/s" % ceil_before)
+    w, main_res = bench_workload(torch, W, qp, args.workload, args.steps, args.warmup)
+    also = None
+    if not args.no_also and args.also and args.also != args.workload:
+        _, also = bench_workload(torch, W, qp, args.also, args.steps, args.warmup)
+    ceil_after = None if args.no_ceiling else max(copy_ceiling(torch, 512 << 20),
+                                                  copy_ceiling(torch, 2 << 30))
+    log("bench: copy ceiling after = %s GB/s" % ceil_after)
+    kat_after = known_answer_check(torch, W, qp)
+    ceiling = max(ceil_before, ceil_after) if ceil_before else None
+
+    value = main_res["gbps_wall"]
+    achieved = main_res["gbps_kernel_mean"]
+    traffic = recorded_traffic(main_res["workload"])
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["wall_s_per_step"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": main_res["workload"], "tokens": w.num_tokens, "heads": w.num_heads,
+                   "head_dim": 512, "io": "bf16 q/kv in, bf16 q out in place, fp8 e4m3 + ue8m0 cache",
+                   "cache": "%d blocks x %d slots x 584 B" % (w.num_blocks, w.block_size),
+                   "launch": main_res["launch"]},
+        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "copy_ceiling_gbps": round(ceiling, 1) if ceiling else None,
+        "copy_ceiling_before_after": [round(ceil_before, 1) if ceil_before else None,
+                                      round(ceil_after, 1) if ceil_after else None],
+        "frac_of_copy": round(value / ceiling, 4) if ceiling else None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": KERNEL_NAME,
+                     "kernel_us_mean": round(main_res["kernel_s_mean"] * 1e6, 2),
+                     "bytes_per_launch": main_res["bytes_per_step"]},
+        "known_answer_before_after": [kat_before, kat_after],
+    }
+    if also:
+        out["also"] = {"workload": also["workload"], "value": round(also["gbps_wall"], 1),
+                       "kernel_gbps": round(also["gbps_kernel_mean"], 1),
+                       "ms_per_step": round(also["wall_s_per_step"] * 1e3, 4),
+                       "frac_of_peak": round(also["gbps_wall"] / PEAK_HBM_GBPS, 4),
+                       "frac_of_copy": round(also["gbps_wall"] / ceiling, 4) if ceiling else None,
+                       "launch": also["launch"], "bytes_per_step": also["bytes_per_step"]}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(torch, W, args.workload)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+// Host side of the qkv_prep C ABI: argument checks, the launch-shape
+// heuristic and the launch.  Declarations and contracts: include/qkv_prep.h.
+#include "qkv_prep.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "qkv_prep_internal.h"
+
+struct qkv_prep {
+    qkv_prep_config cfg;
+    int device;
+    int num_cus;
+    bool sync;  // QKV_PREP_SYNC=1: wait for the stream inside run
+    bool log;   // QKV_PREP_LOG=1: print each launch shape to stderr
+};
+
+namespace {
+
+bool env_flag(const char *name)
+{
+    const char *v = std::getenv(name);
+    return v && v[0] == '1';
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Launch shape for T tokens.
+//  * sets_per_wave: how many 4-row sets a wavefront loads before computing.
+//    More sets per wave means more bytes in flight per wave and fewer waves
+//    to launch, but fewer workgroups to spread over the 256 CUs; small
+//    batches keep one set per wave so every CU gets work.
+//  * waves_per_block: 4 (256 threads) unless forced.
+//  * convert: the gfx950 conversion instructions (same bits as the integer
+//    rounding, checked by the tests) unless forced.
+qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
+{
+    qkvp::LaunchShape s;
+    const int64_t q_sets = ceil_div(T * c.num_heads, qkvp::kRowsPerSet);
+    const int64_t kv_sets = ceil_div(T, qkvp::kRowsPerSet);
+    s.waves_per_block = c.waves_per_block ? c.waves_per_block : 4;
+    if (c.sets_per_wave) {
+        s.sets_per_wave = c.sets_per_wave;
+    } else {
+        // Aim for at least ~32 wavefronts per CU before going wider.
+        const int64_t cus = num_cus > 0 ? num_cus : 256;
+        if (q_sets >= 4 * 32 * cus)
+            s.sets_per_wave = 4;
+        else if (q_sets >= 2 * 32 * cus)
+            s.sets_per_wave = 2;
+        else
+            s.sets_per_wave = 1;
+    }
+    s.convert = c.convert ? c.convert : 1;
+    s.kv_blocks = ceil_div(kv_sets, s.waves_per_block);
+    s.q_blocks = ceil_div(ceil_div(q_sets, s.sets_per_wave), s.waves_per_block);
+    return s;
+}
+
+int check_config(const qkv_prep_config *cfg)
+{
+    if (!cfg)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (cfg->num_heads < 1 || cfg->block_size < 1 || !(cfg->eps >= 0.0f) || cfg->eps > 3.4e38f)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (cfg->sets_per_wave != 0 && cfg->sets_per_wave != 1 && cfg->sets_per_wave != 2 &&
+        cfg->sets_per_wave != 4)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (cfg->waves_per_block != 0 && cfg->waves_per_block != 1 && cfg->waves_per_block != 2 &&
+        cfg->waves_per_block != 4 && cfg->waves_per_block != 8)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (cfg->convert < 0 || cfg->convert > 2)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (cfg->head_dim != qkvp::kHeadDim || cfg->rope_dim != qkvp::kRopeDim)
+        return QKV_PREP_ERR_UNSUPPORTED;
+    return QKV_PREP_OK;
+}
+
+// Everything qkv_prep_run checks before it touches the device.
+int check_args(const qkv_prep_config &c, int num_cus, const qkv_prep_args *a)
+{
+    if (!a)
+        return QKV_PREP_ERR_INVALID_ARG;
+    const int64_t T = a->num_tokens;
+    if (T < 0 || a->num_blocks < 0 || a->max_position < 1)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (T == 0)
+        return QKV_PREP_OK;
+    if (!a->q || !a->kv || !a->kv_norm_w || !a->positions || !a->cos_sin || !a->slot_mapping ||
+        (a->num_blocks > 0 && !a->kv_cache))
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (!aligned(a->q, 16) || !aligned(a->kv, 16) || !aligned(a->kv_norm_w, 16) ||
+        (a->q_norm_w && !aligned(a->q_norm_w, 16)) || !aligned(a->cos_sin, 16) ||
+        (a->kv_cache && !aligned(a->kv_cache, 16)) || !aligned(a->positions, 8) ||
+        !aligned(a->slot_mapping, 8))
+        return QKV_PREP_ERR_MISALIGNED;
+    const int64_t H = c.num_heads;
+    const int64_t B = c.block_size;
+    // Row and slot indices are 32-bit inside the kernel; addresses are 64-bit.
+    if (T > (int64_t)0x7fffffff / H || a->num_blocks > (int64_t)0x7fffffff / B ||
+        a->max_position > ((int64_t)1 << 40))
+        return QKV_PREP_ERR_UNSUPPORTED;
+    // The dispatch counts work-items in 32 bits.
+    const qkvp::LaunchShape s = choose_shape(c, num_cus, T);
+    if ((s.kv_blocks + s.q_blocks) * 64 * s.waves_per_block >= ((int64_t)1 << 32))
+        return QKV_PREP_ERR_UNSUPPORTED;
+    return QKV_PREP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qkv_prep_strerror(int code)
+{
+    switch (code) {
+    case QKV_PREP_OK: return "ok";
+    case QKV_PREP_ERR_INVALID_ARG: return "invalid argument";
+    case QKV_PREP_ERR_UNSUPPORTED: return "unsupported shape";
+    case QKV_PREP_ERR_MISALIGNED: return "misaligned pointer";
+    case QKV_PREP_ERR_NO_DEVICE: return "no such HIP device";
+    case QKV_PREP_ERR_LAUNCH: return "kernel launch failed";
+    case QKV_PREP_ERR_DEVICE: return "device error during the call";
+    default: return "unknown qkv_prep error";
+    }
+}
+
+int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim)
+{
+    return num_heads >= 1 && head_dim == qkvp::kHeadDim && rope_dim == qkvp::kRopeDim;
+}
+
+int qkv_prep_create(const qkv_prep_config *cfg, int device, qkv_prep_t *out)
+{
+    if (!out)
+        return QKV_PREP_ERR_INVALID_ARG;
+    const int rc = check_config(cfg);
+    if (rc != QKV_PREP_OK)
+        return rc;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return QKV_PREP_ERR_NO_DEVICE;
+    }
+    if (device < 0 || device >= count)
+        return QKV_PREP_ERR_NO_DEVICE;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+        (void)hipGetLastError();
+        return QKV_PREP_ERR_NO_DEVICE;
+    }
+    qkv_prep *h = new (std::nothrow) qkv_prep;
+    if (!h)
+        return QKV_PREP_ERR_INVALID_ARG;
+    h->cfg = *cfg;
+    h->device = device;
+    h->num_cus = cus;
+    h->sync = env_flag("QKV_PREP_SYNC");
+    h->log = env_flag("QKV_PREP_LOG");
+    *out = h;
+    return QKV_PREP_OK;
+}
+
+int qkv_prep_destroy(qkv_prep_t h)
+{
+    delete h;
+    return QKV_PREP_OK;
+}
+
+int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t num_tokens,
+                          qkv_prep_launch *out)
+{
+    const int rc = check_config(cfg);
+    if (rc != QKV_PREP_OK)
+        return rc;
+    if (!out || num_tokens < 0)
+        return QKV_PREP_ERR_INVALID_ARG;
+    const qkvp::LaunchShape s = choose_shape(*cfg, num_cus, num_tokens);
+    out->sets_per_wave = s.sets_per_wave;
+    out->waves_per_block = s.waves_per_block;
+    out->convert = s.convert;
+    out->kv_blocks = num_tokens ? s.kv_blocks : 0;
+    out->q_blocks = num_tokens ? s.q_blocks : 0;
+    out->grid = out->kv_blocks + out->q_blocks;
+    return QKV_PREP_OK;
+}
+
+int qkv_prep_validate(const qkv_prep_config *cfg, const qkv_prep_args *args)
+{
+    const int rc = check_config(cfg);
+    return rc != QKV_PREP_OK ? rc : check_args(*cfg, 0, args);
+}
+
+int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
+{
+    if (!h)
+        return QKV_PREP_ERR_INVALID_ARG;
+    const int rc_args = check_args(h->cfg, h->num_cus, a);
+    if (rc_args != QKV_PREP_OK || a->num_tokens == 0)
+        return rc_args;
+    const int64_t T = a->num_tokens;
+    const int64_t H = h->cfg.num_heads;
+    const int64_t B = h->cfg.block_size;
+    const qkvp::LaunchShape s = choose_shape(h->cfg, h->num_cus, T);
+
+    qkvp::KernelArgs k;
+    k.q = static_cast<uint16_t *>(a->q);
+    k.kv = static_cast<const uint16_t *>(a->kv);
+    k.q_w = static_cast<const uint16_t *>(a->q_norm_w);
+    k.kv_w = static_cast<const uint16_t *>(a->kv_norm_w);
+    k.positions = a->positions;
+    k.cos_sin = a->cos_sin;
+    k.slot_mapping = a->slot_mapping;
+    k.cache = static_cast<uint8_t *>(a->kv_cache);
+    k.max_position = a->max_position;
+    k.num_slots = a->num_blocks * B;
+    k.q_rows = T * H;
+    k.num_tokens = T;
+    k.q_sets = (T * H + qkvp::kRowsPerSet - 1) / qkvp::kRowsPerSet;
+    k.kv_sets = (T + qkvp::kRowsPerSet - 1) / qkvp::kRowsPerSet;
+    k.num_heads = (uint32_t)H;
+    k.block_size = (uint32_t)B;
+    k.kv_blocks = (uint32_t)s.kv_blocks;
+    k.eps = h->cfg.eps;
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) {
+        (void)hipGetLastError();
+        return QKV_PREP_ERR_NO_DEVICE;
+    }
+    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return QKV_PREP_ERR_NO_DEVICE;
+    }
+    if (h->log)
+        std::fprintf(stderr, "qkv_prep: T=%lld H=%lld sets/wave=%d waves/block=%d convert=%d grid=%lld+%lld\n",
+                     (long long)T, (long long)H, s.sets_per_wave, s.waves_per_block, s.convert,
+                     (long long)s.kv_blocks, (long long)s.q_blocks);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = QKV_PREP_OK;
+    if (qkvp::launch_qkv_prep(k, s, st) != hipSuccess)
+        rc = QKV_PREP_ERR_LAUNCH;
+    else if (h->sync && hipStreamSynchronize(st) != hipSuccess)
+        rc = QKV_PREP_ERR_DEVICE;
+    if (prev != h->device)
+        (void)hipSetDevice(prev);
+    return rc;
+}
+
+}  // extern "C"

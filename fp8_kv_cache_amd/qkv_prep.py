@@ -1,0 +1,216 @@
+"""Python binding of the qkv_prep C ABI (include/qkv_prep.h).
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+of libqkv_prep.so.  The functions keep the C names; ``QkvPrep`` is a small
+convenience wrapper that takes torch tensors (torch supplies device memory and
+the stream, nothing else).  There is no fallback: if the library is missing
+the import of this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqkv_prep.so")
+
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_UNSUPPORTED = 2
+ERR_MISALIGNED = 3
+ERR_NO_DEVICE = 4
+ERR_LAUNCH = 5
+ERR_DEVICE = 6
+
+HEAD_DIM = 512
+NOPE_DIM = 448
+ROPE_DIM = 64
+SLOT_DATA_BYTES = 576
+SLOT_SCALE_BYTES = 8
+SLOT_BYTES = 584
+
+CONVERT_INTEGER = 1
+CONVERT_INSTRUCTIONS = 2
+
+# Every symbol the header declares (checked by the ABI tests).
+EXPORTED = ("qkv_prep_create", "qkv_prep_run", "qkv_prep_destroy", "qkv_prep_supported",
+            "qkv_prep_launch_shape", "qkv_prep_validate", "qkv_prep_strerror")
+
+
+class QkvPrepConfig(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("sets_per_wave", ctypes.c_int32),
+                ("waves_per_block", ctypes.c_int32), ("convert", ctypes.c_int32)]
+
+
+class QkvPrepArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("q_norm_w", ctypes.c_void_p),
+                ("kv_norm_w", ctypes.c_void_p), ("positions", ctypes.c_void_p),
+                ("cos_sin", ctypes.c_void_p), ("max_position", ctypes.c_int64),
+                ("slot_mapping", ctypes.c_void_p), ("kv_cache", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int64), ("num_tokens", ctypes.c_int64)]
+
+
+class QkvPrepLaunch(ctypes.Structure):
+    _fields_ = [("sets_per_wave", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
+                ("convert", ctypes.c_int32), ("kv_blocks", ctypes.c_int64),
+                ("q_blocks", ctypes.c_int64), ("grid", ctypes.c_int64)]
+
+
+class QkvPrepError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__("%s: %s (code %d)" % (what or "qkv_prep", qkv_prep_strerror(code), code))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libqkv_prep.so is not built (%s); run `python -m fp8_kv_cache_amd.build`"
+                          % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.qkv_prep_create.argtypes = [P(QkvPrepConfig), ctypes.c_int, P(ctypes.c_void_p)]
+    L.qkv_prep_create.restype = ctypes.c_int
+    L.qkv_prep_run.argtypes = [ctypes.c_void_p, P(QkvPrepArgs), ctypes.c_void_p]
+    L.qkv_prep_run.restype = ctypes.c_int
+    L.qkv_prep_destroy.argtypes = [ctypes.c_void_p]
+    L.qkv_prep_destroy.restype = ctypes.c_int
+    L.qkv_prep_supported.argtypes = [ctypes.c_int32] * 3
+    L.qkv_prep_supported.restype = ctypes.c_int
+    L.qkv_prep_launch_shape.argtypes = [P(QkvPrepConfig), ctypes.c_int32, ctypes.c_int64,
+                                        P(QkvPrepLaunch)]
+    L.qkv_prep_launch_shape.restype = ctypes.c_int
+    L.qkv_prep_validate.argtypes = [P(QkvPrepConfig), P(QkvPrepArgs)]
+    L.qkv_prep_validate.restype = ctypes.c_int
+    L.qkv_prep_strerror.argtypes = [ctypes.c_int]
+    L.qkv_prep_strerror.restype = ctypes.c_char_p
+    return L
+
+
+_lib = _load()
+
+
+def library():
+    return _lib
+
+
+def make_config(num_heads, *, block_size=64, eps=1e-6, sets_per_wave=0, waves_per_block=0,
+                convert=0) -> QkvPrepConfig:
+    return QkvPrepConfig(num_heads, HEAD_DIM, ROPE_DIM, block_size, eps, sets_per_wave,
+                         waves_per_block, convert)
+
+
+# ------------------------------------------------------------ C-named calls
+
+def qkv_prep_strerror(code: int) -> str:
+    return _lib.qkv_prep_strerror(code).decode()
+
+
+def qkv_prep_supported(num_heads: int, head_dim: int = HEAD_DIM, rope_dim: int = ROPE_DIM) -> bool:
+    return bool(_lib.qkv_prep_supported(num_heads, head_dim, rope_dim))
+
+
+def qkv_prep_create(cfg: QkvPrepConfig, device: int = 0) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    rc = _lib.qkv_prep_create(ctypes.byref(cfg), device, ctypes.byref(h))
+    if rc != OK:
+        raise QkvPrepError(rc, "qkv_prep_create")
+    return h
+
+
+def qkv_prep_run(handle, args: QkvPrepArgs, stream=None) -> None:
+    rc = _lib.qkv_prep_run(handle, ctypes.byref(args), stream)
+    if rc != OK:
+        raise QkvPrepError(rc, "qkv_prep_run")
+
+
+def qkv_prep_destroy(handle) -> None:
+    _lib.qkv_prep_destroy(handle)
+
+
+def qkv_prep_launch_shape(cfg: QkvPrepConfig, num_cus: int, num_tokens: int) -> QkvPrepLaunch:
+    out = QkvPrepLaunch()
+    rc = _lib.qkv_prep_launch_shape(ctypes.byref(cfg), num_cus, num_tokens, ctypes.byref(out))
+    if rc != OK:
+        raise QkvPrepError(rc, "qkv_prep_launch_shape")
+    return out
+
+
+def qkv_prep_validate(cfg: QkvPrepConfig, args: QkvPrepArgs) -> int:
+    return _lib.qkv_prep_validate(ctypes.byref(cfg), ctypes.byref(args))
+
+
+# ------------------------------------------------------------ torch wrapper
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
+              num_blocks=None) -> QkvPrepArgs:
+    """Pointers and sizes from torch tensors (no copies, no checks beyond the
+    dtype/contiguity that the C side cannot see)."""
+    import torch
+    for name, t, dt in (("q", q, torch.bfloat16), ("kv", kv, torch.bfloat16),
+                        ("q_norm_w", q_norm_w, torch.bfloat16),
+                        ("kv_norm_w", kv_norm_w, torch.bfloat16),
+                        ("positions", positions, torch.int64), ("cos_sin", cos_sin, torch.float32),
+                        ("slot_mapping", slot_mapping, torch.int64),
+                        ("kv_cache", kv_cache, torch.uint8)):
+        if t is None:
+            continue
+        if t.dtype != dt:
+            raise TypeError("%s must be %s, got %s" % (name, dt, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    T = q.shape[0]
+    if num_blocks is None:
+        num_blocks = kv_cache.shape[0] if kv_cache is not None else 0
+    return QkvPrepArgs(_ptr(q), _ptr(kv), _ptr(q_norm_w), _ptr(kv_norm_w), _ptr(positions),
+                       _ptr(cos_sin), cos_sin.shape[0], _ptr(slot_mapping), _ptr(kv_cache),
+                       num_blocks, T)
+
+
+class QkvPrep:
+    """A qkv_prep handle bound to one device.
+
+    ``op(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache)``
+    enqueues the operator on the current torch stream (or ``stream``)."""
+
+    def __init__(self, num_heads, *, device=0, block_size=64, eps=1e-6, sets_per_wave=0,
+                 waves_per_block=0, convert=0):
+        self.cfg = make_config(num_heads, block_size=block_size, eps=eps,
+                               sets_per_wave=sets_per_wave, waves_per_block=waves_per_block,
+                               convert=convert)
+        self.device = device
+        self.handle = qkv_prep_create(self.cfg, device)
+
+    def __call__(self, q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
+                 stream=None):
+        import torch
+        if q.dim() != 3 or q.shape[1] != self.cfg.num_heads or q.shape[2] != HEAD_DIM:
+            raise ValueError("q must be [T, %d, 512]" % self.cfg.num_heads)
+        if kv_cache is not None and kv_cache.numel() % (self.cfg.block_size * SLOT_BYTES):
+            raise ValueError("kv_cache must be [num_blocks, block_size*584] bytes")
+        args = make_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
+                         None if kv_cache is None
+                         else kv_cache.numel() // (self.cfg.block_size * SLOT_BYTES))
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        qkv_prep_run(self.handle, args, stream)
+        return q
+
+    def launch_shape(self, num_tokens, num_cus=256) -> QkvPrepLaunch:
+        return qkv_prep_launch_shape(self.cfg, num_cus, num_tokens)
+
+    def close(self):
+        if self.handle:
+            qkv_prep_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

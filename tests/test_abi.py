@@ -1,0 +1,186 @@
+"""The C ABI library on the host: it loads, exports every function the header
+declares, checks its arguments with the documented codes, and reports the
+launch shape it would use.  None of this launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from fp8_kv_cache_amd import qkv_prep as qp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkv_prep.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qkv_prep_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(qp.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(qp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_struct_sizes_match_the_header_layout():
+    assert ctypes.sizeof(qp.QkvPrepConfig) == 32
+    assert ctypes.sizeof(qp.QkvPrepArgs) == 88
+    assert ctypes.sizeof(qp.QkvPrepLaunch) == 40
+
+
+def test_strerror_and_supported():
+    assert qp.qkv_prep_strerror(qp.OK) == "ok"
+    assert "misaligned" in qp.qkv_prep_strerror(qp.ERR_MISALIGNED)
+    assert "unknown" in qp.qkv_prep_strerror(99)
+    assert qp.qkv_prep_supported(64)
+    assert qp.qkv_prep_supported(1)
+    assert not qp.qkv_prep_supported(0)
+    assert not qp.qkv_prep_supported(64, 576, 64)
+    assert not qp.qkv_prep_supported(64, 512, 32)
+
+
+def _good_args(T=16, num_blocks=4):
+    base = 1 << 20
+    return qp.QkvPrepArgs(base, base + 0x100000, base + 0x200000, base + 0x200400,
+                          base + 0x300000, base + 0x400000, 4096, base + 0x500000,
+                          base + 0x600000, num_blocks, T)
+
+
+def test_validate_accepts_good_arguments_and_empty_batch():
+    cfg = qp.make_config(8)
+    assert qp.qkv_prep_validate(cfg, _good_args()) == qp.OK
+    a = _good_args(T=0)
+    a.q = None
+    a.kv = None
+    assert qp.qkv_prep_validate(cfg, a) == qp.OK
+    a = _good_args()
+    a.q_norm_w = None                     # weightless q norm is allowed
+    assert qp.qkv_prep_validate(cfg, a) == qp.OK
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("q", None, qp.ERR_INVALID_ARG),
+    ("kv", None, qp.ERR_INVALID_ARG),
+    ("kv_norm_w", None, qp.ERR_INVALID_ARG),
+    ("positions", None, qp.ERR_INVALID_ARG),
+    ("cos_sin", None, qp.ERR_INVALID_ARG),
+    ("slot_mapping", None, qp.ERR_INVALID_ARG),
+    ("kv_cache", None, qp.ERR_INVALID_ARG),
+    ("num_tokens", -1, qp.ERR_INVALID_ARG),
+    ("num_blocks", -1, qp.ERR_INVALID_ARG),
+    ("max_position", 0, qp.ERR_INVALID_ARG),
+    ("q", (1 << 20) + 8, qp.ERR_MISALIGNED),
+    ("kv", (1 << 20) + 0x100002, qp.ERR_MISALIGNED),
+    ("q_norm_w", (1 << 20) + 0x200004, qp.ERR_MISALIGNED),
+    ("cos_sin", (1 << 20) + 0x400004, qp.ERR_MISALIGNED),
+    ("kv_cache", (1 << 20) + 0x600008, qp.ERR_MISALIGNED),
+    ("positions", (1 << 20) + 0x300004, qp.ERR_MISALIGNED),
+    ("slot_mapping", (1 << 20) + 0x500002, qp.ERR_MISALIGNED),
+    ("num_tokens", 1 << 30, qp.ERR_UNSUPPORTED),      # T*H rows past 2^31
+    ("max_position", (1 << 40) + 1, qp.ERR_UNSUPPORTED),
+])
+def test_validate_rejects(field, value, code):
+    a = _good_args()
+    setattr(a, field, value)
+    assert qp.qkv_prep_validate(qp.make_config(8), a) == code
+
+
+def test_cache_may_be_null_without_blocks():
+    a = _good_args(num_blocks=0)
+    a.kv_cache = None
+    assert qp.qkv_prep_validate(qp.make_config(8), a) == qp.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads=0), qp.ERR_INVALID_ARG),
+    (dict(block_size=0), qp.ERR_INVALID_ARG),
+    (dict(eps=-1.0), qp.ERR_INVALID_ARG),
+    (dict(eps=float("nan")), qp.ERR_INVALID_ARG),
+    (dict(sets_per_wave=3), qp.ERR_INVALID_ARG),
+    (dict(waves_per_block=16), qp.ERR_INVALID_ARG),
+    (dict(convert=3), qp.ERR_INVALID_ARG),
+])
+def test_bad_config(kw, code):
+    base = dict(num_heads=8, block_size=64, eps=1e-6)
+    base.update(kw)
+    cfg = qp.make_config(base.pop("num_heads"), **base)
+    assert qp.qkv_prep_validate(cfg, _good_args()) == code
+    with pytest.raises(qp.QkvPrepError) as e:
+        qp.qkv_prep_launch_shape(cfg, 256, 16)
+    assert e.value.code == code
+
+
+def test_unsupported_head_dim():
+    cfg = qp.make_config(8)
+    cfg.head_dim = 576
+    assert qp.qkv_prep_validate(cfg, _good_args()) == qp.ERR_UNSUPPORTED
+
+
+def test_launch_shape_heuristic():
+    cfg = qp.make_config(64)
+    small = qp.qkv_prep_launch_shape(cfg, 256, 16)
+    assert small.sets_per_wave == 1 and small.waves_per_block == 4
+    assert small.kv_blocks == 1 and small.q_blocks == 64 and small.grid == 65
+    assert qp.qkv_prep_launch_shape(cfg, 256, 0).grid == 0
+    big = qp.qkv_prep_launch_shape(cfg, 256, 32768)
+    assert big.sets_per_wave == 4
+    assert big.q_blocks == (32768 * 64 // 4) // 4 // 4
+    assert big.kv_blocks == 32768 // 4 // 4
+    forced = qp.qkv_prep_launch_shape(qp.make_config(64, sets_per_wave=2, waves_per_block=8,
+                                                     convert=1), 256, 1000)
+    assert (forced.sets_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
+    assert forced.q_blocks == -(-(-(-1000 * 64 // 4) // 2) // 8)
+    # ragged: T*H not a multiple of 4
+    odd = qp.qkv_prep_launch_shape(qp.make_config(3), 256, 5)
+    assert odd.q_blocks == 1 and odd.kv_blocks == 1
+
+
+def test_run_without_handle_is_rejected():
+    assert qp.library().qkv_prep_run(None, ctypes.byref(_good_args()), None) == qp.ERR_INVALID_ARG
+    assert qp.library().qkv_prep_destroy(None) == qp.OK
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
+def test_create_without_a_device_reports_no_device():
+    with pytest.raises(qp.QkvPrepError) as e:
+        qp.qkv_prep_create(qp.make_config(8), 0)
+    assert e.value.code == qp.ERR_NO_DEVICE
+
+
+def test_create_rejects_bad_config_before_touching_a_device():
+    with pytest.raises(qp.QkvPrepError) as e:
+        qp.qkv_prep_create(qp.make_config(0), 0)
+    assert e.value.code == qp.ERR_INVALID_ARG
+
+
+def test_ctypes_layout_matches_the_c_compiler(tmp_path):
+    # Compile a few lines of C against the header and compare every field
+    # offset with the ctypes mirror.
+    import subprocess
+    fields = {"qkv_prep_config": qp.QkvPrepConfig, "qkv_prep_args": qp.QkvPrepArgs,
+              "qkv_prep_launch": qp.QkvPrepLaunch}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "qkv_prep.h"', "int main(void){"]
+    for cname, cls in fields.items():
+        lines.append('printf("%%zu\\n", sizeof(%s));' % cname)
+        for f, _ in cls._fields_:
+            lines.append('printf("%%zu\\n", offsetof(%s, %s));' % (cname, f))
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = []
+    for cls in fields.values():
+        want.append(ctypes.sizeof(cls))
+        want += [getattr(cls, f).offset for f, _ in cls._fields_]
+    assert got == want

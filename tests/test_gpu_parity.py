@@ -1,0 +1,222 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Every token of every case is compared (the oracle runs over token chunks on
+the host cores); see tests/parity.py for the bar.  Inputs are drawn on the GPU
+and copied to the host for the oracle."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_kv_cache_amd import workloads as W
+
+from parity import assert_bit_exact, assert_within_bar, run_and_compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check(w, *, q_weight=True, exact=True, **cfg):
+    note("case %s cfg=%s q_weight=%s" % (w.label, cfg, q_weight))
+    inp = W.make_inputs(w, device=DEV, q_weight=True)
+    res = run_and_compare(w, inp, q_weight=q_weight, **cfg)
+    note("  -> %s" % res)
+    if exact:
+        assert_bit_exact(res)
+    else:
+        assert_within_bar(res)
+    return res
+
+
+# ----------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("convert", [1, 2])
+def test_tiny(convert):
+    res = check(W.WORKLOADS["tiny"], convert=convert)
+    assert res["valid_slots"] == 14
+
+
+@pytest.mark.parametrize("convert", [1, 2])
+def test_decode_2048x64(convert):
+    check(W.WORKLOADS["decode"], convert=convert)
+
+
+def test_prefill_32768x64():
+    check(W.WORKLOADS["prefill"])
+
+
+def test_prefill_wide_32768x128():
+    check(W.WORKLOADS["prefill_wide"])
+
+
+def test_long_131072x128():
+    check(W.WORKLOADS["long"], exact=True)
+
+
+# ----------------------------------------------------------------- launch shapes
+
+SHAPES = [(1, 8), (4, 8), (17, 64), (64, 3), (511, 64), (777, 5), (1000, 1), (4096, 128)]
+
+
+@pytest.mark.parametrize("T,H", SHAPES)
+@pytest.mark.parametrize("spw,wpb", [(1, 1), (1, 4), (2, 8), (4, 2), (4, 4)])
+def test_forced_launch_shapes(T, H, spw, wpb):
+    check(W.custom(T, H, seed=100 + T + H), sets_per_wave=spw, waves_per_block=wpb,
+          convert=2 if (T + spw) % 2 else 1)
+
+
+@pytest.mark.parametrize("T,H", [(1, 64), (17, 8), (512, 64), (2048, 128)])
+def test_weightless_q(T, H):
+    check(W.custom(T, H, seed=200 + T), q_weight=False)
+
+
+@pytest.mark.parametrize("block_size", [1, 5, 16, 64, 256])
+def test_block_sizes(block_size):
+    check(W.custom(300, 8, seed=300 + block_size, block_size=block_size))
+
+
+def test_skips_and_out_of_range_slots():
+    w = W.custom(256, 16, seed=401, num_skip=40)
+    inp = W.make_inputs(w, device=DEV)
+    s = inp["slot_mapping"]
+    cap = w.num_blocks * w.block_size
+    s[3] = cap
+    s[7] = cap + 12345
+    s[9] = -(1 << 40)
+    s[11] = 1 << 45
+    res = run_and_compare(w, inp)
+    note("skips -> %s" % res)
+    assert_bit_exact(res)
+
+
+def test_all_slots_skipped_and_empty_cache():
+    w = W.custom(100, 8, seed=402, num_blocks=1, block_size=64)
+    inp = W.make_inputs(w, device=DEV)
+    inp["slot_mapping"].fill_(-1)
+    res = run_and_compare(w, inp)
+    assert res["valid_slots"] == 0
+    assert_bit_exact(res)
+
+
+def test_positions_at_both_ends_of_the_table():
+    w = W.custom(64, 8, seed=403, max_position=77)
+    inp = W.make_inputs(w, device=DEV)
+    inp["positions"][::2] = 0
+    inp["positions"][1::2] = 76
+    assert_bit_exact(run_and_compare(w, inp))
+
+
+def test_outlier_rows_and_eps_zero():
+    w = W.custom(512, 16, seed=404, outlier_frac=0.05, eps=0.0)
+    assert_bit_exact(run_and_compare(w, W.make_inputs(w, device=DEV)))
+
+
+# ----------------------------------------------------------------- hand case
+
+def test_hand_derived_slot_on_gpu():
+    # The kv slot whose every byte the oracle tests derive by hand: a row of
+    # ones at eps = 0 and position 0 with crafted weights (zeros, -0, exact
+    # 448, ties in E4M3, subnormal codes).
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    w = np.ones(512, np.float32)
+    w[0] = 3.5
+    w[64], w[65], w[66] = 3.5, 1.0625, 1.1875
+    w[128:192] = -0.0
+    w[192:256] = 448.0
+    w[256:320] = 2.0 ** -10
+    w[320], w[321], w[322] = 1.0, 2.0 ** -16, 3 * 2.0 ** -18
+    w[323:384] = 2.0 ** -18
+    w[384] = -3.5
+    kvw = torch.from_numpy(oracle.f32_to_bf16(w).view(np.int16)).view(torch.bfloat16)
+    for convert in (1, 2):
+        nb, bs = 2, 4
+        cache = torch.full((nb, bs * 584), 0xA5, dtype=torch.uint8, device=DEV)
+        q = torch.ones((1, 1, 512), dtype=torch.bfloat16, device=DEV)
+        kv = torch.ones((1, 512), dtype=torch.bfloat16, device=DEV)
+        cs = torch.from_numpy(W.rope_table(8)).to(DEV)
+        pos = torch.zeros(1, dtype=torch.int64, device=DEV)
+        slot = torch.tensor([6], dtype=torch.int64, device=DEV)
+        op = QkvPrep(1, block_size=bs, eps=0.0, convert=convert)
+        op(q, kv, None, kvw.to(DEV), pos, cs, slot, cache)
+        torch.cuda.synchronize()
+        want = np.full((nb, bs * 584), 0xA5, np.uint8)
+        q_want = oracle.qkv_prep(np.full((1, 1, 512), 0x3F80, np.uint16),
+                                 np.full((1, 512), 0x3F80, np.uint16), None,
+                                 oracle.f32_to_bf16(w), np.zeros(1, np.int64), W.rope_table(8),
+                                 np.array([6]), want, nb, bs, 0.0)
+        assert np.array_equal(cache.cpu().numpy(), want), convert
+        assert np.array_equal(W.as_u16(q), q_want), convert
+
+
+# ----------------------------------------------------------------- behaviour
+
+def test_empty_batch_is_a_no_op():
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    w = W.custom(0, 8, seed=405)
+    inp = W.make_inputs(w, device=DEV)
+    before = inp["cache"].clone()
+    op = QkvPrep(8)
+    op(inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+       inp["slot_mapping"], inp["cache"])
+    torch.cuda.synchronize()
+    assert torch.equal(before, inp["cache"])
+
+
+def test_repeat_runs_are_byte_identical():
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    w = W.custom(4096, 64, seed=406)
+    inp = W.make_inputs(w, device=DEV)
+    outs = []
+    for _ in range(3):
+        q = inp["q"].clone()
+        c = inp["cache"].clone()
+        QkvPrep(64)(q, inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+                    inp["slot_mapping"], c)
+        torch.cuda.synchronize()
+        outs.append((q.view(torch.int16).cpu(), c.cpu()))
+    for q, c in outs[1:]:
+        assert torch.equal(q, outs[0][0]) and torch.equal(c, outs[0][1])
+
+
+def test_side_stream_and_conversion_modes_agree():
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    w = W.custom(1500, 32, seed=407)
+    inp = W.make_inputs(w, device=DEV)
+    results = []
+    s = torch.cuda.Stream()
+    for convert in (1, 2):
+        q = inp["q"].clone()
+        c = inp["cache"].clone()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            QkvPrep(32, convert=convert)(q, inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"],
+                                         inp["cos_sin"], inp["slot_mapping"], c)
+        s.synchronize()
+        results.append((q.view(torch.int16).cpu(), c.cpu()))
+    assert torch.equal(results[0][0], results[1][0])
+    assert torch.equal(results[0][1], results[1][1])
+
+
+def test_bad_arguments_touch_nothing():
+    from fp8_kv_cache_amd import qkv_prep as qp
+    w = W.custom(64, 8, seed=408)
+    inp = W.make_inputs(w, device=DEV)
+    before_q = inp["q"].clone()
+    before_c = inp["cache"].clone()
+    op = qp.QkvPrep(8)
+    args = qp.make_args(inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"],
+                        inp["cos_sin"], inp["slot_mapping"], inp["cache"])
+    args.q = args.q + 2                                   # misaligned
+    with pytest.raises(qp.QkvPrepError) as e:
+        qp.qkv_prep_run(op.handle, args, None)
+    assert e.value.code == qp.ERR_MISALIGNED
+    torch.cuda.synchronize()
+    assert torch.equal(before_q, inp["q"]) and torch.equal(before_c, inp["cache"])
