@@ -33,30 +33,24 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Launch shape for T tokens.
 //  * sets_per_wave: how many 4-row sets a wavefront loads before computing.
-//    More sets per wave means more bytes in flight per wave and fewer waves
-//    to launch, but fewer workgroups to spread over the 256 CUs; small
-//    batches keep one set per wave so every CU gets work.
-//  * waves_per_block: 4 (256 threads) unless forced.
-//  * convert: the gfx950 conversion instructions (same bits as the integer
-//    rounding, checked by the tests) unless forced.
+//    Measured on MI355X (32768x64 and 131072x128): one set per wave is the
+//    fastest; more sets raise VGPR use (71 -> 102 -> 154) and cut occupancy by
+//    more than the extra loads in flight give back.
+//  * waves_per_block: 8 (512 threads) for large batches; small batches use 4
+//    so that more workgroups spread over the compute units.
+//  * convert: the integer rounding path unless forced (both give the same
+//    bits; the tests check this).
 qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
 {
     qkvp::LaunchShape s;
     const int64_t q_sets = ceil_div(T * c.num_heads, qkvp::kRowsPerSet);
     const int64_t kv_sets = ceil_div(T, qkvp::kRowsPerSet);
-    s.waves_per_block = c.waves_per_block ? c.waves_per_block : 4;
-    if (c.sets_per_wave) {
-        s.sets_per_wave = c.sets_per_wave;
-    } else {
-        // Aim for at least ~32 wavefronts per CU before going wider.
-        const int64_t cus = num_cus > 0 ? num_cus : 256;
-        if (q_sets >= 4 * 32 * cus)
-            s.sets_per_wave = 4;
-        else if (q_sets >= 2 * 32 * cus)
-            s.sets_per_wave = 2;
-        else
-            s.sets_per_wave = 1;
-    }
+    const int64_t cus = num_cus > 0 ? num_cus : 256;
+    s.sets_per_wave = c.sets_per_wave ? c.sets_per_wave : 1;
+    if (c.waves_per_block)
+        s.waves_per_block = c.waves_per_block;
+    else
+        s.waves_per_block = q_sets >= 64 * 8 * cus ? 8 : 4;
     s.convert = c.convert ? c.convert : 1;
     s.kv_blocks = ceil_div(kv_sets, s.waves_per_block);
     s.q_blocks = ceil_div(ceil_div(q_sets, s.sets_per_wave), s.waves_per_block);

@@ -1,0 +1,55 @@
+// Streaming copy used as a bandwidth ceiling (see include/qkv_prep_probe.h).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qkv_prep_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// One 16-byte non-temporal load and store per lane, 256-lane blocks: the
+// fastest of the copy shapes measured on MI355X (1, 2, 4, 8 and 16 loads per
+// lane; 256, 512 and 1024 lanes per block; plain or non-temporal; natural or
+// XCD-contiguous block order): about 6.4-6.5 TB/s at 0.5-4 GiB.
+constexpr int kUnroll = 1;
+constexpr int kThreads = 256;
+
+// Block b copies kUnroll * kThreads consecutive 16-byte units; all loads are
+// issued before the first store.
+__global__ __launch_bounds__(kThreads) void stream_copy(u32x4 *dst, const u32x4 *src, int64_t n)
+{
+    const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = base + (int64_t)u * kThreads;
+        if (i < n)
+            v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = base + (int64_t)u * kThreads;
+        if (i < n)
+            __builtin_nontemporal_store(v[u], dst + i);
+    }
+}
+
+}  // namespace
+
+extern "C" int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, void *stream)
+{
+    if (bytes < 0 || (bytes > 0 && (!dst || !src)) || (bytes & 15) ||
+        (reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
+        return 1;
+    if (bytes == 0)
+        return 0;
+    const int64_t n = bytes / 16;
+    const int64_t per_block = (int64_t)kThreads * kUnroll;
+    const int64_t blocks = (n + per_block - 1) / per_block;
+    if (blocks >= ((int64_t)1 << 31))
+        return 1;
+    hipLaunchKernelGGL(stream_copy, dim3((uint32_t)blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<u32x4 *>(dst),
+                       static_cast<const u32x4 *>(src), n);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}

@@ -34,7 +34,8 @@ CONVERT_INSTRUCTIONS = 2
 
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("qkv_prep_create", "qkv_prep_run", "qkv_prep_destroy", "qkv_prep_supported",
-            "qkv_prep_launch_shape", "qkv_prep_validate", "qkv_prep_strerror")
+            "qkv_prep_launch_shape", "qkv_prep_validate", "qkv_prep_strerror",
+            "qkv_prep_probe_copy")
 
 
 class QkvPrepConfig(ctypes.Structure):
@@ -85,6 +86,9 @@ def _load():
     L.qkv_prep_validate.restype = ctypes.c_int
     L.qkv_prep_strerror.argtypes = [ctypes.c_int]
     L.qkv_prep_strerror.restype = ctypes.c_char_p
+    L.qkv_prep_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
+    L.qkv_prep_probe_copy.restype = ctypes.c_int
     return L
 
 
@@ -139,6 +143,13 @@ def qkv_prep_launch_shape(cfg: QkvPrepConfig, num_cus: int, num_tokens: int) -> 
 
 def qkv_prep_validate(cfg: QkvPrepConfig, args: QkvPrepArgs) -> int:
     return _lib.qkv_prep_validate(ctypes.byref(cfg), ctypes.byref(args))
+
+
+def qkv_prep_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:
+    """The streaming-copy probe of include/qkv_prep_probe.h (a bandwidth ceiling)."""
+    rc = _lib.qkv_prep_probe_copy(dst_ptr, src_ptr, nbytes, stream)
+    if rc != OK:
+        raise QkvPrepError(rc, "qkv_prep_probe_copy")
 
 
 # ------------------------------------------------------------ torch wrapper

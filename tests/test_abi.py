@@ -11,13 +11,16 @@ import torch
 from fp8_kv_cache_amd import qkv_prep as qp
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "qkv_prep.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qkv_prep_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(qkv_prep_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_and_binding_agree():
@@ -131,9 +134,9 @@ def test_launch_shape_heuristic():
     assert small.kv_blocks == 1 and small.q_blocks == 64 and small.grid == 65
     assert qp.qkv_prep_launch_shape(cfg, 256, 0).grid == 0
     big = qp.qkv_prep_launch_shape(cfg, 256, 32768)
-    assert big.sets_per_wave == 4
-    assert big.q_blocks == (32768 * 64 // 4) // 4 // 4
-    assert big.kv_blocks == 32768 // 4 // 4
+    assert big.sets_per_wave == 1 and big.waves_per_block == 8
+    assert big.q_blocks == (32768 * 64 // 4) // 8
+    assert big.kv_blocks == 32768 // 4 // 8
     forced = qp.qkv_prep_launch_shape(qp.make_config(64, sets_per_wave=2, waves_per_block=8,
                                                      convert=1), 256, 1000)
     assert (forced.sets_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
@@ -141,6 +144,15 @@ def test_launch_shape_heuristic():
     # ragged: T*H not a multiple of 4
     odd = qp.qkv_prep_launch_shape(qp.make_config(3), 256, 5)
     assert odd.q_blocks == 1 and odd.kv_blocks == 1
+
+
+def test_probe_copy_rejects_bad_arguments_without_launching():
+    lib = qp.library()
+    assert lib.qkv_prep_probe_copy(None, None, 0, None) == qp.OK
+    assert lib.qkv_prep_probe_copy(None, None, 16, None) == qp.ERR_INVALID_ARG
+    assert lib.qkv_prep_probe_copy(1 << 20, 2 << 20, 15, None) == qp.ERR_INVALID_ARG
+    assert lib.qkv_prep_probe_copy((1 << 20) + 8, 2 << 20, 16, None) == qp.ERR_INVALID_ARG
+    assert lib.qkv_prep_probe_copy(1 << 20, 2 << 20, -16, None) == qp.ERR_INVALID_ARG
 
 
 def test_run_without_handle_is_rejected():

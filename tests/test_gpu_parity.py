@@ -98,7 +98,7 @@ def test_skips_and_out_of_range_slots():
 
 
 def test_all_slots_skipped_and_empty_cache():
-    w = W.custom(100, 8, seed=402, num_blocks=1, block_size=64)
+    w = W.custom(100, 8, seed=402, num_blocks=2, block_size=64)
     inp = W.make_inputs(w, device=DEV)
     inp["slot_mapping"].fill_(-1)
     res = run_and_compare(w, inp)
@@ -220,3 +220,14 @@ def test_bad_arguments_touch_nothing():
     assert e.value.code == qp.ERR_MISALIGNED
     torch.cuda.synchronize()
     assert torch.equal(before_q, inp["q"]) and torch.equal(before_c, inp["cache"])
+
+
+def test_probe_copy_copies():
+    from fp8_kv_cache_amd import qkv_prep as qp
+    for n in (16, 4096 * 16 + 48, 3 << 20):
+        src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)
+        dst = torch.zeros_like(src)
+        qp.qkv_prep_probe_copy(dst.data_ptr(), src.data_ptr(), n,
+                               torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
