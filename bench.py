@@ -131,7 +131,7 @@ def bench_workload(torch, W, qp, name, steps, warmup):
         "kernel_s_mean": statistics.fmean(kernel_s),
         "kernel_s_median": statistics.median(kernel_s),
         "kernel_s_min": min(kernel_s),
-        "launch": {"sets_per_wave": shape.sets_per_wave, "waves_per_block": shape.waves_per_block,
+        "launch": {"rows_per_wave": shape.rows_per_wave, "waves_per_block": shape.waves_per_block,
                    "convert": shape.convert, "grid": shape.grid},
         "valid_slots": valid,
     }

@@ -32,28 +32,31 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Launch shape for T tokens.
-//  * sets_per_wave: how many 4-row sets a wavefront loads before computing.
-//    Measured on MI355X (32768x64 and 131072x128): one set per wave is the
-//    fastest; more sets raise VGPR use (71 -> 102 -> 154) and cut occupancy by
-//    more than the extra loads in flight give back.
-//  * waves_per_block: 8 (512 threads) for large batches; small batches use 4
-//    so that more workgroups spread over the compute units.
-//  * convert: the integer rounding path unless forced (both give the same
-//    bits; the tests check this).
+//  * rows_per_wave: q rows a wavefront loads before computing.  One row per
+//    wavefront (one 16-byte chunk per lane) streams best on MI355X; more rows
+//    per wavefront are used only when one row per wavefront would need 2^32 or
+//    more work-items in the dispatch.
+//  * waves_per_block: 4 (256 lanes), the measured optimum for this shape.
+//  * convert: the gfx950 conversion instructions (bit-identical to the integer
+//    rounding, which the tests check on every workload).
 qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
 {
+    (void)num_cus;
     qkvp::LaunchShape s;
-    const int64_t q_sets = ceil_div(T * c.num_heads, qkvp::kRowsPerSet);
-    const int64_t kv_sets = ceil_div(T, qkvp::kRowsPerSet);
-    const int64_t cus = num_cus > 0 ? num_cus : 256;
-    s.sets_per_wave = c.sets_per_wave ? c.sets_per_wave : 1;
-    if (c.waves_per_block)
-        s.waves_per_block = c.waves_per_block;
-    else
-        s.waves_per_block = q_sets >= 64 * 8 * cus ? 8 : 4;
-    s.convert = c.convert ? c.convert : 1;
-    s.kv_blocks = ceil_div(kv_sets, s.waves_per_block);
-    s.q_blocks = ceil_div(ceil_div(q_sets, s.sets_per_wave), s.waves_per_block);
+    const int64_t q_rows = T * c.num_heads;
+    s.waves_per_block = c.waves_per_block ? c.waves_per_block : 4;
+    s.convert = c.convert ? c.convert : 2;
+    s.kv_blocks = ceil_div(T, s.waves_per_block);
+    if (c.rows_per_wave) {
+        s.rows_per_wave = c.rows_per_wave;
+    } else {
+        s.rows_per_wave = 1;
+        while (s.rows_per_wave < 4 &&
+               (s.kv_blocks + ceil_div(ceil_div(q_rows, s.rows_per_wave), s.waves_per_block)) * 64 *
+                       s.waves_per_block >= ((int64_t)1 << 32))
+            s.rows_per_wave *= 2;
+    }
+    s.q_blocks = ceil_div(ceil_div(q_rows, s.rows_per_wave), s.waves_per_block);
     return s;
 }
 
@@ -63,8 +66,8 @@ int check_config(const qkv_prep_config *cfg)
         return QKV_PREP_ERR_INVALID_ARG;
     if (cfg->num_heads < 1 || cfg->block_size < 1 || !(cfg->eps >= 0.0f) || cfg->eps > 3.4e38f)
         return QKV_PREP_ERR_INVALID_ARG;
-    if (cfg->sets_per_wave != 0 && cfg->sets_per_wave != 1 && cfg->sets_per_wave != 2 &&
-        cfg->sets_per_wave != 4)
+    if (cfg->rows_per_wave != 0 && cfg->rows_per_wave != 1 && cfg->rows_per_wave != 2 &&
+        cfg->rows_per_wave != 4)
         return QKV_PREP_ERR_INVALID_ARG;
     if (cfg->waves_per_block != 0 && cfg->waves_per_block != 1 && cfg->waves_per_block != 2 &&
         cfg->waves_per_block != 4 && cfg->waves_per_block != 8)
@@ -176,7 +179,7 @@ int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t n
     if (!out || num_tokens < 0)
         return QKV_PREP_ERR_INVALID_ARG;
     const qkvp::LaunchShape s = choose_shape(*cfg, num_cus, num_tokens);
-    out->sets_per_wave = s.sets_per_wave;
+    out->rows_per_wave = s.rows_per_wave;
     out->waves_per_block = s.waves_per_block;
     out->convert = s.convert;
     out->kv_blocks = num_tokens ? s.kv_blocks : 0;
@@ -216,11 +219,10 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     k.num_slots = a->num_blocks * B;
     k.q_rows = T * H;
     k.num_tokens = T;
-    k.q_sets = (T * H + qkvp::kRowsPerSet - 1) / qkvp::kRowsPerSet;
-    k.kv_sets = (T + qkvp::kRowsPerSet - 1) / qkvp::kRowsPerSet;
-    k.num_heads = (uint32_t)H;
     k.block_size = (uint32_t)B;
     k.kv_blocks = (uint32_t)s.kv_blocks;
+    k.heads = qkvp::make_fastdiv((uint32_t)H);
+    k.blocks = qkvp::make_fastdiv((uint32_t)B);
     k.eps = h->cfg.eps;
 
     int prev = -1;
@@ -233,8 +235,8 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
         return QKV_PREP_ERR_NO_DEVICE;
     }
     if (h->log)
-        std::fprintf(stderr, "qkv_prep: T=%lld H=%lld sets/wave=%d waves/block=%d convert=%d grid=%lld+%lld\n",
-                     (long long)T, (long long)H, s.sets_per_wave, s.waves_per_block, s.convert,
+        std::fprintf(stderr, "qkv_prep: T=%lld H=%lld rows/wave=%d waves/block=%d convert=%d grid=%lld+%lld\n",
+                     (long long)T, (long long)H, s.rows_per_wave, s.waves_per_block, s.convert,
                      (long long)s.kv_blocks, (long long)s.q_blocks);
     hipStream_t st = static_cast<hipStream_t>(stream);
     int rc = QKV_PREP_OK;

@@ -13,7 +13,24 @@ constexpr int kRopeDim = 64;
 constexpr int kSlotData = 576;
 constexpr int kSlotScale = 8;
 constexpr int kSlotBytes = 584;
-constexpr int kRowsPerSet = 4;  // a wavefront works on 4 rows at once, 16 lanes each
+
+// Unsigned division by a fixed divisor d >= 1 for dividends n < 2^31:
+// n / d == (umulhi(n, mul) + n) >> shift, with shift = ceil(log2 d) and
+// mul = floor(2^32 (2^shift - d) / d) + 1 (the round-up method of Granlund
+// and Montgomery; n < 2^31 keeps umulhi + n inside 32 bits).
+struct FastDiv {
+    uint32_t mul;
+    uint32_t shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < d)
+        ++l;
+    const uint64_t m = ((((uint64_t)1 << 32) * ((1ull << l) - d)) / d) + 1;
+    return FastDiv{(uint32_t)m, l};
+}
 
 struct KernelArgs {
     uint16_t *q;
@@ -25,19 +42,18 @@ struct KernelArgs {
     const int64_t *slot_mapping;
     uint8_t *cache;
     int64_t max_position;
-    int64_t num_slots;         // num_blocks * block_size
-    int64_t q_rows;            // T * H
+    int64_t num_slots;         // num_blocks * block_size (< 2^31)
+    int64_t q_rows;            // T * H (< 2^31)
     int64_t num_tokens;        // T
-    int64_t q_sets;            // ceil(q_rows / 4)
-    int64_t kv_sets;           // ceil(T / 4)
-    uint32_t num_heads;
     uint32_t block_size;
-    uint32_t kv_blocks;        // workgroups [0, kv_blocks) take kv sets
+    uint32_t kv_blocks;        // workgroups [0, kv_blocks) take kv rows
+    FastDiv heads;             // divides a q row index by H
+    FastDiv blocks;            // divides a slot by block_size
     float eps;
 };
 
 struct LaunchShape {
-    int sets_per_wave;    // q sets per wavefront (1, 2, 4)
+    int rows_per_wave;    // q rows per wavefront (1, 2, 4)
     int waves_per_block;  // 1, 2, 4, 8
     int convert;          // 1 integer rounding, 2 conversion instructions
     int64_t kv_blocks;

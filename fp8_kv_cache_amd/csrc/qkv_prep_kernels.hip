@@ -9,25 +9,29 @@
 // contraction and no MFMA is used.
 //
 // Work decomposition (a gfx950 design, not the pages' Triton/CUDA tilings):
-//  * A wavefront works on a "set" of 4 rows at once, 16 lanes (a DPP row) per
-//    512-wide row.  Lane j of a row holds the 16-byte chunks j, j+16, j+32 and
-//    j+48 (8 bf16 each), so each load/store instruction moves 4 x 256
-//    contiguous bytes, fully coalesced.
-//  * The sum of squares follows the fixed order of the numerics contract:
-//    each chunk sequentially, then adjacent chunk pairs.  Within a 16-lane row
-//    the first four tree levels are DPP adds (quad_perm xor1, xor2,
-//    row_half_mirror, row_mirror); levels five and six are in-lane adds of the
-//    four chunk groups.  No cross-row permute or LDS is needed.
-//  * All heads of a token share one cos/sin row (the Ascend 910B section of the
-//    FlagGems page removes a per-head re-gather); here only the 8 lanes that
-//    hold rope chunks read it, 32 bytes each.
-//  * Several sets' loads are issued before any arithmetic (the sglang page's
-//    "K tokens per block" load-level parallelism, as sets per wavefront), and
-//    the once-read q/kv rows use non-temporal loads and stores.
-//  * q sets and kv sets go to different workgroups of the same launch (the
-//    FlagGems page merges the Q and KV launches); kv workgroups come first in
-//    dispatch order, so their quantization work overlaps the q stream instead
-//    of trailing it.
+//  * One wavefront per 512-wide row: lane l holds the 16-byte chunk l (dims
+//    8l..8l+7), so a row is one fully coalesced 1 KiB load and one 1 KiB store.
+//    Measured on MI355X, this shape streams at the copy ceiling (~6.5 TB/s) at
+//    every footprint, while shapes with several loads per lane in flight (4 rows
+//    per wave, or several rows per wave) lose 6-15% once the footprint passes a
+//    few GiB.  Four-wave (256-lane) workgroups, non-temporal loads and stores.
+//  * The sum of squares follows the fixed order of the numerics contract: each
+//    chunk sequentially, then adjacent chunk pairs.  Levels 1-4 are DPP adds
+//    inside a 16-lane row (quad_perm xor1, xor2, row_half_mirror, row_mirror);
+//    level 5 pairs rows 0+1 and 2+3 with v_permlane16_swap and level 6 pairs
+//    the halves with v_permlane32_swap (both gfx950 instructions).  Every lane
+//    ends with the same bits.  No LDS.
+//  * A wavefront's row belongs to one token, so the token index (a fixed-point
+//    division by H), the position and the cos/sin row address are wave-uniform
+//    scalar values; only the 8 lanes holding rope chunks read the table
+//    (all heads of a token share it: the Ascend 910B section of the FlagGems
+//    page removes a per-head re-gather).
+//  * q rows and kv rows go to different workgroups of one launch (the FlagGems
+//    page merges the Q and KV launches); kv workgroups come first in dispatch
+//    order, so their quantization overlaps the q stream instead of trailing it.
+//  * Several rows per wavefront (the sglang page's "K tokens per block"
+//    load-level parallelism) remains available through the launch shape, but
+//    one row per wavefront is the measured optimum here.
 #include "qkv_prep_internal.h"
 
 namespace qkvp {
@@ -38,18 +42,28 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kRopeLane = kNopeDim / 8;  // lanes 56..63 hold the rope chunks
+
 // ------------------------------------------------------------------ memory
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_stream(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_stream2(u32x2 *p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv d)
+{
+    return (__umulhi(n, d.mul) + n) >> d.shift;
+}
+
 // ------------------------------------------------------------------ bf16
 
-__device__ __forceinline__ float bf16_elem(const u32x4 &d, int e)
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 &d, float (&x)[8])
 {
-    const uint32_t u = d[e >> 1];
-    return (e & 1) ? __uint_as_float(u & 0xffff0000u) : __uint_as_float(u << 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(d[i] << 16);
+        x[2 * i + 1] = __uint_as_float(d[i] & 0xffff0000u);
+    }
 }
 
 // Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even.
@@ -67,6 +81,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
         b = (b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u;
         return a | b;
     }
+}
+
+template <bool HW>
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&y)[8])
+{
+    return u32x4{pack_bf16<HW>(y[0], y[1]), pack_bf16<HW>(y[2], y[3]),
+                 pack_bf16<HW>(y[4], y[5]), pack_bf16<HW>(y[6], y[7])};
 }
 
 // ------------------------------------------------------------------ E4M3
@@ -115,14 +136,13 @@ __device__ __forceinline__ int ue8m0_exponent(uint32_t amax_bits)
     return e < -127 ? -127 : e;
 }
 
-// ------------------------------------------------------------------ DPP
+// ------------------------------------------------------------------ cross-lane
 
 constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
 constexpr int kDppXor1 = quad_perm(1, 0, 3, 2);
 constexpr int kDppXor2 = quad_perm(2, 3, 0, 1);
 constexpr int kDppHalfMirror = 0x141;  // lane i of an 8-lane half reads lane 7-i
 constexpr int kDppMirror = 0x140;      // lane i of a 16-lane row reads lane 15-i
-constexpr int kDppRor8 = 0x128;        // lane i of a 16-lane row reads lane (i+8) mod 16
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v)
@@ -136,16 +156,24 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
 
-// Tree levels 1-4 over the 16 lanes of a DPP row.  After each level both
-// partners hold the same bits (IEEE addition commutes), so mirrors act as
-// xor-4 and xor-8 exchanges.
-__device__ __forceinline__ float tree16(float v)
+// Sum over all 64 lanes in the adjacent-pairs order.  Levels 1-4 inside each
+// 16-lane row: after each level both partners hold the same bits (IEEE
+// addition commutes), so the mirrors act as xor-4 and xor-8 exchanges.
+// Level 5: v_permlane16_swap(v, v) yields rows (0,0,2,2) and (1,1,3,3), whose
+// sum is row0+row1 | row2+row3 in every lane.  Level 6: v_permlane32_swap(s, s)
+// yields halves (lo, lo) and (hi, hi).
+__device__ __forceinline__ float wave_sum_ordered(float v)
 {
     v = v + dpp_f32<kDppXor1>(v);
     v = v + dpp_f32<kDppXor2>(v);
     v = v + dpp_f32<kDppHalfMirror>(v);
     v = v + dpp_f32<kDppMirror>(v);
-    return v;
+    const uint32_t b = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    const float s = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const uint32_t c = __float_as_uint(s);
+    const auto h = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
 }
 
 // Max over the 8-lane half of a DPP row (one quantization block of 64 dims).
@@ -159,38 +187,17 @@ __device__ __forceinline__ uint32_t max8(uint32_t v)
 
 // ------------------------------------------------------------------ row math
 
-__device__ __forceinline__ float chunk_sum_squares(const u32x4 &d)
+// inv = 1 / sqrt(S/512 + eps).  S * 2^-9 is the correctly rounded S/512;
+// __builtin_sqrtf and '/' are the correctly rounded IEEE operations.
+__device__ __forceinline__ float inv_rms(const float (&x)[8], float eps)
 {
     float acc = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = bf16_elem(d, e);
-        acc = __builtin_fmaf(x, x, acc);  // x*x is exact for bf16 x
-    }
-    return acc;
-}
-
-// inv = 1 / sqrt(S/512 + eps): S * 2^-9 is the correctly rounded S/512;
-// __builtin_sqrtf and '/' are the correctly rounded IEEE operations.
-__device__ __forceinline__ float inv_rms(const u32x4 (&d)[4], float eps)
-{
-    const float g0 = tree16(chunk_sum_squares(d[0]));
-    const float g1 = tree16(chunk_sum_squares(d[1]));
-    const float g2 = tree16(chunk_sum_squares(d[2]));
-    const float g3 = tree16(chunk_sum_squares(d[3]));
-    const float s = (g0 + g1) + (g2 + g3);
+    for (int e = 0; e < 8; ++e)
+        acc = __builtin_fmaf(x[e], x[e], acc);  // x*x is exact for bf16 x
+    const float s = wave_sum_ordered(acc);
     const float v = s * 0.001953125f + eps;
     return 1.0f / __builtin_sqrtf(v);
-}
-
-template <bool HAS_W>
-__device__ __forceinline__ void normalize8(const u32x4 &x, const u32x4 &w, float inv, float (&y)[8])
-{
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float t = bf16_elem(x, e) * inv;
-        y[e] = HAS_W ? t * bf16_elem(w, e) : t;
-    }
 }
 
 // Rotate the 4 interleaved pairs of one rope chunk.
@@ -206,158 +213,125 @@ __device__ __forceinline__ void rope8(float (&y)[8], const f32x4 &c, const f32x4
     }
 }
 
-template <bool HW>
-__device__ __forceinline__ u32x4 pack_bf16x8(const float (&y)[8])
-{
-    return u32x4{pack_bf16<HW>(y[0], y[1]), pack_bf16<HW>(y[2], y[3]),
-                 pack_bf16<HW>(y[4], y[5]), pack_bf16<HW>(y[6], y[7])};
-}
-
 __device__ __forceinline__ int64_t clamp_position(int64_t p, int64_t max_position)
 {
     return p < 0 ? 0 : (p >= max_position ? max_position - 1 : p);
 }
 
-// ------------------------------------------------------------------ q sets
+// ------------------------------------------------------------------ q rows
 
-// U consecutive sets of 4 q rows.  Every lane takes part in the DPP trees, so
-// rows past the end are computed on zeros and simply not stored.
+// U consecutive q rows, one per pass, all loads issued first.  `row0` is
+// wave-uniform, so every branch below is uniform too, except the rope lanes.
 template <int U, bool HAS_W, bool HW>
-__device__ __forceinline__ void q_sets(const KernelArgs &a, int64_t set0, uint32_t quarter, uint32_t j)
+__device__ __forceinline__ void q_rows(const KernelArgs &a, int64_t row0, uint32_t lane)
 {
-    int64_t row[U];
-    bool ok[U];
     int64_t pos[U];
+    bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        row[u] = (set0 + u) * kRowsPerSet + quarter;
-        ok[u] = row[u] < a.q_rows;
-        const uint32_t tok = ok[u] ? (uint32_t)row[u] / a.num_heads : 0u;
-        pos[u] = a.positions[tok];
+        const int64_t row = row0 + u;
+        ok[u] = row < a.q_rows;
+        pos[u] = ok[u] ? a.positions[fastdiv((uint32_t)row, a.heads)] : 0;
     }
-    u32x4 d[U][4];
+    u32x4 d[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + row[u] * kHeadDim) + j;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            d[u][k] = ok[u] ? load_stream(src + 16 * k) : u32x4{0u, 0u, 0u, 0u};
-    }
-    u32x4 w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        w[k] = HAS_W ? reinterpret_cast<const u32x4 *>(a.q_w)[j + 16 * k] : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < U; ++u)
+        d[u] = ok[u] ? load_stream(reinterpret_cast<const u32x4 *>(a.q + (row0 + u) * kHeadDim) + lane)
+                     : u32x4{0u, 0u, 0u, 0u};
+    float w[8];
+    if (HAS_W)
+        unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.q_w)[lane], w);
     f32x4 cv[U], sv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         cv[u] = f32x4{1.f, 1.f, 1.f, 1.f};
         sv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (j >= 8) {
+        if (lane >= kRopeLane) {
             const f32x4 *cs = reinterpret_cast<const f32x4 *>(
                 a.cos_sin + clamp_position(pos[u], a.max_position) * kRopeDim);
-            cv[u] = cs[j - 8];
-            sv[u] = cs[j];
+            cv[u] = cs[lane - kRopeLane];
+            sv[u] = cs[lane - kRopeLane + 8];
         }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const float inv = inv_rms(d[u], a.eps);
-        u32x4 *dst = reinterpret_cast<u32x4 *>(a.q + row[u] * kHeadDim) + j;
+        if (!ok[u])
+            break;
+        float x[8], y[8];
+        unpack_bf16x8(d[u], x);
+        const float inv = inv_rms(x, a.eps);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float y[8];
-            normalize8<HAS_W>(d[u][k], w[k], inv, y);
-            if (k == 3 && j >= 8)
-                rope8(y, cv[u], sv[u]);
-            const u32x4 out = pack_bf16x8<HW>(y);
-            if (ok[u])
-                store_stream(dst + 16 * k, out);
+        for (int e = 0; e < 8; ++e) {
+            const float t = x[e] * inv;
+            y[e] = HAS_W ? t * w[e] : t;
         }
+        if (lane >= kRopeLane)
+            rope8(y, cv[u], sv[u]);
+        store_stream(reinterpret_cast<u32x4 *>(a.q + (row0 + u) * kHeadDim) + lane, pack_bf16x8<HW>(y));
     }
 }
 
-// ------------------------------------------------------------------ kv sets
+// ------------------------------------------------------------------ kv row
 
-// One set = the kv rows of 4 consecutive tokens, one per 16-lane row.  In lane
-// j, chunk register k holds dims 8(j+16k)..+7, i.e. quantization block
-// 2k + (j >= 8); register 3 of lanes 8..15 is the rope chunk.
+// One token's kv row.  Lane l < 56 holds dims 8l..8l+7 of quantization block
+// l/8 and writes their 8 codes; lanes 56..63 hold the rope dims and write 16
+// bytes of rotated bf16 each; one lane writes the 8-byte scale record.
 template <bool HW>
-__device__ __forceinline__ void kv_set(const KernelArgs &a, int64_t set, uint32_t quarter, uint32_t j)
+__device__ __forceinline__ void kv_row(const KernelArgs &a, int64_t t, uint32_t lane)
 {
-    const int64_t t = set * kRowsPerSet + quarter;
-    const int64_t slot = t < a.num_tokens ? a.slot_mapping[t] : -1;
-    const bool valid = slot >= 0 && slot < a.num_slots;
-    const int64_t pos = valid ? a.positions[t] : 0;
-    u32x4 d[4], w[4];
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.kv + t * kHeadDim) + j;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        d[k] = valid ? load_stream(src + 16 * k) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        w[k] = reinterpret_cast<const u32x4 *>(a.kv_w)[j + 16 * k];
+    const int64_t slot = a.slot_mapping[t];
+    if (slot < 0 || slot >= a.num_slots)
+        return;  // wave-uniform: the whole wavefront skips this token
+    const u32x4 d = load_stream(reinterpret_cast<const u32x4 *>(a.kv + t * kHeadDim) + lane);
+    float w[8];
+    unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.kv_w)[lane], w);
     f32x4 cv = f32x4{1.f, 1.f, 1.f, 1.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (j >= 8 && valid) {
+    if (lane >= kRopeLane) {
         const f32x4 *cs = reinterpret_cast<const f32x4 *>(
-            a.cos_sin + clamp_position(pos, a.max_position) * kRopeDim);
-        cv = cs[j - 8];
-        sv = cs[j];
+            a.cos_sin + clamp_position(a.positions[t], a.max_position) * kRopeDim);
+        cv = cs[lane - kRopeLane];
+        sv = cs[lane - kRopeLane + 8];
     }
 
-    const float inv = inv_rms(d, a.eps);
-    float y[4][8];
+    float x[8], y[8];
+    unpack_bf16x8(d, x);
+    const float inv = inv_rms(x, a.eps);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        normalize8<true>(d[k], w[k], inv, y[k]);
+    for (int e = 0; e < 8; ++e)
+        y[e] = (x[e] * inv) * w[e];
 
     // Block amax over the 8 lanes of a half row, then the UE8M0 exponent.
-    uint32_t ebyte[4];
-    float inv_scale[4];
+    uint32_t m = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            m = max(m, __float_as_uint(y[k][e]) & 0x7fffffffu);
-        const int ex = ue8m0_exponent(max8(m));
-        ebyte[k] = (uint32_t)(ex + 127);
-        inv_scale[k] = __uint_as_float((uint32_t)(127 - ex) << 23);  // exactly 2^-ex
-    }
-    uint32_t epart[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        epart[k] = dpp_u32<kDppRor8>(ebyte[k]);  // the other half row's block
+    for (int e = 0; e < 8; ++e)
+        m = max(m, __float_as_uint(y[e]) & 0x7fffffffu);
+    const int ex = ue8m0_exponent(max8(m));
+    const float inv_scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // exactly 2^-ex
+    const uint32_t ebyte = (uint32_t)(ex + 127);
+    // Exponent bytes of blocks 0..6 (lanes 0, 8, ..., 48), wave-uniform.
+    const uint32_t rec0 = __builtin_amdgcn_readlane(ebyte, 0) | (__builtin_amdgcn_readlane(ebyte, 8) << 8) |
+                          (__builtin_amdgcn_readlane(ebyte, 16) << 16) |
+                          (__builtin_amdgcn_readlane(ebyte, 24) << 24);
+    const uint32_t rec1 = __builtin_amdgcn_readlane(ebyte, 32) | (__builtin_amdgcn_readlane(ebyte, 40) << 8) |
+                          (__builtin_amdgcn_readlane(ebyte, 48) << 16);
 
-    if (j >= 8)
-        rope8(y[3], cv, sv);
-
-    if (!valid)
-        return;
     const uint32_t s32 = (uint32_t)slot;
-    const uint32_t blk = s32 / a.block_size;
+    const uint32_t blk = fastdiv(s32, a.blocks);
     const uint32_t sib = s32 - blk * a.block_size;
     uint8_t *base = a.cache + (int64_t)blk * a.block_size * kSlotBytes;
     uint8_t *data = base + (int64_t)sib * kSlotData;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        if (k < 3 || j < 8) {
-            const float sc = inv_scale[k];
-            const u32x2 codes = {
-                pack_e4m3<HW>(y[k][0] * sc, y[k][1] * sc, y[k][2] * sc, y[k][3] * sc),
-                pack_e4m3<HW>(y[k][4] * sc, y[k][5] * sc, y[k][6] * sc, y[k][7] * sc)};
-            store_stream2(reinterpret_cast<u32x2 *>(data) + (j + 16 * k), codes);
-        } else {
-            store_stream(reinterpret_cast<u32x4 *>(data + kNopeDim) + (j - 8), pack_bf16x8<HW>(y[3]));
-        }
+    if (lane < kRopeLane) {
+        const u32x2 codes = {pack_e4m3<HW>(y[0] * inv_scale, y[1] * inv_scale, y[2] * inv_scale, y[3] * inv_scale),
+                             pack_e4m3<HW>(y[4] * inv_scale, y[5] * inv_scale, y[6] * inv_scale, y[7] * inv_scale)};
+        store_stream2(reinterpret_cast<u32x2 *>(data) + lane, codes);
+    } else {
+        rope8(y, cv, sv);
+        store_stream(reinterpret_cast<u32x4 *>(data + kNopeDim) + (lane - kRopeLane), pack_bf16x8<HW>(y));
     }
-    if (j == 0) {
-        // Blocks 0, 2, 4, 6 are this lane's; 1, 3, 5 come from lane 8.
-        const u32x2 rec = {ebyte[0] | (epart[0] << 8) | (ebyte[1] << 16) | (epart[1] << 24),
-                           ebyte[2] | (epart[2] << 8) | (ebyte[3] << 16)};
+    if (lane == 0)
         store_stream2(reinterpret_cast<u32x2 *>(base + (int64_t)a.block_size * kSlotData +
                                                 (int64_t)sib * kSlotScale),
-                      rec);
-    }
+                      u32x2{rec0, rec1});
 }
 
 // ------------------------------------------------------------------ kernel
@@ -366,19 +340,17 @@ template <int U, bool HAS_W, bool HW>
 __global__ __launch_bounds__(512) void qkv_prep_kernel(KernelArgs a)
 {
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t quarter = lane >> 4;
-    const uint32_t j = lane & 15u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t waves_per_block = blockDim.x >> 6;
     if (blockIdx.x < a.kv_blocks) {
-        const int64_t set = (int64_t)blockIdx.x * waves_per_block + wave;
-        if (set < a.kv_sets)
-            kv_set<HW>(a, set, quarter, j);
+        const int64_t t = (int64_t)blockIdx.x * waves_per_block + wave;
+        if (t < a.num_tokens)
+            kv_row<HW>(a, t, lane);
     } else {
         const int64_t wv = (int64_t)(blockIdx.x - a.kv_blocks) * waves_per_block + wave;
-        const int64_t set0 = wv * U;
-        if (set0 < a.q_sets)
-            q_sets<U, HAS_W, HW>(a, set0, quarter, j);
+        const int64_t row0 = wv * U;
+        if (row0 < a.q_rows)
+            q_rows<U, HAS_W, HW>(a, row0, lane);
     }
 }
 
@@ -407,7 +379,7 @@ hipError_t launch_qkv_prep(const KernelArgs &a, const LaunchShape &s, hipStream_
     const dim3 block(64u * (uint32_t)s.waves_per_block);
     const bool has_w = a.q_w != nullptr;
     const bool hw = s.convert == 2;
-    switch (s.sets_per_wave) {
+    switch (s.rows_per_wave) {
     case 1: return launch_u<1>(a, has_w, hw, grid, block, stream);
     case 2: return launch_u<2>(a, has_w, hw, grid, block, stream);
     case 4: return launch_u<4>(a, has_w, hw, grid, block, stream);

@@ -41,7 +41,7 @@ EXPORTED = ("qkv_prep_create", "qkv_prep_run", "qkv_prep_destroy", "qkv_prep_sup
 class QkvPrepConfig(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("rope_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("eps", ctypes.c_float), ("sets_per_wave", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rows_per_wave", ctypes.c_int32),
                 ("waves_per_block", ctypes.c_int32), ("convert", ctypes.c_int32)]
 
 
@@ -54,7 +54,7 @@ class QkvPrepArgs(ctypes.Structure):
 
 
 class QkvPrepLaunch(ctypes.Structure):
-    _fields_ = [("sets_per_wave", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
+    _fields_ = [("rows_per_wave", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
                 ("convert", ctypes.c_int32), ("kv_blocks", ctypes.c_int64),
                 ("q_blocks", ctypes.c_int64), ("grid", ctypes.c_int64)]
 
@@ -99,9 +99,9 @@ def library():
     return _lib
 
 
-def make_config(num_heads, *, block_size=64, eps=1e-6, sets_per_wave=0, waves_per_block=0,
+def make_config(num_heads, *, block_size=64, eps=1e-6, rows_per_wave=0, waves_per_block=0,
                 convert=0) -> QkvPrepConfig:
-    return QkvPrepConfig(num_heads, HEAD_DIM, ROPE_DIM, block_size, eps, sets_per_wave,
+    return QkvPrepConfig(num_heads, HEAD_DIM, ROPE_DIM, block_size, eps, rows_per_wave,
                          waves_per_block, convert)
 
 
@@ -189,10 +189,10 @@ class QkvPrep:
     ``op(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache)``
     enqueues the operator on the current torch stream (or ``stream``)."""
 
-    def __init__(self, num_heads, *, device=0, block_size=64, eps=1e-6, sets_per_wave=0,
+    def __init__(self, num_heads, *, device=0, block_size=64, eps=1e-6, rows_per_wave=0,
                  waves_per_block=0, convert=0):
         self.cfg = make_config(num_heads, block_size=block_size, eps=eps,
-                               sets_per_wave=sets_per_wave, waves_per_block=waves_per_block,
+                               rows_per_wave=rows_per_wave, waves_per_block=waves_per_block,
                                convert=convert)
         self.device = device
         self.handle = qkv_prep_create(self.cfg, device)

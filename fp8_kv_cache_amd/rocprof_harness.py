@@ -49,7 +49,8 @@ def log(msg):
 def run_pass(name, rocprof_args, workload, launches, out, timeout):
     d = os.path.join(out, name)
     os.makedirs(d, exist_ok=True)
-    cmd = ["rocprofv3"] + rocprof_args + ["--output-format", "csv", "-d", d, "-o", name, "--",
+    rel = os.path.relpath(d, ROOT)
+    cmd = ["rocprofv3"] + rocprof_args + ["--output-format", "csv", "-d", rel, "-o", name, "--",
                                           "python3", "bench.py", "--mode", "profile",
                                           "--workload", workload, "--launches", str(launches)]
     log("pass %s: %s" % (name, " ".join(cmd)))
@@ -114,7 +115,7 @@ def main():
     from fp8_kv_cache_amd import workloads as W
     w = W.WORKLOADS[args.workload]
     label = "%s_%dx%d" % (w.name, w.num_tokens, w.num_heads)
-    out = os.path.abspath(args.out)
+    out = os.path.abspath(os.path.join(ROOT, args.out))
     os.makedirs(out, exist_ok=True)
     passes = args.passes.split(",")
     summary = {"workload": label, "kernel_sha": kernel_sha()}

@@ -63,7 +63,7 @@ typedef struct {
     int32_t rope_dim;         /* must be 64 (the trailing dims of each row) */
     int32_t block_size;       /* B >= 1 cache slots per block */
     float eps;                /* >= 0, finite; added to the mean square */
-    int32_t sets_per_wave;    /* 0 = launch heuristic; 1, 2 or 4 forces it */
+    int32_t rows_per_wave;    /* 0 = launch heuristic; 1, 2 or 4 q rows per wavefront */
     int32_t waves_per_block;  /* 0 = launch heuristic; 1, 2, 4 or 8 forces it */
     int32_t convert;          /* 0 = heuristic, 1 = integer bf16/E4M3 rounding,
                                  2 = gfx950 conversion instructions; both give
@@ -101,7 +101,7 @@ typedef struct {
 
 /* What qkv_prep_run launches for a given T (for logging and sweeps). */
 typedef struct {
-    int32_t sets_per_wave;
+    int32_t rows_per_wave;
     int32_t waves_per_block;
     int32_t convert;          /* 1 integer, 2 instructions */
     int64_t kv_blocks;        /* workgroups that handle kv rows (dispatched first) */

@@ -107,7 +107,7 @@ def test_cache_may_be_null_without_blocks():
     (dict(block_size=0), qp.ERR_INVALID_ARG),
     (dict(eps=-1.0), qp.ERR_INVALID_ARG),
     (dict(eps=float("nan")), qp.ERR_INVALID_ARG),
-    (dict(sets_per_wave=3), qp.ERR_INVALID_ARG),
+    (dict(rows_per_wave=3), qp.ERR_INVALID_ARG),
     (dict(waves_per_block=16), qp.ERR_INVALID_ARG),
     (dict(convert=3), qp.ERR_INVALID_ARG),
 ])
@@ -130,20 +130,43 @@ def test_unsupported_head_dim():
 def test_launch_shape_heuristic():
     cfg = qp.make_config(64)
     small = qp.qkv_prep_launch_shape(cfg, 256, 16)
-    assert small.sets_per_wave == 1 and small.waves_per_block == 4
-    assert small.kv_blocks == 1 and small.q_blocks == 64 and small.grid == 65
+    assert small.rows_per_wave == 1 and small.waves_per_block == 4 and small.convert == 2
+    assert small.kv_blocks == 4 and small.q_blocks == 16 * 64 // 4 and small.grid == 260
     assert qp.qkv_prep_launch_shape(cfg, 256, 0).grid == 0
-    big = qp.qkv_prep_launch_shape(cfg, 256, 32768)
-    assert big.sets_per_wave == 1 and big.waves_per_block == 8
-    assert big.q_blocks == (32768 * 64 // 4) // 8
-    assert big.kv_blocks == 32768 // 4 // 8
-    forced = qp.qkv_prep_launch_shape(qp.make_config(64, sets_per_wave=2, waves_per_block=8,
+    big = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 131072)
+    assert big.rows_per_wave == 1 and big.waves_per_block == 4
+    assert big.q_blocks == 131072 * 128 // 4 and big.kv_blocks == 131072 // 4
+    # a batch whose one-row-per-wavefront grid would pass 2^32 work-items
+    huge = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 600000)
+    assert huge.rows_per_wave == 2
+    assert (huge.kv_blocks + huge.q_blocks) * 64 * 4 < 2 ** 32
+    forced = qp.qkv_prep_launch_shape(qp.make_config(64, rows_per_wave=2, waves_per_block=8,
                                                      convert=1), 256, 1000)
-    assert (forced.sets_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
-    assert forced.q_blocks == -(-(-(-1000 * 64 // 4) // 2) // 8)
-    # ragged: T*H not a multiple of 4
+    assert (forced.rows_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
+    assert forced.q_blocks == -(-(-(-1000 * 64 // 2)) // 8)
+    assert forced.kv_blocks == -(-1000 // 8)
     odd = qp.qkv_prep_launch_shape(qp.make_config(3), 256, 5)
-    assert odd.q_blocks == 1 and odd.kv_blocks == 1
+    assert odd.q_blocks == 4 and odd.kv_blocks == 2
+
+
+def test_fast_division_used_by_the_kernel():
+    # The kernel divides row indices by H and slots by the block size with a
+    # multiply-high and shift (constants from the host).  Check the scheme on
+    # the host with the same formula, against Python's integer division.
+    import random
+    rng = random.Random(3)
+    for d in list(range(1, 300)) + [511, 512, 513, 1000, 4095, 4096, 65535, 65536, 1 << 20,
+                                   (1 << 31) - 1, 1 << 31]:
+        l = 0
+        while (1 << l) < d:
+            l += 1
+        m = ((1 << 32) * ((1 << l) - d)) // d + 1
+        assert 0 < m < (1 << 32) or d == 1 or d == (1 << l)
+        ns = [0, 1, d - 1, d, d + 1, (1 << 31) - 1] + [rng.randrange(1 << 31) for _ in range(300)]
+        for n in ns:
+            if n >= (1 << 31):
+                continue
+            assert ((((n * m) >> 32) + n) >> l) == n // d, (d, n)
 
 
 def test_probe_copy_rejects_bad_arguments_without_launching():
