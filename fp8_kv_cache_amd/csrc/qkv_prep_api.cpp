@@ -36,7 +36,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //    wavefront (one 16-byte chunk per lane) streams best on MI355X; more rows
 //    per wavefront are used only when one row per wavefront would need 2^32 or
 //    more work-items in the dispatch.
-//  * waves_per_block: 4 (256 lanes), the measured optimum for this shape.
+//  * waves_per_block: 1 (64-lane workgroups).  Measured on MI355X with four
+//    interleaved rounds per shape: 1 wave per workgroup beats 2, 4 and 8 on
+//    2048x64, 32768x64, 32768x128 and 131072x128 (by 1-5%).
 //  * convert: the gfx950 conversion instructions (bit-identical to the integer
 //    rounding, which the tests check on every workload).
 qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
@@ -44,7 +46,7 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     (void)num_cus;
     qkvp::LaunchShape s;
     const int64_t q_rows = T * c.num_heads;
-    s.waves_per_block = c.waves_per_block ? c.waves_per_block : 4;
+    s.waves_per_block = c.waves_per_block ? c.waves_per_block : 1;
     s.convert = c.convert ? c.convert : 2;
     s.kv_blocks = ceil_div(T, s.waves_per_block);
     if (c.rows_per_wave) {

@@ -72,6 +72,9 @@ def lib():
         L.orc_qkv_prep.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64,
                                    i32, f32, ctypes.c_int]
         L.orc_qkv_prep.restype = ctypes.c_int
+        L.orc_qkv_prep_bf16_store.argtypes = L.orc_qkv_prep.argtypes
+        L.orc_qkv_prep_bf16_store.restype = ctypes.c_int
+        L.orc_gather_dequant.argtypes = [vp, i64, i32, vp, i64, vp]
         L.orc_f32_to_bf16_array.argtypes = [vp, vp, i64]
         L.orc_f32_to_e4m3_array.argtypes = [vp, vp, i64]
         L.orc_ue8m0_exponent_array.argtypes = [vp, vp, i64]
@@ -163,11 +166,12 @@ def slot_offsets(slot, num_blocks, block_size):
 # ---------------------------------------------------------------- operator
 
 def qkv_prep(q, kv, q_w, kv_w, positions, cos_sin, slot_mapping, cache,
-             num_blocks, block_size, eps, nthreads=1):
+             num_blocks, block_size, eps, nthreads=1, kv_store="fp8"):
     """Run the whole operator on host arrays.
 
     q: uint16 [T, H, 512] (bf16 bits) -- not modified; the new q is returned.
-    cache: uint8 [num_blocks, block_size*584] -- updated in place.
+    cache: uint8 [num_blocks, block_size*584] for kv_store="fp8", or
+    [num_blocks, block_size*1024] for kv_store="bf16" -- updated in place.
     Returns the new q (uint16 [T, H, 512])."""
     q = _c(np.asarray(q, dtype=np.uint16), np.uint16)
     T, H = q.shape[0], q.shape[1]
@@ -179,14 +183,28 @@ def qkv_prep(q, kv, q_w, kv_w, positions, cos_sin, slot_mapping, cache,
     slot_mapping = _c(np.asarray(slot_mapping, dtype=np.int64), np.int64)
     if not (cache.flags["C_CONTIGUOUS"] and cache.dtype == np.uint8):
         raise TypeError("cache must be a contiguous uint8 array")
-    if cache.size != num_blocks * block_size * SLOT_BYTES:
-        raise ValueError("cache size does not match num_blocks*block_size*584")
+    slot_bytes = {"fp8": SLOT_BYTES, "bf16": 1024}[kv_store]
+    if cache.size != num_blocks * block_size * slot_bytes:
+        raise ValueError("cache size does not match num_blocks*block_size*%d" % slot_bytes)
     assert kv.shape == (T, HEAD_DIM) and positions.shape == (T,) and slot_mapping.shape == (T,)
     out = np.empty_like(q)
-    rc = lib().orc_qkv_prep(T, H, _p(q), _p(out), _p(kv), _p(q_w), _p(kv_w),
+    fn = lib().orc_qkv_prep if kv_store == "fp8" else lib().orc_qkv_prep_bf16_store
+    rc = fn(T, H, _p(q), _p(out), _p(kv), _p(q_w), _p(kv_w),
                             _p(positions), _p(cos_sin), cos_sin.shape[0],
                             _p(slot_mapping), _p(cache), int(num_blocks), int(block_size),
                             float(eps), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments (position out of range?)")
+    return out
+
+
+def gather_dequant(cache, num_blocks, block_size, slots):
+    """Read slots back out of an FP8 + UE8M0 cache: fp32 [n, 512] (zeros for
+    skipped slots)."""
+    if not (cache.flags["C_CONTIGUOUS"] and cache.dtype == np.uint8):
+        raise TypeError("cache must be a contiguous uint8 array")
+    slots = _c(np.asarray(slots, dtype=np.int64).reshape(-1), np.int64)
+    out = np.empty((slots.size, HEAD_DIM), np.float32)
+    lib().orc_gather_dequant(_p(cache), int(num_blocks), int(block_size), _p(slots), slots.size,
+                             _p(out))
     return out

@@ -298,6 +298,21 @@ static void insert_fp8_slot(const float *y, const float *z, uint8_t *cache,
     }
 }
 
+/* bf16-store variant of the insert: the slot holds the bf16 of all 512
+ * values after the rotation (dims 0..447 are the normalized, weighted values;
+ * 448..511 the rotated ones), 1024 bytes, no quantization ([SG] Motivation
+ * and Speed Tests: the kernel's second store path).  Slot s of the cache is at
+ * byte s * 1024, whatever the block split. */
+static void insert_bf16_slot(const float *z, uint8_t *cache, int64_t slot)
+{
+    uint8_t *data = cache + slot * 1024;
+    for (int j = 0; j < ORC_HEAD_DIM; ++j) {
+        uint16_t h = orc_f32_to_bf16(z[j]);
+        data[2 * j] = (uint8_t)(h & 0xff);
+        data[2 * j + 1] = (uint8_t)(h >> 8);
+    }
+}
+
 /* The operator over tokens [0, num_tokens).
  *   q_in, q_out   bf16 [T][H][512]; q_out may equal q_in (in place)
  *   kv            bf16 [T][512]
@@ -309,12 +324,12 @@ static void insert_fp8_slot(const float *y, const float *z, uint8_t *cache,
  *   nthreads      >= 1; tokens are independent, so they may run on several
  *                 threads (valid slots must be distinct, as for the kernel)
  * Returns 0, or -1 when an argument is unusable (nothing is written then). */
-int orc_qkv_prep(int64_t num_tokens, int32_t num_heads,
-                 const uint16_t *q_in, uint16_t *q_out, const uint16_t *kv,
-                 const uint16_t *q_w, const uint16_t *kv_w,
-                 const int64_t *positions, const float *cos_sin, int64_t max_position,
-                 const int64_t *slot_mapping, uint8_t *cache, int64_t num_blocks,
-                 int32_t block_size, float eps, int nthreads)
+static int qkv_prep_store(int64_t num_tokens, int32_t num_heads,
+                          const uint16_t *q_in, uint16_t *q_out, const uint16_t *kv,
+                          const uint16_t *q_w, const uint16_t *kv_w,
+                          const int64_t *positions, const float *cos_sin, int64_t max_position,
+                          const int64_t *slot_mapping, uint8_t *cache, int64_t num_blocks,
+                          int32_t block_size, float eps, int nthreads, int bf16_store)
 {
     if (num_tokens < 0 || num_heads < 1 || max_position < 1 || nthreads < 1)
         return -1;
@@ -335,10 +350,71 @@ int orc_qkv_prep(int64_t num_tokens, int32_t num_heads,
         int64_t data_off, scale_off;
         if (orc_slot_offsets(slot_mapping[t], num_blocks, block_size, &data_off, &scale_off)) {
             orc_row(kv + t * ORC_HEAD_DIM, kv_w, eps, cs, y, z, NULL);
-            insert_fp8_slot(y, z, cache, data_off, scale_off);
+            if (bf16_store)
+                insert_bf16_slot(z, cache, slot_mapping[t]);
+            else
+                insert_fp8_slot(y, z, cache, data_off, scale_off);
         }
     }
     return 0;
+}
+
+int orc_qkv_prep(int64_t num_tokens, int32_t num_heads,
+                 const uint16_t *q_in, uint16_t *q_out, const uint16_t *kv,
+                 const uint16_t *q_w, const uint16_t *kv_w,
+                 const int64_t *positions, const float *cos_sin, int64_t max_position,
+                 const int64_t *slot_mapping, uint8_t *cache, int64_t num_blocks,
+                 int32_t block_size, float eps, int nthreads)
+{
+    return qkv_prep_store(num_tokens, num_heads, q_in, q_out, kv, q_w, kv_w, positions, cos_sin,
+                          max_position, slot_mapping, cache, num_blocks, block_size, eps,
+                          nthreads, 0);
+}
+
+/* Same operator with the bf16 cache: cache is uint8 [num_blocks][block_size*1024]. */
+int orc_qkv_prep_bf16_store(int64_t num_tokens, int32_t num_heads,
+                            const uint16_t *q_in, uint16_t *q_out, const uint16_t *kv,
+                            const uint16_t *q_w, const uint16_t *kv_w,
+                            const int64_t *positions, const float *cos_sin, int64_t max_position,
+                            const int64_t *slot_mapping, uint8_t *cache, int64_t num_blocks,
+                            int32_t block_size, float eps, int nthreads)
+{
+    return qkv_prep_store(num_tokens, num_heads, q_in, q_out, kv, q_w, kv_w, positions, cos_sin,
+                          max_position, slot_mapping, cache, num_blocks, block_size, eps,
+                          nthreads, 1);
+}
+
+/* ------------------------------------------------------------------ */
+/* Cache reader                                                        */
+/* ------------------------------------------------------------------ */
+
+/* Dequantize-and-gather: the reader of this cache (the 1Cat-vLLM PR 1280 page,
+ * change 5 "compressed KV gather", names dequantize_and_gather_k_cache as the
+ * step that reads the FP8 DeepSeek-V4 cache back out; its layout is this
+ * file's R7).  For each of n slots: dims 0..447 are
+ * E4M3 code * 2^(byte - 127) of their 64-block, dims 448..511 the stored bf16
+ * rope values; a slot outside [0, num_blocks*block_size) gives a row of
+ * zeros.  The products are exact in fp32 (4 significant bits times a power of
+ * two inside the fp32 range).  out: fp32 [n][512]. */
+void orc_gather_dequant(const uint8_t *cache, int64_t num_blocks, int32_t block_size,
+                        const int64_t *slots, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float *row = out + i * ORC_HEAD_DIM;
+        int64_t data_off, scale_off;
+        if (!orc_slot_offsets(slots[i], num_blocks, block_size, &data_off, &scale_off)) {
+            for (int j = 0; j < ORC_HEAD_DIM; ++j)
+                row[j] = 0.0f;
+            continue;
+        }
+        const uint8_t *data = cache + data_off;
+        const uint8_t *scale = cache + scale_off;
+        for (int j = 0; j < ORC_NOPE_DIM; ++j)
+            row[j] = (float)ldexp(orc_e4m3_to_f64(data[j]), (int)scale[j / ORC_QBLOCK] - 127);
+        for (int j = 0; j < ORC_ROPE_DIM; ++j)
+            row[ORC_NOPE_DIM + j] = orc_bf16_to_f32(
+                (uint16_t)(data[ORC_NOPE_DIM + 2 * j] | (data[ORC_NOPE_DIM + 2 * j + 1] << 8)));
+    }
 }
 
 /* ------------------------------------------------------------------ */

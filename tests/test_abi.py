@@ -130,22 +130,22 @@ def test_unsupported_head_dim():
 def test_launch_shape_heuristic():
     cfg = qp.make_config(64)
     small = qp.qkv_prep_launch_shape(cfg, 256, 16)
-    assert small.rows_per_wave == 1 and small.waves_per_block == 4 and small.convert == 2
-    assert small.kv_blocks == 4 and small.q_blocks == 16 * 64 // 4 and small.grid == 260
+    assert small.rows_per_wave == 1 and small.waves_per_block == 1 and small.convert == 2
+    assert small.kv_blocks == 16 and small.q_blocks == 16 * 64 and small.grid == 16 * 65
     assert qp.qkv_prep_launch_shape(cfg, 256, 0).grid == 0
     big = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 131072)
-    assert big.rows_per_wave == 1 and big.waves_per_block == 4
-    assert big.q_blocks == 131072 * 128 // 4 and big.kv_blocks == 131072 // 4
+    assert big.rows_per_wave == 1 and big.waves_per_block == 1
+    assert big.q_blocks == 131072 * 128 and big.kv_blocks == 131072
     # a batch whose one-row-per-wavefront grid would pass 2^32 work-items
     huge = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 600000)
     assert huge.rows_per_wave == 2
-    assert (huge.kv_blocks + huge.q_blocks) * 64 * 4 < 2 ** 32
+    assert (huge.kv_blocks + huge.q_blocks) * 64 * huge.waves_per_block < 2 ** 32
     forced = qp.qkv_prep_launch_shape(qp.make_config(64, rows_per_wave=2, waves_per_block=8,
                                                      convert=1), 256, 1000)
     assert (forced.rows_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
     assert forced.q_blocks == -(-(-(-1000 * 64 // 2)) // 8)
     assert forced.kv_blocks == -(-1000 // 8)
-    odd = qp.qkv_prep_launch_shape(qp.make_config(3), 256, 5)
+    odd = qp.qkv_prep_launch_shape(qp.make_config(3, waves_per_block=4), 256, 5)
     assert odd.q_blocks == 4 and odd.kv_blocks == 2
 
 
