@@ -76,6 +76,8 @@ int check_config(const qkv_prep_config *cfg)
         return QKV_PREP_ERR_INVALID_ARG;
     if (cfg->convert < 0 || cfg->convert > 2)
         return QKV_PREP_ERR_INVALID_ARG;
+    if (cfg->kv_store != QKV_PREP_KV_FP8 && cfg->kv_store != QKV_PREP_KV_BF16)
+        return QKV_PREP_ERR_INVALID_ARG;
     if (cfg->head_dim != qkvp::kHeadDim || cfg->rope_dim != qkvp::kRopeDim)
         return QKV_PREP_ERR_UNSUPPORTED;
     return QKV_PREP_OK;
@@ -108,6 +110,26 @@ int check_args(const qkv_prep_config &c, int num_cus, const qkv_prep_args *a)
     // The dispatch counts work-items in 32 bits.
     const qkvp::LaunchShape s = choose_shape(c, num_cus, T);
     if ((s.kv_blocks + s.q_blocks) * 64 * s.waves_per_block >= ((int64_t)1 << 32))
+        return QKV_PREP_ERR_UNSUPPORTED;
+    return QKV_PREP_OK;
+}
+
+int check_gather(const qkv_prep_config &c, const qkv_prep_gather_args *a)
+{
+    if (!a)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (c.kv_store != QKV_PREP_KV_FP8)
+        return QKV_PREP_ERR_UNSUPPORTED;
+    if (a->n < 0 || a->num_blocks < 0 ||
+        (a->out_dtype != QKV_PREP_OUT_F32 && a->out_dtype != QKV_PREP_OUT_BF16))
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (a->n == 0)
+        return QKV_PREP_OK;
+    if (!a->slots || !a->out || (a->num_blocks > 0 && !a->kv_cache))
+        return QKV_PREP_ERR_INVALID_ARG;
+    if ((a->kv_cache && !aligned(a->kv_cache, 16)) || !aligned(a->out, 16) || !aligned(a->slots, 8))
+        return QKV_PREP_ERR_MISALIGNED;
+    if (a->num_blocks > (int64_t)0x7fffffff / c.block_size || a->n >= ((int64_t)1 << 26))
         return QKV_PREP_ERR_UNSUPPORTED;
     return QKV_PREP_OK;
 }
@@ -226,6 +248,7 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     k.heads = qkvp::make_fastdiv((uint32_t)H);
     k.blocks = qkvp::make_fastdiv((uint32_t)B);
     k.eps = h->cfg.eps;
+    k.bf16_store = h->cfg.kv_store == QKV_PREP_KV_BF16;
 
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) {
@@ -243,6 +266,42 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     hipStream_t st = static_cast<hipStream_t>(stream);
     int rc = QKV_PREP_OK;
     if (qkvp::launch_qkv_prep(k, s, st) != hipSuccess)
+        rc = QKV_PREP_ERR_LAUNCH;
+    else if (h->sync && hipStreamSynchronize(st) != hipSuccess)
+        rc = QKV_PREP_ERR_DEVICE;
+    if (prev != h->device)
+        (void)hipSetDevice(prev);
+    return rc;
+}
+
+int qkv_prep_gather(qkv_prep_t h, const qkv_prep_gather_args *a, void *stream)
+{
+    if (!h)
+        return QKV_PREP_ERR_INVALID_ARG;
+    const int rc_args = check_gather(h->cfg, a);
+    if (rc_args != QKV_PREP_OK || a->n == 0)
+        return rc_args;
+    qkvp::GatherArgs g;
+    g.cache = static_cast<const uint8_t *>(a->kv_cache);
+    g.slots = a->slots;
+    g.out = a->out;
+    g.num_slots = a->num_blocks * h->cfg.block_size;
+    g.n = a->n;
+    g.block_size = (uint32_t)h->cfg.block_size;
+    g.blocks = qkvp::make_fastdiv((uint32_t)h->cfg.block_size);
+    g.out_bf16 = a->out_dtype == QKV_PREP_OUT_BF16;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) {
+        (void)hipGetLastError();
+        return QKV_PREP_ERR_NO_DEVICE;
+    }
+    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return QKV_PREP_ERR_NO_DEVICE;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = QKV_PREP_OK;
+    if (qkvp::launch_gather(g, 1, st) != hipSuccess)
         rc = QKV_PREP_ERR_LAUNCH;
     else if (h->sync && hipStreamSynchronize(st) != hipSuccess)
         rc = QKV_PREP_ERR_DEVICE;

@@ -32,17 +32,24 @@ SLOT_BYTES = 584
 CONVERT_INTEGER = 1
 CONVERT_INSTRUCTIONS = 2
 
+KV_FP8 = 0
+KV_BF16 = 1
+BF16_SLOT_BYTES = 1024
+OUT_F32 = 0
+OUT_BF16 = 1
+
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("qkv_prep_create", "qkv_prep_run", "qkv_prep_destroy", "qkv_prep_supported",
             "qkv_prep_launch_shape", "qkv_prep_validate", "qkv_prep_strerror",
-            "qkv_prep_probe_copy")
+            "qkv_prep_gather", "qkv_prep_probe_copy")
 
 
 class QkvPrepConfig(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("rope_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("rows_per_wave", ctypes.c_int32),
-                ("waves_per_block", ctypes.c_int32), ("convert", ctypes.c_int32)]
+                ("waves_per_block", ctypes.c_int32), ("convert", ctypes.c_int32),
+                ("kv_store", ctypes.c_int32)]
 
 
 class QkvPrepArgs(ctypes.Structure):
@@ -51,6 +58,12 @@ class QkvPrepArgs(ctypes.Structure):
                 ("cos_sin", ctypes.c_void_p), ("max_position", ctypes.c_int64),
                 ("slot_mapping", ctypes.c_void_p), ("kv_cache", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int64), ("num_tokens", ctypes.c_int64)]
+
+
+class QkvPrepGatherArgs(ctypes.Structure):
+    _fields_ = [("kv_cache", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
+                ("slots", ctypes.c_void_p), ("n", ctypes.c_int64), ("out", ctypes.c_void_p),
+                ("out_dtype", ctypes.c_int32)]
 
 
 class QkvPrepLaunch(ctypes.Structure):
@@ -86,6 +99,8 @@ def _load():
     L.qkv_prep_validate.restype = ctypes.c_int
     L.qkv_prep_strerror.argtypes = [ctypes.c_int]
     L.qkv_prep_strerror.restype = ctypes.c_char_p
+    L.qkv_prep_gather.argtypes = [ctypes.c_void_p, P(QkvPrepGatherArgs), ctypes.c_void_p]
+    L.qkv_prep_gather.restype = ctypes.c_int
     L.qkv_prep_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_void_p]
     L.qkv_prep_probe_copy.restype = ctypes.c_int
@@ -100,9 +115,9 @@ def library():
 
 
 def make_config(num_heads, *, block_size=64, eps=1e-6, rows_per_wave=0, waves_per_block=0,
-                convert=0) -> QkvPrepConfig:
+                convert=0, kv_store=KV_FP8) -> QkvPrepConfig:
     return QkvPrepConfig(num_heads, HEAD_DIM, ROPE_DIM, block_size, eps, rows_per_wave,
-                         waves_per_block, convert)
+                         waves_per_block, convert, kv_store)
 
 
 # ------------------------------------------------------------ C-named calls
@@ -143,6 +158,12 @@ def qkv_prep_launch_shape(cfg: QkvPrepConfig, num_cus: int, num_tokens: int) -> 
 
 def qkv_prep_validate(cfg: QkvPrepConfig, args: QkvPrepArgs) -> int:
     return _lib.qkv_prep_validate(ctypes.byref(cfg), ctypes.byref(args))
+
+
+def qkv_prep_gather(handle, args: QkvPrepGatherArgs, stream=None) -> None:
+    rc = _lib.qkv_prep_gather(handle, ctypes.byref(args), stream)
+    if rc != OK:
+        raise QkvPrepError(rc, "qkv_prep_gather")
 
 
 def qkv_prep_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:
@@ -190,10 +211,11 @@ class QkvPrep:
     enqueues the operator on the current torch stream (or ``stream``)."""
 
     def __init__(self, num_heads, *, device=0, block_size=64, eps=1e-6, rows_per_wave=0,
-                 waves_per_block=0, convert=0):
+                 waves_per_block=0, convert=0, kv_store=KV_FP8):
         self.cfg = make_config(num_heads, block_size=block_size, eps=eps,
                                rows_per_wave=rows_per_wave, waves_per_block=waves_per_block,
-                               convert=convert)
+                               convert=convert, kv_store=kv_store)
+        self.slot_bytes = SLOT_BYTES if kv_store == KV_FP8 else BF16_SLOT_BYTES
         self.device = device
         self.handle = qkv_prep_create(self.cfg, device)
 
@@ -202,15 +224,34 @@ class QkvPrep:
         import torch
         if q.dim() != 3 or q.shape[1] != self.cfg.num_heads or q.shape[2] != HEAD_DIM:
             raise ValueError("q must be [T, %d, 512]" % self.cfg.num_heads)
-        if kv_cache is not None and kv_cache.numel() % (self.cfg.block_size * SLOT_BYTES):
-            raise ValueError("kv_cache must be [num_blocks, block_size*584] bytes")
+        per_block = self.cfg.block_size * self.slot_bytes
+        if kv_cache is not None and kv_cache.numel() % per_block:
+            raise ValueError("kv_cache must be [num_blocks, block_size*%d] bytes" % self.slot_bytes)
         args = make_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
-                         None if kv_cache is None
-                         else kv_cache.numel() // (self.cfg.block_size * SLOT_BYTES))
+                         None if kv_cache is None else kv_cache.numel() // per_block)
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
         qkv_prep_run(self.handle, args, stream)
         return q
+
+    def gather(self, kv_cache, slots, out, stream=None):
+        """Read `slots` back out of an FP8 cache into `out` ([n, 512] fp32 or bf16)."""
+        import torch
+        if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous():
+            raise TypeError("kv_cache must be a contiguous uint8 tensor")
+        if slots.dtype != torch.int64 or not slots.is_contiguous():
+            raise TypeError("slots must be a contiguous int64 tensor")
+        if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_contiguous():
+            raise TypeError("out must be a contiguous float32 or bfloat16 tensor")
+        if out.shape != (slots.numel(), HEAD_DIM):
+            raise ValueError("out must be [n, 512]")
+        args = QkvPrepGatherArgs(kv_cache.data_ptr(), kv_cache.numel() // (self.cfg.block_size * SLOT_BYTES),
+                                 slots.data_ptr(), slots.numel(), out.data_ptr(),
+                                 OUT_F32 if out.dtype == torch.float32 else OUT_BF16)
+        if stream is None:
+            stream = torch.cuda.current_stream(out.device).cuda_stream
+        qkv_prep_gather(self.handle, args, stream)
+        return out
 
     def launch_shape(self, num_tokens, num_cus=256) -> QkvPrepLaunch:
         return qkv_prep_launch_shape(self.cfg, num_cus, num_tokens)

@@ -68,9 +68,22 @@ typedef struct {
     int32_t convert;          /* 0 = heuristic, 1 = integer bf16/E4M3 rounding,
                                  2 = gfx950 conversion instructions; both give
                                  the same bits (tests check this) */
+    int32_t kv_store;         /* QKV_PREP_KV_FP8 (0): the FP8 + UE8M0 slot below;
+                                 QKV_PREP_KV_BF16 (1): the bf16-store path of the
+                                 sglang PR 33358 page (Motivation: the kernel's
+                                 second store path), a slot of 1024 bytes holding
+                                 the bf16 of all 512 values after the rotation
+                                 (dims 0..447 normalized and weighted, 448..511
+                                 rotated); slot s at byte s * 1024 */
 } qkv_prep_config;
 
-/* Per-call tensors.  Layouts are dense row-major.
+#define QKV_PREP_KV_FP8 0
+#define QKV_PREP_KV_BF16 1
+#define QKV_PREP_BF16_SLOT_BYTES 1024
+
+/* Per-call tensors.  Layouts are dense row-major.  (kv_cache below is the
+ * FP8 layout; with kv_store = QKV_PREP_KV_BF16 it is uint8
+ * [num_blocks][B * 1024] instead.)
  *   q            bf16 [T][H][512], read and overwritten in place; 16-B aligned
  *   kv           bf16 [T][512], read only; 16-B aligned
  *   q_norm_w     bf16 [512], or NULL for a weightless q RMSNorm; 16-B aligned
@@ -109,6 +122,25 @@ typedef struct {
     int64_t grid;             /* kv_blocks + q_blocks */
 } qkv_prep_launch;
 
+/* Arguments of the cache reader (qkv_prep_gather).
+ *   kv_cache   uint8 [num_blocks][B * 584], an FP8 + UE8M0 cache written by
+ *              qkv_prep_run (layout above); 16-B aligned
+ *   slots      int64 [n]: the slots to read; one outside [0, num_blocks * B)
+ *              reads as a row of zeros
+ *   out        [n][512] of out_dtype; 16-B aligned
+ *   out_dtype  QKV_PREP_OUT_F32 (0) or QKV_PREP_OUT_BF16 (1)              */
+typedef struct {
+    const void *kv_cache;
+    int64_t num_blocks;
+    const int64_t *slots;
+    int64_t n;                /* >= 0; 0 is a no-op */
+    void *out;
+    int32_t out_dtype;
+} qkv_prep_gather_args;
+
+#define QKV_PREP_OUT_F32 0
+#define QKV_PREP_OUT_BF16 1
+
 /* Create a handle for device `device`.  Validates cfg, reads the device's
  * compute-unit count for the launch heuristic, and stores host state only.
  * Returns QKV_PREP_ERR_NO_DEVICE when no HIP device exists or the index is
@@ -141,6 +173,16 @@ int qkv_prep_create(const qkv_prep_config *cfg, int device, qkv_prep_t *out);
  *           nearest even (e4m3fn, subnormals kept, sign kept); scale byte e+127;
  *           rope bytes = bf16 of the rotated values. */
 int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *args, void *stream);
+
+/* Read slots back out of an FP8 + UE8M0 cache (the reader of this cache; the
+ * 1Cat-vLLM PR 1280 page, change 5, names it dequantize_and_gather_k_cache).
+ * Enqueue on `stream` and return.  Row i of out: dims 0..447 are
+ * code * 2^(scale byte - 127) of their 64-dim block (exact in fp32; the bf16
+ * output is that value rounded to nearest even), dims 448..511 the stored bf16
+ * rope values.  Uses the handle's device and block_size; the handle must have
+ * been created with kv_store = QKV_PREP_KV_FP8.  Argument errors are reported
+ * as for qkv_prep_run, with nothing launched. */
+int qkv_prep_gather(qkv_prep_t h, const qkv_prep_gather_args *args, void *stream);
 
 /* Release a handle.  NULL is a no-op.  Returns QKV_PREP_OK. */
 int qkv_prep_destroy(qkv_prep_t h);

@@ -73,7 +73,28 @@ def compare_cache(got, want, roles):
     return out
 
 
-def run_and_compare(w, inp, *, q_weight=True, chunk_tokens=4096, **cfg):
+def compare_bf16_cache(got, want, slots, num_slots):
+    """bf16-store cache: every valid slot's 512 values within 1 bf16 ulp, every
+    other byte untouched."""
+    got = np.asarray(got).reshape(-1)
+    want = np.asarray(want).reshape(-1)
+    s = np.asarray(slots, np.int64)
+    s = np.unique(s[(s >= 0) & (s < num_slots)])
+    mask = np.zeros(got.size, bool)
+    mask[(s[:, None] * 1024 + np.arange(1024)[None, :]).ravel()] = True
+    out = {"cache_exact_mismatch": int(np.count_nonzero(got[~mask] != want[~mask]))}
+    g16 = got[mask].view(np.uint16)
+    w16 = want[mask].view(np.uint16)
+    d = np.abs(bf16_ord(g16) - bf16_ord(w16))
+    out["rope_max_ulp"] = int(d.max()) if d.size else 0      # all 512 values are bf16 here
+    out["rope_inexact"] = int(np.count_nonzero(d))
+    out["code_max_step"] = 0
+    out["code_inexact"] = 0
+    out["cache_bytes_differ"] = int(np.count_nonzero(got != want))
+    return out
+
+
+def run_and_compare(w, inp, *, q_weight=True, chunk_tokens=4096, kv_store=0, **cfg):
     """Run the HIP operator on the GPU-made inputs ``inp`` and check every
     token against the oracle.  The inputs stay untouched (q and the cache are
     cloned on the device first)."""
@@ -82,8 +103,16 @@ def run_and_compare(w, inp, *, q_weight=True, chunk_tokens=4096, **cfg):
     T, H = w.num_tokens, w.num_heads
     q_w = inp["q_w"] if q_weight else None
     q_run = inp["q"].clone()
-    cache_run = inp["cache"].clone()
-    op = QkvPrep(H, device=q_run.device.index or 0, block_size=w.block_size, eps=w.eps, **cfg)
+    if kv_store == 0:
+        cache_run = inp["cache"].clone()
+    else:
+        cache_run = torch.randint(0, 256, (w.num_blocks, w.block_size * 1024), dtype=torch.uint8,
+                                  device=q_run.device, generator=torch.Generator(
+                                      device=q_run.device).manual_seed(w.seed + 77))
+    torch.cuda.synchronize()
+    want_cache = cache_run.cpu().numpy().copy()      # the poison, before the launch
+    op = QkvPrep(H, device=q_run.device.index or 0, block_size=w.block_size, eps=w.eps,
+                 kv_store=kv_store, **cfg)
     op(q_run, inp["kv"], q_w, inp["kv_w"], inp["positions"], inp["cos_sin"],
        inp["slot_mapping"], cache_run)
     torch.cuda.synchronize()
@@ -94,7 +123,6 @@ def run_and_compare(w, inp, *, q_weight=True, chunk_tokens=4096, **cfg):
     kvh = W.as_u16(inp["kv"])
     qw = None if q_w is None else W.as_u16(q_w)
     kvw = W.as_u16(inp["kv_w"])
-    want_cache = inp["cache"].cpu().numpy().copy()
     res = {"q_max_ulp": 0, "q_inexact": 0, "tokens": T}
     nth = oracle_threads()
     for t0 in range(0, T, chunk_tokens):
@@ -102,12 +130,17 @@ def run_and_compare(w, inp, *, q_weight=True, chunk_tokens=4096, **cfg):
         qb = W.as_u16(inp["q"][t0:t1])
         qa = W.as_u16(q_run[t0:t1])
         want = oracle.qkv_prep(qb, kvh[t0:t1], qw, kvw, pos[t0:t1], cs, slots[t0:t1], want_cache,
-                               w.num_blocks, w.block_size, w.eps, nth)
+                               w.num_blocks, w.block_size, w.eps, nth,
+                               kv_store="fp8" if kv_store == 0 else "bf16")
         d = np.abs(bf16_ord(qa) - bf16_ord(want))
         res["q_max_ulp"] = max(res["q_max_ulp"], int(d.max()) if d.size else 0)
         res["q_inexact"] += int(np.count_nonzero(d))
-    roles = byte_roles(slots, w.num_blocks, w.block_size)
-    res.update(compare_cache(cache_run.cpu().numpy(), want_cache, roles))
+    if kv_store == 0:
+        roles = byte_roles(slots, w.num_blocks, w.block_size)
+        res.update(compare_cache(cache_run.cpu().numpy(), want_cache, roles))
+    else:
+        res.update(compare_bf16_cache(cache_run.cpu().numpy(), want_cache, slots,
+                                      w.num_blocks * w.block_size))
     res["valid_slots"] = int(((slots >= 0) & (slots < w.num_blocks * w.block_size)).sum())
     return res
 

@@ -34,9 +34,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_struct_sizes_match_the_header_layout():
-    assert ctypes.sizeof(qp.QkvPrepConfig) == 32
+    assert ctypes.sizeof(qp.QkvPrepConfig) == 36
     assert ctypes.sizeof(qp.QkvPrepArgs) == 88
     assert ctypes.sizeof(qp.QkvPrepLaunch) == 40
+    assert ctypes.sizeof(qp.QkvPrepGatherArgs) == 48
 
 
 def test_strerror_and_supported():
@@ -110,6 +111,7 @@ def test_cache_may_be_null_without_blocks():
     (dict(rows_per_wave=3), qp.ERR_INVALID_ARG),
     (dict(waves_per_block=16), qp.ERR_INVALID_ARG),
     (dict(convert=3), qp.ERR_INVALID_ARG),
+    (dict(kv_store=2), qp.ERR_INVALID_ARG),
 ])
 def test_bad_config(kw, code):
     base = dict(num_heads=8, block_size=64, eps=1e-6)
@@ -178,6 +180,11 @@ def test_probe_copy_rejects_bad_arguments_without_launching():
     assert lib.qkv_prep_probe_copy(1 << 20, 2 << 20, -16, None) == qp.ERR_INVALID_ARG
 
 
+def test_gather_without_handle_is_rejected():
+    args = qp.QkvPrepGatherArgs(1 << 20, 4, 2 << 20, 8, 3 << 20, qp.OUT_F32)
+    assert qp.library().qkv_prep_gather(None, ctypes.byref(args), None) == qp.ERR_INVALID_ARG
+
+
 def test_run_without_handle_is_rejected():
     assert qp.library().qkv_prep_run(None, ctypes.byref(_good_args()), None) == qp.ERR_INVALID_ARG
     assert qp.library().qkv_prep_destroy(None) == qp.OK
@@ -201,7 +208,7 @@ def test_ctypes_layout_matches_the_c_compiler(tmp_path):
     # offset with the ctypes mirror.
     import subprocess
     fields = {"qkv_prep_config": qp.QkvPrepConfig, "qkv_prep_args": qp.QkvPrepArgs,
-              "qkv_prep_launch": qp.QkvPrepLaunch}
+              "qkv_prep_launch": qp.QkvPrepLaunch, "qkv_prep_gather_args": qp.QkvPrepGatherArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "qkv_prep.h"', "int main(void){"]
     for cname, cls in fields.items():
         lines.append('printf("%%zu\\n", sizeof(%s));' % cname)

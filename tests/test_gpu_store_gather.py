@@ -1,0 +1,117 @@
+"""GPU checks of the bf16-store cache mode and of the cache reader, through
+the C ABI, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_kv_cache_amd import qkv_prep as qp
+from fp8_kv_cache_amd import workloads as W
+
+from parity import assert_bit_exact, run_and_compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------- bf16 store
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_bf16_store_workloads(name):
+    w = W.WORKLOADS[name]
+    note("bf16 store %s" % w.label)
+    res = run_and_compare(w, W.make_inputs(w, device=DEV), kv_store=qp.KV_BF16)
+    note("  -> %s" % res)
+    assert_bit_exact(res)
+
+
+@pytest.mark.parametrize("T,H,bs,convert", [(1, 8, 1, 1), (17, 3, 5, 2), (777, 64, 16, 1),
+                                            (2048, 128, 64, 2)])
+def test_bf16_store_shapes(T, H, bs, convert):
+    w = W.custom(T, H, seed=600 + T, block_size=bs, num_skip=min(T // 4, 10))
+    res = run_and_compare(w, W.make_inputs(w, device=DEV), kv_store=qp.KV_BF16, convert=convert)
+    assert_bit_exact(res)
+
+
+# ----------------------------------------------------------------- reader
+
+def _insert(w, inp):
+    op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
+    q = inp["q"].clone()
+    cache = inp["cache"].clone()
+    op(q, inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+       inp["slot_mapping"], cache)
+    torch.cuda.synchronize()
+    return op, cache
+
+
+@pytest.mark.parametrize("name,bs", [("decode", None), ("custom", 5), ("custom", 1)])
+def test_gather_matches_the_oracle_reader(name, bs):
+    w = W.WORKLOADS["decode"] if name == "decode" else W.custom(500, 4, seed=700 + bs,
+                                                                 block_size=bs, num_skip=9)
+    inp = W.make_inputs(w, device=DEV)
+    op, cache = _insert(w, inp)
+    cap = w.num_blocks * w.block_size
+    slots = inp["slot_mapping"].clone()
+    extra = torch.tensor([-1, cap, cap + 7, -(1 << 40), 1 << 40], dtype=torch.int64, device=DEV)
+    probe = torch.cat([slots.flip(0), extra])              # out of order, plus invalid slots
+    host_cache = cache.cpu().numpy()
+    want = oracle.gather_dequant(host_cache, w.num_blocks, w.block_size, probe.cpu().numpy())
+    out32 = torch.full((probe.numel(), 512), float("nan"), dtype=torch.float32, device=DEV)
+    op.gather(cache, probe, out32)
+    out16 = torch.full((probe.numel(), 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    op.gather(cache, probe, out16)
+    torch.cuda.synchronize()
+    got32 = out32.cpu().numpy()
+    assert np.array_equal(got32.view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(W.as_u16(out16), oracle.f32_to_bf16(want))
+    assert np.all(got32[-len(extra):] == 0)
+
+
+def test_gather_round_trip_within_e4m3_bound():
+    w = W.custom(1024, 8, seed=710)
+    inp = W.make_inputs(w, device=DEV)
+    op, cache = _insert(w, inp)
+    out = torch.empty((w.num_tokens, 512), dtype=torch.float32, device=DEV)
+    op.gather(cache, inp["slot_mapping"], out)
+    torch.cuda.synchronize()
+    cs = inp["cos_sin"].cpu().numpy()[inp["positions"].cpu().numpy()]
+    y, z, _, _ = oracle.rows(W.as_u16(inp["kv"]), W.as_u16(inp["kv_w"]), w.eps, cs)
+    got = out.cpu().numpy().astype(np.float64)
+    _, scales = oracle.quant_rows(y[:, :448])
+    e = np.repeat(scales.astype(int) - 127, 64, axis=1)
+    assert np.all(np.abs(got[:, :448] - y[:, :448]) <=
+                  np.maximum(2.0 ** -4 * np.abs(y[:, :448]), np.ldexp(1.0, e - 10)))
+    assert np.array_equal(out.cpu().numpy()[:, 448:], oracle.bf16_to_f32(oracle.f32_to_bf16(z[:, 448:])))
+
+
+def test_gather_empty_and_bad_arguments():
+    w = W.custom(64, 8, seed=711)
+    inp = W.make_inputs(w, device=DEV)
+    op, cache = _insert(w, inp)
+    out = torch.zeros((0, 512), dtype=torch.float32, device=DEV)
+    op.gather(cache, inp["slot_mapping"][:0], out)          # n == 0: no-op
+    out = torch.zeros((4, 512), dtype=torch.float32, device=DEV)
+    args = qp.QkvPrepGatherArgs(cache.data_ptr(), w.num_blocks, inp["slot_mapping"].data_ptr(), 4,
+                                out.data_ptr() + 4, qp.OUT_F32)
+    with pytest.raises(qp.QkvPrepError) as e:
+        qp.qkv_prep_gather(op.handle, args, None)
+    assert e.value.code == qp.ERR_MISALIGNED
+    args = qp.QkvPrepGatherArgs(cache.data_ptr(), w.num_blocks, inp["slot_mapping"].data_ptr(), 4,
+                                out.data_ptr(), 7)
+    with pytest.raises(qp.QkvPrepError) as e:
+        qp.qkv_prep_gather(op.handle, args, None)
+    assert e.value.code == qp.ERR_INVALID_ARG
+    bf = qp.QkvPrep(8, kv_store=qp.KV_BF16)
+    args = qp.QkvPrepGatherArgs(cache.data_ptr(), w.num_blocks, inp["slot_mapping"].data_ptr(), 4,
+                                out.data_ptr(), qp.OUT_F32)
+    with pytest.raises(qp.QkvPrepError) as e:
+        qp.qkv_prep_gather(bf.handle, args, None)
+    assert e.value.code == qp.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
