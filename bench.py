@@ -96,6 +96,57 @@ def copy_ceilings(torch, qp):
 
 # ----------------------------------------------------------------- one workload
 
+def time_launches(torch, fn, steps):
+    """Per-launch HIP-event durations (on torch's current stream, which is the
+    stream the library launches on) and the wall time of all `steps`."""
+    stream = torch.cuda.current_stream()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in events:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events], wall
+
+
+def bench_variants(torch, W, qp, steps, warmup):
+    """The two neighbouring paths on the Prefill workload: the bf16-store cache
+    mode (1024-byte slots, no quantization) and the cache reader gathering all
+    32768 slots back to bf16."""
+    out = {}
+    w = W.WORKLOADS["prefill"]
+    inp = W.make_inputs(w, device="cuda")
+    cache16 = torch.zeros((w.num_blocks, w.block_size * 1024), dtype=torch.uint8, device="cuda")
+    op16 = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps, kv_store=qp.KV_BF16)
+    args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+            inp["slot_mapping"], cache16)
+    for _ in range(warmup):
+        op16(*args)
+    ks, wall = time_launches(torch, lambda: op16(*args), steps)
+    nbytes = W.algorithmic_bytes(w.num_tokens, w.num_heads, w.num_tokens, slot_bytes=1024)
+    out["bf16_store prefill 32768x64"] = {"gbps": round(nbytes * steps / wall / 1e9, 1),
+                                          "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2),
+                                          "bytes_per_launch": nbytes}
+    op8 = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
+    op8(*args[:-1], inp["cache"])
+    rows = torch.empty((w.num_tokens, 512), dtype=torch.bfloat16, device="cuda")
+    g = lambda: op8.gather(inp["cache"], inp["slot_mapping"], rows)
+    for _ in range(warmup):
+        g()
+    ks, wall = time_launches(torch, g, steps)
+    nbytes = W.gather_bytes(w.num_tokens, w.num_tokens, 2)
+    out["gather bf16 32768 slots"] = {"gbps": round(nbytes * steps / wall / 1e9, 1),
+                                      "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2),
+                                      "bytes_per_launch": nbytes}
+    del inp, args, cache16, rows
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_workload(torch, W, qp, name, steps, warmup):
     w = W.WORKLOADS[name]
     log("bench: drawing %s inputs on the GPU" % w.label)
@@ -105,25 +156,14 @@ def bench_workload(torch, W, qp, name, steps, warmup):
     nbytes = W.algorithmic_bytes(w.num_tokens, w.num_heads, valid)
     op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
     shape = op.launch_shape(w.num_tokens)
-    stream = torch.cuda.current_stream()
     args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
             inp["slot_mapping"], inp["cache"])
     log("bench: %s warmup %d" % (w.label, warmup))
     for _ in range(warmup):
         op(*args)
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
     log("bench: %s timing %d steps" % (w.label, steps))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in events:
-        e0.record(stream)
-        op(*args)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_s = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events]
+    kernel_s, wall = time_launches(torch, lambda: op(*args), steps)
     res = {
         "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
         "bytes_per_step": nbytes,
@@ -269,6 +309,7 @@ def main():
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--mode", choices=["bench", "profile"], default="bench",
                     help="profile: a short fixed program for rocprofv3 (no JSON line)")
     ap.add_argument("--launches", type=int, default=5)
@@ -295,6 +336,7 @@ def main():
     also = None
     if not args.no_also and args.also and args.also != args.workload:
         _, also = bench_workload(torch, W, qp, args.also, args.steps, args.warmup)
+    variants = None if args.no_variants else bench_variants(torch, W, qp, args.steps, args.warmup)
     ceil_after = None if args.no_ceiling else copy_ceilings(torch, qp)
     log("bench: copy ceilings after = %s GB/s" % ceil_after)
     kat_after = known_answer_check(torch, W, qp)
@@ -341,6 +383,8 @@ def main():
                        "frac_of_peak": round(also["gbps_wall"] / PEAK_HBM_GBPS, 4),
                        "frac_of_copy": round(also["gbps_wall"] / ceiling, 4) if ceiling else None,
                        "launch": also["launch"], "bytes_per_step": also["bytes_per_step"]}
+    if variants:
+        out["variants"] = variants
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(torch, W, args.workload)
     print(json.dumps(out), flush=True)

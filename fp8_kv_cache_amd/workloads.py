@@ -184,13 +184,21 @@ def make_inputs(w: Workload, device="cpu", *, seed=None, q_weight=True):
                 block_size=w.block_size, eps=w.eps)
 
 
-def algorithmic_bytes(num_tokens: int, num_heads: int, num_valid_slots: int) -> int:
+def algorithmic_bytes(num_tokens: int, num_heads: int, num_valid_slots: int,
+                      slot_bytes: int = SLOT_BYTES) -> int:
     """Bytes the operator must move once: q read and written (2 x 1 KiB per head),
     the kv row read (1 KiB), position and slot read (16 B), the token's cos/sin
-    row read (256 B), the 584-byte slot written for each valid slot, and the two
-    512-entry bf16 weights read once (2 KiB)."""
+    row read (256 B), the slot written for each valid slot (584 bytes in the
+    FP8 cache, 1024 in the bf16 one), and the two 512-entry bf16 weights read
+    once (2 KiB)."""
     return (num_tokens * (2048 * num_heads + 1024 + 16 + 256)
-            + 584 * num_valid_slots + 2048)
+            + slot_bytes * num_valid_slots + 2048)
+
+
+def gather_bytes(num_rows: int, num_valid: int, out_bytes_per_value: int) -> int:
+    """Bytes the cache reader must move: the 8-byte slot index per row, the
+    584-byte slot of each valid row, and the 512-value output row."""
+    return num_rows * (8 + 512 * out_bytes_per_value) + SLOT_BYTES * num_valid
 
 
 def as_u16(t: torch.Tensor) -> np.ndarray:
