@@ -51,7 +51,13 @@ def lib():
     global _lib
     if _lib is None:
         build(force=False)
-        L = ctypes.CDLL(_LIB)
+        _lib = configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def configure(L):
+    """Declare the C signatures on a loaded oracle library."""
+    if True:
         vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
         L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_bf16_to_f32.restype = f32
@@ -80,8 +86,7 @@ def lib():
         L.orc_ue8m0_exponent_array.argtypes = [vp, vp, i64]
         L.orc_rows.argtypes = [i64, vp, vp, f32, vp, vp, vp, vp]
         L.orc_quant_rows.argtypes = [i64, vp, vp, vp]
-        _lib = L
-    return _lib
+    return L
 
 
 def _c(a, dtype):

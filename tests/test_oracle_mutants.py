@@ -1,0 +1,132 @@
+"""The pins are strong enough to catch plausible mistakes in the oracle.
+
+Each case below plants one mistake in a copy of oracle/qkv_oracle.c (on the
+CPU, in a temporary directory), builds it, points the oracle module at it and
+runs the CPU pin tests until one fails.  Every planted mistake must be caught;
+the unmodified source must pass the same battery."""
+import ctypes
+import inspect
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+import test_oracle_formats as T_FMT
+import test_oracle_op as T_OP
+import test_oracle_row as T_ROW
+import test_oracle_store_gather as T_SG
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "qkv_oracle.c")
+
+# Pin tests in increasing cost, so that a mutant is usually caught within
+# milliseconds.  The slow strided cross-checks against torch's casts come last.
+SLOW = {"test_bf16_matches_torch_cast_on_strided_patterns", "test_e4m3_matches_torch_cast_in_range"}
+
+
+def battery():
+    tests = []
+    for mod in (T_FMT, T_ROW, T_OP, T_SG):
+        for name, fn in inspect.getmembers(mod, inspect.isfunction):
+            if name.startswith("test_") and fn.__module__ == mod.__name__:
+                tests.append((name in SLOW, name, fn))
+    tests.sort(key=lambda t: t[0])
+    return [(n, f) for _, n, f in tests]
+
+
+# (name, text in the source, replacement): one plausible mistake each.
+MUTANTS = [
+    ("bf16 ties to odd", "r = ((lo >> 16) & 1u) ? hi : lo;", "r = ((lo >> 16) & 1u) ? lo : hi;"),
+    ("bf16 truncates", "if (below < above)\n        r = lo;", "if (1)\n        r = lo;"),
+    ("e4m3 bias 8 (fnuz)", "int biased = ex + 7;", "int biased = ex + 8;"),
+    ("e4m3 truncates", "double q = nearbyint((2.0 * f - 1.0) * 8.0);",
+     "double q = floor((2.0 * f - 1.0) * 8.0);"),
+    ("e4m3 subnormal step 2^-10", "double m = nearbyint(a * 512.0);", "double m = nearbyint(a * 1024.0);"),
+    ("e4m3 saturates at 240", "if (biased > 15 || (biased == 15 && q == 7.0))",
+     "if (biased > 14 || (biased == 14 && q == 7.0))"),
+    ("e4m3 decode bias", "v = ldexp(1.0 + m / 8.0, e - 7);", "v = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("ue8m0 boundary off by one", "while (a <= ldexp(448.0, e - 1))", "while (a < ldexp(448.0, e - 1))"),
+    ("ue8m0 against 256", "while (a > ldexp(448.0, e))\n        e += 1;\n    while (a <= ldexp(448.0, e - 1))",
+     "while (a > ldexp(256.0, e))\n        e += 1;\n    while (a <= ldexp(256.0, e - 1))"),
+    ("ue8m0 lower clamp -126", "if (e < -127)\n        e = -127;", "if (e < -126)\n        e = -126;"),
+    ("sum of squares drops a term", "for (int k = 0; k < 8; ++k) {", "for (int k = 0; k < 7; ++k) {"),
+    ("sum of squares sequential",
+     "for (int n = 64; n > 1; n /= 2)\n        for (int i = 0; i < n / 2; ++i)\n            c[i] = c[2 * i] + c[2 * i + 1];",
+     "for (int i = 1; i < 64; ++i)\n        c[0] = c[0] + c[i];"),
+    ("sum of squares pairs (l, l+32) first",
+     "for (int n = 64; n > 1; n /= 2)\n        for (int i = 0; i < n / 2; ++i)\n            c[i] = c[2 * i] + c[2 * i + 1];",
+     "for (int n = 64; n > 1; n /= 2)\n        for (int i = 0; i < n / 2; ++i)\n            c[i] = c[i] + c[i + n / 2];"),
+    ("mean over 448 dims", "float mean_sq = sum_sq / 512.0f;", "float mean_sq = sum_sq / 448.0f;"),
+    ("eps outside the root", "float v = mean_sq + eps;\n    float r = sqrtf(v);\n    return 1.0f / r;",
+     "float v = mean_sq;\n    float r = sqrtf(v) + eps;\n    return 1.0f / r;"),
+    ("gemma 1+w", "y[j] = w ? t * orc_bf16_to_f32(w[j]) : t;",
+     "y[j] = w ? t * (1.0f + orc_bf16_to_f32(w[j])) : t;"),
+    ("weight index reversed", "y[j] = w ? t * orc_bf16_to_f32(w[j]) : t;",
+     "y[j] = w ? t * orc_bf16_to_f32(w[511 - j]) : t;"),
+    ("rope sign", "z[ORC_NOPE_DIM + 2 * i] = fmaf(a, c, -bs);", "z[ORC_NOPE_DIM + 2 * i] = fmaf(a, c, bs);"),
+    ("rope cos/sin swapped", "float c = cs[i];\n        float sn = cs[ORC_NPAIR + i];",
+     "float sn = cs[i];\n        float c = cs[ORC_NPAIR + i];"),
+    ("rope half-split pairs", "float a = y[ORC_NOPE_DIM + 2 * i];\n        float b = y[ORC_NOPE_DIM + 2 * i + 1];",
+     "float a = y[ORC_NOPE_DIM + i];\n        float b = y[ORC_NOPE_DIM + 32 + i];"),
+    ("scale byte bias 128", "return (uint8_t)(e + 127);", "return (uint8_t)(e + 128);"),
+    ("pad byte not zero", "scale[ORC_NQBLOCK] = 0;", "scale[ORC_NQBLOCK] = 0xff;"),
+    ("interleaved slot records", "*data_off = base + s * ORC_SLOT_DATA;", "*data_off = base + s * ORC_SLOT_BYTES;"),
+    ("capacity slot written", "if (slot < 0 || block_size <= 0 || slot >= num_blocks * (int64_t)block_size)",
+     "if (slot < 0 || block_size <= 0 || slot > num_blocks * (int64_t)block_size)"),
+    ("rope bytes big-endian", "data[ORC_NOPE_DIM + 2 * j] = (uint8_t)(h & 0xff);\n        data[ORC_NOPE_DIM + 2 * j + 1] = (uint8_t)(h >> 8);",
+     "data[ORC_NOPE_DIM + 2 * j] = (uint8_t)(h >> 8);\n        data[ORC_NOPE_DIM + 2 * j + 1] = (uint8_t)(h & 0xff);"),
+    ("quantized from the wrong block", "scale[b] = orc_quant_block(y + b * ORC_QBLOCK, data + b * ORC_QBLOCK);",
+     "scale[b] = orc_quant_block(y + (b ^ 1) * ORC_QBLOCK, data + b * ORC_QBLOCK);"),
+    ("bf16 store unrotated", "insert_bf16_slot(z, cache, slot_mapping[t]);", "insert_bf16_slot(y, cache, slot_mapping[t]);"),
+    ("gather exponent bias", "(int)scale[j / ORC_QBLOCK] - 127", "(int)scale[j / ORC_QBLOCK] - 128"),
+]
+
+
+def build_variant(tmp_path, text):
+    src = tmp_path / "mut.c"
+    src.write_text(text)
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+                    "-fPIC", "-shared", str(src), "-o", str(lib), "-lm"], check=True)
+    return str(lib)
+
+
+def first_failure_in_child(lib_path):
+    """Run the battery against the library at lib_path in a child process (a
+    planted mistake may write out of bounds).  Returns the first failing test,
+    "crash: <signal>" if the child died, or None if every pin passed."""
+    code = (
+        "import ctypes, sys\n"
+        "import oracle, test_oracle_mutants as M\n"
+        "oracle._lib = oracle.configure(ctypes.CDLL(sys.argv[1]))\n"
+        "for slow in (False, True):\n"
+        "    for name, fn in M.battery():\n"
+        "        if (name in M.SLOW) != slow:\n"
+        "            continue\n"
+        "        try:\n"
+        "            fn()\n"
+        "        except Exception:\n"
+        "            print('FAILED', name); sys.exit(0)\n"
+        "print('PASSED')\n")
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ)
+    env["PYTHONPATH"] = os.pathsep.join([here, os.path.dirname(here), env.get("PYTHONPATH", "")])
+    res = subprocess.run([sys.executable, "-c", code, lib_path], capture_output=True, text=True,
+                         env=env, timeout=300)
+    if res.returncode != 0:
+        return "crash: %d" % res.returncode
+    last = res.stdout.strip().splitlines()[-1]
+    return None if last == "PASSED" else last.split(" ", 1)[1]
+
+
+def test_unmodified_oracle_passes_the_battery(tmp_path):
+    assert first_failure_in_child(build_variant(tmp_path, open(SRC).read())) is None
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation site not found exactly once: %s" % name
+    caught = first_failure_in_child(build_variant(tmp_path, text.replace(old, new)))
+    assert caught is not None, "no pin catches: %s" % name
