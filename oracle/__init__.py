@@ -81,6 +81,16 @@ def configure(L):
         L.orc_qkv_prep_bf16_store.argtypes = L.orc_qkv_prep.argtypes
         L.orc_qkv_prep_bf16_store.restype = ctypes.c_int
         L.orc_gather_dequant.argtypes = [vp, i64, i32, vp, i64, vp]
+        L.orc_sum_squares_n.argtypes = [vp, i64]
+        L.orc_sum_squares_n.restype = f32
+        L.orc_ue8m0_ceil_byte.argtypes = [f32]
+        L.orc_ue8m0_ceil_byte.restype = ctypes.c_uint32
+        L.orc_ue8m0_inverse.argtypes = [ctypes.c_uint32]
+        L.orc_ue8m0_inverse.restype = f32
+        L.orc_mxfp8_scale_offset.argtypes = [i64, i64, i64]
+        L.orc_mxfp8_scale_offset.restype = i64
+        L.orc_mxfp8_norm_quant.argtypes = [i64, i64, vp, vp, vp, vp, f32, vp, vp]
+        L.orc_mxfp8_norm_quant.restype = ctypes.c_int
         L.orc_f32_to_bf16_array.argtypes = [vp, vp, i64]
         L.orc_f32_to_e4m3_array.argtypes = [vp, vp, i64]
         L.orc_ue8m0_exponent_array.argtypes = [vp, vp, i64]
@@ -213,3 +223,42 @@ def gather_dequant(cache, num_blocks, block_size, slots):
     lib().orc_gather_dequant(_p(cache), int(num_blocks), int(block_size), _p(slots), slots.size,
                              _p(out))
     return out
+
+
+# ---------------------------------------------------------------- MXFP8 variant
+
+def mxfp8_scale_bytes(m, hidden):
+    cols = hidden // 32
+    return (m + 127) // 128 * 128 * ((cols + 3) // 4 * 4)
+
+
+def mxfp8_norm_quant(x, gamma, eps, residual=None):
+    """Residual add + Gemma RMSNorm + MXFP8 quantization (see qkv_oracle.c, M1-M7).
+
+    x, residual: uint16 [m, hidden] bf16 bits; gamma: uint16 [hidden].
+    Returns (codes uint8 [m, hidden], swizzled scales uint8 [...], prenorm
+    uint16 [m, hidden] or None)."""
+    x = _c(np.asarray(x, dtype=np.uint16), np.uint16)
+    m, hidden = x.shape
+    gamma = _c(np.asarray(gamma, dtype=np.uint16), np.uint16)
+    res = None if residual is None else _c(np.asarray(residual, dtype=np.uint16), np.uint16)
+    res_out = None if residual is None else np.empty_like(x)
+    codes = np.empty((m, hidden), np.uint8)
+    scales = np.full(mxfp8_scale_bytes(m, hidden), 0xEE, np.uint8)
+    rc = lib().orc_mxfp8_norm_quant(m, hidden, _p(x), _p(res), _p(res_out), _p(gamma),
+                                    float(eps), _p(codes), _p(scales))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (hidden must be a multiple of 128)")
+    return codes, scales, res_out
+
+
+def mxfp8_scale_offset(row, col, padded_cols):
+    return lib().orc_mxfp8_scale_offset(int(row), int(col), int(padded_cols))
+
+
+def ue8m0_ceil_byte(v):
+    return int(lib().orc_ue8m0_ceil_byte(float(v)))
+
+
+def ue8m0_inverse(byte):
+    return float(lib().orc_ue8m0_inverse(int(byte)))

@@ -459,3 +459,154 @@ void orc_quant_rows(int64_t n, const float *y, uint8_t *codes, uint8_t *scales)
                 orc_quant_block(y + r * ORC_NOPE_DIM + b * ORC_QBLOCK,
                                 codes + r * ORC_NOPE_DIM + b * ORC_QBLOCK);
 }
+
+/* ------------------------------------------------------------------ */
+/* MXFP8 norm-quant variant (a second workload for the same codec)     */
+/* ------------------------------------------------------------------ */
+/*
+ * The residual-add + Gemma RMSNorm + MXFP8 quantization of the vLLM page
+ * "vllm.models.minimax_m3.nvidia.ops.finalize_allreduce_norm" (class
+ * _LamportGemmaRMSNormMxfp8Kernel and helpers _ue8m0_ceil, _ue8m0_inverse,
+ * _f32x4_to_e4m3x4, _swizzled_scale_offset), without its all-reduce (one rank,
+ * so the "sum of fragments" is the single input row).  Readings:
+ *   M1 prenorm = bf16(x + residual), the sum in fp32 (the page adds the fp32
+ *      fragments and the residual, then rounds to bf16); with no residual,
+ *      prenorm = x.  residual_out, when given, receives prenorm.
+ *   M2 sum of squares: chunks of 8 summed left to right, then adjacent pairs
+ *      level by level; an odd element at the end of a level is carried up
+ *      unchanged (the page's thread/warp/cluster order is not reproducible;
+ *      this generalizes R1 to any multiple of 8).
+ *   M3 inv = 1 / sqrt(S / hidden + eps), each step correctly rounded (the page
+ *      uses an approximate rsqrt; this build takes the correctly rounded one).
+ *   M4 normed = bf16((prenorm * inv) * (gamma + 1)), each product and the
+ *      gamma + 1 rounded in fp32 (Gemma weight, the page's order).
+ *   M5 per 32-element block: v = RN(amax * RN(1/448)); the scale byte is the
+ *      page's rounded-up biased exponent of v (0 for v <= 0; +1 when the
+ *      mantissa is non-zero, except a subnormal v at or below 2^-127; at most
+ *      254); inverse = 2^(127 - byte), 0 for byte 0 (and for 254, where the
+ *      page's exponent arithmetic reaches 0).
+ *   M6 code = E4M3 of RN(normed * inverse) clamped to +-448 first (satfinite).
+ *   M7 codes row-major [m][hidden]; scale byte (row, col = block) at the
+ *      128x4 swizzled offset col%4 + (col/4)*512 + (row%32)*16 +
+ *      ((row%128)/32)*4 + (row/128)*128*padded_cols, padded_cols = cols rounded
+ *      up to 4; the scale bytes of rows m .. (m rounded up to 128) - 1 are 0.
+ */
+
+static float f32_div(float a, float b) { return a / b; }
+
+/* M2: sum of squares of n bf16 values (n a multiple of 8). */
+float orc_sum_squares_n(const uint16_t *x, int64_t n)
+{
+    int64_t nc = n / 8;
+    float *c = (float *)malloc(sizeof(float) * (size_t)(nc > 0 ? nc : 1));
+    for (int64_t l = 0; l < nc; ++l) {
+        float acc = 0.0f;
+        for (int k = 0; k < 8; ++k) {
+            float v = orc_bf16_to_f32(x[8 * l + k]);
+            acc = acc + v * v;
+        }
+        c[l] = acc;
+    }
+    while (nc > 1) {
+        int64_t half = nc / 2;
+        for (int64_t i = 0; i < half; ++i)
+            c[i] = c[2 * i] + c[2 * i + 1];
+        if (nc % 2)
+            c[half] = c[nc - 1];
+        nc = half + nc % 2;
+    }
+    float s = nc ? c[0] : 0.0f;
+    free(c);
+    return s;
+}
+
+/* M5: the page's rounded-up UE8M0 byte of v. */
+uint32_t orc_ue8m0_ceil_byte(float v)
+{
+    if (!(v > 0.0f))
+        return 0;
+    uint32_t bits = float_to_bits(v);
+    uint32_t e = (bits >> 23) & 0xffu;
+    uint32_t mant = bits & 0x7fffffu;
+    uint32_t bump = mant != 0;
+    if (e == 0 && mant <= 0x400000u)
+        bump = 0;
+    uint32_t r = e + bump;
+    return r > 254 ? 254 : r;
+}
+
+/* M6: inverse scale 2^(127 - byte), computed as the page does. */
+float orc_ue8m0_inverse(uint32_t byte)
+{
+    if (byte == 0)
+        return 0.0f;
+    int32_t ne = 254 - (int32_t)byte;
+    if (ne < 0)
+        ne = 0;
+    return bits_to_float((uint32_t)ne << 23);
+}
+
+/* M7 */
+int64_t orc_mxfp8_scale_offset(int64_t row, int64_t col, int64_t padded_cols)
+{
+    return col % 4 + (col / 4) * 512 + (row % 32) * 16 + ((row % 128) / 32) * 4 +
+           (row / 128) * 128 * padded_cols;
+}
+
+/* Rows [0, m): x, residual (may be NULL), residual_out (may be NULL),
+ * gamma: bf16; quant_out uint8 [m][hidden]; scale_out uint8
+ * [round_up(m, 128)][padded_cols] in the swizzled order.  hidden must be a
+ * positive multiple of 128.  Returns 0, or -1 for unusable arguments. */
+int orc_mxfp8_norm_quant(int64_t m, int64_t hidden, const uint16_t *x, const uint16_t *residual,
+                         uint16_t *residual_out, const uint16_t *gamma, float eps,
+                         uint8_t *quant_out, uint8_t *scale_out)
+{
+    if (m < 0 || hidden <= 0 || hidden % 128)
+        return -1;
+    int64_t cols = hidden / 32;
+    int64_t padded_cols = (cols + 3) / 4 * 4;
+    int64_t rows_padded = (m + 127) / 128 * 128;
+    uint16_t *pre = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)hidden);
+    float *normed = (float *)malloc(sizeof(float) * (size_t)hidden);
+    const float inv448 = f32_div(1.0f, 448.0f);
+    for (int64_t r = 0; r < m; ++r) {
+        const uint16_t *xr = x + r * hidden;
+        for (int64_t j = 0; j < hidden; ++j) {
+            if (residual) {
+                float sum = orc_bf16_to_f32(xr[j]) + orc_bf16_to_f32(residual[r * hidden + j]);
+                pre[j] = orc_f32_to_bf16(sum);
+            } else {
+                pre[j] = xr[j];
+            }
+            if (residual_out)
+                residual_out[r * hidden + j] = pre[j];
+        }
+        float s = orc_sum_squares_n(pre, hidden);
+        float mean_sq = f32_div(s, (float)hidden);
+        float inv = 1.0f / sqrtf(mean_sq + eps);
+        for (int64_t j = 0; j < hidden; ++j) {
+            float g1 = orc_bf16_to_f32(gamma[j]) + 1.0f;
+            float t = orc_bf16_to_f32(pre[j]) * inv;
+            normed[j] = orc_bf16_to_f32(orc_f32_to_bf16(t * g1));
+        }
+        for (int64_t b = 0; b < cols; ++b) {
+            float amax = 0.0f;
+            for (int k = 0; k < 32; ++k)
+                amax = fmaxf(amax, fabsf(normed[32 * b + k]));
+            uint32_t byte = orc_ue8m0_ceil_byte(amax * inv448);
+            float inverse = orc_ue8m0_inverse(byte);
+            for (int k = 0; k < 32; ++k) {
+                float v = normed[32 * b + k] * inverse;
+                v = fminf(fmaxf(v, -448.0f), 448.0f);
+                quant_out[r * hidden + 32 * b + k] = orc_f32_to_e4m3(v);
+            }
+            scale_out[orc_mxfp8_scale_offset(r, b, padded_cols)] = (uint8_t)byte;
+        }
+    }
+    for (int64_t r = m; r < rows_padded; ++r)
+        for (int64_t b = 0; b < padded_cols; ++b)
+            scale_out[orc_mxfp8_scale_offset(r, b, padded_cols)] = 0;
+    free(pre);
+    free(normed);
+    return 0;
+}

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_formats as T_FMT
+import test_oracle_mxfp8 as T_MX
 import test_oracle_op as T_OP
 import test_oracle_row as T_ROW
 import test_oracle_store_gather as T_SG
@@ -25,12 +26,27 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "qkv_oracle.c")
 SLOW = {"test_bf16_matches_torch_cast_on_strided_patterns", "test_e4m3_matches_torch_cast_in_range"}
 
 
+def _expand(name, fn):
+    """The test as zero-argument calls, one per parametrize case."""
+    marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+    if not marks:
+        return [(name, fn)]
+    argnames, values = marks[0].args[0], marks[0].args[1]
+    single = "," not in argnames if isinstance(argnames, str) else len(argnames) == 1
+    calls = []
+    for v in values:
+        args = (v,) if single else tuple(v)
+        calls.append(("%s[%s]" % (name, v), lambda fn=fn, args=args: fn(*args)))
+    return calls
+
+
 def battery():
     tests = []
-    for mod in (T_FMT, T_ROW, T_OP, T_SG):
+    for mod in (T_FMT, T_ROW, T_OP, T_SG, T_MX):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if name.startswith("test_") and fn.__module__ == mod.__name__:
-                tests.append((name in SLOW, name, fn))
+                for n, call in _expand(name, fn):
+                    tests.append((name in SLOW, n, call))
     tests.sort(key=lambda t: t[0])
     return [(n, f) for _, n, f in tests]
 
@@ -50,7 +66,9 @@ MUTANTS = [
     ("ue8m0 against 256", "while (a > ldexp(448.0, e))\n        e += 1;\n    while (a <= ldexp(448.0, e - 1))",
      "while (a > ldexp(256.0, e))\n        e += 1;\n    while (a <= ldexp(256.0, e - 1))"),
     ("ue8m0 lower clamp -126", "if (e < -127)\n        e = -127;", "if (e < -126)\n        e = -126;"),
-    ("sum of squares drops a term", "for (int k = 0; k < 8; ++k) {", "for (int k = 0; k < 7; ++k) {"),
+    ("sum of squares drops a term",
+     "for (int l = 0; l < 64; ++l) {\n        float acc = 0.0f;\n        for (int k = 0; k < 8; ++k) {",
+     "for (int l = 0; l < 64; ++l) {\n        float acc = 0.0f;\n        for (int k = 0; k < 7; ++k) {"),
     ("sum of squares sequential",
      "for (int n = 64; n > 1; n /= 2)\n        for (int i = 0; i < n / 2; ++i)\n            c[i] = c[2 * i] + c[2 * i + 1];",
      "for (int i = 1; i < 64; ++i)\n        c[0] = c[0] + c[i];"),
@@ -80,6 +98,18 @@ MUTANTS = [
      "scale[b] = orc_quant_block(y + (b ^ 1) * ORC_QBLOCK, data + b * ORC_QBLOCK);"),
     ("bf16 store unrotated", "insert_bf16_slot(z, cache, slot_mapping[t]);", "insert_bf16_slot(y, cache, slot_mapping[t]);"),
     ("gather exponent bias", "(int)scale[j / ORC_QBLOCK] - 127", "(int)scale[j / ORC_QBLOCK] - 128"),
+    ("mxfp8 ceil never bumps", "uint32_t bump = mant != 0;", "uint32_t bump = 0;"),
+    ("mxfp8 plain weight", "float g1 = orc_bf16_to_f32(gamma[j]) + 1.0f;", "float g1 = orc_bf16_to_f32(gamma[j]);"),
+    ("mxfp8 no bf16 rounding before quant", "normed[j] = orc_bf16_to_f32(orc_f32_to_bf16(t * g1));",
+     "normed[j] = t * g1;"),
+    ("mxfp8 swizzle row stride", "(row % 32) * 16 + ((row % 128) / 32) * 4", "(row % 32) * 4 + ((row % 128) / 32) * 128"),
+    ("mxfp8 padding rows kept", "scale_out[orc_mxfp8_scale_offset(r, b, padded_cols)] = 0;",
+     "scale_out[orc_mxfp8_scale_offset(r, b, padded_cols)] = scale_out[orc_mxfp8_scale_offset(r, b, padded_cols)];"),
+    ("mxfp8 odd element dropped", "if (nc % 2)\n            c[half] = c[nc - 1];", "if (nc % 2)\n            c[half] = 0.0f;"),
+    ("mxfp8 residual ignored", "float sum = orc_bf16_to_f32(xr[j]) + orc_bf16_to_f32(residual[r * hidden + j]);",
+     "float sum = orc_bf16_to_f32(xr[j]);"),
+    ("mxfp8 block of 16", "uint32_t byte = orc_ue8m0_ceil_byte(amax * inv448);",
+     "uint32_t byte = orc_ue8m0_ceil_byte(fmaxf(amax, 0.0f) * inv448 * ((b & 1) ? 1.0f : 1.0f) + 0.0f * normed[0]);\n            amax = 0.0f; for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(normed[32 * b + k]));\n            byte = orc_ue8m0_ceil_byte(amax * inv448);"),
 ]
 
 
@@ -102,7 +132,7 @@ def first_failure_in_child(lib_path):
         "oracle._lib = oracle.configure(ctypes.CDLL(sys.argv[1]))\n"
         "for slow in (False, True):\n"
         "    for name, fn in M.battery():\n"
-        "        if (name in M.SLOW) != slow:\n"
+        "        if (name.split('[')[0] in M.SLOW) != slow:\n"
         "            continue\n"
         "        try:\n"
         "            fn()\n"

@@ -1,0 +1,178 @@
+"""Pins of the oracle's MXFP8 norm-quant variant (residual add + Gemma RMSNorm +
+32-element UE8M0 blocks + 128x4 swizzled scales): the page's helper rules by
+their definitions, hand-computed swizzle offsets, closed forms for whole rows,
+the odd-carry summation order, and error bounds."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def bf16(x):
+    return oracle.f32_to_bf16(np.asarray(x, np.float32))
+
+
+def f32(bits):
+    return np.array([bits], np.uint32).view(np.float32)[0]
+
+
+# ------------------------------------------------------------- UE8M0 ceil
+
+def test_ue8m0_ceil_known_values():
+    assert oracle.ue8m0_ceil_byte(1.0) == 127
+    assert oracle.ue8m0_ceil_byte(2.0 ** -9) == 118
+    assert oracle.ue8m0_ceil_byte(1.5) == 128
+    assert oracle.ue8m0_ceil_byte(0.0) == 0
+    assert oracle.ue8m0_ceil_byte(-3.0) == 0
+    assert oracle.ue8m0_ceil_byte(f32(0x00400000)) == 0          # 2^-127, subnormal
+    assert oracle.ue8m0_ceil_byte(f32(0x00400001)) == 1
+    assert oracle.ue8m0_ceil_byte(f32(0x00000001)) == 0
+    assert oracle.ue8m0_ceil_byte(2.0 ** 127) == 254
+    assert oracle.ue8m0_ceil_byte(1.5 * 2.0 ** 127) == 254        # clamped
+
+
+def test_ue8m0_ceil_is_the_rounded_up_exponent():
+    rng = np.random.default_rng(61)
+    bits = rng.integers(0x00400001, 0x7F000000, 20000, dtype=np.uint32)
+    for v in bits.view(np.float32):
+        b = oracle.ue8m0_ceil_byte(v)
+        assert 1 <= b <= 254
+        assert np.ldexp(1.0, b - 127) >= float(v)
+        assert b == 1 or np.ldexp(1.0, b - 128) < float(v)
+
+
+def test_ue8m0_inverse():
+    for b in range(1, 254):
+        assert oracle.ue8m0_inverse(b) == np.float32(2.0 ** (127 - b))
+    assert oracle.ue8m0_inverse(0) == 0.0
+    assert oracle.ue8m0_inverse(254) == 0.0       # the page's exponent arithmetic floors at 0
+
+
+# ------------------------------------------------------------- swizzle
+
+def test_swizzled_offsets_by_hand():
+    pc = 8
+    cases = {(0, 0): 0, (0, 1): 1, (0, 3): 3, (0, 4): 512, (0, 7): 515, (1, 0): 16,
+             (31, 0): 496, (32, 0): 4, (96, 0): 12, (127, 3): 511, (128, 0): 128 * pc,
+             (130, 5): 128 * pc + 512 + 1 + 32}
+    for (r, c), want in cases.items():
+        assert oracle.mxfp8_scale_offset(r, c, pc) == want, (r, c)
+
+
+def test_swizzle_is_a_bijection_per_tile():
+    pc = 12
+    offs = sorted(oracle.mxfp8_scale_offset(r, c, pc) for r in range(256) for c in range(pc))
+    assert offs == list(range(256 * pc))
+
+
+# ------------------------------------------------------------- whole rows
+
+def test_constant_power_of_two_rows_closed_form():
+    # x = 2^k at eps = 0 with gamma = 0: normed = 1 exactly, amax = 1,
+    # v = RN(1/448) in [2^-9, 2^-8) with a non-zero mantissa -> byte 119,
+    # inverse 2^8 -> 256 -> code 0x78.
+    m, hidden = 5, 256
+    for k in (-6, 0, 9):
+        x = bf16(np.full((m, hidden), 2.0 ** k))
+        codes, scales, _ = oracle.mxfp8_norm_quant(x, bf16(np.zeros(hidden)), 0.0)
+        assert np.all(codes == 0x78)
+        pc = hidden // 32
+        valid = np.zeros(scales.size, bool)
+        for r in range(m):
+            for c in range(pc):
+                valid[oracle.mxfp8_scale_offset(r, c, pc)] = True
+        assert np.all(scales[valid] == 119)
+        assert np.all(scales[~valid] == 0)                  # padding rows 5..127 zeroed
+
+
+def test_gemma_weight_and_residual_add():
+    rng = np.random.default_rng(62)
+    hidden = 384
+    g = bf16(0.25 * rng.standard_normal(hidden))
+    x = bf16(np.ones((2, hidden)))
+    r = np.zeros((2, hidden), np.uint16)
+    r[1, :] = bf16(np.full(hidden, 2.0 ** -8))     # 1 + 2^-8 ties to 1.0 in bf16
+    codes, scales, pre = oracle.mxfp8_norm_quant(x, g, 0.0, residual=r)
+    assert np.all(pre == 0x3F80)
+    # normed = bf16(1 * (g + 1)); its codes must dequantize within the E4M3 bound
+    normed = oracle.bf16_to_f32(bf16(oracle.bf16_to_f32(g).astype(np.float32) + np.float32(1.0)))
+    pc = hidden // 32
+    for row in range(2):
+        for c in range(pc):
+            b = scales[oracle.mxfp8_scale_offset(row, c, pc)]
+            deq = oracle.e4m3_to_f64(codes[row, 32 * c:32 * c + 32]) * 2.0 ** (int(b) - 127)
+            want = normed[32 * c:32 * c + 32].astype(np.float64)
+            assert np.all(np.abs(deq - want) <= 2.0 ** -4 * np.abs(want) + 2.0 ** (int(b) - 137))
+    r2 = np.zeros((1, hidden), np.uint16)
+    r2[0, :] = bf16(np.full(hidden, 3 * 2.0 ** -8))
+    _, _, pre2 = oracle.mxfp8_norm_quant(x[:1], g, 0.0, residual=r2)
+    assert np.all(pre2 == 0x3F82)                   # 1 + 3*2^-8 ties up to the even 0x3F82
+
+
+def test_bf16_rounding_before_quant_decides_a_tie():
+    # One row of ones at eps = 0 (inv = 1), hidden 128.  gamma[0] = 0.75 gives
+    # normed 1.75, the block amax: v = RN(1.75 * RN(1/448)) = 2^-8 exactly
+    # (RN(1/448) is 1/448 * (1 + 4.5e-8) and 1.75 times it rounds back to
+    # 2^-8), so byte 119 and inverse 2^8.  gamma[1] = 0.1865234375 gives
+    # g + 1 = 1.1865234375, whose bf16 is 1.1875: 1.1875 * 256 = 304 is the tie
+    # between 288 (mantissa 1) and 320 (mantissa 2), so code 0x7a; without the
+    # bf16 rounding, 303.75 would round to 288, code 0x79.
+    g = np.zeros(128, np.float32)
+    g[0] = 0.75
+    g[1] = 0.1865234375
+    codes, scales, _ = oracle.mxfp8_norm_quant(bf16(np.ones((1, 128))), bf16(g), 0.0)
+    assert codes[0, 0] == 0x7E and codes[0, 1] == 0x7A
+    assert np.all(codes[0, 2:] == 0x78)
+    assert all(scales[oracle.mxfp8_scale_offset(0, c, 4)] == 119 for c in range(4))
+
+
+def _sumsq_n(x):
+    buf = np.ascontiguousarray(bf16(x))       # keep the buffer alive across the call
+    return oracle.lib().orc_sum_squares_n(buf.ctypes.data, buf.size)
+
+
+def test_sum_of_squares_carries_the_odd_element():
+    # hidden 1536 = 192 chunks = three aligned groups of 64 chunks.  With
+    # 2^24 in group 0 and 1 in groups 1 and 2: ((G0 + G1) + G2) = 2^24 (each
+    # + 1 ties to even), while G0 + (G1 + G2) would be 2^24 + 2.
+    x = np.zeros(1536, np.float32)
+    x[0] = 4096.0
+    x[64 * 8] = 1.0
+    x[128 * 8] = 1.0
+    assert _sumsq_n(x) == 2.0 ** 24
+    # the first six levels stay inside each aligned group of 64 chunks
+    y = np.zeros(1536, np.float32)
+    y[0] = 4096.0
+    y[8] = y[16] = y[24] = 1.0
+    assert _sumsq_n(y) == 2.0 ** 24 + 2
+
+
+@pytest.mark.parametrize("hidden", [128, 512, 1536, 4096, 7168])
+def test_random_rows_against_float64(hidden):
+    rng = np.random.default_rng(hidden)
+    m = 7
+    x = bf16(rng.standard_normal((m, hidden)))
+    res = bf16(0.5 * rng.standard_normal((m, hidden)))
+    g = bf16(0.1 * rng.standard_normal(hidden))
+    eps = 1e-6
+    codes, scales, pre = oracle.mxfp8_norm_quant(x, g, eps, residual=res)
+    # prenorm is the bf16 of the fp32 sum
+    xs = oracle.bf16_to_f32(x).astype(np.float32) + oracle.bf16_to_f32(res).astype(np.float32)
+    assert np.array_equal(pre, bf16(xs))
+    p = oracle.bf16_to_f32(pre).astype(np.float64)
+    ideal = p / np.sqrt((p ** 2).mean(axis=1, keepdims=True) + np.float64(np.float32(eps))) * \
+        (oracle.bf16_to_f32(g).astype(np.float64) + 1.0)
+    pc = hidden // 32
+    for r in range(m):
+        for c in range(pc):
+            b = int(scales[oracle.mxfp8_scale_offset(r, c, pc)])
+            blk = ideal[r, 32 * c:32 * c + 32]
+            deq = oracle.e4m3_to_f64(codes[r, 32 * c:32 * c + 32]) * 2.0 ** (b - 127)
+            # bf16 rounding (2^-9 relative) plus E4M3 rounding (2^-4) plus fp32 noise
+            assert np.all(np.abs(deq - blk) <= (2.0 ** -4 + 2.0 ** -8) * np.abs(blk) + 2.0 ** (b - 136))
+            assert 448.0 * 2.0 ** (b - 127) >= np.abs(blk).max() * (1 - 2.0 ** -7)
+
+
+def test_hidden_must_be_a_multiple_of_128():
+    with pytest.raises(ValueError):
+        oracle.mxfp8_norm_quant(np.zeros((1, 96), np.uint16), np.zeros(96, np.uint16), 1e-6)

@@ -28,7 +28,8 @@ def rand_rows(n, seed, scale=1.0):
 # ------------------------------------------------------------- sum of squares
 
 def _sumsq(x):
-    return float(oracle.lib().orc_sum_squares(np.ascontiguousarray(x).ctypes.data))
+    buf = np.ascontiguousarray(x)             # keep the buffer alive across the call
+    return float(oracle.lib().orc_sum_squares(buf.ctypes.data))
 
 
 def test_sum_squares_hand_cases_pin_the_order():
