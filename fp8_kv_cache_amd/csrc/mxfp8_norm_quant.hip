@@ -1,0 +1,226 @@
+// Residual add + Gemma RMSNorm + MXFP8 quantization for gfx950 (the second
+// operator of include/qkv_prep_mxfp8.h).  One wavefront per row: lane l holds
+// the 16-byte chunks l, l + 64, ..., l + 64 (K - 1) (K = hidden / 512), so every
+// load and store instruction of the wavefront is one contiguous 1 KiB segment.
+// The six in-wavefront tree levels reduce each aligned group of 64 chunks
+// (the same DPP + permlane order as the main operator); the K group sums are
+// then added in-lane in adjacent pairs with the odd one carried, which is the
+// numerics contract's order.  A 32-element scale block is 4 consecutive chunks
+// held by 4 consecutive lanes, so its amax is two DPP max steps.
+#include "qkvp_device.h"
+#include "qkv_prep.h"
+#include "qkv_prep_mxfp8.h"
+
+namespace qkvp {
+namespace {
+
+using namespace dev;
+
+struct MxArgs {
+    const uint16_t *x;
+    const uint16_t *residual;
+    uint16_t *residual_out;
+    const uint16_t *gamma;
+    uint8_t *quant_out;
+    uint8_t *scale_out;
+    int64_t m;
+    int64_t rows_padded;
+    int32_t hidden;
+    int32_t padded_cols;
+    float eps;
+};
+
+__device__ __forceinline__ int64_t swizzled_offset(int64_t row, int64_t col, int64_t padded_cols)
+{
+    return (col & 3) + (col >> 2) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (row >> 7) * 128 * padded_cols;
+}
+
+// The page's rounded-up biased exponent of v.
+__device__ __forceinline__ uint32_t ue8m0_ceil_byte(float v)
+{
+    if (!(v > 0.0f))
+        return 0;
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t e = bits >> 23;
+    const uint32_t mant = bits & 0x7fffffu;
+    const uint32_t bump = (mant != 0 && !(e == 0 && mant <= 0x400000u)) ? 1u : 0u;
+    return min(e + bump, 254u);
+}
+
+__device__ __forceinline__ uint32_t max4(uint32_t v)
+{
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    return v;
+}
+
+template <int K, bool HAS_RES>
+__global__ __launch_bounds__(256) void mxfp8_kernel(MxArgs a)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= a.rows_padded)
+        return;
+    if (row >= a.m) {
+        // Padding rows of the last 128-row tile: zero scale bytes.
+        for (int c = lane; c < a.padded_cols; c += 64)
+            a.scale_out[swizzled_offset(row, c, a.padded_cols)] = 0;
+        return;
+    }
+    const int64_t base = row * a.hidden;
+    u32x4 p[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int64_t e0 = base + 8 * (lane + 64 * j);
+        const u32x4 xv = load_stream(reinterpret_cast<const u32x4 *>(a.x + e0));
+        if constexpr (HAS_RES) {
+            const u32x4 rv = load_stream(reinterpret_cast<const u32x4 *>(a.residual + e0));
+            float xf[8], rf[8], sf[8];
+            unpack_bf16x8(xv, xf);
+            unpack_bf16x8(rv, rf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sf[e] = xf[e] + rf[e];
+            p[j] = pack_bf16x8<true>(sf);
+        } else {
+            p[j] = xv;
+        }
+    }
+    if (a.residual_out) {
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            store_stream(reinterpret_cast<u32x4 *>(a.residual_out + base + 8 * (lane + 64 * j)), p[j]);
+    }
+
+    // Sum of squares: each aligned group of 64 chunks in the wavefront, then
+    // the K group sums in adjacent pairs, carrying an odd last one.
+    float g[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        float x[8];
+        unpack_bf16x8(p[j], x);
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc = __builtin_fmaf(x[e], x[e], acc);
+        g[j] = wave_sum_ordered(acc);
+    }
+#pragma unroll
+    for (int n = K; n > 1; n = (n + 1) / 2) {
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i)
+            g[i] = g[2 * i] + g[2 * i + 1];
+        if (n % 2)
+            g[n / 2] = g[n - 1];
+    }
+    const float inv = 1.0f / __builtin_sqrtf(g[0] / (float)a.hidden + a.eps);
+    const float inv448 = 1.0f / 448.0f;
+
+    float gm[8];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int chunk = lane + 64 * j;
+        unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.gamma)[chunk], gm);
+        float x[8], nv[8];
+        unpack_bf16x8(p[j], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            nv[e] = (x[e] * inv) * (gm[e] + 1.0f);
+        float n[8];
+        unpack_bf16x8(pack_bf16x8<true>(nv), n);          // rounded to bf16
+        uint32_t mx = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            mx = max(mx, __float_as_uint(n[e]) & 0x7fffffffu);
+        const float amax = __uint_as_float(max4(mx));
+        const uint32_t byte = ue8m0_ceil_byte(amax * inv448);
+        const int32_t ne = 254 - (int32_t)byte;
+        const float inverse = byte == 0 ? 0.0f : __uint_as_float((uint32_t)(ne > 0 ? ne : 0) << 23);
+        float q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            q[e] = fminf(fmaxf(n[e] * inverse, -448.0f), 448.0f);
+        const u32x2 codes = {pack_e4m3<true>(q[0], q[1], q[2], q[3]), pack_e4m3<true>(q[4], q[5], q[6], q[7])};
+        store_stream2(reinterpret_cast<u32x2 *>(a.quant_out + base) + chunk, codes);
+        if ((lane & 3) == 0)
+            a.scale_out[swizzled_offset(row, chunk >> 2, a.padded_cols)] = (uint8_t)byte;
+    }
+}
+
+template <int K>
+hipError_t launch_k(const MxArgs &a, hipStream_t st)
+{
+    const int wpb = 4;
+    const dim3 grid((uint32_t)((a.rows_padded + wpb - 1) / wpb)), block(64u * wpb);
+    if (a.residual)
+        hipLaunchKernelGGL((mxfp8_kernel<K, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((mxfp8_kernel<K, false>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+}  // namespace qkvp
+
+extern "C" int64_t qkv_prep_mxfp8_scale_bytes(int64_t m, int32_t hidden)
+{
+    if (m < 0 || hidden <= 0 || hidden % 128)
+        return -1;
+    const int64_t cols = hidden / 32;
+    return (m + 127) / 128 * 128 * ((cols + 3) / 4 * 4);
+}
+
+extern "C" int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *a, void *stream)
+{
+    using namespace qkvp;
+    if (!a || a->m < 0 || !(a->eps >= 0.0f) || a->eps > 3.4e38f)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (a->hidden <= 0 || a->hidden % 512 || a->hidden > 8192)
+        return QKV_PREP_ERR_UNSUPPORTED;
+    if (a->m == 0)
+        return QKV_PREP_OK;
+    if (!a->x || !a->gamma || !a->quant_out || !a->scale_out)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (!aligned16(a->x) || !aligned16(a->gamma) || !aligned16(a->quant_out) ||
+        (a->residual && !aligned16(a->residual)) || (a->residual_out && !aligned16(a->residual_out)))
+        return QKV_PREP_ERR_MISALIGNED;
+    const int64_t rows_padded = (a->m + 127) / 128 * 128;
+    if (rows_padded * 64 >= ((int64_t)1 << 32))
+        return QKV_PREP_ERR_UNSUPPORTED;
+    MxArgs k;
+    k.x = static_cast<const uint16_t *>(a->x);
+    k.residual = static_cast<const uint16_t *>(a->residual);
+    k.residual_out = static_cast<uint16_t *>(a->residual_out);
+    k.gamma = static_cast<const uint16_t *>(a->gamma);
+    k.quant_out = static_cast<uint8_t *>(a->quant_out);
+    k.scale_out = static_cast<uint8_t *>(a->scale_out);
+    k.m = a->m;
+    k.rows_padded = rows_padded;
+    k.hidden = a->hidden;
+    k.padded_cols = (a->hidden / 32 + 3) / 4 * 4;
+    k.eps = a->eps;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (a->hidden / 512) {
+    case 1: e = launch_k<1>(k, st); break;
+    case 2: e = launch_k<2>(k, st); break;
+    case 3: e = launch_k<3>(k, st); break;
+    case 4: e = launch_k<4>(k, st); break;
+    case 5: e = launch_k<5>(k, st); break;
+    case 6: e = launch_k<6>(k, st); break;
+    case 7: e = launch_k<7>(k, st); break;
+    case 8: e = launch_k<8>(k, st); break;
+    case 9: e = launch_k<9>(k, st); break;
+    case 10: e = launch_k<10>(k, st); break;
+    case 11: e = launch_k<11>(k, st); break;
+    case 12: e = launch_k<12>(k, st); break;
+    case 13: e = launch_k<13>(k, st); break;
+    case 14: e = launch_k<14>(k, st); break;
+    case 15: e = launch_k<15>(k, st); break;
+    case 16: e = launch_k<16>(k, st); break;
+    default: return QKV_PREP_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? QKV_PREP_OK : QKV_PREP_ERR_LAUNCH;
+}

@@ -41,7 +41,8 @@ OUT_BF16 = 1
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("qkv_prep_create", "qkv_prep_run", "qkv_prep_destroy", "qkv_prep_supported",
             "qkv_prep_launch_shape", "qkv_prep_validate", "qkv_prep_strerror",
-            "qkv_prep_gather", "qkv_prep_probe_copy")
+            "qkv_prep_gather", "qkv_prep_probe_copy", "qkv_prep_mxfp8_norm_quant",
+            "qkv_prep_mxfp8_scale_bytes")
 
 
 class QkvPrepConfig(ctypes.Structure):
@@ -64,6 +65,13 @@ class QkvPrepGatherArgs(ctypes.Structure):
     _fields_ = [("kv_cache", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
                 ("slots", ctypes.c_void_p), ("n", ctypes.c_int64), ("out", ctypes.c_void_p),
                 ("out_dtype", ctypes.c_int32)]
+
+
+class QkvPrepMxfp8Args(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("residual_out", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("quant_out", ctypes.c_void_p), ("scale_out", ctypes.c_void_p),
+                ("m", ctypes.c_int64), ("hidden", ctypes.c_int32), ("eps", ctypes.c_float)]
 
 
 class QkvPrepLaunch(ctypes.Structure):
@@ -101,6 +109,10 @@ def _load():
     L.qkv_prep_strerror.restype = ctypes.c_char_p
     L.qkv_prep_gather.argtypes = [ctypes.c_void_p, P(QkvPrepGatherArgs), ctypes.c_void_p]
     L.qkv_prep_gather.restype = ctypes.c_int
+    L.qkv_prep_mxfp8_norm_quant.argtypes = [P(QkvPrepMxfp8Args), ctypes.c_void_p]
+    L.qkv_prep_mxfp8_norm_quant.restype = ctypes.c_int
+    L.qkv_prep_mxfp8_scale_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    L.qkv_prep_mxfp8_scale_bytes.restype = ctypes.c_int64
     L.qkv_prep_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_void_p]
     L.qkv_prep_probe_copy.restype = ctypes.c_int
@@ -164,6 +176,38 @@ def qkv_prep_gather(handle, args: QkvPrepGatherArgs, stream=None) -> None:
     rc = _lib.qkv_prep_gather(handle, ctypes.byref(args), stream)
     if rc != OK:
         raise QkvPrepError(rc, "qkv_prep_gather")
+
+
+def qkv_prep_mxfp8_scale_bytes(m: int, hidden: int) -> int:
+    return _lib.qkv_prep_mxfp8_scale_bytes(m, hidden)
+
+
+def qkv_prep_mxfp8_norm_quant(args: QkvPrepMxfp8Args, stream=None) -> None:
+    rc = _lib.qkv_prep_mxfp8_norm_quant(ctypes.byref(args), stream)
+    if rc != OK:
+        raise QkvPrepError(rc, "qkv_prep_mxfp8_norm_quant")
+
+
+def mxfp8_norm_quant(x, gamma, eps, *, residual=None, residual_out=None, quant_out=None,
+                     scale_out=None, stream=None):
+    """Torch wrapper of qkv_prep_mxfp8_norm_quant: x [m, hidden] bf16.  Returns
+    (codes uint8 [m, hidden], swizzled scales uint8 [...])."""
+    import torch
+    m, hidden = x.shape
+    for name, t in (("x", x), ("gamma", gamma), ("residual", residual), ("residual_out", residual_out)):
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
+            raise TypeError("%s must be a contiguous bfloat16 tensor" % name)
+    if quant_out is None:
+        quant_out = torch.empty((m, hidden), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        n = qkv_prep_mxfp8_scale_bytes(m, hidden)
+        scale_out = torch.empty(max(n, 0), dtype=torch.uint8, device=x.device)
+    args = QkvPrepMxfp8Args(x.data_ptr(), _ptr(residual), _ptr(residual_out), gamma.data_ptr(),
+                            quant_out.data_ptr(), scale_out.data_ptr(), m, hidden, eps)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    qkv_prep_mxfp8_norm_quant(args, stream)
+    return quant_out, scale_out
 
 
 def qkv_prep_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:

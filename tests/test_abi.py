@@ -19,7 +19,7 @@ def declared_functions():
     names = set()
     for h in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b(qkv_prep_[a-z_]+)\s*\(", text))
+        names |= set(re.findall(r"\b(qkv_prep_[a-z0-9_]+)\s*\(", text))
     return sorted(names)
 
 
@@ -38,6 +38,7 @@ def test_struct_sizes_match_the_header_layout():
     assert ctypes.sizeof(qp.QkvPrepArgs) == 88
     assert ctypes.sizeof(qp.QkvPrepLaunch) == 40
     assert ctypes.sizeof(qp.QkvPrepGatherArgs) == 48
+    assert ctypes.sizeof(qp.QkvPrepMxfp8Args) == 64
 
 
 def test_strerror_and_supported():
@@ -208,8 +209,10 @@ def test_ctypes_layout_matches_the_c_compiler(tmp_path):
     # offset with the ctypes mirror.
     import subprocess
     fields = {"qkv_prep_config": qp.QkvPrepConfig, "qkv_prep_args": qp.QkvPrepArgs,
-              "qkv_prep_launch": qp.QkvPrepLaunch, "qkv_prep_gather_args": qp.QkvPrepGatherArgs}
-    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "qkv_prep.h"', "int main(void){"]
+              "qkv_prep_launch": qp.QkvPrepLaunch, "qkv_prep_gather_args": qp.QkvPrepGatherArgs,
+              "qkv_prep_mxfp8_args": qp.QkvPrepMxfp8Args}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "qkv_prep.h"',
+             '#include "qkv_prep_mxfp8.h"', "int main(void){"]
     for cname, cls in fields.items():
         lines.append('printf("%%zu\\n", sizeof(%s));' % cname)
         for f, _ in cls._fields_:
@@ -226,3 +229,32 @@ def test_ctypes_layout_matches_the_c_compiler(tmp_path):
         want.append(ctypes.sizeof(cls))
         want += [getattr(cls, f).offset for f, _ in cls._fields_]
     assert got == want
+
+
+def test_mxfp8_scale_bytes_and_argument_checks():
+    assert qp.qkv_prep_mxfp8_scale_bytes(1, 512) == 128 * 16
+    assert qp.qkv_prep_mxfp8_scale_bytes(128, 7168) == 128 * 224
+    assert qp.qkv_prep_mxfp8_scale_bytes(129, 1024) == 256 * 32
+    assert qp.qkv_prep_mxfp8_scale_bytes(0, 512) == 0
+    assert qp.qkv_prep_mxfp8_scale_bytes(4, 96) == -1
+    good = dict(x=1 << 20, residual=None, residual_out=None, gamma=2 << 20, quant_out=3 << 20,
+                scale_out=4 << 20, m=4, hidden=1024, eps=1e-6)
+
+    def code(**kw):
+        d = dict(good)
+        d.update(kw)
+        a = qp.QkvPrepMxfp8Args(d["x"], d["residual"], d["residual_out"], d["gamma"],
+                                d["quant_out"], d["scale_out"], d["m"], d["hidden"], d["eps"])
+        return qp.library().qkv_prep_mxfp8_norm_quant(ctypes.byref(a), None)
+    assert code(m=0) == qp.OK
+    assert code(m=-1) == qp.ERR_INVALID_ARG
+    assert code(eps=-1.0) == qp.ERR_INVALID_ARG
+    assert code(x=None) == qp.ERR_INVALID_ARG
+    assert code(gamma=None) == qp.ERR_INVALID_ARG
+    assert code(scale_out=None) == qp.ERR_INVALID_ARG
+    assert code(hidden=768) == qp.ERR_UNSUPPORTED
+    assert code(hidden=8704) == qp.ERR_UNSUPPORTED
+    assert code(x=(1 << 20) + 2) == qp.ERR_MISALIGNED
+    assert code(residual=(5 << 20) + 4) == qp.ERR_MISALIGNED
+    assert code(residual_out=(6 << 20) + 8) == qp.ERR_MISALIGNED
+    assert code(m=1 << 26) == qp.ERR_UNSUPPORTED

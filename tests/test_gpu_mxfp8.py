@@ -1,0 +1,69 @@
+"""GPU check of the MXFP8 norm-quant operator (include/qkv_prep_mxfp8.h)
+against the oracle: every code, every swizzled scale byte (the scale buffer is
+poisoned first, so a byte written twice, missed or outside the layout shows)
+and the residual output."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_kv_cache_amd import qkv_prep as qp
+from fp8_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def draw(m, hidden, seed, scale=1.0):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    x = (scale * torch.randn((m, hidden), generator=g, device=DEV)).to(torch.bfloat16)
+    r = (0.5 * torch.randn((m, hidden), generator=g, device=DEV)).to(torch.bfloat16)
+    gamma = (0.1 * torch.randn(hidden, generator=g, device=DEV)).to(torch.bfloat16)
+    return x, r, gamma
+
+
+@pytest.mark.parametrize("m,hidden,with_res,with_out", [
+    (1, 512, False, False), (5, 1024, True, True), (127, 1536, True, False),
+    (128, 4096, False, True), (300, 7168, True, True), (129, 8192, True, True),
+    (64, 2560, False, False), (1000, 3072, True, True)])
+def test_mxfp8_matches_the_oracle(m, hidden, with_res, with_out):
+    x, r, gamma = draw(m, hidden, 900 + m + hidden)
+    eps = 1e-6
+    nbytes = qp.qkv_prep_mxfp8_scale_bytes(m, hidden)
+    scales = torch.full((nbytes,), 0xEE, dtype=torch.uint8, device=DEV)
+    codes = torch.full((m, hidden), 0xEE, dtype=torch.uint8, device=DEV)
+    res_out = torch.full((m, hidden), float("nan"), dtype=torch.bfloat16, device=DEV) if with_out else None
+    qp.mxfp8_norm_quant(x, gamma, eps, residual=r if with_res else None, residual_out=res_out,
+                        quant_out=codes, scale_out=scales)
+    torch.cuda.synchronize()
+    want_codes, want_scales, want_pre = oracle.mxfp8_norm_quant(
+        W.as_u16(x), W.as_u16(gamma), eps, residual=W.as_u16(r) if with_res else None)
+    got_codes = codes.cpu().numpy()
+    got_scales = scales.cpu().numpy()
+    assert np.array_equal(got_scales, want_scales), np.count_nonzero(got_scales != want_scales)
+    d = np.abs(oracle.e4m3_to_f64(got_codes) - oracle.e4m3_to_f64(want_codes))
+    assert np.count_nonzero(got_codes != want_codes) == 0, int(np.count_nonzero(got_codes != want_codes))
+    if with_out:
+        want = want_pre if with_res else W.as_u16(x)
+        assert np.array_equal(W.as_u16(res_out), want)
+
+
+def test_mxfp8_outlier_rows_and_zero_rows():
+    m, hidden = 256, 2048
+    x, r, gamma = draw(m, hidden, 950, scale=1.0)
+    x[3] *= 1000.0
+    x[7] = 0.0
+    eps = 1e-5
+    codes, scales = qp.mxfp8_norm_quant(x, gamma, eps)
+    torch.cuda.synchronize()
+    wc, ws, _ = oracle.mxfp8_norm_quant(W.as_u16(x), W.as_u16(gamma), eps)
+    assert np.array_equal(codes.cpu().numpy(), wc)
+    assert np.array_equal(scales.cpu().numpy(), ws)
+
+
+def test_mxfp8_empty_is_a_no_op():
+    x = torch.zeros((0, 512), dtype=torch.bfloat16, device=DEV)
+    gamma = torch.zeros(512, dtype=torch.bfloat16, device=DEV)
+    codes, scales = qp.mxfp8_norm_quant(x, gamma, 1e-6)
+    assert codes.numel() == 0 and scales.numel() == 0
