@@ -114,9 +114,9 @@ def time_launches(torch, fn, steps):
 
 
 def bench_variants(torch, W, qp, steps, warmup):
-    """The two neighbouring paths on the Prefill workload: the bf16-store cache
-    mode (1024-byte slots, no quantization) and the cache reader gathering all
-    32768 slots back to bf16."""
+    """The neighbouring paths: on the Prefill workload the bf16-store cache mode
+    (1024-byte slots, no quantization) and the cache reader gathering all 32768
+    slots back to bf16; and the MXFP8 norm-quant operator on 16384 x 7168."""
     out = {}
     w = W.WORKLOADS["prefill"]
     inp = W.make_inputs(w, device="cuda")
@@ -143,6 +143,27 @@ def bench_variants(torch, W, qp, steps, warmup):
                                       "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2),
                                       "bytes_per_launch": nbytes}
     del inp, args, cache16, rows
+    torch.cuda.empty_cache()
+    # MXFP8 norm-quant: 16384 rows of 7168 (a DeepSeek-sized hidden state),
+    # with the residual add and the residual output.
+    m, hidden = 16384, 7168
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    x = torch.randn((m, hidden), generator=gen, device="cuda").to(torch.bfloat16)
+    r = torch.randn((m, hidden), generator=gen, device="cuda").to(torch.bfloat16)
+    gamma = (0.1 * torch.randn(hidden, generator=gen, device="cuda")).to(torch.bfloat16)
+    res_out = torch.empty_like(x)
+    codes = torch.empty((m, hidden), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(qp.qkv_prep_mxfp8_scale_bytes(m, hidden), dtype=torch.uint8, device="cuda")
+    f = lambda: qp.mxfp8_norm_quant(x, gamma, 1e-6, residual=r, residual_out=res_out,
+                                    quant_out=codes, scale_out=scales)
+    for _ in range(warmup):
+        f()
+    ks, wall = time_launches(torch, f, steps)
+    nbytes = m * hidden * (2 + 2 + 2 + 1) + scales.numel() + 2 * hidden
+    out["mxfp8_norm_quant 16384x7168 (+residual)"] = {
+        "gbps": round(nbytes * steps / wall / 1e9, 1),
+        "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2), "bytes_per_launch": nbytes}
+    del x, r, res_out, codes, scales
     torch.cuda.empty_cache()
     return out
 
@@ -253,7 +274,6 @@ def cpu_baseline(torch, W, name, target_s=12.0, sample_tokens=4096):
 def recorded_traffic(workload_label):
     """HBM bytes per dispatch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source (else None)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "qkv_prep_counters_%s.txt" % workload_label.replace(" ", "_"))
     if not os.path.exists(path):
         return None
@@ -264,9 +284,8 @@ def recorded_traffic(workload_label):
                 rec = json.loads(line)
     if not rec:
         return None
-    src = os.path.join(ROOT, "fp8_kv_cache_amd", "csrc", "qkv_prep_kernels.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if rec.get("kernel_sha") != sha:
+    from fp8_kv_cache_amd.rocprof_harness import kernel_sha
+    if rec.get("kernel_sha") != kernel_sha():
         return None
     return rec.get("hbm_bytes_per_dispatch")
 

@@ -32,14 +32,20 @@ import time
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-KERNEL_SRC = os.path.join(PKG, "csrc", "qkv_prep_kernels.hip")
+# The sources that define the operator's kernel; the counter summaries carry
+# their hash so that a stale summary is never reported as current.
+KERNEL_SRCS = [os.path.join(PKG, "csrc", f) for f in
+               ("qkv_prep_kernels.hip", "qkvp_device.h", "qkv_prep_internal.h")]
 OP_KERNEL = "qkv_prep_kernel"
 COPY_KERNEL = "stream_copy"
 COPY_BYTES = 512 << 20
 
 
 def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def log(msg):
