@@ -1,12 +1,14 @@
 // Residual add + Gemma RMSNorm + MXFP8 quantization for gfx950 (the second
-// operator of include/qkv_prep_mxfp8.h).  One wavefront per row: lane l holds
-// the 16-byte chunks l, l + 64, ..., l + 64 (K - 1) (K = hidden / 512), so every
-// load and store instruction of the wavefront is one contiguous 1 KiB segment.
-// The six in-wavefront tree levels reduce each aligned group of 64 chunks
-// (the same DPP + permlane order as the main operator); the K group sums are
-// then added in-lane in adjacent pairs with the odd one carried, which is the
-// numerics contract's order.  A 32-element scale block is 4 consecutive chunks
-// held by 4 consecutive lanes, so its amax is two DPP max steps.
+// operator of include/qkv_prep_mxfp8.h).  A workgroup takes one row of
+// K = hidden / 512 groups of 64 16-byte chunks; each wavefront holds G groups
+// (G = 2, or 1 for odd K), lane l holding chunk l of each, so every load and
+// store instruction is one coalesced 1 KiB segment.  Each wavefront reduces
+// its groups with the same DPP + permlane order as the main operator and
+// leaves the group sums in LDS; after one barrier every wavefront adds the K
+// group sums in adjacent pairs, carrying an odd last one (the numerics
+// contract's order), so all of them hold the same bits.  A 32-element scale
+// block is 4 consecutive chunks held by 4 consecutive lanes, so its amax is
+// two DPP max steps.
 #include "qkvp_device.h"
 #include "qkv_prep.h"
 #include "qkv_prep_mxfp8.h"
@@ -54,27 +56,29 @@ __device__ __forceinline__ uint32_t max4(uint32_t v)
     return v;
 }
 
-template <int K, bool HAS_RES>
-__global__ __launch_bounds__(256) void mxfp8_kernel(MxArgs a)
+// G groups of 64 chunks per wavefront, K / G wavefronts per row.
+template <int K, int G, bool HAS_RES>
+__global__ __launch_bounds__(1024) void mxfp8_kernel(MxArgs a)
 {
+    static_assert(K % G == 0, "groups must split evenly over the wavefronts");
+    __shared__ float group_sum[K];
     const uint32_t lane = threadIdx.x & 63u;
-    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (row >= a.rows_padded)
-        return;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row = blockIdx.x;
     if (row >= a.m) {
         // Padding rows of the last 128-row tile: zero scale bytes.
-        for (int c = lane; c < a.padded_cols; c += 64)
+        for (int c = threadIdx.x; c < a.padded_cols; c += blockDim.x)
             a.scale_out[swizzled_offset(row, c, a.padded_cols)] = 0;
         return;
     }
-    const int64_t base = row * a.hidden;
-    u32x4 p[K];
+    const int64_t rbase = row * a.hidden;
+    u32x4 p[G];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-        const int64_t e0 = base + 8 * (lane + 64 * j);
-        const u32x4 xv = load_stream(reinterpret_cast<const u32x4 *>(a.x + e0));
+    for (int j = 0; j < G; ++j) {
+        const int chunk = (int)((w * G + j) * 64 + lane);
+        const u32x4 xv = load_stream(reinterpret_cast<const u32x4 *>(a.x + rbase) + chunk);
         if constexpr (HAS_RES) {
-            const u32x4 rv = load_stream(reinterpret_cast<const u32x4 *>(a.residual + e0));
+            const u32x4 rv = load_stream(reinterpret_cast<const u32x4 *>(a.residual + rbase) + chunk);
             float xf[8], rf[8], sf[8];
             unpack_bf16x8(xv, xf);
             unpack_bf16x8(rv, rf);
@@ -88,15 +92,12 @@ __global__ __launch_bounds__(256) void mxfp8_kernel(MxArgs a)
     }
     if (a.residual_out) {
 #pragma unroll
-        for (int j = 0; j < K; ++j)
-            store_stream(reinterpret_cast<u32x4 *>(a.residual_out + base + 8 * (lane + 64 * j)), p[j]);
+        for (int j = 0; j < G; ++j)
+            store_stream(reinterpret_cast<u32x4 *>(a.residual_out + rbase) + (w * G + j) * 64 + lane, p[j]);
     }
-
-    // Sum of squares: each aligned group of 64 chunks in the wavefront, then
-    // the K group sums in adjacent pairs, carrying an odd last one.
     float g[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
+    for (int j = 0; j < G; ++j) {
         float x[8];
         unpack_bf16x8(p[j], x);
         float acc = 0.0f;
@@ -104,6 +105,18 @@ __global__ __launch_bounds__(256) void mxfp8_kernel(MxArgs a)
         for (int e = 0; e < 8; ++e)
             acc = __builtin_fmaf(x[e], x[e], acc);
         g[j] = wave_sum_ordered(acc);
+    }
+    if constexpr (K != G) {
+        // Several wavefronts per row: exchange the group sums through LDS.
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                group_sum[w * G + j] = g[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            g[j] = group_sum[j];
     }
 #pragma unroll
     for (int n = K; n > 1; n = (n + 1) / 2) {
@@ -116,17 +129,15 @@ __global__ __launch_bounds__(256) void mxfp8_kernel(MxArgs a)
     const float inv = 1.0f / __builtin_sqrtf(g[0] / (float)a.hidden + a.eps);
     const float inv448 = 1.0f / 448.0f;
 
-    float gm[8];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-        const int chunk = lane + 64 * j;
-        unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.gamma)[chunk], gm);
-        float x[8], nv[8];
+    for (int j = 0; j < G; ++j) {
+        const int chunk = (int)((w * G + j) * 64 + lane);
+        float x[8], gm[8], nv[8], n[8];
         unpack_bf16x8(p[j], x);
+        unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.gamma)[chunk], gm);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             nv[e] = (x[e] * inv) * (gm[e] + 1.0f);
-        float n[8];
         unpack_bf16x8(pack_bf16x8<true>(nv), n);          // rounded to bf16
         uint32_t mx = 0;
 #pragma unroll
@@ -141,21 +152,28 @@ __global__ __launch_bounds__(256) void mxfp8_kernel(MxArgs a)
         for (int e = 0; e < 8; ++e)
             q[e] = fminf(fmaxf(n[e] * inverse, -448.0f), 448.0f);
         const u32x2 codes = {pack_e4m3<true>(q[0], q[1], q[2], q[3]), pack_e4m3<true>(q[4], q[5], q[6], q[7])};
-        store_stream2(reinterpret_cast<u32x2 *>(a.quant_out + base) + chunk, codes);
+        store_stream2(reinterpret_cast<u32x2 *>(a.quant_out + rbase) + chunk, codes);
         if ((lane & 3) == 0)
             a.scale_out[swizzled_offset(row, chunk >> 2, a.padded_cols)] = (uint8_t)byte;
     }
 }
 
+// Groups of 64 chunks per wavefront for a row of K groups.  Measured on
+// MI355X at hidden 1024-8192 (two interleaved rounds): two groups per
+// wavefront (K/2 wavefronts per row) is the fastest or tied everywhere; one
+// group per wavefront is within 2%; one wavefront per row loses up to 60% at
+// large K (VGPR pressure).  Odd K uses one group per wavefront.
+constexpr int groups_per_wave(int K) { return K % 2 == 0 ? 2 : 1; }
+
 template <int K>
 hipError_t launch_k(const MxArgs &a, hipStream_t st)
 {
-    const int wpb = 4;
-    const dim3 grid((uint32_t)((a.rows_padded + wpb - 1) / wpb)), block(64u * wpb);
+    constexpr int G = groups_per_wave(K);
+    const dim3 grid((uint32_t)a.rows_padded), block(64u * (K / G));
     if (a.residual)
-        hipLaunchKernelGGL((mxfp8_kernel<K, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((mxfp8_kernel<K, G, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((mxfp8_kernel<K, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((mxfp8_kernel<K, G, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -187,7 +205,7 @@ extern "C" int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *a, void *str
         (a->residual && !aligned16(a->residual)) || (a->residual_out && !aligned16(a->residual_out)))
         return QKV_PREP_ERR_MISALIGNED;
     const int64_t rows_padded = (a->m + 127) / 128 * 128;
-    if (rows_padded * 64 >= ((int64_t)1 << 32))
+    if (rows_padded >= ((int64_t)1 << 31) || rows_padded * a->hidden / 8 >= ((int64_t)1 << 32))
         return QKV_PREP_ERR_UNSUPPORTED;
     MxArgs k;
     k.x = static_cast<const uint16_t *>(a->x);
