@@ -113,10 +113,32 @@ def time_launches(torch, fn, steps):
     return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events], wall
 
 
+def time_cold(torch, fn, reps, scratch):
+    """Per-launch HIP-event durations with L2 and the MALL flushed before each
+    launch: a 1 GiB scratch write, on the same stream and outside the events."""
+    stream = torch.cuda.current_stream()
+    out = []
+    for k in range(reps):
+        scratch.fill_(k & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        out.append((e0, e1))
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in out]
+
+
+def p90(xs):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(0.9 * len(xs)))]
+
+
 def bench_variants(torch, W, qp, steps, warmup):
     """The neighbouring paths: on the Prefill workload the bf16-store cache mode
-    (1024-byte slots, no quantization) and the cache reader gathering all 32768
-    slots back to bf16; and the MXFP8 norm-quant operator on 16384 x 7168."""
+    (1024-byte slots, no quantization); the cache reader gathering every slot of
+    a 4096 x 64-slot cache (262144 rows, in a random order) to bf16 and to fp32;
+    and the MXFP8 norm-quant operator on 16384 x 7168."""
     out = {}
     w = W.WORKLOADS["prefill"]
     inp = W.make_inputs(w, device="cuda")
@@ -131,18 +153,30 @@ def bench_variants(torch, W, qp, steps, warmup):
     out["bf16_store prefill 32768x64"] = {"gbps": round(nbytes * steps / wall / 1e9, 1),
                                           "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2),
                                           "bytes_per_launch": nbytes}
-    op8 = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
-    op8(*args[:-1], inp["cache"])
-    rows = torch.empty((w.num_tokens, 512), dtype=torch.bfloat16, device="cuda")
-    g = lambda: op8.gather(inp["cache"], inp["slot_mapping"], rows)
-    for _ in range(warmup):
-        g()
-    ks, wall = time_launches(torch, g, steps)
-    nbytes = W.gather_bytes(w.num_tokens, w.num_tokens, 2)
-    out["gather bf16 32768 slots"] = {"gbps": round(nbytes * steps / wall / 1e9, 1),
-                                      "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2),
-                                      "bytes_per_launch": nbytes}
-    del inp, args, cache16, rows
+    del inp, args, cache16
+    torch.cuda.empty_cache()
+    # The cache reader over a whole cache: the Decode-like cache, 4096 blocks
+    # of 64 slots, every slot read once in a random order.
+    wd = W.WORKLOADS["decode"]
+    cap = wd.num_blocks * wd.block_size
+    gen = torch.Generator(device="cuda").manual_seed(78)
+    cache = torch.randint(0, 256, (wd.num_blocks, wd.block_size * W.SLOT_BYTES), dtype=torch.uint8,
+                          device="cuda", generator=gen)
+    cache.view(wd.num_blocks, -1)[:, wd.block_size * 576:].zero_()    # finite scales (bytes 0)
+    slots = torch.randperm(cap, device="cuda", generator=gen).to(torch.int64)
+    opd = qp.QkvPrep(wd.num_heads, block_size=wd.block_size, eps=wd.eps)
+    for dtype, nb in ((torch.bfloat16, 2), (torch.float32, 4)):
+        rows = torch.empty((cap, 512), dtype=dtype, device="cuda")
+        g = lambda: opd.gather(cache, slots, rows)
+        for _ in range(warmup):
+            g()
+        ks, wall = time_launches(torch, g, steps)
+        nbytes = W.gather_bytes(cap, cap, nb)
+        out["gather %s %d slots" % (str(dtype).split(".")[1], cap)] = {
+            "gbps": round(nbytes * steps / wall / 1e9, 1),
+            "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2), "bytes_per_launch": nbytes}
+        del rows
+    del cache, slots
     torch.cuda.empty_cache()
     # MXFP8 norm-quant: 16384 rows of 7168 (a DeepSeek-sized hidden state),
     # with the residual add and the residual output.
@@ -185,6 +219,10 @@ def bench_workload(torch, W, qp, name, steps, warmup):
     torch.cuda.synchronize()
     log("bench: %s timing %d steps" % (w.label, steps))
     kernel_s, wall = time_launches(torch, lambda: op(*args), steps)
+    log("bench: %s cold-cache launches" % w.label)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold_s = time_cold(torch, lambda: op(*args), min(steps, 10), scratch)
+    del scratch
     res = {
         "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
         "bytes_per_step": nbytes,
@@ -192,6 +230,9 @@ def bench_workload(torch, W, qp, name, steps, warmup):
         "kernel_s_mean": statistics.fmean(kernel_s),
         "kernel_s_median": statistics.median(kernel_s),
         "kernel_s_min": min(kernel_s),
+        "kernel_s_p90": p90(kernel_s),
+        "kernel_s_median_cold": statistics.median(cold_s),
+        "kernel_s_p90_cold": p90(cold_s),
         "launch": {"rows_per_wave": shape.rows_per_wave, "waves_per_block": shape.waves_per_block,
                    "convert": shape.convert, "grid": shape.grid},
         "valid_slots": valid,
@@ -393,6 +434,8 @@ def main():
                      "traffic": traffic, "kernel": KERNEL_NAME,
                      "kernel_us_mean": round(main_res["kernel_s_mean"] * 1e6, 2),
                      "bytes_per_launch": main_res["bytes_per_step"]},
+        "kernel_us": {k: round(main_res["kernel_s_" + k] * 1e6, 2)
+                      for k in ("median", "min", "p90", "median_cold", "p90_cold")},
         "known_answer_before_after": [kat_before, kat_after],
     }
     if also:
@@ -401,6 +444,8 @@ def main():
                        "ms_per_step": round(also["wall_s_per_step"] * 1e3, 4),
                        "frac_of_peak": round(also["gbps_wall"] / PEAK_HBM_GBPS, 4),
                        "frac_of_copy": round(also["gbps_wall"] / ceiling, 4) if ceiling else None,
+                       "kernel_us": {k: round(also["kernel_s_" + k] * 1e6, 2)
+                                     for k in ("median", "min", "p90", "median_cold", "p90_cold")},
                        "launch": also["launch"], "bytes_per_step": also["bytes_per_step"]}
     if variants:
         out["variants"] = variants

@@ -1,0 +1,125 @@
+// Cache reader for the FP8 + UE8M0 paged cache written by qkv_prep_kernel:
+// dequantize and gather slots back into fp32 or bf16 rows (the cache layout is
+// the one stated in include/qkv_prep.h).  HBM bound: 584 bytes read and 1 or
+// 2 KiB written per row, one wavefront per row, non-temporal stores.
+#include "qkvp_device.h"
+
+namespace qkvp {
+namespace {
+
+using namespace dev;
+
+constexpr int kRopeLane = kNopeDim / 8;  // lanes 56..63 hold the rope chunks
+
+// code * 2^(b - 127) is exact in fp32 (E4M3 has 4 significant bits; 2^-127,
+// the scale of byte 0, is the fp32 subnormal 0x00400000).
+__device__ __forceinline__ float scale_of_byte(uint32_t b)
+{
+    return __uint_as_float(b ? (b << 23) : 0x00400000u);
+}
+
+// Four E4M3 codes (byte k of `codes` is dim k) times a power-of-two scale.
+__device__ __forceinline__ u32x4 dequant4(uint32_t codes, float scale)
+{
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
+    return u32x4{__float_as_uint(lo[0] * scale), __float_as_uint(lo[1] * scale),
+                 __float_as_uint(hi[0] * scale), __float_as_uint(hi[1] * scale)};
+}
+
+// bf16 rows: one wavefront per output row.  Lane l < 56 reads the 8 codes of
+// dims 8l..8l+7 and the scale byte of their block; lanes 56..63 read 16 bytes
+// of rope bf16; each lane stores its 16 output bytes, so the wavefront's one
+// store covers the 1 KiB row.
+__device__ __forceinline__ void gather_row_bf16(const GatherArgs &a, int64_t i, uint32_t lane)
+{
+    const int64_t slot = a.slots[i];
+    float v[8];
+    if (slot < 0 || slot >= a.num_slots) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = 0.0f;
+    } else {
+        const uint32_t s32 = (uint32_t)slot;
+        const uint32_t blk = fastdiv(s32, a.blocks);
+        const uint32_t sib = s32 - blk * a.block_size;
+        const uint8_t *base = a.cache + (int64_t)blk * a.block_size * kSlotBytes;
+        const uint8_t *data = base + (int64_t)sib * kSlotData;
+        if (lane < kRopeLane) {
+            const u32x2 codes = *(reinterpret_cast<const u32x2 *>(data) + lane);
+            const uint32_t b = base[(int64_t)a.block_size * kSlotData + (int64_t)sib * kSlotScale + lane / 8];
+            const float scale = scale_of_byte(b);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 d = dequant4(codes[h], scale);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[4 * h + e] = __uint_as_float(d[e]);
+            }
+        } else {
+            unpack_bf16x8(*(reinterpret_cast<const u32x4 *>(data + kNopeDim) + (lane - kRopeLane)), v);
+        }
+    }
+    store_stream(reinterpret_cast<u32x4 *>(a.out) + i * 64 + lane, pack_bf16x8<true>(v));
+}
+
+// fp32 rows (2 KiB): lane l owns dims 4l..4l+3 and 256+4l..256+4l+3, so each
+// of the wavefront's two 16-byte stores covers 1 KiB of the row contiguously.
+// Dims 4l.. sit in quantization block l/16 (0..3); dims 256+4l.. in block
+// 4 + l/16 for l < 48, and are rope dims 448 + 4(l - 48).. for l >= 48.  Every
+// lane reads the slot's 8-byte scale record (one broadcast load).
+__device__ __forceinline__ void gather_row_f32(const GatherArgs &a, int64_t i, uint32_t lane)
+{
+    const int64_t slot = a.slots[i];
+    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    if (slot >= 0 && slot < a.num_slots) {
+        const uint32_t s32 = (uint32_t)slot;
+        const uint32_t blk = fastdiv(s32, a.blocks);
+        const uint32_t sib = s32 - blk * a.block_size;
+        const uint8_t *base = a.cache + (int64_t)blk * a.block_size * kSlotBytes;
+        const uint8_t *data = base + (int64_t)sib * kSlotData;
+        const u32x2 rec = *reinterpret_cast<const u32x2 *>(base + (int64_t)a.block_size * kSlotData +
+                                                          (int64_t)sib * kSlotScale);
+        const uint32_t shift = 8u * (lane >> 4);
+        lo = dequant4(reinterpret_cast<const uint32_t *>(data)[lane], scale_of_byte((rec[0] >> shift) & 0xffu));
+        if (lane < 48) {
+            hi = dequant4(reinterpret_cast<const uint32_t *>(data + 256)[lane],
+                          scale_of_byte((rec[1] >> shift) & 0xffu));
+        } else {
+            const u32x2 r = reinterpret_cast<const u32x2 *>(data + kNopeDim)[lane - 48];
+            hi = u32x4{r[0] << 16, r[0] & 0xffff0000u, r[1] << 16, r[1] & 0xffff0000u};
+        }
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.out) + i * 128;
+    store_stream(dst + lane, lo);
+    store_stream(dst + 64 + lane, hi);
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(512) void gather_kernel(GatherArgs a)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t i = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+    if (i < a.n) {
+        if constexpr (OUT_BF16)
+            gather_row_bf16(a, i, lane);
+        else
+            gather_row_f32(a, i, lane);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather(const GatherArgs &a, int waves_per_block, hipStream_t stream)
+{
+    const int64_t blocks = (a.n + waves_per_block - 1) / waves_per_block;
+    const dim3 grid((uint32_t)blocks), block(64u * (uint32_t)waves_per_block);
+    if (a.out_bf16)
+        hipLaunchKernelGGL(gather_kernel<true>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(gather_kernel<false>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace qkvp

@@ -200,65 +200,6 @@ __device__ __forceinline__ void kv_row(const KernelArgs &a, int64_t t, uint32_t 
                       u32x2{rec0, rec1});
 }
 
-// ------------------------------------------------------------------ reader
-
-// One wavefront per output row.  Lane l < 56 reads the 8 codes of dims
-// 8l..8l+7 and the scale byte of their block; lanes 56..63 read 16 bytes of
-// rope bf16.  code * 2^(b - 127) is exact in fp32 (E4M3 has 4 significant
-// bits; 2^-127, the scale of byte 0, is the fp32 subnormal 0x00400000).
-template <bool OUT_BF16>
-__device__ __forceinline__ void gather_row(const GatherArgs &a, int64_t i, uint32_t lane)
-{
-    const int64_t slot = a.slots[i];
-    float v[8];
-    if (slot < 0 || slot >= a.num_slots) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = 0.0f;
-    } else {
-        const uint32_t s32 = (uint32_t)slot;
-        const uint32_t blk = fastdiv(s32, a.blocks);
-        const uint32_t sib = s32 - blk * a.block_size;
-        const uint8_t *base = a.cache + (int64_t)blk * a.block_size * kSlotBytes;
-        const uint8_t *data = base + (int64_t)sib * kSlotData;
-        if (lane < kRopeLane) {
-            const u32x2 codes = *(reinterpret_cast<const u32x2 *>(data) + lane);
-            const uint32_t b = base[(int64_t)a.block_size * kSlotData + (int64_t)sib * kSlotScale + lane / 8];
-            const float scale = __uint_as_float(b ? (b << 23) : 0x00400000u);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(codes[h], false);
-                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(codes[h], true);
-                v[4 * h + 0] = lo[0] * scale;
-                v[4 * h + 1] = lo[1] * scale;
-                v[4 * h + 2] = hi[0] * scale;
-                v[4 * h + 3] = hi[1] * scale;
-            }
-        } else {
-            unpack_bf16x8(*(reinterpret_cast<const u32x4 *>(data + kNopeDim) + (lane - kRopeLane)), v);
-        }
-    }
-    if constexpr (OUT_BF16) {
-        store_stream(reinterpret_cast<u32x4 *>(a.out) + i * 64 + lane, pack_bf16x8<true>(v));
-    } else {
-        u32x4 *dst = reinterpret_cast<u32x4 *>(a.out) + i * 128 + 2 * lane;
-        store_stream(dst, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                __float_as_uint(v[3])});
-        store_stream(dst + 1, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
-                                    __float_as_uint(v[7])});
-    }
-}
-
-template <bool OUT_BF16>
-__global__ __launch_bounds__(512) void gather_kernel(GatherArgs a)
-{
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t i = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
-    if (i < a.n)
-        gather_row<OUT_BF16>(a, i, lane);
-}
-
 // ------------------------------------------------------------------ kernel
 
 template <int U, bool HAS_W, bool HW>
@@ -297,17 +238,6 @@ hipError_t launch_u(const KernelArgs &a, bool has_w, bool hw, dim3 grid, dim3 bl
 }
 
 }  // namespace
-
-hipError_t launch_gather(const GatherArgs &a, int waves_per_block, hipStream_t stream)
-{
-    const int64_t blocks = (a.n + waves_per_block - 1) / waves_per_block;
-    const dim3 grid((uint32_t)blocks), block(64u * (uint32_t)waves_per_block);
-    if (a.out_bf16)
-        hipLaunchKernelGGL(gather_kernel<true>, grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL(gather_kernel<false>, grid, block, 0, stream, a);
-    return hipGetLastError();
-}
 
 hipError_t launch_qkv_prep(const KernelArgs &a, const LaunchShape &s, hipStream_t stream)
 {

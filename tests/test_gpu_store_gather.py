@@ -115,3 +115,39 @@ def test_gather_empty_and_bad_arguments():
     assert e.value.code == qp.ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+def _nan_aware_equal(got_bits, want_bits, nan_mask_got, nan_mask_want):
+    """Equal bit patterns, except that a NaN may carry any payload."""
+    return np.array_equal(nan_mask_got, nan_mask_want) and \
+        np.array_equal(got_bits[~nan_mask_want], want_bits[~nan_mask_want])
+
+
+@pytest.mark.parametrize("bs,nb", [(64, 96), (7, 300)])
+def test_gather_arbitrary_cache_bytes(bs, nb):
+    # Every byte of the cache random: all 256 codes (NaN codes 0x7f/0xff
+    # included), every scale byte 0..254 and random rope bf16.  Every slot is
+    # read once in a random order, plus invalid slots.
+    note("gather arbitrary bytes: block_size %d, %d blocks" % (bs, nb))
+    rng = np.random.default_rng(720 + bs)
+    host = rng.integers(0, 256, (nb, bs * W.SLOT_BYTES), dtype=np.uint8)
+    host[:, bs * 576:] = rng.integers(0, 255, (nb, bs * 8), dtype=np.uint8)   # scale bytes <= 254
+    cap = nb * bs
+    probe = np.concatenate([rng.permutation(cap), [-1, cap, -5, cap + 1]]).astype(np.int64)
+    want = oracle.gather_dequant(host, nb, bs, probe)
+    cache = torch.from_numpy(host).to(DEV)
+    slots = torch.from_numpy(probe).to(DEV)
+    op = qp.QkvPrep(8, block_size=bs)
+    out32 = torch.full((probe.size, 512), 7.0, dtype=torch.float32, device=DEV)
+    out16 = torch.full((probe.size, 512), 7.0, dtype=torch.bfloat16, device=DEV)
+    op.gather(cache, slots, out32)
+    op.gather(cache, slots, out16)
+    torch.cuda.synchronize()
+    got32 = out32.cpu().numpy()
+    assert np.isnan(want).any() and np.isinf(want).any()        # the odd values are exercised
+    assert _nan_aware_equal(got32.view(np.uint32), want.view(np.uint32), np.isnan(got32), np.isnan(want))
+    got16 = W.as_u16(out16)
+    want16 = oracle.f32_to_bf16(want)
+    is_nan16 = lambda u: ((u & 0x7F80) == 0x7F80) & ((u & 0x007F) != 0)
+    assert _nan_aware_equal(got16, want16, is_nan16(got16), np.isnan(want))
+    assert np.all(got32[cap:] == 0) and np.all(got16[cap:] == 0)
