@@ -134,71 +134,34 @@ def p90(xs):
     return xs[min(len(xs) - 1, int(0.9 * len(xs)))]
 
 
-def bench_variants(torch, W, qp, steps, warmup):
-    """The neighbouring paths: on the Prefill workload the bf16-store cache mode
-    (1024-byte slots, no quantization); the cache reader gathering every slot of
-    a 4096 x 64-slot cache (262144 rows, in a random order) to bf16 and to fp32;
-    and the MXFP8 norm-quant operator on 16384 x 7168."""
+def bench_variants(torch, qp, steps, warmup):
+    """The neighbouring paths, each timed like the operator: the bf16-store cache
+    mode on the Prefill workload (1024-byte slots, no quantization); the cache
+    reader gathering every slot of a 4096 x 64-slot cache (262144 rows) to bf16
+    and to fp32 as a block-table walk, and to fp32 in a fully random slot order;
+    and the MXFP8 norm-quant operator on 16384 x 7168 with the residual add and
+    the residual output."""
+    from fp8_kv_cache_amd import variants as V
     out = {}
-    w = W.WORKLOADS["prefill"]
-    inp = W.make_inputs(w, device="cuda")
-    cache16 = torch.zeros((w.num_blocks, w.block_size * 1024), dtype=torch.uint8, device="cuda")
-    op16 = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps, kv_store=qp.KV_BF16)
-    args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
-            inp["slot_mapping"], cache16)
-    for _ in range(warmup):
-        op16(*args)
-    ks, wall = time_launches(torch, lambda: op16(*args), steps)
-    nbytes = W.algorithmic_bytes(w.num_tokens, w.num_heads, w.num_tokens, slot_bytes=1024)
-    out["bf16_store prefill 32768x64"] = {"gbps": round(nbytes * steps / wall / 1e9, 1),
-                                          "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2),
-                                          "bytes_per_launch": nbytes}
-    del inp, args, cache16
-    torch.cuda.empty_cache()
-    # The cache reader over a whole cache: the Decode-like cache, 4096 blocks
-    # of 64 slots, every slot read once in a random order.
-    wd = W.WORKLOADS["decode"]
-    cap = wd.num_blocks * wd.block_size
-    gen = torch.Generator(device="cuda").manual_seed(78)
-    cache = torch.randint(0, 256, (wd.num_blocks, wd.block_size * W.SLOT_BYTES), dtype=torch.uint8,
-                          device="cuda", generator=gen)
-    cache.view(wd.num_blocks, -1)[:, wd.block_size * 576:].zero_()    # finite scales (bytes 0)
-    slots = torch.randperm(cap, device="cuda", generator=gen).to(torch.int64)
-    opd = qp.QkvPrep(wd.num_heads, block_size=wd.block_size, eps=wd.eps)
-    for dtype, nb in ((torch.bfloat16, 2), (torch.float32, 4)):
-        rows = torch.empty((cap, 512), dtype=dtype, device="cuda")
-        g = lambda: opd.gather(cache, slots, rows)
+    for name in V.VARIANTS:
+        t = V.target(name)
+        log("bench: variant %s" % t.label)
+        fn = V.setup(t, torch, qp)
         for _ in range(warmup):
-            g()
-        ks, wall = time_launches(torch, g, steps)
-        nbytes = W.gather_bytes(cap, cap, nb)
-        out["gather %s %d slots" % (str(dtype).split(".")[1], cap)] = {
-            "gbps": round(nbytes * steps / wall / 1e9, 1),
-            "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2), "bytes_per_launch": nbytes}
-        del rows
-    del cache, slots
-    torch.cuda.empty_cache()
-    # MXFP8 norm-quant: 16384 rows of 7168 (a DeepSeek-sized hidden state),
-    # with the residual add and the residual output.
-    m, hidden = 16384, 7168
-    gen = torch.Generator(device="cuda").manual_seed(77)
-    x = torch.randn((m, hidden), generator=gen, device="cuda").to(torch.bfloat16)
-    r = torch.randn((m, hidden), generator=gen, device="cuda").to(torch.bfloat16)
-    gamma = (0.1 * torch.randn(hidden, generator=gen, device="cuda")).to(torch.bfloat16)
-    res_out = torch.empty_like(x)
-    codes = torch.empty((m, hidden), dtype=torch.uint8, device="cuda")
-    scales = torch.empty(qp.qkv_prep_mxfp8_scale_bytes(m, hidden), dtype=torch.uint8, device="cuda")
-    f = lambda: qp.mxfp8_norm_quant(x, gamma, 1e-6, residual=r, residual_out=res_out,
-                                    quant_out=codes, scale_out=scales)
-    for _ in range(warmup):
-        f()
-    ks, wall = time_launches(torch, f, steps)
-    nbytes = m * hidden * (2 + 2 + 2 + 1) + scales.numel() + 2 * hidden
-    out["mxfp8_norm_quant 16384x7168 (+residual)"] = {
-        "gbps": round(nbytes * steps / wall / 1e9, 1),
-        "kernel_us_mean": round(statistics.fmean(ks) * 1e6, 2), "bytes_per_launch": nbytes}
-    del x, r, res_out, codes, scales
-    torch.cuda.empty_cache()
+            fn()
+        ks, wall = time_launches(torch, fn, steps)
+        del fn
+        torch.cuda.empty_cache()
+        mean = statistics.fmean(ks)
+        out[t.label] = {
+            "gbps": round(t.alg_bytes * steps / wall / 1e9, 1),
+            "kernel_us_mean": round(mean * 1e6, 2),
+            "kernel_us_median": round(statistics.median(ks) * 1e6, 2),
+            "roofline": {"bound": "hbm", "kernel": t.kernel, "achieved": round(t.alg_bytes / mean / 1e9, 1),
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(t.alg_bytes / mean / 1e9 / PEAK_HBM_GBPS, 4),
+                         "traffic": recorded_traffic(t), "bytes_per_launch": t.alg_bytes},
+        }
     return out
 
 
@@ -312,10 +275,10 @@ def cpu_baseline(torch, W, name, target_s=12.0, sample_tokens=4096):
 
 # ----------------------------------------------------------------- counters
 
-def recorded_traffic(workload_label):
-    """HBM bytes per dispatch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "qkv_prep_counters_%s.txt" % workload_label.replace(" ", "_"))
+def recorded_traffic(t):
+    """HBM bytes per dispatch of target t from the committed rocprofv3 counter
+    summary, if it was taken on the current source of t's kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", "%s_counters_%s.txt" % (t.prefix, t.label))
     if not os.path.exists(path):
         return None
     rec = None
@@ -326,28 +289,28 @@ def recorded_traffic(workload_label):
     if not rec:
         return None
     from fp8_kv_cache_amd.rocprof_harness import kernel_sha
-    if rec.get("kernel_sha") != kernel_sha():
+    if rec.get("kernel_sha") != kernel_sha(t.family):
         return None
     return rec.get("hbm_bytes_per_dispatch")
 
 
 # ----------------------------------------------------------------- main
 
-def profile_run(torch, W, qp, name, launches, copy_bytes=512 << 20, copies=3):
-    """A short program for rocprofv3: a few launches of the operator on the
-    workload, then a few launches of the library's streaming-copy probe over a
-    buffer of known size (its FETCH_SIZE/WRITE_SIZE calibrate the counters
-    against bytes that are known exactly)."""
-    w = W.WORKLOADS[name]
-    inp = W.make_inputs(w, device="cuda")
-    op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
+def profile_run(torch, qp, name, launches, copy_bytes=512 << 20, copies=3):
+    """A short program for rocprofv3: a few launches of one target (the
+    operator on a workload, or a neighbouring path), then a few launches of the
+    library's streaming-copy probe over a buffer of known size (its
+    FETCH_SIZE/WRITE_SIZE calibrate the counters against bytes that are known
+    exactly)."""
+    from fp8_kv_cache_amd import variants as V
+    t = V.target(name)
+    fn = V.setup(t, torch, qp)
     torch.cuda.synchronize()
     for i in range(launches):
-        op(inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
-           inp["slot_mapping"], inp["cache"])
+        fn()
         torch.cuda.synchronize()
-        log("profile: %s launch %d done" % (w.label, i))
-    del inp
+        log("profile: %s launch %d done" % (t.label, i))
+    del fn
     torch.cuda.empty_cache()
     src = torch.ones(copy_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -364,7 +327,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--workload", default="prefill",
+                    help="an operator workload; in profile mode also a variant target "
+                         "(bf16store_prefill, gather_bf16, gather_f32, gather_f32_shuffled, mxfp8)")
     ap.add_argument("--also", default="long")
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -381,13 +346,14 @@ def main():
 
     import torch
     from fp8_kv_cache_amd import qkv_prep as qp
+    from fp8_kv_cache_amd import variants as V
     from fp8_kv_cache_amd import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.mode == "profile":
-        profile_run(torch, W, qp, args.workload, args.launches)
+        profile_run(torch, qp, args.workload, args.launches)
         return
     kat_before = known_answer_check(torch, W, qp)
     ceil_before = None if args.no_ceiling else copy_ceilings(torch, qp)
@@ -396,7 +362,7 @@ def main():
     also = None
     if not args.no_also and args.also and args.also != args.workload:
         _, also = bench_workload(torch, W, qp, args.also, args.steps, args.warmup)
-    variants = None if args.no_variants else bench_variants(torch, W, qp, args.steps, args.warmup)
+    variants = None if args.no_variants else bench_variants(torch, qp, args.steps, args.warmup)
     ceil_after = None if args.no_ceiling else copy_ceilings(torch, qp)
     log("bench: copy ceilings after = %s GB/s" % ceil_after)
     kat_after = known_answer_check(torch, W, qp)
@@ -406,7 +372,7 @@ def main():
 
     value = main_res["gbps_wall"]
     achieved = main_res["gbps_kernel_mean"]
-    traffic = recorded_traffic(main_res["workload"])
+    traffic = recorded_traffic(V.target(args.workload))
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -446,7 +412,8 @@ def main():
                        "frac_of_copy": round(also["gbps_wall"] / ceiling, 4) if ceiling else None,
                        "kernel_us": {k: round(also["kernel_s_" + k] * 1e6, 2)
                                      for k in ("median", "min", "p90", "median_cold", "p90_cold")},
-                       "launch": also["launch"], "bytes_per_step": also["bytes_per_step"]}
+                       "launch": also["launch"], "bytes_per_step": also["bytes_per_step"],
+                       "traffic": recorded_traffic(V.target(args.also))}
     if variants:
         out["variants"] = variants
     if not args.no_cpu_baseline:

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <new>
 
+#include "qkv_prep_gather.h"
 #include "qkv_prep_internal.h"
 
 struct qkv_prep {

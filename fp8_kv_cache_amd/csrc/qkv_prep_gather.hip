@@ -2,6 +2,7 @@
 // dequantize and gather slots back into fp32 or bf16 rows (the cache layout is
 // the one stated in include/qkv_prep.h).  HBM bound: 584 bytes read and 1 or
 // 2 KiB written per row, one wavefront per row, non-temporal stores.
+#include "qkv_prep_gather.h"
 #include "qkvp_device.h"
 
 namespace qkvp {
@@ -95,12 +96,27 @@ __device__ __forceinline__ void gather_row_f32(const GatherArgs &a, int64_t i, u
     store_stream(dst + 64 + lane, hi);
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin, and each XCD has its
+// own L2.  Rows next to each other in the slot list usually read neighbouring
+// slots (a block-table walk reads a block's slots in order), which share cache
+// lines: 8 scale records per 64-byte segment, and the 128-byte line where one
+// slot's data ends and the next begins.  So workgroup b takes a row such that
+// every XCD gets `chunk` consecutive rows out of each window of 8 * chunk
+// (a bijection of [0, grid) when grid is a multiple of 8 * chunk).
+__device__ __forceinline__ uint32_t xcd_row_block(uint32_t b, uint32_t chunk)
+{
+    if (chunk == 0)
+        return b;
+    const uint32_t win = 8u * chunk, w = b / win, r = b - w * win;
+    return w * win + (r & 7u) * chunk + (r >> 3);
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a)
 {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t i = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+    const int64_t i = (int64_t)xcd_row_block(blockIdx.x, a.xcd_chunk) * (blockDim.x >> 6) + wave;
     if (i < a.n) {
         if constexpr (OUT_BF16)
             gather_row_bf16(a, i, lane);
@@ -113,12 +129,20 @@ __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a)
 
 hipError_t launch_gather(const GatherArgs &a, int waves_per_block, hipStream_t stream)
 {
-    const int64_t blocks = (a.n + waves_per_block - 1) / waves_per_block;
+    GatherArgs g = a;
+    int64_t blocks = (a.n + waves_per_block - 1) / waves_per_block;
+    // 64 rows per XCD chunk (a cache block's worth of slots at the usual block
+    // size).  Measured on MI355X over a 262144-slot block-table walk: fp32 rows
+    // 6.5 -> 7.1 TB/s, bf16 rows 6.0 -> 6.3 TB/s; every slot in a random order:
+    // +2.5%.  Small grids keep the plain order (the padding would cost more).
+    g.xcd_chunk = blocks >= 4096 ? 64u : 0u;
+    if (g.xcd_chunk)
+        blocks = (blocks + 8 * g.xcd_chunk - 1) / (8 * g.xcd_chunk) * (8 * g.xcd_chunk);
     const dim3 grid((uint32_t)blocks), block(64u * (uint32_t)waves_per_block);
     if (a.out_bf16)
-        hipLaunchKernelGGL(gather_kernel<true>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL(gather_kernel<true>, grid, block, 0, stream, g);
     else
-        hipLaunchKernelGGL(gather_kernel<false>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL(gather_kernel<false>, grid, block, 0, stream, g);
     return hipGetLastError();
 }
 

@@ -53,17 +53,6 @@ struct KernelArgs {
     int32_t bf16_store;        // 1: kv slots are 1024 bytes of bf16, no quantization
 };
 
-struct GatherArgs {
-    const uint8_t *cache;
-    const int64_t *slots;
-    void *out;
-    int64_t num_slots;         // num_blocks * block_size (< 2^31)
-    int64_t n;                 // rows to read
-    uint32_t block_size;
-    FastDiv blocks;
-    int32_t out_bf16;          // 0: fp32 rows, 1: bf16 rows
-};
-
 struct LaunchShape {
     int rows_per_wave;    // q rows per wavefront (1, 2, 4)
     int waves_per_block;  // 1, 2, 4, 8
@@ -74,8 +63,5 @@ struct LaunchShape {
 
 // Enqueue the kernel.  Returns the hipError_t of the launch.
 hipError_t launch_qkv_prep(const KernelArgs &a, const LaunchShape &s, hipStream_t stream);
-
-// Enqueue the cache reader: one wavefront per row, `waves_per_block` per workgroup.
-hipError_t launch_gather(const GatherArgs &a, int waves_per_block, hipStream_t stream);
 
 }  // namespace qkvp

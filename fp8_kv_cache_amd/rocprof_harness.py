@@ -1,22 +1,30 @@
-"""rocprofv3 harness for the qkv_prep kernel.
+"""rocprofv3 harness for the library's kernels.
 
-Runs ``bench.py --mode profile`` (a few launches of the operator on one
-workload, then the library's streaming-copy probe over 512 MiB) under
-rocprofv3, one pass
-per counter group, each as a child process with its own time limit:
+Runs ``bench.py --mode profile`` (a few launches of one target: the operator on
+a workload, or one of the neighbouring paths named in variants.py; then the
+library's streaming-copy probe over 512 MiB) under rocprofv3, one pass per
+counter group, each as a child process with its own time limit:
 
   trace   --kernel-trace --stats           per-kernel average duration
   fetch   --pmc FETCH_SIZE                 HBM bytes read per dispatch (KiB)
   write   --pmc WRITE_SIZE                 HBM bytes written per dispatch (KiB)
+  reqs    --pmc TCC_EA0_RDREQ_{32B,64B,128B}_sum TCC_EA0_RDREQ_sum
+                                           read requests by size
   waves   --pmc <wave counters>            occupancy
 
 and writes short text summaries (the figures and the exact commands) to the
 output directory.  The copy probe's counters against its known byte count
 give the scale factor applied to the operator's counters (on gfx950 with this
 ROCm, FETCH_SIZE reads about half of the bytes a copy is known to fetch, while
-WRITE_SIZE matches).
+WRITE_SIZE matches).  FETCH_SIZE's expression counts a read request as 128
+bytes only through TCC_BUBBLE, and on gfx950 the 128-byte requests land in its
+64-byte term: one scale factor is exact for a kernel whose reads are all
+128-byte requests (the copy, the operator) but double-counts 32- and 64-byte
+ones.  The reqs pass therefore also counts read bytes from the request-size
+counters directly (32, 64 and 128 bytes each), with no calibration.
 
     python -m fp8_kv_cache_amd.rocprof_harness --workload prefill --out gpurun_out/prof
+    python -m fp8_kv_cache_amd.rocprof_harness --workload mxfp8 --out gpurun_out/prof
 """
 from __future__ import annotations
 
@@ -32,19 +40,20 @@ import time
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-# The sources that define the operator's kernel; the counter summaries carry
-# their hash so that a stale summary is never reported as current.
-KERNEL_SRCS = [os.path.join(PKG, "csrc", f) for f in
-               ("qkv_prep_kernels.hip", "qkvp_device.h", "qkv_prep_internal.h")]
-OP_KERNEL = "qkv_prep_kernel"
 COPY_KERNEL = "stream_copy"
 COPY_BYTES = 512 << 20
+REQ_COUNTERS = ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
+                "TCC_EA0_RDREQ_sum")
 
 
-def kernel_sha() -> str:
+def kernel_sha(family: str = "op") -> str:
+    """Hash of the sources that define a kernel family; the counter summaries
+    carry it so that a stale summary is never reported as current."""
+    sys.path.insert(0, ROOT)
+    from fp8_kv_cache_amd.variants import SOURCES
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        h.update(open(path, "rb").read())
+    for f in SOURCES[family]:
+        h.update(open(os.path.join(PKG, "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -114,17 +123,17 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--out", default="gpurun_out/prof")
     ap.add_argument("--launches", type=int, default=5)
-    ap.add_argument("--passes", default="trace,fetch,write,waves")
+    ap.add_argument("--passes", default="trace,fetch,write,reqs,waves")
     ap.add_argument("--wave-counters", default="OccupancyPercent,MeanOccupancyPerCU,SQ_WAVES")
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
-    from fp8_kv_cache_amd import workloads as W
-    w = W.WORKLOADS[args.workload]
-    label = "%s_%dx%d" % (w.name, w.num_tokens, w.num_heads)
+    from fp8_kv_cache_amd import variants as V
+    t = V.target(args.workload)
+    label, op_kernel, prefix = t.label, t.kernel, t.prefix
     out = os.path.abspath(os.path.join(ROOT, args.out))
     os.makedirs(out, exist_ok=True)
     passes = args.passes.split(",")
-    summary = {"workload": label, "kernel_sha": kernel_sha()}
+    summary = {"workload": label, "kernel": op_kernel, "kernel_sha": kernel_sha(t.family)}
     cmds = {}
 
     if "trace" in passes:
@@ -132,7 +141,7 @@ def main():
                           out, 300)
         cmds["trace"] = cmd
         rows = kernel_stats(d)
-        lines = ["# rocprofv3 kernel trace, workload %s" % label,
+        lines = ["# rocprofv3 kernel trace, kernel %s, workload %s" % (op_kernel, label),
                  "# command (from the repository root): %s" % " ".join(cmd),
                  "# kernel source sha256[:16] = %s" % summary["kernel_sha"], "",
                  "%-70s %6s %14s %14s %14s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
@@ -141,11 +150,11 @@ def main():
             lines.append("%-70s %6s %14.2f %14.2f %14.2f" % (
                 name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3))
-            if OP_KERNEL in r["Name"]:
+            if op_kernel in r["Name"]:
                 summary["op_avg_us"] = float(r["AverageNs"]) / 1e3
                 summary["op_calls"] = int(r["Calls"])
         text = "\n".join(lines) + "\n"
-        open(os.path.join(out, "qkv_prep_kernel_trace_%s.txt" % label), "w").write(text)
+        open(os.path.join(out, "%s_kernel_trace_%s.txt" % (prefix, label)), "w").write(text)
         log(text)
 
     fetch = write = None
@@ -157,9 +166,31 @@ def main():
         cmd, d = run_pass("write", ["--pmc", "WRITE_SIZE"], args.workload, 3, out, 180)
         cmds["write"] = cmd
         write = per_dispatch(counter_rows(d), "WRITE_SIZE")
+    reqs = None
+    if "reqs" in passes:
+        cmd, d = run_pass("reqs", ["--pmc"] + list(REQ_COUNTERS), args.workload, 3, out, 180)
+        cmds["reqs"] = cmd
+        rows = counter_rows(d)
+        reqs = {c: per_dispatch(rows, c) for c in REQ_COUNTERS}
+
+        def by_size(kernel):
+            vals = {c: pick(reqs[c], kernel)[1] for c in REQ_COUNTERS}
+            if not all(vals.values()):
+                return None, None
+            per = [32 * a + 64 * b + 128 * c for a, b, c in zip(
+                vals["TCC_EA0_RDREQ_32B_sum"], vals["TCC_EA0_RDREQ_64B_sum"], vals["TCC_EA0_RDREQ_128B_sum"])]
+            total = [a + b + c for a, b, c in zip(
+                vals["TCC_EA0_RDREQ_32B_sum"], vals["TCC_EA0_RDREQ_64B_sum"], vals["TCC_EA0_RDREQ_128B_sum"])]
+            i = per.index(min(per))
+            return per[i], {"32B": vals["TCC_EA0_RDREQ_32B_sum"][i], "64B": vals["TCC_EA0_RDREQ_64B_sum"][i],
+                            "128B": vals["TCC_EA0_RDREQ_128B_sum"][i], "all": vals["TCC_EA0_RDREQ_sum"][i],
+                            "sized": total[i]}
+
+        summary["op_read_bytes_by_request"], summary["op_read_requests"] = by_size(op_kernel)
+        summary["copy_read_bytes_by_request"], summary["copy_read_requests"] = by_size(COPY_KERNEL)
     if fetch is not None and write is not None:
-        op_name, op_f = pick(fetch, OP_KERNEL)
-        _, op_w = pick(write, OP_KERNEL)
+        op_name, op_f = pick(fetch, op_kernel)
+        _, op_w = pick(write, op_kernel)
         cp_name, cp_f = pick(fetch, COPY_KERNEL)
         _, cp_w = pick(write, COPY_KERNEL)
         kib = 1024.0
@@ -169,10 +200,7 @@ def main():
         w_scale = COPY_BYTES / (min(cp_w) * kib) if cp_w else 1.0
         op_fetch = min(op_f) * kib if op_f else None
         op_write = min(op_w) * kib if op_w else None
-        valid = w.num_tokens  # every workload but tiny fills a slot per token
-        alg = W.algorithmic_bytes(w.num_tokens, w.num_heads, valid)
-        alg_read = w.num_tokens * (1024 * w.num_heads + 1024 + 16 + 256) + 2048
-        alg_write = w.num_tokens * 1024 * w.num_heads + 584 * valid
+        alg, alg_read, alg_write = t.alg_bytes, t.read_bytes, t.write_bytes
         summary.update({
             "copy_kernel": cp_name, "copy_fetch_kib": min(cp_f) if cp_f else None,
             "copy_write_kib": min(cp_w) if cp_w else None, "fetch_scale": f_scale,
@@ -184,39 +212,47 @@ def main():
         if op_fetch and op_write:
             summary["hbm_bytes_per_dispatch"] = op_fetch * f_scale + op_write * w_scale
             summary["hbm_over_alg"] = summary["hbm_bytes_per_dispatch"] / alg
-        lines = ["# rocprofv3 FETCH_SIZE / WRITE_SIZE, workload %s" % label,
+        if summary.get("op_read_bytes_by_request") and op_write:
+            summary["hbm_bytes_by_request"] = summary["op_read_bytes_by_request"] + op_write * w_scale
+            summary["by_request_over_alg"] = summary["hbm_bytes_by_request"] / alg
+            summary["read_by_request_over_alg_read"] = summary["op_read_bytes_by_request"] / alg_read
+        lines = ["# rocprofv3 FETCH_SIZE / WRITE_SIZE, kernel %s, workload %s" % (op_kernel, label),
                  "# commands (from the repository root):",
                  "#   %s" % " ".join(cmds["fetch"]), "#   %s" % " ".join(cmds["write"]),
                  "# counters are KiB per dispatch; the %d-byte streaming-copy probe calibrates them"
                  % COPY_BYTES,
-                 "# (scale = known bytes / counted bytes); the minimum over dispatches is used", ""]
+                 "# (scale = known bytes / counted bytes); the minimum over dispatches is used",
+                 "# reads by request size (no calibration): %s" % (" ".join(cmds["reqs"]) if "reqs" in cmds
+                                                                    else "not taken"), ""]
         for k in ("copy_kernel", "copy_fetch_kib", "copy_write_kib", "fetch_scale", "write_scale",
                   "op_fetch_bytes_raw", "op_write_bytes_raw", "op_fetch_bytes", "op_write_bytes",
                   "alg_read_bytes", "alg_write_bytes", "alg_bytes", "hbm_bytes_per_dispatch",
-                  "hbm_over_alg"):
+                  "hbm_over_alg", "copy_read_bytes_by_request", "copy_read_requests",
+                  "op_read_bytes_by_request", "op_read_requests", "read_by_request_over_alg_read",
+                  "hbm_bytes_by_request", "by_request_over_alg"):
             lines.append("%-24s %s" % (k, summary.get(k)))
         lines += ["", "# machine-readable:", json.dumps({k: summary.get(k) for k in (
-            "workload", "kernel_sha", "hbm_bytes_per_dispatch", "op_fetch_bytes", "op_write_bytes",
-            "alg_bytes", "fetch_scale", "write_scale")})]
+            "workload", "kernel", "kernel_sha", "hbm_bytes_per_dispatch", "op_fetch_bytes", "op_write_bytes",
+            "alg_bytes", "fetch_scale", "write_scale", "op_read_bytes_by_request", "hbm_bytes_by_request")})]
         text = "\n".join(lines) + "\n"
-        open(os.path.join(out, "qkv_prep_counters_%s.txt" % label), "w").write(text)
+        open(os.path.join(out, "%s_counters_%s.txt" % (prefix, label)), "w").write(text)
         log(text)
 
     if "waves" in passes:
         ctrs = args.wave_counters.split(",")
         cmd, d = run_pass("waves", ["--pmc"] + ctrs, args.workload, 3, out, 180)
         rows = counter_rows(d)
-        lines = ["# rocprofv3 wave counters, workload %s" % label,
+        lines = ["# rocprofv3 wave counters, kernel %s, workload %s" % (op_kernel, label),
                  "# command (from the repository root): %s" % " ".join(cmd), ""]
         for c in ctrs:
-            name, vals = pick(per_dispatch(rows, c), OP_KERNEL)
+            name, vals = pick(per_dispatch(rows, c), op_kernel)
             lines.append("%-20s %s" % (c, vals))
         lines.append("")
         lines.append("OccupancyPercent = 400 * sum(SQ_WAVE_CYCLES) / GRBM_GUI_ACTIVE / CUs / 32 "
                      "(resident waves as a share of 32 wave slots per CU); MeanOccupancyPerCU = "
                      "mean resident waves per CU (rocprofv3 derived counters)")
         text = "\n".join(lines) + "\n"
-        open(os.path.join(out, "qkv_prep_waves_%s.txt" % label), "w").write(text)
+        open(os.path.join(out, "%s_waves_%s.txt" % (prefix, label)), "w").write(text)
         log(text)
 
     json.dump(summary, open(os.path.join(out, "summary_%s.json" % label), "w"), indent=1)

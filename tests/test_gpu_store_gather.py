@@ -151,3 +151,31 @@ def test_gather_arbitrary_cache_bytes(bs, nb):
     is_nan16 = lambda u: ((u & 0x7F80) == 0x7F80) & ((u & 0x007F) != 0)
     assert _nan_aware_equal(got16, want16, is_nan16(got16), np.isnan(want))
     assert np.all(got32[cap:] == 0) and np.all(got16[cap:] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gather_full_cache_block_walk(dtype):
+    # The benchmarked configuration: every slot of the 4096 x 64-slot cache as
+    # a block-table walk (blocks shuffled, slots in order), here with the last
+    # 3 rows dropped so that the final window of rows is ragged.
+    w = W.WORKLOADS["decode"]
+    bs, nb = w.block_size, w.num_blocks
+    note("gather full cache %s: %d x %d slots" % (dtype, nb, bs))
+    rng = np.random.default_rng(730)
+    host = rng.integers(0, 256, (nb, bs * W.SLOT_BYTES), dtype=np.uint8)
+    host[:, bs * 576:] = rng.integers(100, 140, (nb, bs * 8), dtype=np.uint8)
+    probe = (rng.permutation(nb)[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)[:-3].astype(np.int64)
+    want = oracle.gather_dequant(host, nb, bs, probe)
+    cache = torch.from_numpy(host).to(DEV)
+    op = qp.QkvPrep(w.num_heads, block_size=bs)
+    out = torch.full((probe.size, 512), 7.0, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                     device=DEV)
+    op.gather(cache, torch.from_numpy(probe).to(DEV), out)
+    torch.cuda.synchronize()
+    if dtype == "f32":
+        got = out.cpu().numpy()
+        assert _nan_aware_equal(got.view(np.uint32), want.view(np.uint32), np.isnan(got), np.isnan(want))
+    else:
+        got = W.as_u16(out)
+        is_nan16 = ((got & 0x7F80) == 0x7F80) & ((got & 0x007F) != 0)
+        assert _nan_aware_equal(got, oracle.f32_to_bf16(want), is_nan16, np.isnan(want))
