@@ -32,6 +32,48 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Makes the handle's device current for the guard's lifetime and restores the
+// caller's current device afterwards.
+class DeviceScope {
+public:
+    explicit DeviceScope(int device)
+    {
+        if (hipGetDevice(&prev_) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        if (prev_ != device && hipSetDevice(device) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        ok_ = true;
+        switched_ = prev_ != device;
+    }
+    ~DeviceScope()
+    {
+        if (switched_)
+            (void)hipSetDevice(prev_);
+    }
+    DeviceScope(const DeviceScope &) = delete;
+    DeviceScope &operator=(const DeviceScope &) = delete;
+    bool ok() const { return ok_; }
+
+private:
+    int prev_ = -1;
+    bool ok_ = false;
+    bool switched_ = false;
+};
+
+// Launch result, then (with QKV_PREP_SYNC=1) the stream's.
+int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)
+{
+    if (launched != hipSuccess)
+        return QKV_PREP_ERR_LAUNCH;
+    if (h->sync && hipStreamSynchronize(st) != hipSuccess)
+        return QKV_PREP_ERR_DEVICE;
+    return QKV_PREP_OK;
+}
+
 // Launch shape for T tokens.
 //  * rows_per_wave: q rows a wavefront loads before computing.  One row per
 //    wavefront (one 16-byte chunk per lane) streams best on MI355X; more rows
@@ -231,7 +273,7 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     const int64_t B = h->cfg.block_size;
     const qkvp::LaunchShape s = choose_shape(h->cfg, h->num_cus, T);
 
-    qkvp::KernelArgs k;
+    qkvp::KernelArgs k{};
     k.q = static_cast<uint16_t *>(a->q);
     k.kv = static_cast<const uint16_t *>(a->kv);
     k.q_w = static_cast<const uint16_t *>(a->q_norm_w);
@@ -251,28 +293,15 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     k.eps = h->cfg.eps;
     k.bf16_store = h->cfg.kv_store == QKV_PREP_KV_BF16;
 
-    int prev = -1;
-    if (hipGetDevice(&prev) != hipSuccess) {
-        (void)hipGetLastError();
+    DeviceScope dev(h->device);
+    if (!dev.ok())
         return QKV_PREP_ERR_NO_DEVICE;
-    }
-    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) {
-        (void)hipGetLastError();
-        return QKV_PREP_ERR_NO_DEVICE;
-    }
     if (h->log)
         std::fprintf(stderr, "qkv_prep: T=%lld H=%lld rows/wave=%d waves/block=%d convert=%d grid=%lld+%lld\n",
                      (long long)T, (long long)H, s.rows_per_wave, s.waves_per_block, s.convert,
                      (long long)s.kv_blocks, (long long)s.q_blocks);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    int rc = QKV_PREP_OK;
-    if (qkvp::launch_qkv_prep(k, s, st) != hipSuccess)
-        rc = QKV_PREP_ERR_LAUNCH;
-    else if (h->sync && hipStreamSynchronize(st) != hipSuccess)
-        rc = QKV_PREP_ERR_DEVICE;
-    if (prev != h->device)
-        (void)hipSetDevice(prev);
-    return rc;
+    return finish(h, qkvp::launch_qkv_prep(k, s, st), st);
 }
 
 int qkv_prep_gather(qkv_prep_t h, const qkv_prep_gather_args *a, void *stream)
@@ -282,7 +311,7 @@ int qkv_prep_gather(qkv_prep_t h, const qkv_prep_gather_args *a, void *stream)
     const int rc_args = check_gather(h->cfg, a);
     if (rc_args != QKV_PREP_OK || a->n == 0)
         return rc_args;
-    qkvp::GatherArgs g;
+    qkvp::GatherArgs g{};
     g.cache = static_cast<const uint8_t *>(a->kv_cache);
     g.slots = a->slots;
     g.out = a->out;
@@ -291,24 +320,11 @@ int qkv_prep_gather(qkv_prep_t h, const qkv_prep_gather_args *a, void *stream)
     g.block_size = (uint32_t)h->cfg.block_size;
     g.blocks = qkvp::make_fastdiv((uint32_t)h->cfg.block_size);
     g.out_bf16 = a->out_dtype == QKV_PREP_OUT_BF16;
-    int prev = -1;
-    if (hipGetDevice(&prev) != hipSuccess) {
-        (void)hipGetLastError();
+    DeviceScope dev(h->device);
+    if (!dev.ok())
         return QKV_PREP_ERR_NO_DEVICE;
-    }
-    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) {
-        (void)hipGetLastError();
-        return QKV_PREP_ERR_NO_DEVICE;
-    }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    int rc = QKV_PREP_OK;
-    if (qkvp::launch_gather(g, 1, st) != hipSuccess)
-        rc = QKV_PREP_ERR_LAUNCH;
-    else if (h->sync && hipStreamSynchronize(st) != hipSuccess)
-        rc = QKV_PREP_ERR_DEVICE;
-    if (prev != h->device)
-        (void)hipSetDevice(prev);
-    return rc;
+    return finish(h, qkvp::launch_gather(g, 1, st), st);
 }
 
 }  // extern "C"

@@ -144,7 +144,8 @@ typedef struct {
 /* Create a handle for device `device`.  Validates cfg, reads the device's
  * compute-unit count for the launch heuristic, and stores host state only.
  * Returns QKV_PREP_ERR_NO_DEVICE when no HIP device exists or the index is
- * out of range, QKV_PREP_ERR_INVALID_ARG / _UNSUPPORTED for a bad cfg.
+ * out of range, QKV_PREP_ERR_INVALID_ARG / _UNSUPPORTED for a bad cfg (and
+ * QKV_PREP_ERR_INVALID_ARG if the small host allocation fails).
  * *out is set only on success; release it with qkv_prep_destroy. */
 int qkv_prep_create(const qkv_prep_config *cfg, int device, qkv_prep_t *out);
 
@@ -180,8 +181,9 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *args, void *stream);
  * code * 2^(scale byte - 127) of their 64-dim block (exact in fp32; the bf16
  * output is that value rounded to nearest even), dims 448..511 the stored bf16
  * rope values.  Uses the handle's device and block_size; the handle must have
- * been created with kv_store = QKV_PREP_KV_FP8.  Argument errors are reported
- * as for qkv_prep_run, with nothing launched. */
+ * been created with kv_store = QKV_PREP_KV_FP8 (else QKV_PREP_ERR_UNSUPPORTED).
+ * Limits: n < 2^26 and num_blocks * B < 2^31 (else QKV_PREP_ERR_UNSUPPORTED).
+ * Argument errors are reported as for qkv_prep_run, with nothing launched. */
 int qkv_prep_gather(qkv_prep_t h, const qkv_prep_gather_args *args, void *stream);
 
 /* Release a handle.  NULL is a no-op.  Returns QKV_PREP_OK. */
@@ -193,7 +195,10 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
 
 /* The launch qkv_prep_run would use for num_tokens tokens with config cfg on
  * a device with num_cus compute units (256 on MI355X).  Pure host code: needs
- * no device, so the launch heuristic can be inspected anywhere. */
+ * no device, so the launch heuristic can be inspected anywhere.  The current
+ * heuristic (one q row per wavefront, one wavefront per workgroup, at every
+ * size) does not depend on num_cus; the argument keeps the signature stable
+ * for a device-dependent one. */
 int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t num_tokens,
                           qkv_prep_launch *out);
 

@@ -205,6 +205,37 @@ def test_side_stream_and_conversion_modes_agree():
     assert torch.equal(results[0][1], results[1][1])
 
 
+def test_concurrent_streams_and_a_shared_handle():
+    # The handle is read-only after create: two handles, and one handle used
+    # on two streams at once, must give the serial results.
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    w1 = W.custom(3000, 16, seed=410, block_size=16)
+    w2 = W.custom(2000, 48, seed=411)
+    i1, i2 = W.make_inputs(w1, device=DEV), W.make_inputs(w2, device=DEV)
+    op1, op2 = QkvPrep(16, block_size=16), QkvPrep(48)
+
+    def run(op, inp, q, c):
+        op(q, inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"], inp["slot_mapping"], c)
+
+    ref = {}
+    for key, op, inp in (("1", op1, i1), ("2", op2, i2)):
+        q, c = inp["q"].clone(), inp["cache"].clone()
+        run(op, inp, q, c)
+        ref[key] = (q, c)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    jobs = [("1", op1, i1, s1), ("2", op2, i2, s2), ("1", op1, i1, s2), ("2", op2, i2, s1),
+            ("1", op1, i1, s1), ("1", op1, i1, s2)]
+    bufs = [(inp["q"].clone(), inp["cache"].clone()) for _, _, inp, _ in jobs]
+    torch.cuda.synchronize()
+    for (_, op, inp, s), (q, c) in zip(jobs, bufs):
+        with torch.cuda.stream(s):
+            run(op, inp, q, c)
+    torch.cuda.synchronize()
+    for (key, _, _, _), (q, c) in zip(jobs, bufs):
+        assert torch.equal(q.view(torch.int16), ref[key][0].view(torch.int16))
+        assert torch.equal(c, ref[key][1])
+
+
 def test_bad_arguments_touch_nothing():
     from fp8_kv_cache_amd import qkv_prep as qp
     w = W.custom(64, 8, seed=408)
