@@ -165,6 +165,35 @@ def bench_variants(torch, qp, steps, warmup):
     return out
 
 
+def bench_configs(torch, W, qp, names, warmup):
+    """The other workloads, event-timed per launch: median, min and p90 over
+    200 launches for the small ones (Tiny, Decode-like) and 30 for the large
+    ones, plus the median of 10 launches with L2 and the MALL flushed first."""
+    from fp8_kv_cache_amd import variants as V
+    out = {}
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for name in names:
+        t = V.target(name)
+        log("bench: config %s" % t.label)
+        fn = V.setup(t, torch, qp)
+        for _ in range(warmup):
+            fn()
+        reps = 200 if t.alg_bytes < (1 << 30) else 30
+        ks, _ = time_launches(torch, fn, reps)
+        cold = time_cold(torch, fn, 10, scratch)
+        del fn
+        torch.cuda.empty_cache()
+        med = statistics.median(ks)
+        out[t.label] = {"gbps_median": round(t.alg_bytes / med / 1e9, 1), "reps": reps,
+                        "kernel_us": {"median": round(med * 1e6, 2), "min": round(min(ks) * 1e6, 2),
+                                      "p90": round(p90(ks) * 1e6, 2),
+                                      "median_cold": round(statistics.median(cold) * 1e6, 2)},
+                        "bytes_per_launch": t.alg_bytes}
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_workload(torch, W, qp, name, steps, warmup):
     w = W.WORKLOADS[name]
     log("bench: drawing %s inputs on the GPU" % w.label)
@@ -362,6 +391,8 @@ def main():
     also = None
     if not args.no_also and args.also and args.also != args.workload:
         _, also = bench_workload(torch, W, qp, args.also, args.steps, args.warmup)
+    others = [n for n in W.WORKLOADS if n not in (args.workload, args.also)]
+    configs = None if args.no_variants else bench_configs(torch, W, qp, others, args.warmup)
     variants = None if args.no_variants else bench_variants(torch, qp, args.steps, args.warmup)
     ceil_after = None if args.no_ceiling else copy_ceilings(torch, qp)
     log("bench: copy ceilings after = %s GB/s" % ceil_after)
@@ -414,6 +445,8 @@ def main():
                                      for k in ("median", "min", "p90", "median_cold", "p90_cold")},
                        "launch": also["launch"], "bytes_per_step": also["bytes_per_step"],
                        "traffic": recorded_traffic(V.target(args.also))}
+    if configs:
+        out["configs"] = configs
     if variants:
         out["variants"] = variants
     if not args.no_cpu_baseline:
