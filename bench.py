@@ -85,10 +85,14 @@ def copy_rate(torch, copier, size_bytes, reps=20, max_rounds=12):
 
 
 def copy_ceilings(torch, qp):
-    """Both ceilings at 512 MiB and 2 GiB: the runtime's hipMemcpyAsync and the
-    library's streaming-copy probe.  The larger rate is the denominator."""
+    """The ceilings at 512 MiB and 2 GiB: the runtime's hipMemcpyAsync, the
+    library's streaming-copy probe and its in-place streaming-update probe (the
+    operator rewrites q in place; counted as bytes read + bytes written).  The
+    largest rate is the denominator."""
     out = {}
-    for label, fn in (("hipMemcpyAsync", DeviceCopy()), ("probe_copy", qp.qkv_prep_probe_copy)):
+    update = lambda dst, src, nbytes, stream: qp.qkv_prep_probe_update(dst, nbytes, stream)
+    for label, fn in (("hipMemcpyAsync", DeviceCopy()), ("probe_copy", qp.qkv_prep_probe_copy),
+                      ("probe_update", update)):
         for size in (512 << 20, 2 << 30):
             out["%s_%dMiB" % (label, size >> 20)] = round(copy_rate(torch, fn, size), 1)
     return out

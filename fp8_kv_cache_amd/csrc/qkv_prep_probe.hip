@@ -1,4 +1,5 @@
-// Streaming copy used as a bandwidth ceiling (see include/qkv_prep_probe.h).
+// Streaming copy and in-place update used as bandwidth ceilings (see
+// include/qkv_prep_probe.h).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,7 +35,41 @@ __global__ __launch_bounds__(kThreads) void stream_copy(u32x4 *dst, const u32x4 
     }
 }
 
+// In-place update, one 16-byte chunk per lane, one wavefront per workgroup.
+// Measured on MI355X at 4 GiB: a store issued right after its load's data
+// arrives streams at only ~4.5 TB/s; pausing the wavefront for a moment
+// (s_sleep 2, ~128 cycles) between the load and the store gives ~6.7 TB/s,
+// above the two-buffer copy.  A wave-wide reduction in the same place does not
+// help (~4.5 TB/s); sleeps of 2 to 32 units are the same.
+constexpr int kUpdateThreads = 64;
+
+__global__ __launch_bounds__(kUpdateThreads) void stream_update(u32x4 *buf, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kUpdateThreads + threadIdx.x;
+    if (i < n) {
+        u32x4 v = __builtin_nontemporal_load(buf + i);
+        v[0] += 1u;
+        __builtin_amdgcn_s_sleep(2);
+        __builtin_nontemporal_store(v, buf + i);
+    }
+}
+
 }  // namespace
+
+extern "C" int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream)
+{
+    if (bytes < 0 || (bytes > 0 && !buf) || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15))
+        return 1;
+    if (bytes == 0)
+        return 0;
+    const int64_t n = bytes / 16;
+    const int64_t blocks = (n + kUpdateThreads - 1) / kUpdateThreads;
+    if (blocks >= ((int64_t)1 << 31))
+        return 1;
+    hipLaunchKernelGGL(stream_update, dim3((uint32_t)blocks), dim3(kUpdateThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<u32x4 *>(buf), n);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
 
 extern "C" int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, void *stream)
 {

@@ -1,14 +1,17 @@
 /*
  * qkv_prep_probe.h -- a measurement probe shipped in libqkv_prep.so next to
- * the operator: a plain streaming device-to-device copy.
+ * the operator: a plain streaming device-to-device copy, and a streaming
+ * in-place update (read and write the same bytes, as the operator does with q).
  *
  * The pages measure the operator against a warm device-to-device copy of the
  * same card ("achievable bandwidth", FlagGems-vllm PR 684, section
  * "Performance against achievable bandwidth").  The runtime's own copy
  * (hipMemcpyAsync) is one such ceiling; this hand-written copy, built with
  * the same load/store idioms as the operator (16-byte non-temporal vector
- * accesses, several in flight per lane), is a second, usually stricter one.
- * It is not part of the operator.
+ * accesses), is a second, usually stricter one.  The in-place update is the
+ * third: the operator rewrites q in place, and on MI355X in-place streaming
+ * reaches a different rate from a copy between two buffers.  None of them is
+ * part of the operator.
  */
 #ifndef QKV_PREP_PROBE_H
 #define QKV_PREP_PROBE_H
@@ -25,6 +28,15 @@ extern "C" {
  * Returns 0 (QKV_PREP_OK), 1 (invalid argument: NULL, negative or unaligned),
  * or 5 (launch failed).  bytes == 0 is a no-op. */
 int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
+/* In-place streaming update of `bytes` bytes at device pointer buf on
+ * `stream`: every 16-byte chunk is read, its first 32-bit word (little-endian
+ * unsigned) is incremented by 1 with wrap-around, and the chunk is written
+ * back to the same address.  The traffic is bytes read + bytes written.
+ * buf 16-byte aligned, bytes a multiple of 16.  Returns 0, 1 (invalid
+ * argument: NULL, negative or unaligned) or 5 (launch failed); bytes == 0 is a
+ * no-op. */
+int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream);
 
 #ifdef __cplusplus
 }

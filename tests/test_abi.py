@@ -172,13 +172,18 @@ def test_fast_division_used_by_the_kernel():
             assert ((((n * m) >> 32) + n) >> l) == n // d, (d, n)
 
 
-def test_probe_copy_rejects_bad_arguments_without_launching():
+def test_probes_reject_bad_arguments_without_launching():
     lib = qp.library()
     assert lib.qkv_prep_probe_copy(None, None, 0, None) == qp.OK
     assert lib.qkv_prep_probe_copy(None, None, 16, None) == qp.ERR_INVALID_ARG
     assert lib.qkv_prep_probe_copy(1 << 20, 2 << 20, 15, None) == qp.ERR_INVALID_ARG
     assert lib.qkv_prep_probe_copy((1 << 20) + 8, 2 << 20, 16, None) == qp.ERR_INVALID_ARG
     assert lib.qkv_prep_probe_copy(1 << 20, 2 << 20, -16, None) == qp.ERR_INVALID_ARG
+    assert lib.qkv_prep_probe_update(None, 0, None) == qp.OK
+    assert lib.qkv_prep_probe_update(None, 16, None) == qp.ERR_INVALID_ARG
+    assert lib.qkv_prep_probe_update(1 << 20, 15, None) == qp.ERR_INVALID_ARG
+    assert lib.qkv_prep_probe_update((1 << 20) + 8, 16, None) == qp.ERR_INVALID_ARG
+    assert lib.qkv_prep_probe_update(1 << 20, -16, None) == qp.ERR_INVALID_ARG
 
 
 def test_gather_without_handle_is_rejected():
