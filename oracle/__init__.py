@@ -181,12 +181,14 @@ def slot_offsets(slot, num_blocks, block_size):
 # ---------------------------------------------------------------- operator
 
 def qkv_prep(q, kv, q_w, kv_w, positions, cos_sin, slot_mapping, cache,
-             num_blocks, block_size, eps, nthreads=1, kv_store="fp8"):
+             num_blocks, block_size, eps, nthreads=1, kv_store="fp8", out=None):
     """Run the whole operator on host arrays.
 
     q: uint16 [T, H, 512] (bf16 bits) -- not modified; the new q is returned.
     cache: uint8 [num_blocks, block_size*584] for kv_store="fp8", or
     [num_blocks, block_size*1024] for kv_store="bf16" -- updated in place.
+    out: optional contiguous uint16 array shaped like q to receive the new q
+    (so that a timing loop allocates nothing).
     Returns the new q (uint16 [T, H, 512])."""
     q = _c(np.asarray(q, dtype=np.uint16), np.uint16)
     T, H = q.shape[0], q.shape[1]
@@ -202,7 +204,10 @@ def qkv_prep(q, kv, q_w, kv_w, positions, cos_sin, slot_mapping, cache,
     if cache.size != num_blocks * block_size * slot_bytes:
         raise ValueError("cache size does not match num_blocks*block_size*%d" % slot_bytes)
     assert kv.shape == (T, HEAD_DIM) and positions.shape == (T,) and slot_mapping.shape == (T,)
-    out = np.empty_like(q)
+    if out is None:
+        out = np.empty_like(q)
+    elif not (out.flags["C_CONTIGUOUS"] and out.dtype == np.uint16 and out.shape == q.shape):
+        raise TypeError("out must be a contiguous uint16 array shaped like q")
     fn = lib().orc_qkv_prep if kv_store == "fp8" else lib().orc_qkv_prep_bf16_store
     rc = fn(T, H, _p(q), _p(out), _p(kv), _p(q_w), _p(kv_w),
                             _p(positions), _p(cos_sin), cos_sin.shape[0],

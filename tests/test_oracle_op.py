@@ -161,6 +161,23 @@ def test_whole_op_q_matches_rows_and_threads_agree():
     assert int((inp["slot_mapping"] >= 0).sum()) == 14
 
 
+def test_preallocated_output_gives_the_same_result():
+    w = W.WORKLOADS["tiny"]
+    inp = W.make_inputs(w)
+    q_out, cache = run_oracle(inp)
+    out = np.full_like(q_out, 0xFFFF)
+    cache2 = inp["cache"].numpy().copy()
+    got = oracle.qkv_prep(W.as_u16(inp["q"]), W.as_u16(inp["kv"]), W.as_u16(inp["q_w"]),
+                          W.as_u16(inp["kv_w"]), inp["positions"].numpy(), inp["cos_sin"].numpy(),
+                          inp["slot_mapping"].numpy(), cache2, inp["num_blocks"], inp["block_size"],
+                          inp["eps"], 2, out=out)
+    assert got is out and np.array_equal(out, q_out) and np.array_equal(cache2, cache)
+    with pytest.raises(TypeError):
+        oracle.qkv_prep(W.as_u16(inp["q"]), W.as_u16(inp["kv"]), None, W.as_u16(inp["kv_w"]),
+                        inp["positions"].numpy(), inp["cos_sin"].numpy(), inp["slot_mapping"].numpy(),
+                        cache2, inp["num_blocks"], inp["block_size"], inp["eps"], 1, out=out[:1])
+
+
 def test_whole_op_q_against_float64_ideal():
     # bf16 output of the fp32 chain vs the float64 evaluation of the same
     # formula: at most one bf16 ulp apart (the fp32 error is ~2^-20 relative,
