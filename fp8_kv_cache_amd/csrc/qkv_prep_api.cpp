@@ -11,6 +11,7 @@
 
 #include "qkv_prep_gather.h"
 #include "qkv_prep_internal.h"
+#include "qkv_prep_launch.h"
 
 struct qkv_prep {
     qkv_prep_config cfg;
@@ -75,10 +76,14 @@ int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)
 }
 
 // Launch shape for T tokens.
-//  * rows_per_wave: q rows a wavefront loads before computing.  One row per
-//    wavefront (one 16-byte chunk per lane) streams best on MI355X; more rows
-//    per wavefront are used only when one row per wavefront would need 2^32 or
-//    more work-items in the dispatch.
+//  * rows_per_wave: 1 (one q row per wavefront), or U = 2, 4 consecutive heads
+//    of one token per wavefront, processed one after another with the token's
+//    position, cos/sin row and the q weight loaded once.  Measured on MI355X
+//    (T = 256..16384, H = 64 and 128, two interleaved rounds): two heads per
+//    wavefront are 2.5-4% faster up to T*H = 2^19 q rows; above that one row
+//    per wavefront ties or wins (by 1-3% at 32768x64 and 131072x128).  Four
+//    heads per wavefront never win; they are used only when fewer wavefronts
+//    would need 2^32 or more work-items in the dispatch.
 //  * waves_per_block: 1 (64-lane workgroups).  Measured on MI355X with four
 //    interleaved rounds per shape: 1 wave per workgroup beats 2, 4 and 8 on
 //    2048x64, 32768x64, 32768x128 and 131072x128 (by 1-5%).
@@ -92,16 +97,18 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     s.waves_per_block = c.waves_per_block ? c.waves_per_block : 1;
     s.convert = c.convert ? c.convert : 2;
     s.kv_blocks = ceil_div(T, s.waves_per_block);
+    // q wavefronts: T * ceil(H / U) (U heads of one token per wavefront)
+    auto q_waves = [&](int u) { return T * ceil_div(c.num_heads, u); };
     if (c.rows_per_wave) {
         s.rows_per_wave = c.rows_per_wave;
     } else {
-        s.rows_per_wave = 1;
+        s.rows_per_wave = q_rows <= ((int64_t)1 << 19) && c.num_heads > 1 ? 2 : 1;
         while (s.rows_per_wave < 4 &&
-               (s.kv_blocks + ceil_div(ceil_div(q_rows, s.rows_per_wave), s.waves_per_block)) * 64 *
+               (s.kv_blocks + ceil_div(q_waves(s.rows_per_wave), s.waves_per_block)) * 64 *
                        s.waves_per_block >= ((int64_t)1 << 32))
             s.rows_per_wave *= 2;
     }
-    s.q_blocks = ceil_div(ceil_div(q_rows, s.rows_per_wave), s.waves_per_block);
+    s.q_blocks = ceil_div(q_waves(s.rows_per_wave), s.waves_per_block);
     return s;
 }
 
@@ -290,6 +297,9 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     k.kv_blocks = (uint32_t)s.kv_blocks;
     k.heads = qkvp::make_fastdiv((uint32_t)H);
     k.blocks = qkvp::make_fastdiv((uint32_t)B);
+    k.num_heads = (uint32_t)H;
+    k.chunks = (uint32_t)ceil_div(H, s.rows_per_wave);
+    k.chunk_div = qkvp::make_fastdiv(k.chunks);
     k.eps = h->cfg.eps;
     k.bf16_store = h->cfg.kv_store == QKV_PREP_KV_BF16;
 

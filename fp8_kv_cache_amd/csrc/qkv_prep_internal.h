@@ -1,5 +1,5 @@
-// Shared between the host API (qkv_prep_api.cpp) and the kernels
-// (qkv_prep_kernels.hip).  Not part of the public ABI.
+// Constants of the cache layout and the fixed-point divider, shared by the
+// host API and every kernel of the library.  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,37 +31,5 @@ inline FastDiv make_fastdiv(uint32_t d)
     const uint64_t m = ((((uint64_t)1 << 32) * ((1ull << l) - d)) / d) + 1;
     return FastDiv{(uint32_t)m, l};
 }
-
-struct KernelArgs {
-    uint16_t *q;
-    const uint16_t *kv;
-    const uint16_t *q_w;       // may be null (weightless q norm)
-    const uint16_t *kv_w;
-    const int64_t *positions;
-    const float *cos_sin;
-    const int64_t *slot_mapping;
-    uint8_t *cache;
-    int64_t max_position;
-    int64_t num_slots;         // num_blocks * block_size (< 2^31)
-    int64_t q_rows;            // T * H (< 2^31)
-    int64_t num_tokens;        // T
-    uint32_t block_size;
-    uint32_t kv_blocks;        // workgroups [0, kv_blocks) take kv rows
-    FastDiv heads;             // divides a q row index by H
-    FastDiv blocks;            // divides a slot by block_size
-    float eps;
-    int32_t bf16_store;        // 1: kv slots are 1024 bytes of bf16, no quantization
-};
-
-struct LaunchShape {
-    int rows_per_wave;    // q rows per wavefront (1, 2, 4)
-    int waves_per_block;  // 1, 2, 4, 8
-    int convert;          // 1 integer rounding, 2 conversion instructions
-    int64_t kv_blocks;
-    int64_t q_blocks;
-};
-
-// Enqueue the kernel.  Returns the hipError_t of the launch.
-hipError_t launch_qkv_prep(const KernelArgs &a, const LaunchShape &s, hipStream_t stream);
 
 }  // namespace qkvp

@@ -30,9 +30,13 @@
 //  * q rows and kv rows go to different workgroups of one launch (the FlagGems
 //    page merges the Q and KV launches); kv workgroups come first in dispatch
 //    order, so their quantization overlaps the q stream instead of trailing it.
-//  * Several rows per wavefront (the sglang page's "K tokens per block"
-//    load-level parallelism) remains available through the launch shape, but
-//    one row per wavefront is the measured optimum here.
+//  * Decode-sized batches (up to 2^19 q rows) take two heads of one token per
+//    wavefront, one after the other, so the token's position, cos/sin row and
+//    the q weight are loaded once per two rows (2.5-4% faster there; the
+//    launch heuristic picks it).  Issuing several rows' loads at once (the
+//    sglang page's "K tokens per block" load-level parallelism) was slower at
+//    every size measured.
+#include "qkv_prep_launch.h"
 #include "qkvp_device.h"
 
 namespace qkvp {
@@ -78,54 +82,77 @@ __device__ __forceinline__ int64_t clamp_position(int64_t p, int64_t max_positio
 
 // ------------------------------------------------------------------ q rows
 
-// U consecutive q rows, one per pass, all loads issued first.  `row0` is
-// wave-uniform, so every branch below is uniform too, except the rope lanes.
-template <int U, bool HAS_W, bool HW>
-__device__ __forceinline__ void q_rows(const KernelArgs &a, int64_t row0, uint32_t lane)
+// One q row per wavefront.  `row` is wave-uniform, so every branch below is
+// uniform too, except the rope lanes.
+template <bool HAS_W, bool HW>
+__device__ __forceinline__ void q_row(const KernelArgs &a, int64_t row, uint32_t lane)
 {
-    int64_t pos[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t row = row0 + u;
-        ok[u] = row < a.q_rows;
-        pos[u] = ok[u] ? a.positions[fastdiv((uint32_t)row, a.heads)] : 0;
-    }
-    u32x4 d[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        d[u] = ok[u] ? load_stream(reinterpret_cast<const u32x4 *>(a.q + (row0 + u) * kHeadDim) + lane)
-                     : u32x4{0u, 0u, 0u, 0u};
+    const int64_t pos = a.positions[fastdiv((uint32_t)row, a.heads)];
+    const u32x4 d = load_stream(reinterpret_cast<const u32x4 *>(a.q + row * kHeadDim) + lane);
     float w[8];
     if (HAS_W)
         unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.q_w)[lane], w);
-    f32x4 cv[U], sv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        cv[u] = f32x4{1.f, 1.f, 1.f, 1.f};
-        sv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (lane >= kRopeLane) {
-            const f32x4 *cs = reinterpret_cast<const f32x4 *>(
-                a.cos_sin + clamp_position(pos[u], a.max_position) * kRopeDim);
-            cv[u] = cs[lane - kRopeLane];
-            sv[u] = cs[lane - kRopeLane + 8];
-        }
+    f32x4 cv = f32x4{1.f, 1.f, 1.f, 1.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (lane >= kRopeLane) {
+        const f32x4 *cs = reinterpret_cast<const f32x4 *>(
+            a.cos_sin + clamp_position(pos, a.max_position) * kRopeDim);
+        cv = cs[lane - kRopeLane];
+        sv = cs[lane - kRopeLane + 8];
     }
+    float x[8], y[8];
+    unpack_bf16x8(d, x);
+    const float inv = inv_rms(x, a.eps);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if (!ok[u])
-            break;
+    for (int e = 0; e < 8; ++e) {
+        const float t = x[e] * inv;
+        y[e] = HAS_W ? t * w[e] : t;
+    }
+    if (lane >= kRopeLane)
+        rope8(y, cv, sv);
+    store_stream(reinterpret_cast<u32x4 *>(a.q + row * kHeadDim) + lane, pack_bf16x8<HW>(y));
+}
+
+// Heads h0 .. h0+n-1 of one token (n = min(U, H - h0)) on one wavefront, one
+// row after another: the token's position, its cos/sin row and the q weight
+// are loaded once for the chunk, then each row is loaded, normalized, rotated
+// and stored in turn (one row's load in flight, as with one row per
+// wavefront).  Measured on MI355X, two heads per wavefront beat one by 2.5-4%
+// up to about 2^19 q rows (decode-sized batches) and tie or lose above.
+template <int U, bool HAS_W, bool HW>
+__device__ __forceinline__ void q_chunk(const KernelArgs &a, uint32_t wv, uint32_t lane)
+{
+    const uint32_t t = fastdiv(wv, a.chunk_div);
+    const uint32_t h0 = (wv - t * a.chunks) * U;
+    const uint32_t n = min((uint32_t)U, a.num_heads - h0);
+    const int64_t row0 = (int64_t)t * a.num_heads + h0;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + row0 * kHeadDim) + lane;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.q + row0 * kHeadDim) + lane;
+    u32x4 d = load_stream(src);
+    float w[8];
+    if (HAS_W)
+        unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.q_w)[lane], w);
+    const int64_t pos = a.positions[t];
+    f32x4 cv = f32x4{1.f, 1.f, 1.f, 1.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (lane >= kRopeLane) {
+        const f32x4 *cs = reinterpret_cast<const f32x4 *>(
+            a.cos_sin + clamp_position(pos, a.max_position) * kRopeDim);
+        cv = cs[lane - kRopeLane];
+        sv = cs[lane - kRopeLane + 8];
+    }
+    for (uint32_t j = 0; j < n; ++j) {
         float x[8], y[8];
-        unpack_bf16x8(d[u], x);
+        unpack_bf16x8(d, x);
         const float inv = inv_rms(x, a.eps);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float t = x[e] * inv;
-            y[e] = HAS_W ? t * w[e] : t;
+            const float tt = x[e] * inv;
+            y[e] = HAS_W ? tt * w[e] : tt;
         }
         if (lane >= kRopeLane)
-            rope8(y, cv[u], sv[u]);
-        store_stream(reinterpret_cast<u32x4 *>(a.q + (row0 + u) * kHeadDim) + lane, pack_bf16x8<HW>(y));
+            rope8(y, cv, sv);
+        store_stream(dst + j * 64, pack_bf16x8<HW>(y));
+        if (j + 1 < n)
+            d = load_stream(src + (j + 1) * 64);
     }
 }
 
@@ -214,9 +241,13 @@ __global__ __launch_bounds__(512) void qkv_prep_kernel(KernelArgs a)
             kv_row<HW>(a, t, lane);
     } else {
         const int64_t wv = (int64_t)(blockIdx.x - a.kv_blocks) * waves_per_block + wave;
-        const int64_t row0 = wv * U;
-        if (row0 < a.q_rows)
-            q_rows<U, HAS_W, HW>(a, row0, lane);
+        if constexpr (U == 1) {
+            if (wv < a.q_rows)
+                q_row<HAS_W, HW>(a, wv, lane);
+        } else {
+            if (wv < a.num_tokens * (int64_t)a.chunks)
+                q_chunk<U, HAS_W, HW>(a, (uint32_t)wv, lane);
+        }
     }
 }
 

@@ -63,7 +63,10 @@ typedef struct {
     int32_t rope_dim;         /* must be 64 (the trailing dims of each row) */
     int32_t block_size;       /* B >= 1 cache slots per block */
     float eps;                /* >= 0, finite; added to the mean square */
-    int32_t rows_per_wave;    /* 0 = launch heuristic; 1, 2 or 4 q rows per wavefront */
+    int32_t rows_per_wave;    /* 0 = launch heuristic; 1 = one q row per wavefront;
+                                 2 or 4 = that many consecutive heads of one
+                                 token per wavefront, one after another (the
+                                 heuristic takes 2 up to 2^19 q rows, else 1) */
     int32_t waves_per_block;  /* 0 = launch heuristic; 1, 2, 4 or 8 forces it */
     int32_t convert;          /* 0 = heuristic, 1 = integer bf16/E4M3 rounding,
                                  2 = gfx950 conversion instructions; both give

@@ -133,8 +133,15 @@ def test_unsupported_head_dim():
 def test_launch_shape_heuristic():
     cfg = qp.make_config(64)
     small = qp.qkv_prep_launch_shape(cfg, 256, 16)
-    assert small.rows_per_wave == 1 and small.waves_per_block == 1 and small.convert == 2
-    assert small.kv_blocks == 16 and small.q_blocks == 16 * 64 and small.grid == 16 * 65
+    # decode-sized: two heads of a token per wavefront, up to 2^19 q rows
+    assert small.rows_per_wave == 2 and small.waves_per_block == 1 and small.convert == 2
+    assert small.kv_blocks == 16 and small.q_blocks == 16 * 32 and small.grid == 16 * 33
+    assert qp.qkv_prep_launch_shape(cfg, 256, 8192).rows_per_wave == 2        # 2^19 rows
+    assert qp.qkv_prep_launch_shape(cfg, 256, 8193).rows_per_wave == 1
+    one_head = qp.qkv_prep_launch_shape(qp.make_config(1), 256, 100)
+    assert one_head.rows_per_wave == 1 and one_head.q_blocks == 100
+    odd_heads = qp.qkv_prep_launch_shape(qp.make_config(5), 256, 10)
+    assert odd_heads.rows_per_wave == 2 and odd_heads.q_blocks == 10 * 3      # ceil(5 / 2) per token
     assert qp.qkv_prep_launch_shape(cfg, 256, 0).grid == 0
     big = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 131072)
     assert big.rows_per_wave == 1 and big.waves_per_block == 1
@@ -146,10 +153,10 @@ def test_launch_shape_heuristic():
     forced = qp.qkv_prep_launch_shape(qp.make_config(64, rows_per_wave=2, waves_per_block=8,
                                                      convert=1), 256, 1000)
     assert (forced.rows_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
-    assert forced.q_blocks == -(-(-(-1000 * 64 // 2)) // 8)
+    assert forced.q_blocks == -(-(1000 * 32) // 8)
     assert forced.kv_blocks == -(-1000 // 8)
     odd = qp.qkv_prep_launch_shape(qp.make_config(3, waves_per_block=4), 256, 5)
-    assert odd.q_blocks == 4 and odd.kv_blocks == 2
+    assert odd.rows_per_wave == 2 and odd.q_blocks == 3 and odd.kv_blocks == 2   # 5 * 2 wavefronts / 4
 
 
 def test_fast_division_used_by_the_kernel():
