@@ -199,9 +199,10 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
 /* The launch qkv_prep_run would use for num_tokens tokens with config cfg on
  * a device with num_cus compute units (256 on MI355X).  Pure host code: needs
  * no device, so the launch heuristic can be inspected anywhere.  The current
- * heuristic (one q row per wavefront, one wavefront per workgroup, at every
- * size) does not depend on num_cus; the argument keeps the signature stable
- * for a device-dependent one. */
+ * heuristic (one wavefront per workgroup; two heads of a token per wavefront
+ * up to 2^19 q rows, one q row per wavefront above) does not depend on
+ * num_cus; the argument keeps the signature stable for a device-dependent
+ * one. */
 int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t num_tokens,
                           qkv_prep_launch *out);
 
