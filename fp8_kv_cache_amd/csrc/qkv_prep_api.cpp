@@ -112,6 +112,13 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     return s;
 }
 
+// Row indices are 32-bit inside the kernel: T * H must stay below 2^31.  Also
+// keeps the launch-shape arithmetic (T * H, T * ceil(H / U)) inside int64.
+bool rows_fit(const qkv_prep_config &c, int64_t T)
+{
+    return T <= (int64_t)0x7fffffff / c.num_heads;
+}
+
 int check_config(const qkv_prep_config *cfg)
 {
     if (!cfg)
@@ -151,10 +158,9 @@ int check_args(const qkv_prep_config &c, int num_cus, const qkv_prep_args *a)
         (a->kv_cache && !aligned(a->kv_cache, 16)) || !aligned(a->positions, 8) ||
         !aligned(a->slot_mapping, 8))
         return QKV_PREP_ERR_MISALIGNED;
-    const int64_t H = c.num_heads;
     const int64_t B = c.block_size;
     // Row and slot indices are 32-bit inside the kernel; addresses are 64-bit.
-    if (T > (int64_t)0x7fffffff / H || a->num_blocks > (int64_t)0x7fffffff / B ||
+    if (!rows_fit(c, T) || a->num_blocks > (int64_t)0x7fffffff / B ||
         a->max_position > ((int64_t)1 << 40))
         return QKV_PREP_ERR_UNSUPPORTED;
     // The dispatch counts work-items in 32 bits.
@@ -252,6 +258,8 @@ int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t n
         return rc;
     if (!out || num_tokens < 0)
         return QKV_PREP_ERR_INVALID_ARG;
+    if (!rows_fit(*cfg, num_tokens))
+        return QKV_PREP_ERR_UNSUPPORTED;
     const qkvp::LaunchShape s = choose_shape(*cfg, num_cus, num_tokens);
     out->rows_per_wave = s.rows_per_wave;
     out->waves_per_block = s.waves_per_block;

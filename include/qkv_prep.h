@@ -202,7 +202,9 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
  * heuristic (one wavefront per workgroup; two heads of a token per wavefront
  * up to 2^19 q rows, one q row per wavefront above) does not depend on
  * num_cus; the argument keeps the signature stable for a device-dependent
- * one. */
+ * one.  Returns QKV_PREP_ERR_INVALID_ARG for a NULL out or num_tokens < 0, and
+ * QKV_PREP_ERR_UNSUPPORTED when num_tokens * num_heads >= 2^31 (the limit of
+ * qkv_prep_run). */
 int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t num_tokens,
                           qkv_prep_launch *out);
 

@@ -155,6 +155,12 @@ def test_launch_shape_heuristic():
     assert (forced.rows_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
     assert forced.q_blocks == -(-(1000 * 32) // 8)
     assert forced.kv_blocks == -(-1000 // 8)
+    # the row limit of qkv_prep_run also bounds the shape query (no overflow)
+    for T in (2 ** 31 // 64, 2 ** 62, 2 ** 63 - 1):
+        with pytest.raises(qp.QkvPrepError) as e:
+            qp.qkv_prep_launch_shape(cfg, 256, T)
+        assert e.value.code == qp.ERR_UNSUPPORTED
+    assert qp.qkv_prep_launch_shape(cfg, 256, 2 ** 31 // 64 - 1).grid > 0
     odd = qp.qkv_prep_launch_shape(qp.make_config(3, waves_per_block=4), 256, 5)
     assert odd.rows_per_wave == 2 and odd.q_blocks == 3 and odd.kv_blocks == 2   # 5 * 2 wavefronts / 4
 
