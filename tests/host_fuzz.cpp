@@ -1,10 +1,16 @@
-// Host-only fuzz of the C ABI's argument checks and launch heuristic, built
-// with -fsanitize=address,undefined by tests/test_host_sanitized.py and linked
-// against the host API with the two kernel launchers stubbed out (nothing here
-// touches a GPU).  Extreme and random configs and arguments go through
-// qkv_prep_validate, qkv_prep_launch_shape, qkv_prep_supported and
-// qkv_prep_strerror; any undefined operation aborts the run, and the returned
-// values are checked against the documented contract.
+// Host-only fuzz of the C ABI, built with -fsanitize=address,undefined by
+// tests/test_host_sanitized.py and linked with the host API only.  The two
+// kernel launchers are stubbed (they record what they were given), and the six
+// HIP runtime calls the host API makes are defined here as a fake two-device
+// runtime, so nothing touches a GPU and no HIP library is linked.
+//  * Extreme and random configs and arguments go through qkv_prep_validate,
+//    qkv_prep_launch_shape, qkv_prep_supported and qkv_prep_strerror.
+//  * Handles are created on the fake devices and qkv_prep_run /
+//    qkv_prep_gather are called with extreme and random arguments: run's code
+//    must equal validate's, a launch happens exactly when the arguments are
+//    valid and non-empty, the launch's arguments and grid must be consistent,
+//    and the caller's current device must be restored after every call.
+// Any undefined operation aborts the run; contract violations are counted.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -15,10 +21,61 @@
 #include "qkv_prep_gather.h"
 #include "qkv_prep_launch.h"
 
+namespace {
+int launches = 0, gathers = 0;
+qkvp::KernelArgs last_k;
+qkvp::LaunchShape last_s;
+qkvp::GatherArgs last_g;
+int fake_current = 0, fake_device_at_launch = -1;
+}  // namespace
+
 namespace qkvp {
-hipError_t launch_qkv_prep(const KernelArgs &, const LaunchShape &, hipStream_t) { return hipSuccess; }
-hipError_t launch_gather(const GatherArgs &, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_qkv_prep(const KernelArgs &a, const LaunchShape &s, hipStream_t)
+{
+    ++launches;
+    last_k = a;
+    last_s = s;
+    fake_device_at_launch = fake_current;
+    return hipSuccess;
+}
+hipError_t launch_gather(const GatherArgs &a, int, hipStream_t)
+{
+    ++gathers;
+    last_g = a;
+    fake_device_at_launch = fake_current;
+    return hipSuccess;
+}
 }  // namespace qkvp
+
+// The fake runtime: two devices of 256 compute units.
+extern "C" {
+hipError_t hipGetDeviceCount(int *count)
+{
+    *count = 2;
+    return hipSuccess;
+}
+hipError_t hipDeviceGetAttribute(int *value, hipDeviceAttribute_t, int device)
+{
+    if (device < 0 || device > 1)
+        return hipErrorInvalidDevice;
+    *value = 256;
+    return hipSuccess;
+}
+hipError_t hipGetDevice(int *device)
+{
+    *device = fake_current;
+    return hipSuccess;
+}
+hipError_t hipSetDevice(int device)
+{
+    if (device < 0 || device > 1)
+        return hipErrorInvalidDevice;
+    fake_current = device;
+    return hipSuccess;
+}
+hipError_t hipGetLastError(void) { return hipSuccess; }
+hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+}
 
 namespace {
 
@@ -136,7 +193,100 @@ int main()
         expect(sup == 0 || sup == 1, "supported is 0/1", i);
         expect(std::strlen(qkv_prep_strerror((int)next())) > 0, "strerror non-empty", i);
     }
-    std::printf("cases %lld, valid argument sets %lld, launch shapes %lld, contract failures %d\n", cases,
-                ok_validate, ok_shape, failures);
+
+    // Handles on the fake devices: run and gather against the contract.
+    long long runs_ok = 0, gathers_ok = 0;
+    for (long long i = 0; i < 100000; ++i) {
+        qkv_prep_config c;
+        std::memset(&c, 0, sizeof(c));
+        c.num_heads = next() % 4 ? (int32_t)(1 + next() % 160) : pick32();
+        c.head_dim = 512;
+        c.rope_dim = 64;
+        c.block_size = next() % 4 ? (int32_t)(1 + next() % 128) : pick32();
+        c.eps = next() % 8 ? 1e-6f : pick_eps();
+        c.kv_store = (int32_t)(next() % 2);
+        const int device = (int)(next() % 3) - (next() % 8 == 0);   // -1..2, mostly 0/1
+        qkv_prep_t h = nullptr;
+        const int rc = qkv_prep_create(&c, device, &h);
+        const bool cfg_ok = c.num_heads >= 1 && c.block_size >= 1 && std::isfinite(c.eps) && c.eps >= 0.0f;
+        expect((rc == QKV_PREP_OK) == (cfg_ok && device >= 0 && device <= 1), "create succeeds iff valid", i);
+        expect((rc == QKV_PREP_OK) == (h != nullptr), "handle set only on success", i);
+        if (rc != QKV_PREP_OK)
+            continue;
+        for (int r = 0; r < 4; ++r) {
+            qkv_prep_args a;
+            std::memset(&a, 0, sizeof(a));
+            a.q = pick_ptr();
+            a.kv = pick_ptr();
+            a.q_norm_w = next() % 2 ? nullptr : pick_ptr();
+            a.kv_norm_w = pick_ptr();
+            a.positions = static_cast<const int64_t *>(pick_ptr());
+            a.cos_sin = static_cast<const float *>(pick_ptr());
+            a.max_position = next() % 2 ? (int64_t)(1 + next() % 200000) : pick64();
+            a.slot_mapping = static_cast<const int64_t *>(pick_ptr());
+            a.kv_cache = pick_ptr();
+            a.num_blocks = next() % 2 ? (int64_t)(next() % 100000) : pick64();
+            a.num_tokens = next() % 2 ? (int64_t)(next() % 300000) : pick64();
+            const int caller = (int)(next() % 2);
+            fake_current = caller;
+            const int before = launches;
+            const int rr = qkv_prep_run(h, &a, nullptr);
+            const int rv = qkv_prep_validate(&c, &a);
+            expect(rr == rv, "run code equals validate code", i);
+            expect(fake_current == caller, "run restores the caller's device", i);
+            const bool launched = launches != before;
+            expect(launched == (rr == QKV_PREP_OK && a.num_tokens > 0), "launch iff valid and non-empty", i);
+            if (launched) {
+                ++runs_ok;
+                expect(fake_device_at_launch == device, "launch on the handle's device", i);
+                const qkvp::KernelArgs &k = last_k;
+                expect(k.q == a.q && k.kv == a.kv && k.cache == a.kv_cache, "pointers passed through", i);
+                expect(k.num_tokens == a.num_tokens && k.q_rows == a.num_tokens * c.num_heads, "sizes", i);
+                expect(k.num_slots == a.num_blocks * c.block_size && k.num_slots < ((int64_t)1 << 31), "slots", i);
+                expect(k.kv_blocks == (uint32_t)last_s.kv_blocks, "kv blocks", i);
+                expect(k.chunks == (uint32_t)((c.num_heads + last_s.rows_per_wave - 1) / last_s.rows_per_wave),
+                       "chunks per token", i);
+                expect((int64_t)k.chunks * a.num_tokens < ((int64_t)1 << 31), "q wavefront index fits", i);
+                expect((last_s.kv_blocks + last_s.q_blocks) * 64 * last_s.waves_per_block < ((int64_t)1 << 32),
+                       "grid fits", i);
+                expect(last_s.q_blocks * last_s.waves_per_block >= a.num_tokens * (int64_t)k.chunks,
+                       "every q wavefront has a slot in the grid", i);
+                expect(last_s.kv_blocks * last_s.waves_per_block >= a.num_tokens, "every kv row covered", i);
+                expect(k.bf16_store == (c.kv_store == QKV_PREP_KV_BF16), "store mode", i);
+            }
+
+            qkv_prep_gather_args g;
+            std::memset(&g, 0, sizeof(g));
+            g.kv_cache = pick_ptr();
+            g.num_blocks = next() % 2 ? (int64_t)(next() % 100000) : pick64();
+            g.slots = static_cast<const int64_t *>(pick_ptr());
+            g.n = next() % 2 ? (int64_t)(next() % 100000) : pick64();
+            g.out = pick_ptr();
+            g.out_dtype = next() % 8 ? (int32_t)(next() % 2) : pick32();
+            fake_current = caller;
+            const int gbefore = gathers;
+            const int rg = qkv_prep_gather(h, &g, nullptr);
+            expect(rg >= 0 && rg <= 6, "gather code", i);
+            expect(fake_current == caller, "gather restores the caller's device", i);
+            const bool glaunched = gathers != gbefore;
+            expect(glaunched == (rg == QKV_PREP_OK && g.n > 0), "gather launch iff valid and non-empty", i);
+            if (c.kv_store == QKV_PREP_KV_BF16)
+                expect(rg == QKV_PREP_ERR_UNSUPPORTED || rg == QKV_PREP_ERR_INVALID_ARG, "bf16 handle has no reader", i);
+            if (glaunched) {
+                ++gathers_ok;
+                expect(last_g.n == g.n && g.n < ((int64_t)1 << 26), "gather rows", i);
+                expect(last_g.num_slots == g.num_blocks * c.block_size && last_g.num_slots < ((int64_t)1 << 31),
+                       "gather slots", i);
+                expect(last_g.out_bf16 == (g.out_dtype == QKV_PREP_OUT_BF16), "gather dtype", i);
+            }
+        }
+        expect(qkv_prep_destroy(h) == QKV_PREP_OK, "destroy", i);
+    }
+    expect(qkv_prep_destroy(nullptr) == QKV_PREP_OK, "destroy NULL", 0);
+    expect(qkv_prep_run(nullptr, nullptr, nullptr) == QKV_PREP_ERR_INVALID_ARG, "run NULL handle", 0);
+    expect(qkv_prep_gather(nullptr, nullptr, nullptr) == QKV_PREP_ERR_INVALID_ARG, "gather NULL handle", 0);
+
+    std::printf("cases %lld, valid argument sets %lld, launch shapes %lld, runs launched %lld, gathers launched "
+                "%lld, contract failures %d\n", cases, ok_validate, ok_shape, runs_ok, gathers_ok, failures);
     return failures ? 1 : 0;
 }
