@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqkv_prep.so")
 SOURCES = [os.path.join(CSRC, "qkv_prep_kernels.hip"), os.path.join(CSRC, "qkv_prep_api.cpp"),
            os.path.join(CSRC, "qkv_prep_gather.hip"), os.path.join(CSRC, "qkv_prep_probe.hip"),
-           os.path.join(CSRC, "mxfp8_norm_quant.hip")]
+           os.path.join(CSRC, "mxfp8_norm_quant.hip"), os.path.join(CSRC, "mxfp8_api.cpp")]
 
 # -ffp-contract=off: no multiply is fused into an add unless the source asks
 # for an fma, so every fp32 step rounds as the numerics contract states.

@@ -9,28 +9,13 @@
 // contract's order), so all of them hold the same bits.  A 32-element scale
 // block is 4 consecutive chunks held by 4 consecutive lanes, so its amax is
 // two DPP max steps.
+#include "mxfp8_launch.h"
 #include "qkvp_device.h"
-#include "qkv_prep.h"
-#include "qkv_prep_mxfp8.h"
 
 namespace qkvp {
 namespace {
 
 using namespace dev;
-
-struct MxArgs {
-    const uint16_t *x;
-    const uint16_t *residual;
-    uint16_t *residual_out;
-    const uint16_t *gamma;
-    uint8_t *quant_out;
-    uint8_t *scale_out;
-    int64_t m;
-    int64_t rows_padded;
-    int32_t hidden;
-    int32_t padded_cols;
-    float eps;
-};
 
 __device__ __forceinline__ int64_t swizzled_offset(int64_t row, int64_t col, int64_t padded_cols)
 {
@@ -177,68 +162,29 @@ hipError_t launch_k(const MxArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-
 }  // namespace
-}  // namespace qkvp
 
-extern "C" int64_t qkv_prep_mxfp8_scale_bytes(int64_t m, int32_t hidden)
+hipError_t launch_mxfp8(const MxArgs &a, hipStream_t st)
 {
-    if (m < 0 || hidden <= 0 || hidden % 128)
-        return -1;
-    const int64_t cols = hidden / 32;
-    return (m + 127) / 128 * 128 * ((cols + 3) / 4 * 4);
-}
-
-extern "C" int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *a, void *stream)
-{
-    using namespace qkvp;
-    if (!a || a->m < 0 || !(a->eps >= 0.0f) || a->eps > 3.4e38f)
-        return QKV_PREP_ERR_INVALID_ARG;
-    if (a->hidden <= 0 || a->hidden % 512 || a->hidden > 8192)
-        return QKV_PREP_ERR_UNSUPPORTED;
-    if (a->m == 0)
-        return QKV_PREP_OK;
-    if (!a->x || !a->gamma || !a->quant_out || !a->scale_out)
-        return QKV_PREP_ERR_INVALID_ARG;
-    if (!aligned16(a->x) || !aligned16(a->gamma) || !aligned16(a->quant_out) ||
-        (a->residual && !aligned16(a->residual)) || (a->residual_out && !aligned16(a->residual_out)))
-        return QKV_PREP_ERR_MISALIGNED;
-    const int64_t rows_padded = (a->m + 127) / 128 * 128;
-    if (rows_padded >= ((int64_t)1 << 31) || rows_padded * a->hidden / 8 >= ((int64_t)1 << 32))
-        return QKV_PREP_ERR_UNSUPPORTED;
-    MxArgs k;
-    k.x = static_cast<const uint16_t *>(a->x);
-    k.residual = static_cast<const uint16_t *>(a->residual);
-    k.residual_out = static_cast<uint16_t *>(a->residual_out);
-    k.gamma = static_cast<const uint16_t *>(a->gamma);
-    k.quant_out = static_cast<uint8_t *>(a->quant_out);
-    k.scale_out = static_cast<uint8_t *>(a->scale_out);
-    k.m = a->m;
-    k.rows_padded = rows_padded;
-    k.hidden = a->hidden;
-    k.padded_cols = (a->hidden / 32 + 3) / 4 * 4;
-    k.eps = a->eps;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    switch (a->hidden / 512) {
-    case 1: e = launch_k<1>(k, st); break;
-    case 2: e = launch_k<2>(k, st); break;
-    case 3: e = launch_k<3>(k, st); break;
-    case 4: e = launch_k<4>(k, st); break;
-    case 5: e = launch_k<5>(k, st); break;
-    case 6: e = launch_k<6>(k, st); break;
-    case 7: e = launch_k<7>(k, st); break;
-    case 8: e = launch_k<8>(k, st); break;
-    case 9: e = launch_k<9>(k, st); break;
-    case 10: e = launch_k<10>(k, st); break;
-    case 11: e = launch_k<11>(k, st); break;
-    case 12: e = launch_k<12>(k, st); break;
-    case 13: e = launch_k<13>(k, st); break;
-    case 14: e = launch_k<14>(k, st); break;
-    case 15: e = launch_k<15>(k, st); break;
-    case 16: e = launch_k<16>(k, st); break;
-    default: return QKV_PREP_ERR_UNSUPPORTED;
+    switch (a.hidden / 512) {
+    case 1: return launch_k<1>(a, st);
+    case 2: return launch_k<2>(a, st);
+    case 3: return launch_k<3>(a, st);
+    case 4: return launch_k<4>(a, st);
+    case 5: return launch_k<5>(a, st);
+    case 6: return launch_k<6>(a, st);
+    case 7: return launch_k<7>(a, st);
+    case 8: return launch_k<8>(a, st);
+    case 9: return launch_k<9>(a, st);
+    case 10: return launch_k<10>(a, st);
+    case 11: return launch_k<11>(a, st);
+    case 12: return launch_k<12>(a, st);
+    case 13: return launch_k<13>(a, st);
+    case 14: return launch_k<14>(a, st);
+    case 15: return launch_k<15>(a, st);
+    case 16: return launch_k<16>(a, st);
+    default: return hipErrorInvalidValue;
     }
-    return e == hipSuccess ? QKV_PREP_OK : QKV_PREP_ERR_LAUNCH;
 }
+
+}  // namespace qkvp

@@ -20,7 +20,7 @@ from fp8_kv_cache_amd import workloads as W
 SOURCES = {
     "op": ("qkv_prep_kernels.hip", "qkv_prep_launch.h", "qkvp_device.h", "qkv_prep_internal.h"),
     "gather": ("qkv_prep_gather.hip", "qkv_prep_gather.h", "qkvp_device.h", "qkv_prep_internal.h"),
-    "mxfp8": ("mxfp8_norm_quant.hip", "qkvp_device.h", "qkv_prep_internal.h"),
+    "mxfp8": ("mxfp8_norm_quant.hip", "mxfp8_launch.h", "qkvp_device.h", "qkv_prep_internal.h"),
 }
 KERNELS = {"op": "qkv_prep_kernel", "gather": "gather_kernel", "mxfp8": "mxfp8_kernel"}
 PREFIX = {"op": "qkv_prep", "gather": "qkv_prep_gather", "mxfp8": "mxfp8_norm_quant"}

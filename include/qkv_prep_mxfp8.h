@@ -47,14 +47,17 @@ typedef struct {
 } qkv_prep_mxfp8_args;
 
 /* Bytes of the swizzled scale buffer for m rows: round_up(m, 128) * hidden/32,
- * or -1 when hidden is not a positive multiple of 128. */
+ * or -1 when m < 0, hidden is not a positive multiple of 128, or the size does
+ * not fit in int64_t. */
 int64_t qkv_prep_mxfp8_scale_bytes(int64_t m, int32_t hidden);
 
 /* Enqueue on `stream` (a hipStream_t; NULL = the null stream) of the current
  * HIP device and return.  Return codes are those of qkv_prep.h:
  * QKV_PREP_ERR_INVALID_ARG (NULL pointer, negative m, bad eps),
  * QKV_PREP_ERR_MISALIGNED, QKV_PREP_ERR_UNSUPPORTED (hidden not a multiple of
- * 512 or above 8192, or too many rows for one dispatch), QKV_PREP_ERR_LAUNCH.
+ * 512 or above 8192, m > 2^31 - 128, or round_up(m, 128) * hidden >= 2^35:
+ * the dispatch indexes rows and 16-byte chunks in 32 bits),
+ * QKV_PREP_ERR_LAUNCH.
  * On an argument error nothing is launched.  No device memory is allocated. */
 int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *args, void *stream);
 

@@ -1,5 +1,6 @@
 // Host-only fuzz of the C ABI, built with -fsanitize=address,undefined by
-// tests/test_host_sanitized.py and linked with the host API only.  The two
+// tests/test_host_sanitized.py and linked with the host API only
+// (qkv_prep_api.cpp, mxfp8_api.cpp).  The two
 // kernel launchers are stubbed (they record what they were given), and the six
 // HIP runtime calls the host API makes are defined here as a fake two-device
 // runtime, so nothing touches a GPU and no HIP library is linked.
@@ -10,6 +11,9 @@
 //    must equal validate's, a launch happens exactly when the arguments are
 //    valid and non-empty, the launch's arguments and grid must be consistent,
 //    and the caller's current device must be restored after every call.
+//  * qkv_prep_mxfp8_scale_bytes and qkv_prep_mxfp8_norm_quant on extreme and
+//    random shapes and pointers: sizes against a 128-bit reference, a launch
+//    exactly when valid, the launch's rows and scale layout.
 // Any undefined operation aborts the run; contract violations are counted.
 #include <cmath>
 #include <cstdint>
@@ -20,6 +24,8 @@
 #include "qkv_prep.h"
 #include "qkv_prep_gather.h"
 #include "qkv_prep_launch.h"
+#include "qkv_prep_mxfp8.h"
+#include "mxfp8_launch.h"
 
 namespace {
 int launches = 0, gathers = 0;
@@ -43,6 +49,14 @@ hipError_t launch_gather(const GatherArgs &a, int, hipStream_t)
     ++gathers;
     last_g = a;
     fake_device_at_launch = fake_current;
+    return hipSuccess;
+}
+int mx_launches = 0;
+MxArgs last_mx;
+hipError_t launch_mxfp8(const MxArgs &a, hipStream_t)
+{
+    ++mx_launches;
+    last_mx = a;
     return hipSuccess;
 }
 }  // namespace qkvp
@@ -286,7 +300,48 @@ int main()
     expect(qkv_prep_run(nullptr, nullptr, nullptr) == QKV_PREP_ERR_INVALID_ARG, "run NULL handle", 0);
     expect(qkv_prep_gather(nullptr, nullptr, nullptr) == QKV_PREP_ERR_INVALID_ARG, "gather NULL handle", 0);
 
+    // The MXFP8 entry points.
+    long long mx_ok = 0;
+    for (long long i = 0; i < 200000; ++i) {
+        const int64_t m = next() % 2 ? (int64_t)(next() % 100000) : pick64();
+        const int32_t hidden = next() % 2 ? (int32_t)(512 * (next() % 18)) : pick32();
+        const int64_t sb = qkv_prep_mxfp8_scale_bytes(m, hidden);
+        if (m < 0 || hidden <= 0 || hidden % 128) {
+            expect(sb == -1, "scale bytes -1 for bad shapes", i);
+        } else {
+            const __int128 want = ((__int128)m + 127) / 128 * 128 * (hidden / 32);
+            expect(want > INT64_MAX ? sb == -1 : (__int128)sb == want, "scale bytes value", i);
+        }
+        qkv_prep_mxfp8_args a;
+        std::memset(&a, 0, sizeof(a));
+        a.x = pick_ptr();
+        a.residual = next() % 2 ? nullptr : pick_ptr();
+        a.residual_out = next() % 2 ? nullptr : pick_ptr();
+        a.gamma = pick_ptr();
+        a.quant_out = pick_ptr();
+        a.scale_out = pick_ptr();
+        a.m = m;
+        a.hidden = hidden;
+        a.eps = next() % 4 ? 1e-6f : pick_eps();
+        const int before = qkvp::mx_launches;
+        const int rc = qkv_prep_mxfp8_norm_quant(&a, nullptr);
+        expect(rc >= 0 && rc <= 6 && rc != QKV_PREP_ERR_NO_DEVICE && rc != QKV_PREP_ERR_DEVICE, "mxfp8 code", i);
+        const bool launched = qkvp::mx_launches != before;
+        expect(launched == (rc == QKV_PREP_OK && m > 0), "mxfp8 launch iff valid and non-empty", i);
+        if (launched) {
+            ++mx_ok;
+            const qkvp::MxArgs &k = qkvp::last_mx;
+            expect(hidden >= 512 && hidden <= 8192 && hidden % 512 == 0, "hidden supported", i);
+            expect(k.rows_padded == (m + 127) / 128 * 128 && k.rows_padded < ((int64_t)1 << 31), "rows", i);
+            expect(k.rows_padded * hidden / 8 < ((int64_t)1 << 32), "chunk indices fit", i);
+            expect(k.padded_cols == hidden / 32 && (int64_t)k.rows_padded * k.padded_cols == sb, "scale layout", i);
+            expect(std::isfinite(k.eps) && k.eps >= 0.0f, "eps", i);
+        }
+    }
+    expect(qkv_prep_mxfp8_norm_quant(nullptr, nullptr) == QKV_PREP_ERR_INVALID_ARG, "mxfp8 NULL", 0);
+
     std::printf("cases %lld, valid argument sets %lld, launch shapes %lld, runs launched %lld, gathers launched "
-                "%lld, contract failures %d\n", cases, ok_validate, ok_shape, runs_ok, gathers_ok, failures);
+                "%lld, mxfp8 launched %lld, contract failures %d\n", cases, ok_validate, ok_shape, runs_ok,
+                gathers_ok, mx_ok, failures);
     return failures ? 1 : 0;
 }
