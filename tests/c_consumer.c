@@ -1,0 +1,175 @@
+/* A C99 consumer of the library: no Python, no torch.  It includes only the
+ * public header and the HIP runtime's C API, allocates device memory, runs
+ * qkv_prep_run and qkv_prep_gather on a small ragged case (37 tokens x 12
+ * heads, 16-slot blocks, skipped and out-of-range slots, a poisoned cache) and
+ * compares q, the whole cache and the gathered rows with the oracle's C
+ * entry points (test infrastructure, compiled into this test program) byte
+ * for byte.  Exit status 0 = bit-exact; the last line printed says which part
+ * differed otherwise. */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "qkv_prep.h"
+
+/* The oracle (oracle/qkv_oracle.c). */
+int orc_qkv_prep(int64_t num_tokens, int32_t num_heads, const uint16_t *q_in, uint16_t *q_out,
+                 const uint16_t *kv, const uint16_t *q_w, const uint16_t *kv_w, const int64_t *positions,
+                 const float *cos_sin, int64_t max_position, const int64_t *slot_mapping, uint8_t *cache,
+                 int64_t num_blocks, int32_t block_size, float eps, int nthreads);
+void orc_gather_dequant(const uint8_t *cache, int64_t num_blocks, int32_t block_size, const int64_t *slots,
+                        int64_t n, float *out);
+
+enum { T = 37, H = 12, B = 16, NB = 5, P = 1000, D = 512 };
+
+static uint64_t state = 0x5DEECE66Dull;
+static uint64_t next(void) /* splitmix64 */
+{
+    uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* A random bf16 bit pattern of magnitude 2^-7 .. 2^4 (any finite value is a
+ * valid input; these are just not extreme). */
+static uint16_t rand_bf16(void)
+{
+    const uint64_t r = next();
+    return (uint16_t)(((r & 1) << 15) | ((120 + (r >> 1) % 12) << 7) | ((r >> 8) & 0x7f));
+}
+
+#define CHECK_HIP(x)                                                                     \
+    do {                                                                                 \
+        if ((x) != hipSuccess) {                                                         \
+            printf("HIP call failed at line %d\n", __LINE__);                            \
+            return 2;                                                                    \
+        }                                                                                \
+    } while (0)
+
+int main(void)
+{
+    static uint16_t q[T * H * D], q_out[T * H * D], q_ref[T * H * D], kv[T * D], qw[D], kvw[D];
+    static int64_t pos[T], slots[T + 2];
+    static float cs[P * 64], rows[(T + 2) * D], rows_ref[(T + 2) * D];
+    static uint8_t cache[NB * B * 584], cache_out[NB * B * 584], cache_ref[NB * B * 584];
+    const size_t qn = sizeof(q), kvn = sizeof(kv), csn = sizeof(cs), cn = sizeof(cache);
+    int i;
+
+    for (i = 0; i < T * H * D; ++i)
+        q[i] = rand_bf16();
+    for (i = 0; i < T * D; ++i)
+        kv[i] = rand_bf16();
+    for (i = 0; i < D; ++i) {
+        qw[i] = (uint16_t)(0x3F80 + (int)(next() % 33) - 16); /* bf16 near 1.0 */
+        kvw[i] = (uint16_t)(0x3F80 + (int)(next() % 33) - 16);
+    }
+    for (i = 0; i < P * 64; ++i)
+        cs[i] = (float)((double)(next() >> 11) / 9007199254740992.0 * 2.0 - 1.0);
+    for (i = 0; i < T; ++i) {
+        pos[i] = (int64_t)(next() % P);
+        slots[i] = (int64_t)((i * 37 + 11) % (NB * B)); /* distinct: 37 is coprime to 80 */
+    }
+    slots[3] = -1;
+    slots[20] = NB * B;      /* at capacity: skipped */
+    slots[T] = -5;           /* two more rows for the reader */
+    slots[T + 1] = 7;
+    for (i = 0; i < (int)cn; ++i)
+        cache[i] = (uint8_t)next();
+
+    void *dq, *dkv, *dqw, *dkvw, *dpos, *dcs, *dslots, *dcache, *drows;
+    CHECK_HIP(hipMalloc(&dq, qn));
+    CHECK_HIP(hipMalloc(&dkv, kvn));
+    CHECK_HIP(hipMalloc(&dqw, sizeof(qw)));
+    CHECK_HIP(hipMalloc(&dkvw, sizeof(kvw)));
+    CHECK_HIP(hipMalloc(&dpos, sizeof(pos)));
+    CHECK_HIP(hipMalloc(&dcs, csn));
+    CHECK_HIP(hipMalloc(&dslots, sizeof(slots)));
+    CHECK_HIP(hipMalloc(&dcache, cn));
+    CHECK_HIP(hipMalloc(&drows, sizeof(rows)));
+    CHECK_HIP(hipMemcpy(dq, q, qn, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dkv, kv, kvn, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dqw, qw, sizeof(qw), hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dkvw, kvw, sizeof(kvw), hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dpos, pos, sizeof(pos), hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dcs, cs, csn, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dslots, slots, sizeof(slots), hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dcache, cache, cn, hipMemcpyHostToDevice));
+
+    qkv_prep_config cfg;
+    memset(&cfg, 0, sizeof(cfg));
+    cfg.num_heads = H;
+    cfg.head_dim = D;
+    cfg.rope_dim = 64;
+    cfg.block_size = B;
+    cfg.eps = 1e-6f;
+    cfg.kv_store = QKV_PREP_KV_FP8;
+    qkv_prep_t h = NULL;
+    int rc = qkv_prep_create(&cfg, 0, &h);
+    if (rc != QKV_PREP_OK) {
+        printf("qkv_prep_create: %s\n", qkv_prep_strerror(rc));
+        return 2;
+    }
+    qkv_prep_args a;
+    memset(&a, 0, sizeof(a));
+    a.q = dq;
+    a.kv = dkv;
+    a.q_norm_w = dqw;
+    a.kv_norm_w = dkvw;
+    a.positions = (const int64_t *)dpos;
+    a.cos_sin = (const float *)dcs;
+    a.max_position = P;
+    a.slot_mapping = (const int64_t *)dslots;
+    a.kv_cache = dcache;
+    a.num_blocks = NB;
+    a.num_tokens = T;
+    rc = qkv_prep_run(h, &a, NULL);
+    if (rc != QKV_PREP_OK) {
+        printf("qkv_prep_run: %s\n", qkv_prep_strerror(rc));
+        return 2;
+    }
+    qkv_prep_gather_args g;
+    memset(&g, 0, sizeof(g));
+    g.kv_cache = dcache;
+    g.num_blocks = NB;
+    g.slots = (const int64_t *)dslots;
+    g.n = T + 2;
+    g.out = drows;
+    g.out_dtype = QKV_PREP_OUT_F32;
+    rc = qkv_prep_gather(h, &g, NULL);
+    if (rc != QKV_PREP_OK) {
+        printf("qkv_prep_gather: %s\n", qkv_prep_strerror(rc));
+        return 2;
+    }
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_HIP(hipMemcpy(q_out, dq, qn, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(cache_out, dcache, cn, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(rows, drows, sizeof(rows), hipMemcpyDeviceToHost));
+    qkv_prep_destroy(h);
+    hipFree(dq); hipFree(dkv); hipFree(dqw); hipFree(dkvw); hipFree(dpos);
+    hipFree(dcs); hipFree(dslots); hipFree(dcache); hipFree(drows);
+
+    memcpy(cache_ref, cache, cn);
+    if (orc_qkv_prep(T, H, q, q_ref, kv, qw, kvw, pos, cs, P, slots, cache_ref, NB, B, 1e-6f, 1) != 0) {
+        printf("oracle rejected the case\n");
+        return 2;
+    }
+    orc_gather_dequant(cache_ref, NB, B, slots, T + 2, rows_ref);
+    if (memcmp(q_out, q_ref, qn) != 0) {
+        printf("c consumer: q differs from the oracle\n");
+        return 1;
+    }
+    if (memcmp(cache_out, cache_ref, cn) != 0) {
+        printf("c consumer: cache differs from the oracle\n");
+        return 1;
+    }
+    if (memcmp(rows, rows_ref, sizeof(rows)) != 0) {
+        printf("c consumer: gathered rows differ from the oracle\n");
+        return 1;
+    }
+    printf("c consumer: q, cache and gathered rows bit-exact (%d tokens x %d heads)\n", T, H);
+    return 0;
+}
