@@ -73,6 +73,14 @@ def test_forced_launch_shapes(T, H, rpw, wpb):
           convert=2 if (T + rpw) % 2 else 1)
 
 
+@pytest.mark.parametrize("T,H", [(1, 48), (17, 96), (511, 48), (2049, 96), (4096, 48)])
+def test_head_counts_the_pages_measure(T, H):
+    # 48 and 96 heads appear in the pages' shape lists; default (heuristic)
+    # launch, ragged token counts.
+    check(W.custom(T, H, seed=300 + T + H, num_skip=min(3, T - 1)))
+    check(W.custom(T, H, seed=301 + T + H), rows_per_wave=1)
+
+
 @pytest.mark.parametrize("T,H", [(1, 64), (17, 8), (512, 64), (2048, 128)])
 def test_weightless_q(T, H):
     check(W.custom(T, H, seed=200 + T), q_weight=False)
