@@ -195,15 +195,15 @@ def mxfp8_norm_quant(x, gamma, eps, *, residual=None, residual_out=None, quant_o
     """Torch wrapper of qkv_prep_mxfp8_norm_quant: x [m, hidden] bf16.  Returns
     (codes uint8 [m, hidden], swizzled scales uint8 [...])."""
     import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [m, hidden]")
     m, hidden = x.shape
-    for name, t in (("x", x), ("gamma", gamma), ("residual", residual), ("residual_out", residual_out)):
-        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
-            raise TypeError("%s must be a contiguous bfloat16 tensor" % name)
     if quant_out is None:
         quant_out = torch.empty((m, hidden), dtype=torch.uint8, device=x.device)
     if scale_out is None:
         n = qkv_prep_mxfp8_scale_bytes(m, hidden)
         scale_out = torch.empty(max(n, 0), dtype=torch.uint8, device=x.device)
+    check_mxfp8_tensors(x, gamma, residual, residual_out, quant_out, scale_out)
     args = QkvPrepMxfp8Args(x.data_ptr(), _ptr(residual), _ptr(residual_out), gamma.data_ptr(),
                             quant_out.data_ptr(), scale_out.data_ptr(), m, hidden, eps)
     if stream is None:
@@ -232,23 +232,87 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _expect(name, t, dtype, shape, device):
+    """One tensor's dtype, contiguity, device and (if given) shape."""
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def check_op_tensors(num_heads, block_size, slot_bytes, device, q, kv, q_norm_w, kv_norm_w, positions,
+                     cos_sin, slot_mapping, kv_cache):
+    """What the C side cannot see, since it takes bare pointers: every
+    tensor's dtype, contiguity, device and shape (q [T, H, 512], kv [T, 512],
+    weights [512], positions and slot_mapping [T], cos_sin [P, 64] with P >= 1,
+    a uint8 cache of whole blocks).  A wrong shape would otherwise become an
+    out-of-bounds access on the device.  Raises TypeError or ValueError."""
+    import torch
+    device = torch.device(device)
+    if q.dim() != 3 or q.shape[1] != num_heads or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [T, %d, 512], got %s" % (num_heads, tuple(q.shape)))
+    T = q.shape[0]
+    _expect("q", q, torch.bfloat16, None, device)
+    _expect("kv", kv, torch.bfloat16, (T, HEAD_DIM), device)
+    if q_norm_w is not None:
+        _expect("q_norm_w", q_norm_w, torch.bfloat16, (HEAD_DIM,), device)
+    _expect("kv_norm_w", kv_norm_w, torch.bfloat16, (HEAD_DIM,), device)
+    _expect("positions", positions, torch.int64, (T,), device)
+    _expect("slot_mapping", slot_mapping, torch.int64, (T,), device)
+    _expect("cos_sin", cos_sin, torch.float32, None, device)
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM or cos_sin.shape[0] < 1:
+        raise ValueError("cos_sin must be [P, 64] with P >= 1, got %s" % (tuple(cos_sin.shape),))
+    if kv_cache is not None:
+        _expect("kv_cache", kv_cache, torch.uint8, None, device)
+        if kv_cache.numel() % (block_size * slot_bytes):
+            raise ValueError("kv_cache must hold whole blocks of %d x %d bytes" % (block_size, slot_bytes))
+
+
+def check_gather_tensors(block_size, device, kv_cache, slots, out):
+    """The cache reader's tensors: a uint8 cache, int64 slots [n], an fp32 or
+    bf16 out [n, 512], all contiguous on `device`."""
+    import torch
+    device = torch.device(device)
+    _expect("kv_cache", kv_cache, torch.uint8, None, device)
+    if kv_cache.numel() % (block_size * SLOT_BYTES):
+        raise ValueError("kv_cache must hold whole blocks of %d x %d bytes" % (block_size, SLOT_BYTES))
+    if slots.dim() != 1:
+        raise ValueError("slots must be 1-D")
+    _expect("slots", slots, torch.int64, None, device)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16, got %s" % out.dtype)
+    _expect("out", out, out.dtype, (slots.numel(), HEAD_DIM), device)
+
+
+def check_mxfp8_tensors(x, gamma, residual, residual_out, quant_out, scale_out):
+    """The MXFP8 operator's tensors: bf16 x [m, hidden], gamma [hidden],
+    residual / residual_out [m, hidden] or None, uint8 codes [m, hidden] and a
+    uint8 scale buffer of at least qkv_prep_mxfp8_scale_bytes(m, hidden)
+    bytes, all contiguous on x's device."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [m, hidden]")
+    m, hidden = x.shape
+    _expect("x", x, torch.bfloat16, None, x.device)
+    _expect("gamma", gamma, torch.bfloat16, (hidden,), x.device)
+    for name, t in (("residual", residual), ("residual_out", residual_out)):
+        if t is not None:
+            _expect(name, t, torch.bfloat16, (m, hidden), x.device)
+    _expect("quant_out", quant_out, torch.uint8, (m, hidden), x.device)
+    _expect("scale_out", scale_out, torch.uint8, None, x.device)
+    need = qkv_prep_mxfp8_scale_bytes(m, hidden)
+    if need > 0 and scale_out.numel() < need:
+        raise ValueError("scale_out needs %d bytes, has %d" % (need, scale_out.numel()))
+
+
 def make_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
               num_blocks=None) -> QkvPrepArgs:
-    """Pointers and sizes from torch tensors (no copies, no checks beyond the
-    dtype/contiguity that the C side cannot see)."""
-    import torch
-    for name, t, dt in (("q", q, torch.bfloat16), ("kv", kv, torch.bfloat16),
-                        ("q_norm_w", q_norm_w, torch.bfloat16),
-                        ("kv_norm_w", kv_norm_w, torch.bfloat16),
-                        ("positions", positions, torch.int64), ("cos_sin", cos_sin, torch.float32),
-                        ("slot_mapping", slot_mapping, torch.int64),
-                        ("kv_cache", kv_cache, torch.uint8)):
-        if t is None:
-            continue
-        if t.dtype != dt:
-            raise TypeError("%s must be %s, got %s" % (name, dt, t.dtype))
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
+    """Pointers and sizes from torch tensors (no copies; the tensors are
+    checked by check_op_tensors first)."""
     T = q.shape[0]
     if num_blocks is None:
         num_blocks = kv_cache.shape[0] if kv_cache is not None else 0
@@ -275,11 +339,10 @@ class QkvPrep:
     def __call__(self, q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
                  stream=None):
         import torch
-        if q.dim() != 3 or q.shape[1] != self.cfg.num_heads or q.shape[2] != HEAD_DIM:
-            raise ValueError("q must be [T, %d, 512]" % self.cfg.num_heads)
+        check_op_tensors(self.cfg.num_heads, self.cfg.block_size, self.slot_bytes,
+                         torch.device("cuda", self.device), q, kv, q_norm_w, kv_norm_w, positions,
+                         cos_sin, slot_mapping, kv_cache)
         per_block = self.cfg.block_size * self.slot_bytes
-        if kv_cache is not None and kv_cache.numel() % per_block:
-            raise ValueError("kv_cache must be [num_blocks, block_size*%d] bytes" % self.slot_bytes)
         args = make_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
                          None if kv_cache is None else kv_cache.numel() // per_block)
         if stream is None:
@@ -290,14 +353,7 @@ class QkvPrep:
     def gather(self, kv_cache, slots, out, stream=None):
         """Read `slots` back out of an FP8 cache into `out` ([n, 512] fp32 or bf16)."""
         import torch
-        if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous():
-            raise TypeError("kv_cache must be a contiguous uint8 tensor")
-        if slots.dtype != torch.int64 or not slots.is_contiguous():
-            raise TypeError("slots must be a contiguous int64 tensor")
-        if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_contiguous():
-            raise TypeError("out must be a contiguous float32 or bfloat16 tensor")
-        if out.shape != (slots.numel(), HEAD_DIM):
-            raise ValueError("out must be [n, 512]")
+        check_gather_tensors(self.cfg.block_size, torch.device("cuda", self.device), kv_cache, slots, out)
         args = QkvPrepGatherArgs(kv_cache.data_ptr(), kv_cache.numel() // (self.cfg.block_size * SLOT_BYTES),
                                  slots.data_ptr(), slots.numel(), out.data_ptr(),
                                  OUT_F32 if out.dtype == torch.float32 else OUT_BF16)

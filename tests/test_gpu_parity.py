@@ -257,6 +257,10 @@ def test_bad_arguments_touch_nothing():
     with pytest.raises(qp.QkvPrepError) as e:
         qp.qkv_prep_run(op.handle, args, None)
     assert e.value.code == qp.ERR_MISALIGNED
+    # a short kv tensor is stopped by the binding before it reaches the device
+    with pytest.raises(ValueError):
+        op(inp["q"], inp["kv"][:-1], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+           inp["slot_mapping"], inp["cache"])
     torch.cuda.synchronize()
     assert torch.equal(before_q, inp["q"]) and torch.equal(before_c, inp["cache"])
 
