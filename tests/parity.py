@@ -145,6 +145,17 @@ def run_and_compare(w, inp, *, q_weight=True, chunk_tokens=4096, kv_store=0, **c
     return res
 
 
+def tiny_weights(seed, lo, hi, device):
+    """bf16 weights of magnitude 2^lo .. 2^(hi+1), random signs (bf16
+    subnormals included below 2^-126): they drive y down to ~1e-38, so kv
+    blocks reach the exponent clamp (scale byte 0) with non-zero codes and q
+    outputs become subnormal."""
+    g = torch.Generator().manual_seed(seed)
+    e = torch.randint(lo, hi, (512,), generator=g).float()
+    sign = torch.where(torch.rand(512, generator=g) < 0.5, -1.0, 1.0)
+    return (sign * torch.exp2(e) * (1 + torch.rand(512, generator=g))).to(torch.bfloat16).to(device)
+
+
 def assert_within_bar(res):
     assert res["cache_exact_mismatch"] == 0, res
     assert res["q_max_ulp"] <= 1, res

@@ -12,7 +12,7 @@ import torch
 import oracle
 from fp8_kv_cache_amd import workloads as W
 
-from parity import assert_bit_exact, assert_within_bar, run_and_compare
+from parity import CODE, EXP, assert_bit_exact, assert_within_bar, byte_roles, run_and_compare, tiny_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,29 @@ def test_head_counts_the_pages_measure(T, H):
     # launch, ragged token counts.
     check(W.custom(T, H, seed=300 + T + H, num_skip=min(3, T - 1)))
     check(W.custom(T, H, seed=301 + T + H), rows_per_wave=1)
+
+
+@pytest.mark.parametrize("rpw", [0, 1])
+def test_exponent_clamp_and_subnormal_outputs(rpw):
+    # Tiny weights: every kv block sits at the exponent clamp (scale byte 0)
+    # with non-zero and subnormal codes, and many q outputs are subnormal bf16.
+    w = W.custom(300, 4, seed=310)
+    inp = W.make_inputs(w, device=DEV)
+    inp["q_w"] = tiny_weights(311, -133, -115, DEV)
+    inp["kv_w"] = tiny_weights(312, -133, -122, DEV)
+    note("case tiny weights rows_per_wave=%d" % rpw)
+    res = run_and_compare(w, inp, rows_per_wave=rpw)
+    note("  -> %s" % res)
+    assert_bit_exact(res)
+    cache = inp["cache"].clone()
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    QkvPrep(4)(inp["q"].clone(), inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+               inp["slot_mapping"], cache)
+    torch.cuda.synchronize()
+    roles = byte_roles(inp["slot_mapping"].cpu().numpy(), w.num_blocks, w.block_size)
+    flat = cache.cpu().numpy().reshape(-1)
+    assert np.all(flat[roles == EXP] == 0)                      # every block at the clamp
+    assert np.count_nonzero(flat[roles == CODE] & 0x7F) > 1000   # ... with real codes
 
 
 @pytest.mark.parametrize("T,H", [(1, 64), (17, 8), (512, 64), (2048, 128)])

@@ -8,7 +8,7 @@ import oracle
 from fp8_kv_cache_amd import qkv_prep as qp
 from fp8_kv_cache_amd import workloads as W
 
-from parity import assert_bit_exact, run_and_compare
+from parity import assert_bit_exact, run_and_compare, tiny_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -179,3 +179,29 @@ def test_gather_full_cache_block_walk(dtype):
         got = W.as_u16(out)
         is_nan16 = ((got & 0x7F80) == 0x7F80) & ((got & 0x007F) != 0)
         assert _nan_aware_equal(got, oracle.f32_to_bf16(want), is_nan16, np.isnan(want))
+
+
+def test_subnormal_values_in_the_bf16_store_and_the_reader():
+    # Tiny weights: the bf16-store slots hold subnormal bf16 values, and the
+    # FP8 slots sit at the exponent clamp (scale 2^-127), so the reader's
+    # products code * 2^-127 are fp32 subnormals.
+    w = W.custom(300, 4, seed=740)
+    inp = W.make_inputs(w, device=DEV)
+    inp["q_w"] = tiny_weights(741, -133, -115, DEV)
+    inp["kv_w"] = tiny_weights(742, -133, -122, DEV)
+    note("tiny weights: bf16 store")
+    assert_bit_exact(run_and_compare(w, inp, kv_store=qp.KV_BF16))
+    note("tiny weights: reader")
+    op, cache = _insert(w, inp)
+    slots = inp["slot_mapping"]
+    want = oracle.gather_dequant(cache.cpu().numpy(), w.num_blocks, w.block_size, slots.cpu().numpy())
+    out32 = torch.empty((slots.numel(), 512), dtype=torch.float32, device=DEV)
+    out16 = torch.empty((slots.numel(), 512), dtype=torch.bfloat16, device=DEV)
+    op.gather(cache, slots, out32)
+    op.gather(cache, slots, out16)
+    torch.cuda.synchronize()
+    got = out32.cpu().numpy()
+    sub = (np.abs(want) < np.float32(2.0 ** -126)) & (want != 0)
+    assert np.count_nonzero(sub) > 1000                      # fp32 subnormals really occur
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(W.as_u16(out16), oracle.f32_to_bf16(want))
