@@ -67,3 +67,30 @@ def test_mxfp8_empty_is_a_no_op():
     gamma = torch.zeros(512, dtype=torch.bfloat16, device=DEV)
     codes, scales = qp.mxfp8_norm_quant(x, gamma, 1e-6)
     assert codes.numel() == 0 and scales.numel() == 0
+
+
+@pytest.mark.parametrize("eps,with_res", [(1e-6, False), (1e-6, True), (1e-30, True)])
+def test_mxfp8_subnormal_inputs(eps, with_res):
+    # bf16 subnormal x (and residual): the squares underflow, the normalized
+    # values are tiny, and the scale bytes sit at the bottom of the range
+    # (2 and 3 at eps = 1e-6, so the inverse scale is 2^125).
+    m, hidden = 130, 1024
+    g = torch.Generator().manual_seed(960)
+    def subnormal_bits():
+        b = torch.randint(0, 128, (m, hidden), generator=g, dtype=torch.int32)
+        b |= torch.randint(0, 2, (m, hidden), generator=g, dtype=torch.int32) << 15
+        return b.to(torch.int16).view(torch.bfloat16).to(DEV)
+    x = subnormal_bits()
+    r = subnormal_bits() if with_res else None
+    gamma = (0.1 * torch.randn(hidden, generator=g)).to(torch.bfloat16).to(DEV)
+    res_out = torch.empty_like(x) if with_res else None
+    codes, scales = qp.mxfp8_norm_quant(x, gamma, eps, residual=r, residual_out=res_out)
+    torch.cuda.synchronize()
+    wc, ws, wp = oracle.mxfp8_norm_quant(W.as_u16(x), W.as_u16(gamma), eps,
+                                         residual=W.as_u16(r) if with_res else None)
+    assert np.array_equal(scales.cpu().numpy(), ws)
+    assert np.array_equal(codes.cpu().numpy(), wc)
+    if with_res:
+        assert np.array_equal(W.as_u16(res_out), wp)
+    if eps == 1e-6:
+        assert set(np.unique(ws).tolist()) <= {0, 1, 2, 3, 4}       # the bottom of the scale range
