@@ -104,6 +104,20 @@ def test_exponent_clamp_and_subnormal_outputs(rpw):
     assert np.count_nonzero(flat[roles == CODE] & 0x7F) > 1000   # ... with real codes
 
 
+def test_sum_of_squares_overflow():
+    # Finite bf16 rows whose fp32 sum of squares overflows (x ~ 2^60..2^70):
+    # inv = 1/sqrt(inf) = 0, so the row's outputs are +-0 (signs kept) and a
+    # kv row becomes zero blocks (scale byte 0, codes +-0).
+    w = W.custom(40, 4, seed=320)
+    inp = W.make_inputs(w, device=DEV)
+    inp["q"][3] *= 2.0 ** 70
+    inp["q"][7, 1] *= 2.0 ** 60
+    inp["kv"][5] *= 2.0 ** 70
+    for rpw in (0, 1):
+        note("case sum-of-squares overflow rows_per_wave=%d" % rpw)
+        assert_bit_exact(run_and_compare(w, inp, rows_per_wave=rpw))
+
+
 @pytest.mark.parametrize("T,H", [(1, 64), (17, 8), (512, 64), (2048, 128)])
 def test_weightless_q(T, H):
     check(W.custom(T, H, seed=200 + T), q_weight=False)
