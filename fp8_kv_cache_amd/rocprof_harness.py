@@ -23,8 +23,8 @@ bytes only through TCC_BUBBLE, and on gfx950 the 128-byte requests land in its
 ones.  The reqs pass therefore also counts read bytes from the request-size
 counters directly (32, 64 and 128 bytes each), with no calibration.
 
-    python -m fp8_kv_cache_amd.rocprof_harness --workload prefill --out gpurun_out/prof
-    python -m fp8_kv_cache_amd.rocprof_harness --workload mxfp8 --out gpurun_out/prof
+    python -m fp8_kv_cache_amd.rocprof_harness --workload prefill --out prof_out
+    python -m fp8_kv_cache_amd.rocprof_harness --workload mxfp8 --out prof_out
 """
 from __future__ import annotations
 
@@ -121,7 +121,7 @@ def pick(d, want):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="prefill")
-    ap.add_argument("--out", default="gpurun_out/prof")
+    ap.add_argument("--out", default="prof_out")
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--passes", default="trace,fetch,write,reqs,waves")
     ap.add_argument("--wave-counters", default="OccupancyPercent,MeanOccupancyPerCU,SQ_WAVES")
