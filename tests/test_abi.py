@@ -276,3 +276,25 @@ def test_mxfp8_scale_bytes_and_argument_checks():
     assert code(residual=(5 << 20) + 4) == qp.ERR_MISALIGNED
     assert code(residual_out=(6 << 20) + 8) == qp.ERR_MISALIGNED
     assert code(m=1 << 26) == qp.ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    # A copy of the package with no libqkv_prep.so: importing the binding must
+    # raise, never fall back to anything else.
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.dirname(qp.__file__)
+    pkg = tmp_path / "fp8_kv_cache_amd"
+    pkg.mkdir()
+    for f in ("__init__.py", "qkv_prep.py", "workloads.py"):
+        shutil.copy(os.path.join(src, f), pkg / f)
+    code = ("import sys; sys.path.insert(0, sys.argv[1])\n"
+            "try:\n"
+            "    import fp8_kv_cache_amd.qkv_prep\n"
+            "except ImportError as e:\n"
+            "    print('ImportError:', e); sys.exit(0)\n"
+            "sys.exit(3)\n")
+    res = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "libqkv_prep.so is not built" in res.stdout
