@@ -67,7 +67,7 @@ SHAPES = [(1, 8), (4, 8), (17, 64), (64, 3), (511, 64), (777, 5), (1000, 1), (40
 
 
 @pytest.mark.parametrize("T,H", SHAPES)
-@pytest.mark.parametrize("rpw,wpb", [(1, 1), (1, 4), (2, 1), (2, 8), (4, 2), (4, 4)])
+@pytest.mark.parametrize("rpw,wpb", [(u, b) for u in (1, 2, 4) for b in (1, 2, 4, 8)])
 def test_forced_launch_shapes(T, H, rpw, wpb):
     check(W.custom(T, H, seed=100 + T + H), rows_per_wave=rpw, waves_per_block=wpb,
           convert=2 if (T + rpw) % 2 else 1)
