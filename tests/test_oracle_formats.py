@@ -91,17 +91,27 @@ def test_e4m3_round_trip_every_code():
     assert np.array_equal(again, codes.astype(np.uint8))
 
 
-def test_e4m3_matches_torch_cast_in_range():
-    # All fp32 magnitudes up to 448 with stride 7, both signs.  Inside this
-    # range torch's float8_e4m3fn cast is plain round-to-nearest-even.
-    chunk = 7 * (1 << 23)
-    for start in range(0, 0x43E00001, chunk):
-        bits = np.arange(start, min(start + chunk, 0x43E00001), 7, dtype=np.uint32)
-        x = bits.view(np.float32)
+def _over_chunks(fn, lo, hi, chunk=1 << 24):
+    """fn(start, stop) over [lo, hi) in chunks, on a thread pool (the oracle's
+    C loops and torch's casts release the GIL).  Returns the failing starts."""
+    from concurrent.futures import ThreadPoolExecutor
+    starts = range(lo, hi, chunk)
+    with ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+        ok = list(ex.map(lambda s: fn(s, min(s + chunk, hi)), starts))
+    return [hex(s) for s, good in zip(starts, ok) if not good]
+
+
+def test_e4m3_matches_torch_cast_on_every_in_range_pattern():
+    # Every fp32 bit pattern of magnitude up to 448 (0 .. 0x43E00000), both
+    # signs: about 2.3e9 values.  Inside this range torch's float8_e4m3fn cast
+    # is plain round-to-nearest-even.
+    def check(start, stop):
+        x = np.arange(start, stop, dtype=np.uint32).view(np.float32)
         x = np.concatenate([x, -x])
         ours = oracle.f32_to_e4m3(x)
         ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-        assert np.array_equal(ours, ref), hex(start)
+        return np.array_equal(ours, ref)
+    assert _over_chunks(check, 0, 0x43E00001) == []
 
 
 def test_e4m3_nearest_search_on_random_values():
@@ -148,6 +158,19 @@ def test_ue8m0_definition_on_random_patterns():
     assert not np.any(prev_fits & (e > -127))
     # the scale is an exact power of two and every scaled value fits 448
     assert np.all(np.abs(av * np.ldexp(1.0, -e)) <= 448.0)
+
+
+def test_ue8m0_definition_on_every_positive_pattern():
+    # Every positive finite fp32 amax (about 2.1e9 patterns): the exponent is
+    # in [-127, 127], amax fits 448 * 2^e, and e - 1 would not fit unless the
+    # clamp at -127 is active.  Comparisons are exact in float64.
+    def check(start, stop):
+        a = np.arange(start, stop, dtype=np.uint32).view(np.float32)
+        e = oracle.ue8m0_exponent(a).astype(np.int64)
+        av = a.astype(np.float64)
+        return bool(np.all((e >= -127) & (e <= 127)) and np.all(av <= np.ldexp(448.0, e)) and
+                    not np.any((av <= np.ldexp(448.0, e - 1)) & (e > -127)))
+    assert _over_chunks(check, 1, 0x7F800000) == []
 
 
 def test_ue8m0_power_of_two_boundaries():

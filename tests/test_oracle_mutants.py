@@ -23,7 +23,11 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "qkv_oracle.c")
 
 # Pin tests in increasing cost, so that a mutant is usually caught within
 # milliseconds.  The slow strided cross-checks against torch's casts come last.
-SLOW = {"test_bf16_matches_torch_cast_on_strided_patterns", "test_e4m3_matches_torch_cast_in_range"}
+SLOW = {"test_bf16_matches_torch_cast_on_strided_patterns"}
+# The exhaustive sweeps (billions of patterns) run once, directly, in
+# test_oracle_formats.py; the battery leaves them out.
+EXHAUSTIVE = {"test_e4m3_matches_torch_cast_on_every_in_range_pattern",
+              "test_ue8m0_definition_on_every_positive_pattern"}
 
 
 def _expand(name, fn):
@@ -44,7 +48,7 @@ def battery():
     tests = []
     for mod in (T_FMT, T_ROW, T_OP, T_SG, T_MX):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
-            if name.startswith("test_") and fn.__module__ == mod.__name__:
+            if name.startswith("test_") and fn.__module__ == mod.__name__ and name not in EXHAUSTIVE:
                 for n, call in _expand(name, fn):
                     tests.append((name in SLOW, n, call))
     tests.sort(key=lambda t: t[0])
