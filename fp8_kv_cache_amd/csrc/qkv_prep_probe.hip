@@ -4,10 +4,12 @@
 #include <stdint.h>
 
 #include "qkv_prep_probe.h"
+#include "qkvp_device.h"
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using qkvp::dev::u32x2;
+using qkvp::dev::u32x4;
 // One 16-byte non-temporal load and store per lane, 256-lane blocks: the
 // fastest of the copy shapes measured on MI355X (1, 2, 4, 8 and 16 loads per
 // lane; 256, 512 and 1024 lanes per block; plain or non-temporal; natural or
@@ -54,7 +56,47 @@ __global__ __launch_bounds__(kUpdateThreads) void stream_update(u32x4 *buf, int6
     }
 }
 
+// The operator's conversions (qkvp::dev::pack_e4m3 / pack_bf16) on four
+// values per thread.
+template <bool HW>
+__global__ __launch_bounds__(256) void convert_probe(const u32x4 *in, uint32_t *e4m3, u32x2 *bf16, int64_t quads)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= quads)
+        return;
+    const u32x4 v = in[i];
+    const float f0 = __uint_as_float(v[0]), f1 = __uint_as_float(v[1]);
+    const float f2 = __uint_as_float(v[2]), f3 = __uint_as_float(v[3]);
+    if (e4m3)
+        e4m3[i] = qkvp::dev::pack_e4m3<HW>(f0, f1, f2, f3);
+    if (bf16)
+        bf16[i] = u32x2{qkvp::dev::pack_bf16<HW>(f0, f1), qkvp::dev::pack_bf16<HW>(f2, f3)};
+}
+
 }  // namespace
+
+extern "C" int qkv_prep_probe_convert(const float *in, int64_t n, void *e4m3_out, void *bf16_out, int32_t convert,
+                                      void *stream)
+{
+    const uintptr_t pi = reinterpret_cast<uintptr_t>(in), pe = reinterpret_cast<uintptr_t>(e4m3_out),
+                    pb = reinterpret_cast<uintptr_t>(bf16_out);
+    if (n < 0 || (n & 3) || n >= ((int64_t)1 << 33) || (convert != 1 && convert != 2) || (pi & 15) ||
+        (pe & 3) || (pb & 7) || (n > 0 && !in))
+        return 1;
+    if (n == 0)
+        return 0;
+    const int64_t quads = n / 4;
+    const dim3 grid((uint32_t)((quads + 255) / 256)), block(256);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(in);
+    uint32_t *e = static_cast<uint32_t *>(e4m3_out);
+    u32x2 *b = static_cast<u32x2 *>(bf16_out);
+    if (convert == 2)
+        hipLaunchKernelGGL(convert_probe<true>, grid, block, 0, st, src, e, b, quads);
+    else
+        hipLaunchKernelGGL(convert_probe<false>, grid, block, 0, st, src, e, b, quads);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
 
 extern "C" int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream)
 {

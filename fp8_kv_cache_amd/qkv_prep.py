@@ -41,7 +41,8 @@ OUT_BF16 = 1
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("qkv_prep_create", "qkv_prep_run", "qkv_prep_destroy", "qkv_prep_supported",
             "qkv_prep_launch_shape", "qkv_prep_validate", "qkv_prep_strerror",
-            "qkv_prep_gather", "qkv_prep_probe_copy", "qkv_prep_probe_update", "qkv_prep_mxfp8_norm_quant",
+            "qkv_prep_gather", "qkv_prep_probe_copy", "qkv_prep_probe_update", "qkv_prep_probe_convert",
+            "qkv_prep_mxfp8_norm_quant",
             "qkv_prep_mxfp8_scale_bytes")
 
 
@@ -118,6 +119,9 @@ def _load():
     L.qkv_prep_probe_copy.restype = ctypes.c_int
     L.qkv_prep_probe_update.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     L.qkv_prep_probe_update.restype = ctypes.c_int
+    L.qkv_prep_probe_convert.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_void_p]
+    L.qkv_prep_probe_convert.restype = ctypes.c_int
     return L
 
 
@@ -217,6 +221,13 @@ def qkv_prep_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) ->
     rc = _lib.qkv_prep_probe_copy(dst_ptr, src_ptr, nbytes, stream)
     if rc != OK:
         raise QkvPrepError(rc, "qkv_prep_probe_copy")
+
+
+def qkv_prep_probe_convert(in_ptr: int, n: int, e4m3_ptr, bf16_ptr, convert: int, stream=None) -> None:
+    """The conversion probe of include/qkv_prep_probe.h (device pointers)."""
+    rc = _lib.qkv_prep_probe_convert(in_ptr, n, e4m3_ptr, bf16_ptr, convert, stream)
+    if rc != OK:
+        raise QkvPrepError(rc, "qkv_prep_probe_convert")
 
 
 def qkv_prep_probe_update(buf_ptr: int, nbytes: int, stream=None) -> None:

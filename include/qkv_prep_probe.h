@@ -1,7 +1,9 @@
 /*
- * qkv_prep_probe.h -- a measurement probe shipped in libqkv_prep.so next to
- * the operator: a plain streaming device-to-device copy, and a streaming
- * in-place update (read and write the same bytes, as the operator does with q).
+ * qkv_prep_probe.h -- probes shipped in libqkv_prep.so next to the operator:
+ * a plain streaming device-to-device copy and a streaming in-place update
+ * (read and write the same bytes, as the operator does with q), used as
+ * bandwidth ceilings; and the operator's fp32 -> E4M3 / bf16 conversions on
+ * an array, for exhaustive checks of the conversion instructions.
  *
  * The pages measure the operator against a warm device-to-device copy of the
  * same card ("achievable bandwidth", FlagGems-vllm PR 684, section
@@ -37,6 +39,20 @@ int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, void *stream)
  * argument: NULL, negative or unaligned) or 5 (launch failed); bytes == 0 is a
  * no-op. */
 int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream);
+
+/* Run the operator's own fp32 conversions on n values of `in`, on `stream`:
+ * e4m3_out[i] = the E4M3 code of in[i] (OCP e4m3fn, round to nearest even;
+ * defined for |in[i]| <= 448, the range the operator converts) and
+ * bf16_out[i] = the bf16 of in[i] (round to nearest even; defined for finite
+ * values).  convert selects the path as in qkv_prep_config: 1 = integer
+ * rounding, 2 = the gfx950 conversion instructions.  Either output may be
+ * NULL.  in 16-byte aligned, e4m3_out 4-byte aligned, bf16_out 8-byte
+ * aligned, n >= 0 a multiple of 4 and below 2^33.  Returns 0, 1 (invalid or
+ * misaligned argument) or 5 (launch failed).  A verification probe: it lets a
+ * test compare the device conversions with a reference on every input
+ * pattern. */
+int qkv_prep_probe_convert(const float *in, int64_t n, void *e4m3_out, void *bf16_out, int32_t convert,
+                           void *stream);
 
 #ifdef __cplusplus
 }

@@ -197,6 +197,15 @@ def test_probes_reject_bad_arguments_without_launching():
     assert lib.qkv_prep_probe_update(1 << 20, 15, None) == qp.ERR_INVALID_ARG
     assert lib.qkv_prep_probe_update((1 << 20) + 8, 16, None) == qp.ERR_INVALID_ARG
     assert lib.qkv_prep_probe_update(1 << 20, -16, None) == qp.ERR_INVALID_ARG
+    conv = lib.qkv_prep_probe_convert
+    assert conv(None, 0, None, None, 2, None) == qp.OK
+    assert conv(None, 4, None, None, 2, None) == qp.ERR_INVALID_ARG            # NULL input
+    assert conv(1 << 20, 6, None, None, 2, None) == qp.ERR_INVALID_ARG         # n not a multiple of 4
+    assert conv(1 << 20, 4, None, None, 3, None) == qp.ERR_INVALID_ARG         # bad path
+    assert conv((1 << 20) + 4, 4, None, None, 1, None) == qp.ERR_INVALID_ARG   # input misaligned
+    assert conv(1 << 20, 4, (2 << 20) + 2, None, 1, None) == qp.ERR_INVALID_ARG
+    assert conv(1 << 20, 4, None, (3 << 20) + 4, 1, None) == qp.ERR_INVALID_ARG
+    assert conv(1 << 20, 1 << 33, None, None, 1, None) == qp.ERR_INVALID_ARG
 
 
 def test_gather_without_handle_is_rejected():
