@@ -201,6 +201,8 @@ def mxfp8_norm_quant(x, gamma, eps, *, residual=None, residual_out=None, quant_o
     import torch
     if x.dim() != 2:
         raise ValueError("x must be [m, hidden]")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device, got %s" % x.device)
     m, hidden = x.shape
     if quant_out is None:
         quant_out = torch.empty((m, hidden), dtype=torch.uint8, device=x.device)
@@ -210,9 +212,11 @@ def mxfp8_norm_quant(x, gamma, eps, *, residual=None, residual_out=None, quant_o
     check_mxfp8_tensors(x, gamma, residual, residual_out, quant_out, scale_out)
     args = QkvPrepMxfp8Args(x.data_ptr(), _ptr(residual), _ptr(residual_out), gamma.data_ptr(),
                             quant_out.data_ptr(), scale_out.data_ptr(), m, hidden, eps)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    qkv_prep_mxfp8_norm_quant(args, stream)
+    # The C call launches on the current device: make it x's.
+    with torch.cuda.device(x.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        qkv_prep_mxfp8_norm_quant(args, stream)
     return quant_out, scale_out
 
 

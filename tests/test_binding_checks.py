@@ -94,3 +94,14 @@ def test_mxfp8_checks():
             qp.check_mxfp8_tensors(*args)
     with pytest.raises(TypeError):
         qp.check_mxfp8_tensors(x.float(), g, None, None, codes, scales)
+
+
+def test_mxfp8_wrapper_rejects_host_tensors():
+    """The wrapper refuses host tensors before any device call (their
+    pointers would reach the kernel otherwise)."""
+    x = torch.zeros((4, 512), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        qp.mxfp8_norm_quant(x, torch.zeros(512, dtype=torch.bfloat16), 1e-6,
+                            quant_out=torch.zeros((4, 512), dtype=torch.uint8),
+                            scale_out=torch.zeros(qp.qkv_prep_mxfp8_scale_bytes(4, 512), dtype=torch.uint8),
+                            stream=0)
