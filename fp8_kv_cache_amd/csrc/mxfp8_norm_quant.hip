@@ -78,7 +78,7 @@ __global__ __launch_bounds__(1024) void mxfp8_kernel(MxArgs a)
     if (a.residual_out) {
 #pragma unroll
         for (int j = 0; j < G; ++j)
-            store_stream(reinterpret_cast<u32x4 *>(a.residual_out + rbase) + (w * G + j) * 64 + lane, p[j]);
+            store_sys(a.residual_out + rbase, (uint32_t)a.hidden * 2u, ((w * G + j) * 64 + lane) * 16u, p[j]);
     }
     float g[K];
 #pragma unroll
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(1024) void mxfp8_kernel(MxArgs a)
         for (int e = 0; e < 8; ++e)
             q[e] = fminf(fmaxf(n[e] * inverse, -448.0f), 448.0f);
         const u32x2 codes = {pack_e4m3<true>(q[0], q[1], q[2], q[3]), pack_e4m3<true>(q[4], q[5], q[6], q[7])};
-        store_stream2(reinterpret_cast<u32x2 *>(a.quant_out + rbase) + chunk, codes);
+        store_sys2(a.quant_out + rbase, (uint32_t)a.hidden, (uint32_t)chunk * 8u, codes);
         if ((lane & 3) == 0)
             a.scale_out[swizzled_offset(row, chunk >> 2, a.padded_cols)] = (uint8_t)byte;
     }

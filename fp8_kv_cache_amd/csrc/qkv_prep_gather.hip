@@ -61,7 +61,7 @@ __device__ __forceinline__ void gather_row_bf16(const GatherArgs &a, int64_t i, 
             unpack_bf16x8(*(reinterpret_cast<const u32x4 *>(data + kNopeDim) + (lane - kRopeLane)), v);
         }
     }
-    store_stream(reinterpret_cast<u32x4 *>(a.out) + i * 64 + lane, pack_bf16x8<true>(v));
+    store_sys(static_cast<uint8_t *>(a.out) + i * 1024, 1024u, lane * 16u, pack_bf16x8<true>(v));
 }
 
 // fp32 rows (2 KiB): lane l owns dims 4l..4l+3 and 256+4l..256+4l+3, so each
@@ -91,9 +91,9 @@ __device__ __forceinline__ void gather_row_f32(const GatherArgs &a, int64_t i, u
             hi = u32x4{r[0] << 16, r[0] & 0xffff0000u, r[1] << 16, r[1] & 0xffff0000u};
         }
     }
-    u32x4 *dst = reinterpret_cast<u32x4 *>(a.out) + i * 128;
-    store_stream(dst + lane, lo);
-    store_stream(dst + 64 + lane, hi);
+    uint8_t *dst = static_cast<uint8_t *>(a.out) + i * 2048;
+    store_sys(dst, 2048u, lane * 16u, lo);
+    store_sys(dst, 2048u, 1024u + lane * 16u, hi);
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin, and each XCD has its

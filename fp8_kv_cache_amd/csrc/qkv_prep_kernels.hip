@@ -15,7 +15,12 @@
 //    every footprint, while shapes with several loads per lane in flight (4 rows
 //    per wave, or several rows per wave) lose 6-15% once the footprint passes a
 //    few GiB.  One-wavefront workgroups (the measured optimum), non-temporal
-//    loads and stores.
+//    loads.
+//  * Stores: with one row per wavefront (the large-batch shape) every store
+//    carries the non-temporal system-scope policy (nt sc1), 1-2% faster than
+//    plain non-temporal stores from 32768x64 up (about 2% at 32768x128 and
+//    131072x128).  The decode-sized shape keeps plain non-temporal stores:
+//    there nt sc1 was ~2% slower (a footprint near the size of the MALL).
 //  * The sum of squares follows the fixed order of the numerics contract: each
 //    chunk sequentially, then adjacent chunk pairs.  Levels 1-4 are DPP adds
 //    inside a 16-lane row (quad_perm xor1, xor2, row_half_mirror, row_mirror);
@@ -109,7 +114,7 @@ __device__ __forceinline__ void q_row(const KernelArgs &a, int64_t row, uint32_t
     }
     if (lane >= kRopeLane)
         rope8(y, cv, sv);
-    store_stream(reinterpret_cast<u32x4 *>(a.q + row * kHeadDim) + lane, pack_bf16x8<HW>(y));
+    store_sys(a.q + row * kHeadDim, kHeadDim * 2u, lane * 16u, pack_bf16x8<HW>(y));
 }
 
 // Heads h0 .. h0+n-1 of one token (n = min(U, H - h0)) on one wavefront, one
@@ -160,8 +165,9 @@ __device__ __forceinline__ void q_chunk(const KernelArgs &a, uint32_t wv, uint32
 
 // One token's kv row.  Lane l < 56 holds dims 8l..8l+7 of quantization block
 // l/8 and writes their 8 codes; lanes 56..63 hold the rope dims and write 16
-// bytes of rotated bf16 each; one lane writes the 8-byte scale record.
-template <bool HW>
+// bytes of rotated bf16 each; one lane writes the 8-byte scale record.  SYS:
+// the stores take the nt sc1 policy (with the one-row-per-wavefront q path).
+template <bool HW, bool SYS>
 __device__ __forceinline__ void kv_row(const KernelArgs &a, int64_t t, uint32_t lane)
 {
     const int64_t slot = a.slot_mapping[t];
@@ -189,7 +195,10 @@ __device__ __forceinline__ void kv_row(const KernelArgs &a, int64_t t, uint32_t 
         // bf16 slot: the rotated row as bf16, slot s at byte s * 1024.
         if (lane >= kRopeLane)
             rope8(y, cv, sv);
-        store_stream(reinterpret_cast<u32x4 *>(a.cache + slot * kBf16SlotBytes) + lane, pack_bf16x8<HW>(y));
+        if constexpr (SYS)
+            store_sys(a.cache + slot * kBf16SlotBytes, kBf16SlotBytes, lane * 16u, pack_bf16x8<HW>(y));
+        else
+            store_stream(reinterpret_cast<u32x4 *>(a.cache + slot * kBf16SlotBytes) + lane, pack_bf16x8<HW>(y));
         return;
     }
 
@@ -216,15 +225,24 @@ __device__ __forceinline__ void kv_row(const KernelArgs &a, int64_t t, uint32_t 
     if (lane < kRopeLane) {
         const u32x2 codes = {pack_e4m3<HW>(y[0] * inv_scale, y[1] * inv_scale, y[2] * inv_scale, y[3] * inv_scale),
                              pack_e4m3<HW>(y[4] * inv_scale, y[5] * inv_scale, y[6] * inv_scale, y[7] * inv_scale)};
-        store_stream2(reinterpret_cast<u32x2 *>(data) + lane, codes);
+        if constexpr (SYS)
+            store_sys2(data, kSlotData, lane * 8u, codes);
+        else
+            store_stream2(reinterpret_cast<u32x2 *>(data) + lane, codes);
     } else {
         rope8(y, cv, sv);
-        store_stream(reinterpret_cast<u32x4 *>(data + kNopeDim) + (lane - kRopeLane), pack_bf16x8<HW>(y));
+        if constexpr (SYS)
+            store_sys(data, kSlotData, kNopeDim + (lane - kRopeLane) * 16u, pack_bf16x8<HW>(y));
+        else
+            store_stream(reinterpret_cast<u32x4 *>(data + kNopeDim) + (lane - kRopeLane), pack_bf16x8<HW>(y));
     }
-    if (lane == 0)
-        store_stream2(reinterpret_cast<u32x2 *>(base + (int64_t)a.block_size * kSlotData +
-                                                (int64_t)sib * kSlotScale),
-                      u32x2{rec0, rec1});
+    if (lane == 0) {
+        uint8_t *rec = base + (int64_t)a.block_size * kSlotData + (int64_t)sib * kSlotScale;
+        if constexpr (SYS)
+            store_sys2(rec, kSlotScale, 0u, u32x2{rec0, rec1});
+        else
+            store_stream2(reinterpret_cast<u32x2 *>(rec), u32x2{rec0, rec1});
+    }
 }
 
 // ------------------------------------------------------------------ kernel
@@ -238,7 +256,7 @@ __global__ __launch_bounds__(512) void qkv_prep_kernel(KernelArgs a)
     if (blockIdx.x < a.kv_blocks) {
         const int64_t t = (int64_t)blockIdx.x * waves_per_block + wave;
         if (t < a.num_tokens)
-            kv_row<HW>(a, t, lane);
+            kv_row<HW, U == 1>(a, t, lane);
     } else {
         const int64_t wv = (int64_t)(blockIdx.x - a.kv_blocks) * waves_per_block + wave;
         if constexpr (U == 1) {

@@ -8,12 +8,16 @@
 
 namespace {
 
+using qkvp::dev::store_sys;
 using qkvp::dev::u32x2;
 using qkvp::dev::u32x4;
-// One 16-byte non-temporal load and store per lane, 256-lane blocks: the
-// fastest of the copy shapes measured on MI355X (1, 2, 4, 8 and 16 loads per
-// lane; 256, 512 and 1024 lanes per block; plain or non-temporal; natural or
-// XCD-contiguous block order): about 6.4-6.5 TB/s at 0.5-4 GiB.
+// One 16-byte non-temporal load and one 16-byte store per lane, 256-lane
+// blocks: the fastest of the copy shapes measured on MI355X (1, 2, 4, 8 and 16
+// loads per lane; 256, 512 and 1024 lanes per block; plain or non-temporal;
+// natural or XCD-contiguous block order), about 6.4-6.5 TB/s at 0.5-4 GiB with
+// non-temporal stores.  A sweep of the load and store cache-policy bits (sc0,
+// sc1, nt) then found the non-temporal system-scope store (nt sc1) best, at
+// ~6.7 TB/s; every load policy with nt set is within noise of the others.
 constexpr int kUnroll = 1;
 constexpr int kThreads = 256;
 
@@ -21,7 +25,8 @@ constexpr int kThreads = 256;
 // issued before the first store.
 __global__ __launch_bounds__(kThreads) void stream_copy(u32x4 *dst, const u32x4 *src, int64_t n)
 {
-    const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+    const int64_t first = (int64_t)blockIdx.x * (kThreads * kUnroll);
+    const int64_t base = first + threadIdx.x;
     u32x4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -33,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void stream_copy(u32x4 *dst, const u32x4 
     for (int u = 0; u < kUnroll; ++u) {
         const int64_t i = base + (int64_t)u * kThreads;
         if (i < n)
-            __builtin_nontemporal_store(v[u], dst + i);
+            store_sys(dst + first, kThreads * kUnroll * 16u, (uint32_t)(i - first) * 16u, v[u]);
     }
 }
 
@@ -42,17 +47,19 @@ __global__ __launch_bounds__(kThreads) void stream_copy(u32x4 *dst, const u32x4 
 // arrives streams at only ~4.5 TB/s; pausing the wavefront for a moment
 // (s_sleep 2, ~128 cycles) between the load and the store gives ~6.7 TB/s,
 // above the two-buffer copy.  A wave-wide reduction in the same place does not
-// help (~4.5 TB/s); sleeps of 2 to 32 units are the same.
+// help (~4.5 TB/s); sleeps of 2 to 32 units are the same.  The nt sc1 store
+// policy adds ~1.5% (~6.8 TB/s at 2 GiB).
 constexpr int kUpdateThreads = 64;
 
 __global__ __launch_bounds__(kUpdateThreads) void stream_update(u32x4 *buf, int64_t n)
 {
-    const int64_t i = (int64_t)blockIdx.x * kUpdateThreads + threadIdx.x;
+    const int64_t first = (int64_t)blockIdx.x * kUpdateThreads;
+    const int64_t i = first + threadIdx.x;
     if (i < n) {
         u32x4 v = __builtin_nontemporal_load(buf + i);
         v[0] += 1u;
         __builtin_amdgcn_s_sleep(2);
-        __builtin_nontemporal_store(v, buf + i);
+        store_sys(buf + first, kUpdateThreads * 16u, threadIdx.x * 16u, v);
     }
 }
 

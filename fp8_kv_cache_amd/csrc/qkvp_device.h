@@ -19,6 +19,31 @@ __device__ __forceinline__ u32x4 load_stream(const u32x4 *p) { return __builtin_
 __device__ __forceinline__ void store_stream(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_stream2(u32x2 *p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 
+// Stores with the non-temporal, system-scope cache policy (the nt and sc1
+// bits), issued through a buffer descriptor: a global store cannot carry sc1
+// from source.  Measured on MI355X with 2 GiB buffers, this store policy lifts
+// a streaming copy from ~6.46 to ~6.70 TB/s and an in-place update from ~6.72
+// to ~6.82 TB/s; the load policy makes no difference there.  `base` must be
+// wave-uniform (the descriptor lives in scalar registers); a store at or past
+// `bytes` from `base` is dropped by the descriptor's range check.
+constexpr int kPolicyNtSc1 = 2 | 16;             // nt | sc1
+constexpr int kRawBufferWord3 = 0x00020000;      // 32-bit data format, no swizzle (gfx9)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kRawBufferWord3);
+}
+
+__device__ __forceinline__ void store_sys(void *base, uint32_t bytes, uint32_t off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, stream_rsrc(base, bytes), (int)off, 0, kPolicyNtSc1);
+}
+
+__device__ __forceinline__ void store_sys2(void *base, uint32_t bytes, uint32_t off, u32x2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, stream_rsrc(base, bytes), (int)off, 0, kPolicyNtSc1);
+}
+
 __device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv d)
 {
     return (__umulhi(n, d.mul) + n) >> d.shift;
