@@ -79,11 +79,15 @@ int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)
 //  * rows_per_wave: 1 (one q row per wavefront), or U = 2, 4 consecutive heads
 //    of one token per wavefront, processed one after another with the token's
 //    position, cos/sin row and the q weight loaded once.  Measured on MI355X
-//    (T = 256..16384, H = 64 and 128, two interleaved rounds): two heads per
-//    wavefront are 2.5-4% faster up to T*H = 2^19 q rows; above that one row
-//    per wavefront ties or wins (by 1-3% at 32768x64 and 131072x128).  Four
-//    heads per wavefront never win; they are used only when fewer wavefronts
-//    would need 2^32 or more work-items in the dispatch.
+//    (T = 64..16384, H = 64 and 128, two interleaved rounds, back-to-back and
+//    with L2 and the MALL flushed before each launch): up to 2^17 q rows
+//    (256 MiB of q, about the MALL's size) two heads per wavefront are up to
+//    10% faster back to back, where q stays cache-resident as it does right after
+//    the kernel that produced it; above 2^17 rows one row per wavefront, with
+//    its system-scope stores, ties or wins in both regimes (by 0.4-5.5%
+//    flushed).
+//    Four heads per wavefront never win; they are used only when fewer
+//    wavefronts would need 2^32 or more work-items in the dispatch.
 //  * waves_per_block: 1 (64-lane workgroups).  Measured on MI355X with four
 //    interleaved rounds per shape: 1 wave per workgroup beats 2, 4 and 8 on
 //    2048x64, 32768x64, 32768x128 and 131072x128 (by 1-5%).
@@ -102,7 +106,7 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     if (c.rows_per_wave) {
         s.rows_per_wave = c.rows_per_wave;
     } else {
-        s.rows_per_wave = q_rows <= ((int64_t)1 << 19) && c.num_heads > 1 ? 2 : 1;
+        s.rows_per_wave = q_rows <= ((int64_t)1 << 17) && c.num_heads > 1 ? 2 : 1;
         while (s.rows_per_wave < 4 &&
                (s.kv_blocks + ceil_div(q_waves(s.rows_per_wave), s.waves_per_block)) * 64 *
                        s.waves_per_block >= ((int64_t)1 << 32))

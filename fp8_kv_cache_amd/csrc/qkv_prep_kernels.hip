@@ -35,12 +35,12 @@
 //  * q rows and kv rows go to different workgroups of one launch (the FlagGems
 //    page merges the Q and KV launches); kv workgroups come first in dispatch
 //    order, so their quantization overlaps the q stream instead of trailing it.
-//  * Decode-sized batches (up to 2^19 q rows) take two heads of one token per
+//  * Decode-sized batches (up to 2^17 q rows) take two heads of one token per
 //    wavefront, one after the other, so the token's position, cos/sin row and
-//    the q weight are loaded once per two rows (2.5-4% faster there; the
-//    launch heuristic picks it).  Issuing several rows' loads at once (the
-//    sglang page's "K tokens per block" load-level parallelism) was slower at
-//    every size measured.
+//    the q weight are loaded once per two rows (up to 10% faster there while q
+//    is cache-resident; the launch heuristic picks it).  Issuing several rows'
+//    loads at once (the sglang page's "K tokens per block" load-level
+//    parallelism) was slower at every size measured.
 #include "qkv_prep_launch.h"
 #include "qkvp_device.h"
 
@@ -121,8 +121,9 @@ __device__ __forceinline__ void q_row(const KernelArgs &a, int64_t row, uint32_t
 // row after another: the token's position, its cos/sin row and the q weight
 // are loaded once for the chunk, then each row is loaded, normalized, rotated
 // and stored in turn (one row's load in flight, as with one row per
-// wavefront).  Measured on MI355X, two heads per wavefront beat one by 2.5-4%
-// up to about 2^19 q rows (decode-sized batches) and tie or lose above.
+// wavefront).  Measured on MI355X, two heads per wavefront beat one by up to
+// 10% up to 2^17 q rows (decode-sized batches) when q is cache-resident, and
+// tie or lose above.
 template <int U, bool HAS_W, bool HW>
 __device__ __forceinline__ void q_chunk(const KernelArgs &a, uint32_t wv, uint32_t lane)
 {

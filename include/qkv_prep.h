@@ -66,7 +66,7 @@ typedef struct {
     int32_t rows_per_wave;    /* 0 = launch heuristic; 1 = one q row per wavefront;
                                  2 or 4 = that many consecutive heads of one
                                  token per wavefront, one after another (the
-                                 heuristic takes 2 up to 2^19 q rows, else 1) */
+                                 heuristic takes 2 up to 2^17 q rows, else 1) */
     int32_t waves_per_block;  /* 0 = launch heuristic; 1, 2, 4 or 8 forces it */
     int32_t convert;          /* 0 = heuristic, 1 = integer bf16/E4M3 rounding,
                                  2 = gfx950 conversion instructions; both give
@@ -200,7 +200,7 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
  * a device with num_cus compute units (256 on MI355X).  Pure host code: needs
  * no device, so the launch heuristic can be inspected anywhere.  The current
  * heuristic (one wavefront per workgroup; two heads of a token per wavefront
- * up to 2^19 q rows, one q row per wavefront above) does not depend on
+ * up to 2^17 q rows, one q row per wavefront above) does not depend on
  * num_cus; the argument keeps the signature stable for a device-dependent
  * one.  Returns QKV_PREP_ERR_INVALID_ARG for a NULL out or num_tokens < 0, and
  * QKV_PREP_ERR_UNSUPPORTED when num_tokens * num_heads >= 2^31 (the limit of

@@ -133,11 +133,11 @@ def test_unsupported_head_dim():
 def test_launch_shape_heuristic():
     cfg = qp.make_config(64)
     small = qp.qkv_prep_launch_shape(cfg, 256, 16)
-    # decode-sized: two heads of a token per wavefront, up to 2^19 q rows
+    # decode-sized: two heads of a token per wavefront, up to 2^17 q rows
     assert small.rows_per_wave == 2 and small.waves_per_block == 1 and small.convert == 2
     assert small.kv_blocks == 16 and small.q_blocks == 16 * 32 and small.grid == 16 * 33
-    assert qp.qkv_prep_launch_shape(cfg, 256, 8192).rows_per_wave == 2        # 2^19 rows
-    assert qp.qkv_prep_launch_shape(cfg, 256, 8193).rows_per_wave == 1
+    assert qp.qkv_prep_launch_shape(cfg, 256, 2048).rows_per_wave == 2        # 2^17 rows
+    assert qp.qkv_prep_launch_shape(cfg, 256, 2049).rows_per_wave == 1
     one_head = qp.qkv_prep_launch_shape(qp.make_config(1), 256, 100)
     assert one_head.rows_per_wave == 1 and one_head.q_blocks == 100
     odd_heads = qp.qkv_prep_launch_shape(qp.make_config(5), 256, 10)
