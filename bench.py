@@ -264,6 +264,25 @@ def known_answer_check(torch, W, qp):
 
 # ----------------------------------------------------------------- CPU baseline
 
+def host_cpu():
+    """The host's CPU model (first `model name` of /proc/cpuinfo) and the
+    number of CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return model, usable
+
+
 def cpu_baseline(torch, W, name, target_s=12.0, sample_tokens=4096):
     """The oracle (plain scalar C, OpenMP over tokens) on a bounded sample of
     the same workload: its first `sample_tokens` tokens, passed over
@@ -304,8 +323,9 @@ def cpu_baseline(torch, W, name, target_s=12.0, sample_tokens=4096):
 
     k, dt = passes(nth, target_s)
     k1, dt1 = passes(1, 2.0)
+    model, usable = host_cpu()
     return {"value": round(nbytes * k / dt / 1e9, 3), "unit": "GB/s", "cores": nth,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": usable,
             "sample": "first %d of %d tokens of %s %dx%d, %d passes in %.1f s" % (
                 n, w.num_tokens, w.name, w.num_tokens, w.num_heads, k, dt),
             "value_1_core": round(nbytes * k1 / dt1 / 1e9, 3)}

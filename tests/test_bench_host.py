@@ -50,3 +50,9 @@ def test_p90():
     assert bench.p90([5.0]) == 5.0
     assert bench.p90(list(range(1, 11))) == 10
     assert bench.p90(list(range(100, 0, -1))) == 91
+
+
+def test_host_cpu():
+    model, usable = bench.host_cpu()
+    assert isinstance(model, str) and model
+    assert usable >= 1
