@@ -1,7 +1,8 @@
 // Cache reader for the FP8 + UE8M0 paged cache written by qkv_prep_kernel:
 // dequantize and gather slots back into fp32 or bf16 rows (the cache layout is
 // the one stated in include/qkv_prep.h).  HBM bound: 584 bytes read and 1 or
-// 2 KiB written per row, one wavefront per row, non-temporal stores.
+// 2 KiB written per row, one wavefront per row, non-temporal system-scope
+// stores (plain loads: a slot's lines are shared with its neighbours).
 #include "qkv_prep_gather.h"
 #include "qkvp_device.h"
 
