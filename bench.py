@@ -101,19 +101,24 @@ def copy_ceilings(torch, qp):
 # ----------------------------------------------------------------- one workload
 
 def time_launches(torch, fn, steps):
-    """Per-launch HIP-event durations (on torch's current stream, which is the
-    stream the library launches on) and the wall time of all `steps`."""
+    """The wall time of `steps` back-to-back launches, bracketed by
+    synchronizations and nothing else inside; then, in a second pass of as
+    many launches, per-launch HIP-event durations (on torch's current stream,
+    which is the stream the library launches on)."""
     stream = torch.cuda.current_stream()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
     for e0, e1 in events:
         e0.record(stream)
         fn()
         e1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events], wall
 
 
