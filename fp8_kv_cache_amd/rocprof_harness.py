@@ -11,6 +11,11 @@ counter group, each as a child process with its own time limit:
   reqs    --pmc TCC_EA0_RDREQ_{32B,64B,128B}_sum TCC_EA0_RDREQ_sum
                                            read requests by size
   waves   --pmc <wave counters>            occupancy
+  bench   --kernel-trace --stats           over bench.py's own timing run of an
+                                           operator workload (no other workload,
+                                           variant, ceiling or CPU baseline), so
+                                           the trace's average duration can be set
+                                           beside the bench's event-timed mean
 
 and writes short text summaries (the figures and the exact commands) to the
 output directory.  The copy probe's counters against its known byte count
@@ -25,6 +30,7 @@ counters directly (32, 64 and 128 bytes each), with no calibration.
 
     python -m fp8_kv_cache_amd.rocprof_harness --workload prefill --out prof_out
     python -m fp8_kv_cache_amd.rocprof_harness --workload mxfp8 --out prof_out
+    python -m fp8_kv_cache_amd.rocprof_harness --workload prefill --passes bench --out prof_out
 """
 from __future__ import annotations
 
@@ -61,23 +67,31 @@ def log(msg):
     print(msg, flush=True)
 
 
-def run_pass(name, rocprof_args, workload, launches, out, timeout):
+def run_pass(name, rocprof_args, workload, launches, out, timeout, bench_args=None):
+    """One rocprofv3 run as a child process: over `bench.py --mode profile`
+    (a few launches of the target), or over `bench.py <bench_args>` when
+    those are given.  Returns the command and the output directory (and, for
+    a bench run, its JSON line)."""
     d = os.path.join(out, name)
     os.makedirs(d, exist_ok=True)
     rel = os.path.relpath(d, ROOT)
+    program = bench_args if bench_args is not None else [
+        "--mode", "profile", "--workload", workload, "--launches", str(launches)]
     cmd = ["rocprofv3"] + rocprof_args + ["--output-format", "csv", "-d", rel, "-o", name, "--",
-                                          "python3", "bench.py", "--mode", "profile",
-                                          "--workload", workload, "--launches", str(launches)]
+                                          "python3", "bench.py"] + program
     log("pass %s: %s" % (name, " ".join(cmd)))
     t0 = time.time()
     res = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=timeout)
     with open(os.path.join(d, "stdout.txt"), "w") as f:
         f.write(res.stdout + "\n--- stderr ---\n" + res.stderr)
     log("pass %s: rc=%d in %.1f s" % (name, res.returncode, time.time() - t0))
-    done = "copies of" in res.stderr
+    # rocprofv3 itself may end with a signal after the program has finished;
+    # the program's own last output says whether it did.
+    json_line = next((ln for ln in res.stdout.splitlines() if ln.startswith('{"metric"')), None)
+    done = "copies of" in res.stderr if bench_args is None else json_line is not None
     if res.returncode != 0 and not done:
         raise RuntimeError("rocprofv3 pass %s failed (rc %d); see %s" % (name, res.returncode, d))
-    return cmd, d
+    return cmd, d, json_line
 
 
 def find_csv(d, suffix):
@@ -125,9 +139,11 @@ def main():
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--passes", default="trace,fetch,write,reqs,waves")
     ap.add_argument("--wave-counters", default="OccupancyPercent,MeanOccupancyPerCU,SQ_WAVES")
+    ap.add_argument("--bench-steps", type=int, default=50)
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     from fp8_kv_cache_amd import variants as V
+    from fp8_kv_cache_amd import workloads as W
     t = V.target(args.workload)
     label, op_kernel, prefix = t.label, t.kernel, t.prefix
     out = os.path.abspath(os.path.join(ROOT, args.out))
@@ -137,8 +153,8 @@ def main():
     cmds = {}
 
     if "trace" in passes:
-        cmd, d = run_pass("trace", ["--kernel-trace", "--stats"], args.workload, args.launches,
-                          out, 300)
+        cmd, d, _ = run_pass("trace", ["--kernel-trace", "--stats"], args.workload, args.launches,
+                             out, 300)
         cmds["trace"] = cmd
         rows = kernel_stats(d)
         lines = ["# rocprofv3 kernel trace, kernel %s, workload %s" % (op_kernel, label),
@@ -159,16 +175,16 @@ def main():
 
     fetch = write = None
     if "fetch" in passes:
-        cmd, d = run_pass("fetch", ["--pmc", "FETCH_SIZE"], args.workload, 3, out, 180)
+        cmd, d, _ = run_pass("fetch", ["--pmc", "FETCH_SIZE"], args.workload, 3, out, 180)
         cmds["fetch"] = cmd
         fetch = per_dispatch(counter_rows(d), "FETCH_SIZE")
     if "write" in passes:
-        cmd, d = run_pass("write", ["--pmc", "WRITE_SIZE"], args.workload, 3, out, 180)
+        cmd, d, _ = run_pass("write", ["--pmc", "WRITE_SIZE"], args.workload, 3, out, 180)
         cmds["write"] = cmd
         write = per_dispatch(counter_rows(d), "WRITE_SIZE")
     reqs = None
     if "reqs" in passes:
-        cmd, d = run_pass("reqs", ["--pmc"] + list(REQ_COUNTERS), args.workload, 3, out, 180)
+        cmd, d, _ = run_pass("reqs", ["--pmc"] + list(REQ_COUNTERS), args.workload, 3, out, 180)
         cmds["reqs"] = cmd
         rows = counter_rows(d)
         reqs = {c: per_dispatch(rows, c) for c in REQ_COUNTERS}
@@ -240,7 +256,7 @@ def main():
 
     if "waves" in passes:
         ctrs = args.wave_counters.split(",")
-        cmd, d = run_pass("waves", ["--pmc"] + ctrs, args.workload, 3, out, 180)
+        cmd, d, _ = run_pass("waves", ["--pmc"] + ctrs, args.workload, 3, out, 180)
         rows = counter_rows(d)
         lines = ["# rocprofv3 wave counters, kernel %s, workload %s" % (op_kernel, label),
                  "# command (from the repository root): %s" % " ".join(cmd), ""]
@@ -253,6 +269,36 @@ def main():
                      "mean resident waves per CU (rocprofv3 derived counters)")
         text = "\n".join(lines) + "\n"
         open(os.path.join(out, "%s_waves_%s.txt" % (prefix, label)), "w").write(text)
+        log(text)
+
+    if "bench" in passes:
+        if t.family != "op" or args.workload not in W.WORKLOADS:
+            raise SystemExit("the bench pass takes an operator workload")
+        bench_args = ["--workload", args.workload, "--steps", str(args.bench_steps), "--warmup", "10",
+                      "--no-also", "--no-variants", "--no-cpu-baseline", "--no-ceiling"]
+        cmd, d, json_line = run_pass("bench", ["--kernel-trace", "--stats"], args.workload, 0, out, 600,
+                                     bench_args=bench_args)
+        rec = json.loads(json_line)
+        rows = kernel_stats(d)
+        shape = rec["config"]["launch"]
+        lines = ["# rocprofv3 kernel trace over bench.py's timing run, kernel %s, workload %s" % (op_kernel, label),
+                 "# command (from the repository root): %s" % " ".join(cmd),
+                 "# kernel source sha256[:16] = %s" % summary["kernel_sha"],
+                 "# the workload's launches of %s (rows_per_wave %d): 10 warmup + %d wall-timed + %d event-timed"
+                 % (op_kernel, shape["rows_per_wave"], args.bench_steps, args.bench_steps)
+                 + " + 10 after a cache flush; the bench's known-answer checks on the tiny workload use the",
+                 "# small-batch template instance (rows_per_wave 2), listed on its own line", "",
+                 "%-70s %6s %14s %14s %14s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+        for r in rows:
+            lines.append("%-70s %6s %14.2f %14.2f %14.2f" % (
+                r["Name"][:70], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3))
+        lines += ["", "# the bench's own figures in the same run (HIP events, kernel_us_mean; wall-clock value):",
+                  "roofline.kernel_us_mean  %s" % rec["roofline"]["kernel_us_mean"],
+                  "kernel_us               %s" % json.dumps(rec["kernel_us"]),
+                  "value_gbps              %s" % rec["value"]]
+        text = "\n".join(lines) + "\n"
+        open(os.path.join(out, "%s_kernel_trace_bench_%s.txt" % (prefix, label)), "w").write(text)
         log(text)
 
     json.dump(summary, open(os.path.join(out, "summary_%s.json" % label), "w"), indent=1)
