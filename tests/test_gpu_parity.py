@@ -81,6 +81,16 @@ def test_head_counts_the_pages_measure(T, H):
     check(W.custom(T, H, seed=301 + T + H), rows_per_wave=1)
 
 
+@pytest.mark.parametrize("T,H", [(2048, 64), (2049, 64), (1024, 128), (1025, 128)])
+def test_both_sides_of_the_launch_threshold(T, H):
+    # The heuristic takes two heads per wavefront up to 2^17 q rows and one
+    # row per wavefront above; default launch on each side of the boundary.
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    shape = QkvPrep(H).launch_shape(T)
+    assert shape.rows_per_wave == (2 if T * H <= 1 << 17 else 1)
+    check(W.custom(T, H, seed=330 + T + H, num_skip=5))
+
+
 @pytest.mark.parametrize("rpw", [0, 1])
 def test_exponent_clamp_and_subnormal_outputs(rpw):
     # Tiny weights: every kv block sits at the exponent clamp (scale byte 0)
