@@ -100,7 +100,7 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     const int64_t q_rows = T * c.num_heads;
     s.waves_per_block = c.waves_per_block ? c.waves_per_block : 1;
     s.convert = c.convert ? c.convert : 2;
-    s.kv_blocks = ceil_div(T, s.waves_per_block);
+    s.kv_blocks = ceil_div(T, (int64_t)qkvp::kKvTokensPerWave * s.waves_per_block);
     // q wavefronts: T * ceil(H / U) (U heads of one token per wavefront)
     auto q_waves = [&](int u) { return T * ceil_div(c.num_heads, u); };
     if (c.rows_per_wave) {

@@ -35,6 +35,9 @@
 //  * q rows and kv rows go to different workgroups of one launch (the FlagGems
 //    page merges the Q and KV launches); kv workgroups come first in dispatch
 //    order, so their quantization overlaps the q stream instead of trailing it.
+//    A kv wavefront takes four consecutive tokens, all their loads issued
+//    together: the kv wavefronts form a latency-bound burst at the start, and
+//    more loads in flight per wavefront shorten it.
 //  * Decode-sized batches (up to 2^17 q rows) take two heads of one token per
 //    wavefront, one after the other, so the token's position, cos/sin row and
 //    the q weight are loaded once per two rows (up to 10% faster there while q
@@ -164,19 +167,15 @@ __device__ __forceinline__ void q_chunk(const KernelArgs &a, uint32_t wv, uint32
 
 // ------------------------------------------------------------------ kv row
 
-// One token's kv row.  Lane l < 56 holds dims 8l..8l+7 of quantization block
-// l/8 and writes their 8 codes; lanes 56..63 hold the rope dims and write 16
-// bytes of rotated bf16 each; one lane writes the 8-byte scale record.  SYS:
-// the stores take the nt sc1 policy (with the one-row-per-wavefront q path).
+// One token's kv row, once its slot (valid) and its row `d` are loaded.  Lane
+// l < 56 holds dims 8l..8l+7 of quantization block l/8 and writes their 8
+// codes; lanes 56..63 hold the rope dims and write 16 bytes of rotated bf16
+// each; one lane writes the 8-byte scale record.  SYS: the stores take the nt
+// sc1 policy (with the one-row-per-wavefront q path).
 template <bool HW, bool SYS>
-__device__ __forceinline__ void kv_row(const KernelArgs &a, int64_t t, uint32_t lane)
+__device__ __forceinline__ void kv_finish(const KernelArgs &a, int64_t t, int64_t slot, const u32x4 &d,
+                                          const float (&w)[8], uint32_t lane)
 {
-    const int64_t slot = a.slot_mapping[t];
-    if (slot < 0 || slot >= a.num_slots)
-        return;  // wave-uniform: the whole wavefront skips this token
-    const u32x4 d = load_stream(reinterpret_cast<const u32x4 *>(a.kv + t * kHeadDim) + lane);
-    float w[8];
-    unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.kv_w)[lane], w);
     f32x4 cv = f32x4{1.f, 1.f, 1.f, 1.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
     if (lane >= kRopeLane) {
         const f32x4 *cs = reinterpret_cast<const f32x4 *>(
@@ -246,6 +245,29 @@ __device__ __forceinline__ void kv_row(const KernelArgs &a, int64_t t, uint32_t 
     }
 }
 
+// The kv rows of tokens t0 .. t0+N-1 on one wavefront: every slot and row load
+// is issued first, then the rows are finished one after another.  A token
+// whose slot is out of range is skipped (wave-uniform) before its row is read.
+template <bool HW, bool SYS, int N>
+__device__ __forceinline__ void kv_rows(const KernelArgs &a, int64_t t0, uint32_t lane)
+{
+    int64_t slot[N];
+    u32x4 d[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        slot[u] = t0 + u < a.num_tokens ? a.slot_mapping[t0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        if (slot[u] >= 0 && slot[u] < a.num_slots)
+            d[u] = load_stream(reinterpret_cast<const u32x4 *>(a.kv + (t0 + u) * kHeadDim) + lane);
+    float w[8];
+    unpack_bf16x8(reinterpret_cast<const u32x4 *>(a.kv_w)[lane], w);
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        if (slot[u] >= 0 && slot[u] < a.num_slots)
+            kv_finish<HW, SYS>(a, t0 + u, slot[u], d[u], w, lane);
+}
+
 // ------------------------------------------------------------------ kernel
 
 template <int U, bool HAS_W, bool HW>
@@ -255,9 +277,9 @@ __global__ __launch_bounds__(512) void qkv_prep_kernel(KernelArgs a)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t waves_per_block = blockDim.x >> 6;
     if (blockIdx.x < a.kv_blocks) {
-        const int64_t t = (int64_t)blockIdx.x * waves_per_block + wave;
+        const int64_t t = ((int64_t)blockIdx.x * waves_per_block + wave) * kKvTokensPerWave;
         if (t < a.num_tokens)
-            kv_row<HW, U == 1>(a, t, lane);
+            kv_rows<HW, U == 1, kKvTokensPerWave>(a, t, lane);
     } else {
         const int64_t wv = (int64_t)(blockIdx.x - a.kv_blocks) * waves_per_block + wave;
         if constexpr (U == 1) {

@@ -120,7 +120,8 @@ typedef struct {
     int32_t rows_per_wave;
     int32_t waves_per_block;
     int32_t convert;          /* 1 integer, 2 instructions */
-    int64_t kv_blocks;        /* workgroups that handle kv rows (dispatched first) */
+    int64_t kv_blocks;        /* workgroups that handle kv rows (dispatched first;
+                                 each wavefront takes 4 consecutive tokens) */
     int64_t q_blocks;         /* workgroups that handle q rows */
     int64_t grid;             /* kv_blocks + q_blocks */
 } qkv_prep_launch;

@@ -265,7 +265,8 @@ int main()
                        "grid fits", i);
                 expect(last_s.q_blocks * last_s.waves_per_block >= a.num_tokens * (int64_t)k.chunks,
                        "every q wavefront has a slot in the grid", i);
-                expect(last_s.kv_blocks * last_s.waves_per_block >= a.num_tokens, "every kv row covered", i);
+                expect(last_s.kv_blocks * last_s.waves_per_block * qkvp::kKvTokensPerWave >= a.num_tokens,
+                       "every kv row covered", i);
                 expect(k.bf16_store == (c.kv_store == QKV_PREP_KV_BF16), "store mode", i);
             }
 

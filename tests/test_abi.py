@@ -135,7 +135,8 @@ def test_launch_shape_heuristic():
     small = qp.qkv_prep_launch_shape(cfg, 256, 16)
     # decode-sized: two heads of a token per wavefront, up to 2^17 q rows
     assert small.rows_per_wave == 2 and small.waves_per_block == 1 and small.convert == 2
-    assert small.kv_blocks == 16 and small.q_blocks == 16 * 32 and small.grid == 16 * 33
+    # kv rows: four consecutive tokens per wavefront
+    assert small.kv_blocks == 4 and small.q_blocks == 16 * 32 and small.grid == 4 + 16 * 32
     assert qp.qkv_prep_launch_shape(cfg, 256, 2048).rows_per_wave == 2        # 2^17 rows
     assert qp.qkv_prep_launch_shape(cfg, 256, 2049).rows_per_wave == 1
     one_head = qp.qkv_prep_launch_shape(qp.make_config(1), 256, 100)
@@ -145,7 +146,7 @@ def test_launch_shape_heuristic():
     assert qp.qkv_prep_launch_shape(cfg, 256, 0).grid == 0
     big = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 131072)
     assert big.rows_per_wave == 1 and big.waves_per_block == 1
-    assert big.q_blocks == 131072 * 128 and big.kv_blocks == 131072
+    assert big.q_blocks == 131072 * 128 and big.kv_blocks == 131072 // 4
     # a batch whose one-row-per-wavefront grid would pass 2^32 work-items
     huge = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 600000)
     assert huge.rows_per_wave == 2
@@ -154,7 +155,7 @@ def test_launch_shape_heuristic():
                                                      convert=1), 256, 1000)
     assert (forced.rows_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
     assert forced.q_blocks == -(-(1000 * 32) // 8)
-    assert forced.kv_blocks == -(-1000 // 8)
+    assert forced.kv_blocks == -(-1000 // (4 * 8))
     # the row limit of qkv_prep_run also bounds the shape query (no overflow)
     for T in (2 ** 31 // 64, 2 ** 62, 2 ** 63 - 1):
         with pytest.raises(qp.QkvPrepError) as e:
@@ -162,7 +163,7 @@ def test_launch_shape_heuristic():
         assert e.value.code == qp.ERR_UNSUPPORTED
     assert qp.qkv_prep_launch_shape(cfg, 256, 2 ** 31 // 64 - 1).grid > 0
     odd = qp.qkv_prep_launch_shape(qp.make_config(3, waves_per_block=4), 256, 5)
-    assert odd.rows_per_wave == 2 and odd.q_blocks == 3 and odd.kv_blocks == 2   # 5 * 2 wavefronts / 4
+    assert odd.rows_per_wave == 2 and odd.q_blocks == 3 and odd.kv_blocks == 1   # ceil(5 / (4 * 4)), ceil(5 * 2 / 4)
 
 
 def test_fast_division_used_by_the_kernel():
