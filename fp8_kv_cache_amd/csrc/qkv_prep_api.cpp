@@ -93,6 +93,14 @@ int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)
 //    2048x64, 32768x64, 32768x128 and 131072x128 (by 1-5%).
 //  * convert: the gfx950 conversion instructions (bit-identical to the integer
 //    rounding, which the tests check on every workload).
+//  * kv_per_wave: 4 consecutive tokens' kv rows per kv wavefront, their loads
+//    issued together, from 2^17 q rows; 1 below.  The kv wavefronts are
+//    dispatched first and form a latency-bound burst.  Measured on MI355X (two
+//    to four alternating rounds): from 2^17 q rows four tokens are 0.8-2.9%
+//    faster (32768x64 +1.3%, 2048x64 +1.9%, 16384x8 +2.9%, 131072x128 even);
+//    below, where the kernel lasts as long as its slowest wavefront, they are
+//    up to 14% slower (256x64 and 512x64), even at 2^16 rows.  Two per
+//    wavefront gain less; eight no more than four.
 qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
 {
     (void)num_cus;
@@ -100,7 +108,8 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     const int64_t q_rows = T * c.num_heads;
     s.waves_per_block = c.waves_per_block ? c.waves_per_block : 1;
     s.convert = c.convert ? c.convert : 2;
-    s.kv_blocks = ceil_div(T, (int64_t)qkvp::kKvTokensPerWave * s.waves_per_block);
+    s.kv_per_wave = c.kv_per_wave ? c.kv_per_wave : (q_rows >= ((int64_t)1 << 17) ? 4 : 1);
+    s.kv_blocks = ceil_div(T, (int64_t)s.kv_per_wave * s.waves_per_block);
     // q wavefronts: T * ceil(H / U) (U heads of one token per wavefront)
     auto q_waves = [&](int u) { return T * ceil_div(c.num_heads, u); };
     if (c.rows_per_wave) {
@@ -138,6 +147,8 @@ int check_config(const qkv_prep_config *cfg)
     if (cfg->convert < 0 || cfg->convert > 2)
         return QKV_PREP_ERR_INVALID_ARG;
     if (cfg->kv_store != QKV_PREP_KV_FP8 && cfg->kv_store != QKV_PREP_KV_BF16)
+        return QKV_PREP_ERR_INVALID_ARG;
+    if (cfg->kv_per_wave != 0 && cfg->kv_per_wave != 1 && cfg->kv_per_wave != 2 && cfg->kv_per_wave != 4)
         return QKV_PREP_ERR_INVALID_ARG;
     if (cfg->head_dim != qkvp::kHeadDim || cfg->rope_dim != qkvp::kRopeDim)
         return QKV_PREP_ERR_UNSUPPORTED;
@@ -268,6 +279,7 @@ int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t n
     out->rows_per_wave = s.rows_per_wave;
     out->waves_per_block = s.waves_per_block;
     out->convert = s.convert;
+    out->kv_per_wave = s.kv_per_wave;
     out->kv_blocks = num_tokens ? s.kv_blocks : 0;
     out->q_blocks = num_tokens ? s.q_blocks : 0;
     out->grid = out->kv_blocks + out->q_blocks;
@@ -307,6 +319,7 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     k.num_tokens = T;
     k.block_size = (uint32_t)B;
     k.kv_blocks = (uint32_t)s.kv_blocks;
+    k.kv_per_wave = (uint32_t)s.kv_per_wave;
     k.heads = qkvp::make_fastdiv((uint32_t)H);
     k.blocks = qkvp::make_fastdiv((uint32_t)B);
     k.num_heads = (uint32_t)H;
@@ -319,8 +332,8 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     if (!dev.ok())
         return QKV_PREP_ERR_NO_DEVICE;
     if (h->log)
-        std::fprintf(stderr, "qkv_prep: T=%lld H=%lld rows/wave=%d waves/block=%d convert=%d grid=%lld+%lld\n",
-                     (long long)T, (long long)H, s.rows_per_wave, s.waves_per_block, s.convert,
+        std::fprintf(stderr, "qkv_prep: T=%lld H=%lld rows/wave=%d kv/wave=%d waves/block=%d convert=%d grid=%lld+%lld\n",
+                     (long long)T, (long long)H, s.rows_per_wave, s.kv_per_wave, s.waves_per_block, s.convert,
                      (long long)s.kv_blocks, (long long)s.q_blocks);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return finish(h, qkvp::launch_qkv_prep(k, s, st), st);

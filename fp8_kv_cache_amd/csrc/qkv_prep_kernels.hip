@@ -35,9 +35,9 @@
 //  * q rows and kv rows go to different workgroups of one launch (the FlagGems
 //    page merges the Q and KV launches); kv workgroups come first in dispatch
 //    order, so their quantization overlaps the q stream instead of trailing it.
-//    A kv wavefront takes four consecutive tokens, all their loads issued
-//    together: the kv wavefronts form a latency-bound burst at the start, and
-//    more loads in flight per wavefront shorten it.
+//    From 2^17 q rows a kv wavefront takes four consecutive tokens, all their
+//    loads issued together: the kv wavefronts form a latency-bound burst at
+//    the start, and more loads in flight per wavefront shorten it.
 //  * Decode-sized batches (up to 2^17 q rows) take two heads of one token per
 //    wavefront, one after the other, so the token's position, cos/sin row and
 //    the q weight are loaded once per two rows (up to 10% faster there while q
@@ -245,9 +245,10 @@ __device__ __forceinline__ void kv_finish(const KernelArgs &a, int64_t t, int64_
     }
 }
 
-// The kv rows of tokens t0 .. t0+N-1 on one wavefront: every slot and row load
-// is issued first, then the rows are finished one after another.  A token
-// whose slot is out of range is skipped (wave-uniform) before its row is read.
+// The kv rows of tokens t0 .. t0+n-1 (n = a.kv_per_wave <= N) on one
+// wavefront: every slot and row load is issued first, then the rows are
+// finished one after another.  A token whose slot is out of range is skipped
+// (wave-uniform) before its row is read.
 template <bool HW, bool SYS, int N>
 __device__ __forceinline__ void kv_rows(const KernelArgs &a, int64_t t0, uint32_t lane)
 {
@@ -255,7 +256,7 @@ __device__ __forceinline__ void kv_rows(const KernelArgs &a, int64_t t0, uint32_
     u32x4 d[N];
 #pragma unroll
     for (int u = 0; u < N; ++u)
-        slot[u] = t0 + u < a.num_tokens ? a.slot_mapping[t0 + u] : -1;
+        slot[u] = (uint32_t)u < a.kv_per_wave && t0 + u < a.num_tokens ? a.slot_mapping[t0 + u] : -1;
 #pragma unroll
     for (int u = 0; u < N; ++u)
         if (slot[u] >= 0 && slot[u] < a.num_slots)
@@ -277,9 +278,9 @@ __global__ __launch_bounds__(512) void qkv_prep_kernel(KernelArgs a)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t waves_per_block = blockDim.x >> 6;
     if (blockIdx.x < a.kv_blocks) {
-        const int64_t t = ((int64_t)blockIdx.x * waves_per_block + wave) * kKvTokensPerWave;
+        const int64_t t = ((int64_t)blockIdx.x * waves_per_block + wave) * a.kv_per_wave;
         if (t < a.num_tokens)
-            kv_rows<HW, U == 1, kKvTokensPerWave>(a, t, lane);
+            kv_rows<HW, U == 1, kMaxKvPerWave>(a, t, lane);
     } else {
         const int64_t wv = (int64_t)(blockIdx.x - a.kv_blocks) * waves_per_block + wave;
         if constexpr (U == 1) {

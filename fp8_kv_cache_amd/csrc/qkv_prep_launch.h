@@ -20,7 +20,8 @@ struct KernelArgs {
     int64_t q_rows;            // T * H (< 2^31)
     int64_t num_tokens;        // T
     uint32_t block_size;
-    uint32_t kv_blocks;        // workgroups [0, kv_blocks) take kv rows (kKvTokensPerWave per wavefront)
+    uint32_t kv_blocks;        // workgroups [0, kv_blocks) take kv rows
+    uint32_t kv_per_wave;      // consecutive tokens' kv rows per wavefront (1, 2 or 4)
     FastDiv heads;             // divides a q row index by H
     FastDiv blocks;            // divides a slot by block_size
     uint32_t num_heads;        // H
@@ -30,16 +31,14 @@ struct KernelArgs {
     int32_t bf16_store;        // 1: kv slots are 1024 bytes of bf16, no quantization
 };
 
-// Consecutive tokens whose kv rows one wavefront takes, their loads issued
-// together (the kv wavefronts run first, as a latency-bound burst: measured on
-// MI355X, 4 per wavefront beat 1 by 1.3% on 32768x64 and 1.9% on 2048x64, and
-// 8 was no better than 4).
-constexpr int kKvTokensPerWave = 4;
+// The most consecutive tokens whose kv rows one wavefront takes.
+constexpr int kMaxKvPerWave = 4;
 
 struct LaunchShape {
     int rows_per_wave;    // q rows per wavefront (1; or 2, 4 heads of one token)
     int waves_per_block;  // 1, 2, 4, 8
     int convert;          // 1 integer rounding, 2 conversion instructions
+    int kv_per_wave;      // tokens' kv rows per kv wavefront (1, 2, 4)
     int64_t kv_blocks;
     int64_t q_blocks;
 };

@@ -51,7 +51,7 @@ class QkvPrepConfig(ctypes.Structure):
                 ("rope_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("rows_per_wave", ctypes.c_int32),
                 ("waves_per_block", ctypes.c_int32), ("convert", ctypes.c_int32),
-                ("kv_store", ctypes.c_int32)]
+                ("kv_store", ctypes.c_int32), ("kv_per_wave", ctypes.c_int32)]
 
 
 class QkvPrepArgs(ctypes.Structure):
@@ -77,7 +77,7 @@ class QkvPrepMxfp8Args(ctypes.Structure):
 
 class QkvPrepLaunch(ctypes.Structure):
     _fields_ = [("rows_per_wave", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
-                ("convert", ctypes.c_int32), ("kv_blocks", ctypes.c_int64),
+                ("convert", ctypes.c_int32), ("kv_per_wave", ctypes.c_int32), ("kv_blocks", ctypes.c_int64),
                 ("q_blocks", ctypes.c_int64), ("grid", ctypes.c_int64)]
 
 
@@ -133,9 +133,9 @@ def library():
 
 
 def make_config(num_heads, *, block_size=64, eps=1e-6, rows_per_wave=0, waves_per_block=0,
-                convert=0, kv_store=KV_FP8) -> QkvPrepConfig:
+                convert=0, kv_store=KV_FP8, kv_per_wave=0) -> QkvPrepConfig:
     return QkvPrepConfig(num_heads, HEAD_DIM, ROPE_DIM, block_size, eps, rows_per_wave,
-                         waves_per_block, convert, kv_store)
+                         waves_per_block, convert, kv_store, kv_per_wave)
 
 
 # ------------------------------------------------------------ C-named calls
@@ -343,10 +343,10 @@ class QkvPrep:
     enqueues the operator on the current torch stream (or ``stream``)."""
 
     def __init__(self, num_heads, *, device=0, block_size=64, eps=1e-6, rows_per_wave=0,
-                 waves_per_block=0, convert=0, kv_store=KV_FP8):
+                 waves_per_block=0, convert=0, kv_store=KV_FP8, kv_per_wave=0):
         self.cfg = make_config(num_heads, block_size=block_size, eps=eps,
                                rows_per_wave=rows_per_wave, waves_per_block=waves_per_block,
-                               convert=convert, kv_store=kv_store)
+                               convert=convert, kv_store=kv_store, kv_per_wave=kv_per_wave)
         self.slot_bytes = SLOT_BYTES if kv_store == KV_FP8 else BF16_SLOT_BYTES
         self.device = device
         self.handle = qkv_prep_create(self.cfg, device)

@@ -78,6 +78,10 @@ typedef struct {
                                  the bf16 of all 512 values after the rotation
                                  (dims 0..447 normalized and weighted, 448..511
                                  rotated); slot s at byte s * 1024 */
+    int32_t kv_per_wave;      /* 0 = launch heuristic; 1, 2 or 4 = that many
+                                 consecutive tokens' kv rows per wavefront, all
+                                 their loads issued together (the heuristic
+                                 takes 4 from 2^17 q rows, else 1) */
 } qkv_prep_config;
 
 #define QKV_PREP_KV_FP8 0
@@ -120,8 +124,8 @@ typedef struct {
     int32_t rows_per_wave;
     int32_t waves_per_block;
     int32_t convert;          /* 1 integer, 2 instructions */
-    int64_t kv_blocks;        /* workgroups that handle kv rows (dispatched first;
-                                 each wavefront takes 4 consecutive tokens) */
+    int32_t kv_per_wave;      /* tokens' kv rows per kv wavefront (1, 2 or 4) */
+    int64_t kv_blocks;        /* workgroups that handle kv rows (dispatched first) */
     int64_t q_blocks;         /* workgroups that handle q rows */
     int64_t grid;             /* kv_blocks + q_blocks */
 } qkv_prep_launch;
@@ -201,7 +205,8 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
  * a device with num_cus compute units (256 on MI355X).  Pure host code: needs
  * no device, so the launch heuristic can be inspected anywhere.  The current
  * heuristic (one wavefront per workgroup; two heads of a token per wavefront
- * up to 2^17 q rows, one q row per wavefront above) does not depend on
+ * up to 2^17 q rows, one q row per wavefront above; four tokens' kv rows per
+ * kv wavefront from 2^17 q rows, one below) does not depend on
  * num_cus; the argument keeps the signature stable for a device-dependent
  * one.  Returns QKV_PREP_ERR_INVALID_ARG for a NULL out or num_tokens < 0, and
  * QKV_PREP_ERR_UNSUPPORTED when num_tokens * num_heads >= 2^31 (the limit of

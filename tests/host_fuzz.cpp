@@ -164,6 +164,7 @@ int main()
         c.waves_per_block = next() % 2 ? 0 : pick32() % 10;
         c.convert = next() % 2 ? 0 : pick32() % 4;
         c.kv_store = next() % 4 ? (int32_t)(next() % 2) : pick32();
+        c.kv_per_wave = next() % 2 ? 0 : pick32() % 6;
 
         const int64_t T = next() % 2 ? (int64_t)(next() % 200000) : pick64();
         qkv_prep_launch sh;
@@ -174,6 +175,7 @@ int main()
             expect(sh.grid == sh.kv_blocks + sh.q_blocks, "grid = kv + q", i);
             expect(sh.kv_blocks >= 0 && sh.q_blocks >= 0, "non-negative blocks", i);
             expect(sh.rows_per_wave == 1 || sh.rows_per_wave == 2 || sh.rows_per_wave == 4, "rows per wave", i);
+            expect(sh.kv_per_wave == 1 || sh.kv_per_wave == 2 || sh.kv_per_wave == 4, "kv rows per wave", i);
             expect(T > 0 || sh.grid == 0, "empty batch launches nothing", i);
         }
 
@@ -265,8 +267,9 @@ int main()
                        "grid fits", i);
                 expect(last_s.q_blocks * last_s.waves_per_block >= a.num_tokens * (int64_t)k.chunks,
                        "every q wavefront has a slot in the grid", i);
-                expect(last_s.kv_blocks * last_s.waves_per_block * qkvp::kKvTokensPerWave >= a.num_tokens,
+                expect(last_s.kv_blocks * last_s.waves_per_block * last_s.kv_per_wave >= a.num_tokens,
                        "every kv row covered", i);
+                expect(k.kv_per_wave == (uint32_t)last_s.kv_per_wave, "kv rows per wavefront", i);
                 expect(k.bf16_store == (c.kv_store == QKV_PREP_KV_BF16), "store mode", i);
             }
 

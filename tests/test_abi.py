@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_struct_sizes_match_the_header_layout():
-    assert ctypes.sizeof(qp.QkvPrepConfig) == 36
+    assert ctypes.sizeof(qp.QkvPrepConfig) == 40
     assert ctypes.sizeof(qp.QkvPrepArgs) == 88
     assert ctypes.sizeof(qp.QkvPrepLaunch) == 40
     assert ctypes.sizeof(qp.QkvPrepGatherArgs) == 48
@@ -113,6 +113,8 @@ def test_cache_may_be_null_without_blocks():
     (dict(waves_per_block=16), qp.ERR_INVALID_ARG),
     (dict(convert=3), qp.ERR_INVALID_ARG),
     (dict(kv_store=2), qp.ERR_INVALID_ARG),
+    (dict(kv_per_wave=3), qp.ERR_INVALID_ARG),
+    (dict(kv_per_wave=8), qp.ERR_INVALID_ARG),
 ])
 def test_bad_config(kw, code):
     base = dict(num_heads=8, block_size=64, eps=1e-6)
@@ -135,8 +137,19 @@ def test_launch_shape_heuristic():
     small = qp.qkv_prep_launch_shape(cfg, 256, 16)
     # decode-sized: two heads of a token per wavefront, up to 2^17 q rows
     assert small.rows_per_wave == 2 and small.waves_per_block == 1 and small.convert == 2
-    # kv rows: four consecutive tokens per wavefront
-    assert small.kv_blocks == 4 and small.q_blocks == 16 * 32 and small.grid == 4 + 16 * 32
+    # kv rows: one token per wavefront below 2^17 q rows
+    assert small.kv_per_wave == 1
+    assert small.kv_blocks == 16 and small.q_blocks == 16 * 32 and small.grid == 16 * 33
+    # four consecutive tokens per kv wavefront from 2^17 q rows
+    assert qp.qkv_prep_launch_shape(cfg, 256, 2047).kv_per_wave == 1
+    at = qp.qkv_prep_launch_shape(cfg, 256, 2048)
+    assert at.kv_per_wave == 4 and at.kv_blocks == 2048 // 4
+    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 16384).kv_per_wave == 4
+    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 4096).kv_per_wave == 1
+    ragged = qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=4), 256, 17)
+    assert ragged.kv_per_wave == 4 and ragged.kv_blocks == 5                  # ceil(17 / 4)
+    assert qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=2, waves_per_block=2),
+                                    256, 9).kv_blocks == 3                    # ceil(9 / (2 * 2))
     assert qp.qkv_prep_launch_shape(cfg, 256, 2048).rows_per_wave == 2        # 2^17 rows
     assert qp.qkv_prep_launch_shape(cfg, 256, 2049).rows_per_wave == 1
     one_head = qp.qkv_prep_launch_shape(qp.make_config(1), 256, 100)
@@ -155,7 +168,7 @@ def test_launch_shape_heuristic():
                                                      convert=1), 256, 1000)
     assert (forced.rows_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
     assert forced.q_blocks == -(-(1000 * 32) // 8)
-    assert forced.kv_blocks == -(-1000 // (4 * 8))
+    assert forced.kv_blocks == -(-1000 // 8)
     # the row limit of qkv_prep_run also bounds the shape query (no overflow)
     for T in (2 ** 31 // 64, 2 ** 62, 2 ** 63 - 1):
         with pytest.raises(qp.QkvPrepError) as e:
@@ -163,7 +176,7 @@ def test_launch_shape_heuristic():
         assert e.value.code == qp.ERR_UNSUPPORTED
     assert qp.qkv_prep_launch_shape(cfg, 256, 2 ** 31 // 64 - 1).grid > 0
     odd = qp.qkv_prep_launch_shape(qp.make_config(3, waves_per_block=4), 256, 5)
-    assert odd.rows_per_wave == 2 and odd.q_blocks == 3 and odd.kv_blocks == 1   # ceil(5 / (4 * 4)), ceil(5 * 2 / 4)
+    assert odd.rows_per_wave == 2 and odd.q_blocks == 3 and odd.kv_blocks == 2   # 5 * 2 wavefronts / 4
 
 
 def test_fast_division_used_by_the_kernel():

@@ -81,6 +81,19 @@ def test_head_counts_the_pages_measure(T, H):
     check(W.custom(T, H, seed=301 + T + H), rows_per_wave=1)
 
 
+@pytest.mark.parametrize("T,H", [(1, 8), (5, 3), (17, 64), (777, 5), (4099, 8)])
+@pytest.mark.parametrize("kv_per_wave", [1, 2, 4])
+def test_forced_kv_rows_per_wavefront(T, H, kv_per_wave):
+    # 1, 2 or 4 consecutive tokens' kv rows per wavefront, at ragged token
+    # counts (a last wavefront with fewer tokens), with skipped slots, under
+    # both q shapes and both cache modes.
+    w = W.custom(T, H, seed=340 + T + H, num_skip=min(T // 3, 7))
+    for rpw in (1, 2):
+        check(w, kv_per_wave=kv_per_wave, rows_per_wave=rpw)
+    res = run_and_compare(w, W.make_inputs(w, device=DEV), kv_store=1, kv_per_wave=kv_per_wave)
+    assert_bit_exact(res)
+
+
 @pytest.mark.parametrize("T,H", [(2048, 64), (2049, 64), (1024, 128), (1025, 128)])
 def test_both_sides_of_the_launch_threshold(T, H):
     # The heuristic takes two heads per wavefront up to 2^17 q rows and one
@@ -88,6 +101,7 @@ def test_both_sides_of_the_launch_threshold(T, H):
     from fp8_kv_cache_amd.qkv_prep import QkvPrep
     shape = QkvPrep(H).launch_shape(T)
     assert shape.rows_per_wave == (2 if T * H <= 1 << 17 else 1)
+    assert shape.kv_per_wave == (4 if T * H >= 1 << 17 else 1)
     check(W.custom(T, H, seed=330 + T + H, num_skip=5))
 
 
