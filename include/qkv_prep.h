@@ -166,7 +166,8 @@ int qkv_prep_create(const qkv_prep_config *cfg, int device, qkv_prep_t *out);
  * inputs.  With QKV_PREP_SYNC=1 in the environment the call also waits for
  * the stream and reports a device error as QKV_PREP_ERR_DEVICE.
  * The handle is read only here, so concurrent calls on different streams
- * are safe.
+ * are safe.  The call allocates no device memory and enqueues nothing but
+ * the one kernel (no memset, no copy), so it can be captured in a HIP graph.
  *
  * Numerics (all fp32, each step rounded to nearest even):
  *   S     = sum of x_j^2: chunk l (8 consecutive dims) summed left to right,
@@ -191,7 +192,8 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *args, void *stream);
  * rope values.  Uses the handle's device and block_size; the handle must have
  * been created with kv_store = QKV_PREP_KV_FP8 (else QKV_PREP_ERR_UNSUPPORTED).
  * Limits: n < 2^26 and num_blocks * B < 2^31 (else QKV_PREP_ERR_UNSUPPORTED).
- * Argument errors are reported as for qkv_prep_run, with nothing launched. */
+ * Argument errors are reported as for qkv_prep_run, with nothing launched.
+ * Like qkv_prep_run, it allocates nothing and enqueues only its kernel. */
 int qkv_prep_gather(qkv_prep_t h, const qkv_prep_gather_args *args, void *stream);
 
 /* Release a handle.  NULL is a no-op.  Returns QKV_PREP_OK. */

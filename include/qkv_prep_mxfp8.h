@@ -58,7 +58,8 @@ int64_t qkv_prep_mxfp8_scale_bytes(int64_t m, int32_t hidden);
  * 512 or above 8192, m > 2^31 - 128, or round_up(m, 128) * hidden >= 2^35:
  * the dispatch indexes rows and 16-byte chunks in 32 bits),
  * QKV_PREP_ERR_LAUNCH.
- * On an argument error nothing is launched.  No device memory is allocated. */
+ * On an argument error nothing is launched.  No device memory is allocated
+ * and only the one kernel is enqueued, so the call can be graph-captured. */
 int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *args, void *stream);
 
 #ifdef __cplusplus
