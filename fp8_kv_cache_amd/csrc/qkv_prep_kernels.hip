@@ -11,13 +11,13 @@
 // Work decomposition (a gfx950 design, not the pages' Triton/CUDA tilings):
 //  * One wavefront per 512-wide row: lane l holds the 16-byte chunk l (dims
 //    8l..8l+7), so a row is one fully coalesced 1 KiB load and one 1 KiB store.
-//    Measured on MI355X, this shape streams at the copy ceiling (~6.5 TB/s) at
-//    every footprint, while shapes with several loads per lane in flight (4 rows
-//    per wave, or several rows per wave) lose 6-15% once the footprint passes a
-//    few GiB.  One-wavefront workgroups (the measured optimum), non-temporal
+//    Measured on MI355X, this shape streams at the copy ceiling at every
+//    footprint (~6.5 TB/s with non-temporal stores), while shapes with several
+//    loads per lane in flight (4 rows per wave, or several rows per wave) lose
+//    6-15% once the footprint passes a few GiB.  One-wavefront workgroups (the measured optimum), non-temporal
 //    loads.
 //  * Stores: with one row per wavefront (the large-batch shape) every store
-//    carries the non-temporal system-scope policy (nt sc1), 1-2% faster than
+//    carries the non-temporal system-scope policy (nt sc1), 1-2.5% faster than
 //    plain non-temporal stores from 32768x64 up (about 2% at 32768x128 and
 //    131072x128).  The decode-sized shape keeps plain non-temporal stores:
 //    there nt sc1 was ~2% slower (a footprint near the size of the MALL).
@@ -41,9 +41,10 @@
 //  * Decode-sized batches (up to 2^17 q rows) take two heads of one token per
 //    wavefront, one after the other, so the token's position, cos/sin row and
 //    the q weight are loaded once per two rows (up to 10% faster there while q
-//    is cache-resident; the launch heuristic picks it).  Issuing several rows'
-//    loads at once (the sglang page's "K tokens per block" load-level
-//    parallelism) was slower at every size measured.
+//    is cache-resident; the launch heuristic picks it).  Issuing several q
+//    rows' loads at once (the sglang page's "K tokens per block" load-level
+//    parallelism) was slower at every size measured; the kv burst above is
+//    the one place where it pays.
 #include "qkv_prep_launch.h"
 #include "qkvp_device.h"
 
