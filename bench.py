@@ -402,6 +402,8 @@ def main():
                     help="profile: a short fixed program for rocprofv3 (no JSON line)")
     ap.add_argument("--launches", type=int, default=5)
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.launches < 1:
+        ap.error("--steps and --launches must be at least 1, --warmup at least 0")
     if args.gpus != 1:
         print("bench.py measures one GPU: this operator is per token and needs no collective; "
               "run with --gpus 1 (see the design notes for how it would shard).", file=sys.stderr)

@@ -22,6 +22,13 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in res.stderr and res.stdout == ""
 
 
+@pytest.mark.parametrize("flags", [["--steps", "0"], ["--warmup", "-1"], ["--launches", "0"]])
+def test_bad_counts_are_refused(flags):
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + flags,
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2 and "at least" in res.stderr and res.stdout == ""
+
+
 def test_committed_profiles_are_current_for_every_target():
     for name in ["prefill", "long"] + list(V.VARIANTS):
         t = V.target(name)
