@@ -183,6 +183,32 @@ def test_positions_at_both_ends_of_the_table():
     assert_bit_exact(run_and_compare(w, inp))
 
 
+@pytest.mark.parametrize("rpw", [1, 2])
+def test_out_of_range_positions_are_clamped(rpw):
+    # Positions outside [0, max_position) break a precondition; the kernel
+    # clamps them into the table, so it reads only table rows, and those
+    # tokens come out as if their position were clamped.  The clamped run is
+    # checked against the oracle; the out-of-range run must equal it byte for
+    # byte (every other token included).
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    w = W.custom(200, 8, seed=405, max_position=100, num_skip=3)
+    inp = W.make_inputs(w, device=DEV)
+    bad = inp["positions"].clone()
+    for i, p in ((3, -1), (10, -2 ** 40), (20, 100), (30, 100 + 12345), (40, 2 ** 62)):
+        bad[i] = p
+    inp["positions"] = bad.clamp(0, 99)
+    assert_bit_exact(run_and_compare(w, inp, rows_per_wave=rpw))
+    op = QkvPrep(8, block_size=w.block_size, eps=w.eps, rows_per_wave=rpw)
+    outs = []
+    for pos in (inp["positions"], bad):
+        q, cache = inp["q"].clone(), inp["cache"].clone()
+        op(q, inp["kv"], inp["q_w"], inp["kv_w"], pos, inp["cos_sin"], inp["slot_mapping"], cache)
+        outs.append((q, cache))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
 def test_outlier_rows_and_eps_zero():
     w = W.custom(512, 16, seed=404, outlier_frac=0.05, eps=0.0)
     assert_bit_exact(run_and_compare(w, W.make_inputs(w, device=DEV)))
