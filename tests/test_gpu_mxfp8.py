@@ -42,11 +42,28 @@ def test_mxfp8_matches_the_oracle(m, hidden, with_res, with_out):
     got_codes = codes.cpu().numpy()
     got_scales = scales.cpu().numpy()
     assert np.array_equal(got_scales, want_scales), np.count_nonzero(got_scales != want_scales)
-    d = np.abs(oracle.e4m3_to_f64(got_codes) - oracle.e4m3_to_f64(want_codes))
     assert np.count_nonzero(got_codes != want_codes) == 0, int(np.count_nonzero(got_codes != want_codes))
     if with_out:
         want = want_pre if with_res else W.as_u16(x)
         assert np.array_equal(W.as_u16(res_out), want)
+
+
+def test_mxfp8_at_the_measured_size():
+    # The size the bench times (16384 x 7168, residual in and out), every code,
+    # scale byte and residual value against the oracle.
+    m, hidden = 16384, 7168
+    print("case mxfp8 %dx%d residual" % (m, hidden), flush=True)
+    x, r, gamma = draw(m, hidden, 990)
+    scales = torch.full((qp.qkv_prep_mxfp8_scale_bytes(m, hidden),), 0xEE, dtype=torch.uint8, device=DEV)
+    codes = torch.empty((m, hidden), dtype=torch.uint8, device=DEV)
+    res_out = torch.empty_like(x)
+    qp.mxfp8_norm_quant(x, gamma, 1e-6, residual=r, residual_out=res_out, quant_out=codes, scale_out=scales)
+    torch.cuda.synchronize()
+    want_codes, want_scales, want_pre = oracle.mxfp8_norm_quant(W.as_u16(x), W.as_u16(gamma), 1e-6,
+                                                                residual=W.as_u16(r))
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
+    assert np.array_equal(codes.cpu().numpy(), want_codes)
+    assert np.array_equal(W.as_u16(res_out), want_pre)
 
 
 def test_mxfp8_outlier_rows_and_zero_rows():
