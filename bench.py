@@ -101,17 +101,24 @@ def copy_ceilings(torch, qp):
 # ----------------------------------------------------------------- one workload
 
 def time_launches(torch, fn, steps):
-    """The wall time of `steps` back-to-back launches, bracketed by
-    synchronizations and nothing else inside; then, in a second pass of as
-    many launches, per-launch HIP-event durations (on torch's current stream,
-    which is the stream the library launches on)."""
+    """The timed region: `steps` back-to-back launches bracketed by
+    synchronizations, with one HIP event just before the first launch and one
+    just after the last, on torch's current stream (the stream the library
+    launches on).  Returns the per-launch durations of a second pass of as many
+    launches, each between two events (for the median, minimum and p90), the
+    wall time of the timed region, and its event time (for the mean launch
+    duration over the timed region)."""
     stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for _ in range(steps):
         fn()
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    region = start.elapsed_time(end) * 1e-3
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
     for e0, e1 in events:
@@ -119,7 +126,7 @@ def time_launches(torch, fn, steps):
         fn()
         e1.record(stream)
     torch.cuda.synchronize()
-    return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events], wall
+    return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events], wall, region
 
 
 def time_cold(torch, fn, reps, scratch):
@@ -158,10 +165,10 @@ def bench_variants(torch, qp, steps, warmup):
         fn = V.setup(t, torch, qp)
         for _ in range(warmup):
             fn()
-        ks, wall = time_launches(torch, fn, steps)
+        ks, wall, region = time_launches(torch, fn, steps)
         del fn
         torch.cuda.empty_cache()
-        mean = statistics.fmean(ks)
+        mean = region / steps
         out[t.label] = {
             "gbps": round(t.alg_bytes * steps / wall / 1e9, 1),
             "kernel_us_mean": round(mean * 1e6, 2),
@@ -188,7 +195,7 @@ def bench_configs(torch, W, qp, names, warmup):
         for _ in range(warmup):
             fn()
         reps = 200 if t.alg_bytes < (1 << 30) else 30
-        ks, _ = time_launches(torch, fn, reps)
+        ks, _, _ = time_launches(torch, fn, reps)
         cold = time_cold(torch, fn, 10, scratch)
         del fn
         torch.cuda.empty_cache()
@@ -219,7 +226,7 @@ def bench_workload(torch, W, qp, name, steps, warmup):
         op(*args)
     torch.cuda.synchronize()
     log("bench: %s timing %d steps" % (w.label, steps))
-    kernel_s, wall = time_launches(torch, lambda: op(*args), steps)
+    kernel_s, wall, region = time_launches(torch, lambda: op(*args), steps)
     log("bench: %s cold-cache launches" % w.label)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     cold_s = time_cold(torch, lambda: op(*args), min(steps, 10), scratch)
@@ -228,7 +235,7 @@ def bench_workload(torch, W, qp, name, steps, warmup):
         "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
         "bytes_per_step": nbytes,
         "wall_s_per_step": wall / steps,
-        "kernel_s_mean": statistics.fmean(kernel_s),
+        "kernel_s_mean": region / steps,
         "kernel_s_median": statistics.median(kernel_s),
         "kernel_s_min": min(kernel_s),
         "kernel_s_p90": p90(kernel_s),
