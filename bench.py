@@ -305,7 +305,7 @@ def cpu_baseline(torch, W, name, target_s=12.0, sample_tokens=4096):
     import numpy as np
     import oracle
     w = W.WORKLOADS[name]
-    nth = max(1, min(16, host_cpu()[1]))        # the GPU machine's CPU share is 16
+    nth = max(1, min(16, host_cpu()[1]))        # at most 16 threads
     n = min(w.num_tokens, sample_tokens)
     sub = W.Workload(w.name, n, w.num_heads, w.max_position, w.num_blocks, w.block_size,
                      w.positions, w.slots, w.seed, num_seqs=max(1, n * w.num_seqs // w.num_tokens),

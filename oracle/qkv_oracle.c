@@ -477,7 +477,7 @@ void orc_quant_rows(int64_t n, const float *y, uint8_t *codes, uint8_t *scales)
  *      unchanged (the page's thread/warp/cluster order is not reproducible;
  *      this generalizes R1 to any multiple of 8).
  *   M3 inv = 1 / sqrt(S / hidden + eps), each step correctly rounded (the page
- *      uses an approximate rsqrt; this build takes the correctly rounded one).
+ *      uses an approximate rsqrt; this oracle takes the correctly rounded one).
  *   M4 normed = bf16((prenorm * inv) * (gamma + 1)), each product and the
  *      gamma + 1 rounded in fp32 (Gemma weight, the page's order).
  *   M5 per 32-element block: v = RN(amax * RN(1/448)); the scale byte is the
