@@ -395,8 +395,8 @@ def profile_run(torch, qp, name, launches, copy_bytes=512 << 20, copies=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill",
                     help="an operator workload; in profile mode also a variant target "
                          "(bf16store_prefill, gather_bf16, gather_f32, gather_f32_shuffled, mxfp8)")
