@@ -139,7 +139,8 @@ def main():
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--passes", default="trace,fetch,write,reqs,waves")
     ap.add_argument("--wave-counters", default="OccupancyPercent,MeanOccupancyPerCU,SQ_WAVES")
-    ap.add_argument("--bench-steps", type=int, default=50)
+    ap.add_argument("--bench-steps", type=int, default=200)
+    ap.add_argument("--bench-warmup", type=int, default=20)
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     from fp8_kv_cache_amd import variants as V
@@ -274,7 +275,7 @@ def main():
     if "bench" in passes:
         if t.family != "op" or args.workload not in W.WORKLOADS:
             raise SystemExit("the bench pass takes an operator workload")
-        bench_args = ["--workload", args.workload, "--steps", str(args.bench_steps), "--warmup", "10",
+        bench_args = ["--workload", args.workload, "--steps", str(args.bench_steps), "--warmup", str(args.bench_warmup),
                       "--no-also", "--no-variants", "--no-cpu-baseline", "--no-ceiling"]
         cmd, d, json_line = run_pass("bench", ["--kernel-trace", "--stats"], args.workload, 0, out, 600,
                                      bench_args=bench_args)
@@ -284,8 +285,8 @@ def main():
         lines = ["# rocprofv3 kernel trace over bench.py's timing run, kernel %s, workload %s" % (op_kernel, label),
                  "# command (from the repository root): %s" % " ".join(cmd),
                  "# kernel source sha256[:16] = %s" % summary["kernel_sha"],
-                 "# the workload's launches of %s (rows_per_wave %d): 10 warmup + %d wall-timed + %d event-timed"
-                 % (op_kernel, shape["rows_per_wave"], args.bench_steps, args.bench_steps)
+                 "# the workload's launches of %s (rows_per_wave %d): %d warmup + %d in the timed region + %d event-timed"
+                 % (op_kernel, shape["rows_per_wave"], args.bench_warmup, args.bench_steps, args.bench_steps)
                  + " + 10 after a cache flush; the bench's known-answer checks on the tiny workload use the",
                  "# small-batch template instance (rows_per_wave 2), listed on its own line", "",
                  "%-70s %6s %14s %14s %14s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
