@@ -166,7 +166,7 @@ __device__ __forceinline__ void q_chunk(const KernelArgs &a, uint32_t wv, uint32
     }
 }
 
-// ------------------------------------------------------------------ kv row
+// ------------------------------------------------------------------ kv rows
 
 // One token's kv row, once its slot (valid) and its row `d` are loaded.  Lane
 // l < 56 holds dims 8l..8l+7 of quantization block l/8 and writes their 8
