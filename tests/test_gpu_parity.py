@@ -94,6 +94,16 @@ def test_forced_kv_rows_per_wavefront(T, H, kv_per_wave):
     assert_bit_exact(res)
 
 
+@pytest.mark.parametrize("T", [5, 777, 1001])
+@pytest.mark.parametrize("kv_per_wave,wpb", [(2, 2), (4, 2), (4, 8), (2, 8)])
+def test_kv_rows_per_wavefront_with_wider_workgroups(T, kv_per_wave, wpb):
+    # Several kv wavefronts per workgroup, each taking several tokens: the
+    # token index combines the workgroup, the wavefront and kv_per_wave.
+    w = W.custom(T, 5, seed=350 + T + 10 * kv_per_wave + wpb, num_skip=min(T // 3, 7))
+    for rpw in (1, 2):
+        check(w, kv_per_wave=kv_per_wave, waves_per_block=wpb, rows_per_wave=rpw)
+
+
 @pytest.mark.parametrize("T,H", [(2048, 64), (2049, 64), (1024, 128), (1025, 128)])
 def test_both_sides_of_the_launch_threshold(T, H):
     # The heuristic takes two heads per wavefront up to 2^17 q rows and one
