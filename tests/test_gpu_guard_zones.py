@@ -49,7 +49,8 @@ def same_bytes(a, b):
 
 @pytest.mark.parametrize("T,H,rpw,kv_store", [
     (1, 1, 0, qp.KV_FP8), (777, 5, 1, qp.KV_FP8), (777, 5, 2, qp.KV_FP8), (300, 64, 0, qp.KV_FP8),
-    (4096, 64, 1, qp.KV_FP8), (300, 8, 1, qp.KV_BF16), (300, 8, 2, qp.KV_BF16)])
+    (4096, 64, 1, qp.KV_FP8), (300, 8, 1, qp.KV_BF16), (300, 8, 2, qp.KV_BF16),
+    (2051, 64, 0, qp.KV_FP8), (2051, 64, 0, qp.KV_BF16)])   # four tokens per kv wavefront, ragged
 def test_operator_writes_only_q_and_the_cache(T, H, rpw, kv_store):
     w = W.custom(T, H, seed=1300 + T + H, num_skip=min(T // 4, 5))
     inp = W.make_inputs(w, device=DEV)
@@ -58,6 +59,8 @@ def test_operator_writes_only_q_and_the_cache(T, H, rpw, kv_store):
     cache0 = torch.randint(0, 256, (w.num_blocks, w.block_size * slot_bytes), dtype=torch.uint8,
                            device=DEV, generator=g)
     op = qp.QkvPrep(H, block_size=w.block_size, eps=w.eps, rows_per_wave=rpw, kv_store=kv_store)
+    if T * H >= 1 << 17:
+        assert op.launch_shape(T).kv_per_wave == 4
     rest = (inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"], inp["slot_mapping"])
 
     q_ref, cache_ref = inp["q"].clone(), cache0.clone()
