@@ -89,6 +89,17 @@ MUTANTS = [
     ("rope sign", "z[ORC_NOPE_DIM + 2 * i] = fmaf(a, c, -bs);", "z[ORC_NOPE_DIM + 2 * i] = fmaf(a, c, bs);"),
     ("rope cos/sin swapped", "float c = cs[i];\n        float sn = cs[ORC_NPAIR + i];",
      "float sn = cs[i];\n        float c = cs[ORC_NPAIR + i];"),
+    ("rope without fma", "z[ORC_NOPE_DIM + 2 * i] = fmaf(a, c, -bs);", "z[ORC_NOPE_DIM + 2 * i] = a * c - bs;"),
+    ("rope fma on the sine product", "z[ORC_NOPE_DIM + 2 * i] = fmaf(a, c, -bs);",
+     "z[ORC_NOPE_DIM + 2 * i] = fmaf(-b, sn, a * c);"),
+    ("rope second output without fma", "z[ORC_NOPE_DIM + 2 * i + 1] = fmaf(a, sn, bc);",
+     "z[ORC_NOPE_DIM + 2 * i + 1] = a * sn + bc;"),
+    ("rope second output fma on the cosine product", "z[ORC_NOPE_DIM + 2 * i + 1] = fmaf(a, sn, bc);",
+     "z[ORC_NOPE_DIM + 2 * i + 1] = fmaf(b, c, a * sn);"),
+    ("norm weight before inv", "y[j] = w ? t * orc_bf16_to_f32(w[j]) : t;",
+     "y[j] = w ? (orc_bf16_to_f32(x[j]) * orc_bf16_to_f32(w[j])) * inv : t;"),
+    ("norm inv times weight first", "y[j] = w ? t * orc_bf16_to_f32(w[j]) : t;",
+     "y[j] = w ? orc_bf16_to_f32(x[j]) * (inv * orc_bf16_to_f32(w[j])) : t;"),
     ("rope half-split pairs", "float a = y[ORC_NOPE_DIM + 2 * i];\n        float b = y[ORC_NOPE_DIM + 2 * i + 1];",
      "float a = y[ORC_NOPE_DIM + i];\n        float b = y[ORC_NOPE_DIM + 32 + i];"),
     ("scale byte bias 128", "return (uint8_t)(e + 127);", "return (uint8_t)(e + 128);"),
