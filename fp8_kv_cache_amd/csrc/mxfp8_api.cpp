@@ -7,10 +7,11 @@
 #include <cstdint>
 
 #include "mxfp8_launch.h"
+#include "qkv_prep_host.h"
 
 namespace {
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned16(const void *p) { return qkvp::aligned(p, 16); }
 
 // The kernel indexes rows (padded to 128) in 32 bits.
 constexpr int64_t kMaxRows = ((int64_t)1 << 31) - 128;
@@ -30,17 +31,17 @@ extern "C" int64_t qkv_prep_mxfp8_scale_bytes(int64_t m, int32_t hidden)
     return rows_padded * cols;
 }
 
-extern "C" int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *a, void *stream)
+extern "C" int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *a, int device, void *stream)
 {
     if (!a || a->m < 0 || !(a->eps >= 0.0f) || a->eps > 3.4e38f)
         return QKV_PREP_ERR_INVALID_ARG;
-    if (a->hidden <= 0 || a->hidden % 512 || a->hidden > 8192)
+    if (a->hidden <= 0 || a->hidden % 128 || a->hidden > 512 * qkvp::kMxMaxGroups)
         return QKV_PREP_ERR_UNSUPPORTED;
     if (a->m == 0)
         return QKV_PREP_OK;
     if (!a->x || !a->gamma || !a->quant_out || !a->scale_out)
         return QKV_PREP_ERR_INVALID_ARG;
-    if (!aligned16(a->x) || !aligned16(a->gamma) || !aligned16(a->quant_out) ||
+    if (!aligned16(a->x) || !aligned16(a->gamma) || !aligned16(a->quant_out) || !qkvp::aligned(a->scale_out, 4) ||
         (a->residual && !aligned16(a->residual)) || (a->residual_out && !aligned16(a->residual_out)))
         return QKV_PREP_ERR_MISALIGNED;
     if (a->m > kMaxRows)
@@ -58,8 +59,19 @@ extern "C" int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *a, void *str
     k.m = a->m;
     k.rows_padded = rows_padded;
     k.hidden = a->hidden;
-    k.padded_cols = (a->hidden / 32 + 3) / 4 * 4;
+    k.chunks = a->hidden / 8;
+    k.padded_cols = a->hidden / 32;             // a multiple of 4: no column padding
     k.eps = a->eps;
-    return qkvp::launch_mxfp8(k, static_cast<hipStream_t>(stream)) == hipSuccess ? QKV_PREP_OK
-                                                                                 : QKV_PREP_ERR_LAUNCH;
+    if (!qkvp::device_exists(device))
+        return QKV_PREP_ERR_NO_DEVICE;
+    qkvp::DeviceScope scope(device);
+    if (!scope.ok())
+        return QKV_PREP_ERR_NO_DEVICE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (qkvp::launch_mxfp8(k, st) != hipSuccess)
+        return QKV_PREP_ERR_LAUNCH;
+    static const bool sync = qkvp::env_flag("QKV_PREP_SYNC");
+    if (sync && hipStreamSynchronize(st) != hipSuccess)
+        return QKV_PREP_ERR_DEVICE;
+    return QKV_PREP_OK;
 }

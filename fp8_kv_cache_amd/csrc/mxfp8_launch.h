@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace qkvp {
 
 struct MxArgs {
@@ -18,11 +20,16 @@ struct MxArgs {
     int64_t m;
     int64_t rows_padded;
     int32_t hidden;
+    int32_t chunks;            // hidden / 8: 16-byte chunks per row
     int32_t padded_cols;
     float eps;
 };
 
-// Enqueue the kernel for hidden = 512 * K, K = 1..16 (checked by the caller).
+// Rows of up to kMxMaxGroups groups of 512 values (hidden <= 16384).
+constexpr int kMxMaxGroups = 32;
+
+// Enqueue the kernel for hidden a multiple of 128, 128 <= hidden <= 512 *
+// kMxMaxGroups (checked by the caller).
 hipError_t launch_mxfp8(const MxArgs &a, hipStream_t stream);
 
 }  // namespace qkvp

@@ -5,11 +5,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <new>
 
 #include "qkv_prep_gather.h"
+#include "qkv_prep_host.h"
 #include "qkv_prep_internal.h"
 #include "qkv_prep_launch.h"
 
@@ -23,47 +23,11 @@ struct qkv_prep {
 
 namespace {
 
-bool env_flag(const char *name)
-{
-    const char *v = std::getenv(name);
-    return v && v[0] == '1';
-}
-
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+using qkvp::aligned;
+using qkvp::DeviceScope;
+using qkvp::env_flag;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Makes the handle's device current for the guard's lifetime and restores the
-// caller's current device afterwards.
-class DeviceScope {
-public:
-    explicit DeviceScope(int device)
-    {
-        if (hipGetDevice(&prev_) != hipSuccess) {
-            (void)hipGetLastError();
-            return;
-        }
-        if (prev_ != device && hipSetDevice(device) != hipSuccess) {
-            (void)hipGetLastError();
-            return;
-        }
-        ok_ = true;
-        switched_ = prev_ != device;
-    }
-    ~DeviceScope()
-    {
-        if (switched_)
-            (void)hipSetDevice(prev_);
-    }
-    DeviceScope(const DeviceScope &) = delete;
-    DeviceScope &operator=(const DeviceScope &) = delete;
-    bool ok() const { return ok_; }
-
-private:
-    int prev_ = -1;
-    bool ok_ = false;
-    bool switched_ = false;
-};
 
 // Launch result, then (with QKV_PREP_SYNC=1) the stream's.
 int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)

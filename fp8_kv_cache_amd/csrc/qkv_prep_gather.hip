@@ -13,20 +13,19 @@ using namespace dev;
 
 constexpr int kRopeLane = kNopeDim / 8;  // lanes 56..63 hold the rope chunks
 
-// code * 2^(b - 127) is exact in fp32 (E4M3 has 4 significant bits; 2^-127,
-// the scale of byte 0, is the fp32 subnormal 0x00400000).
-__device__ __forceinline__ float scale_of_byte(uint32_t b)
+// Four E4M3 codes (byte k of `codes` is dim k) times 2^(b - 127), b a scale
+// byte 0..255, as v_ldexp_f32: the power is applied to the exponent, never
+// formed as a float, so byte 255 (2^128, past the fp32 range) works like any
+// other.  The results are exact (an E4M3 value has 4 significant bits, and the
+// smallest product, 2^-9 * 2^-127, is an fp32 subnormal) except those of
+// 2^128 and above, which only byte 255 reaches and which become infinity.
+__device__ __forceinline__ u32x4 dequant4(uint32_t codes, uint32_t b)
 {
-    return __uint_as_float(b ? (b << 23) : 0x00400000u);
-}
-
-// Four E4M3 codes (byte k of `codes` is dim k) times a power-of-two scale.
-__device__ __forceinline__ u32x4 dequant4(uint32_t codes, float scale)
-{
+    const int e = (int)b - 127;
     const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
     const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
-    return u32x4{__float_as_uint(lo[0] * scale), __float_as_uint(lo[1] * scale),
-                 __float_as_uint(hi[0] * scale), __float_as_uint(hi[1] * scale)};
+    return u32x4{__float_as_uint(__builtin_ldexpf(lo[0], e)), __float_as_uint(__builtin_ldexpf(lo[1], e)),
+                 __float_as_uint(__builtin_ldexpf(hi[0], e)), __float_as_uint(__builtin_ldexpf(hi[1], e))};
 }
 
 // bf16 rows: one wavefront per output row.  Lane l < 56 reads the 8 codes of
@@ -50,10 +49,9 @@ __device__ __forceinline__ void gather_row_bf16(const GatherArgs &a, int64_t i, 
         if (lane < kRopeLane) {
             const u32x2 codes = *(reinterpret_cast<const u32x2 *>(data) + lane);
             const uint32_t b = base[(int64_t)a.block_size * kSlotData + (int64_t)sib * kSlotScale + lane / 8];
-            const float scale = scale_of_byte(b);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const u32x4 d = dequant4(codes[h], scale);
+                const u32x4 d = dequant4(codes[h], b);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     v[4 * h + e] = __uint_as_float(d[e]);
@@ -83,10 +81,9 @@ __device__ __forceinline__ void gather_row_f32(const GatherArgs &a, int64_t i, u
         const u32x2 rec = *reinterpret_cast<const u32x2 *>(base + (int64_t)a.block_size * kSlotData +
                                                           (int64_t)sib * kSlotScale);
         const uint32_t shift = 8u * (lane >> 4);
-        lo = dequant4(reinterpret_cast<const uint32_t *>(data)[lane], scale_of_byte((rec[0] >> shift) & 0xffu));
+        lo = dequant4(reinterpret_cast<const uint32_t *>(data)[lane], (rec[0] >> shift) & 0xffu);
         if (lane < 48) {
-            hi = dequant4(reinterpret_cast<const uint32_t *>(data + 256)[lane],
-                          scale_of_byte((rec[1] >> shift) & 0xffu));
+            hi = dequant4(reinterpret_cast<const uint32_t *>(data + 256)[lane], (rec[1] >> shift) & 0xffu);
         } else {
             const u32x2 r = reinterpret_cast<const u32x2 *>(data + kNopeDim)[lane - 48];
             hi = u32x4{r[0] << 16, r[0] & 0xffff0000u, r[1] << 16, r[1] & 0xffff0000u};

@@ -1,5 +1,8 @@
-// Streaming copy and in-place update used as bandwidth ceilings (see
-// include/qkv_prep_probe.h).
+// The measurement and verification probes of libqkv_prep_probe.so (see
+// include/qkv_prep_probe.h): a streaming copy and an in-place streaming update
+// used as bandwidth ceilings, and the operators' own number-format code run on
+// arrays so that tests can compare it with a reference on every input pattern.
+// None of this is part of the operators; it is built into its own library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,6 +83,25 @@ __global__ __launch_bounds__(256) void convert_probe(const u32x4 *in, uint32_t *
         bf16[i] = u32x2{qkvp::dev::pack_bf16<HW>(f0, f1), qkvp::dev::pack_bf16<HW>(f2, f3)};
 }
 
+// The two UE8M0 rules on one value per thread: the main operator's scale
+// byte of amax (qkvp::dev::ue8m0_exponent + 127) and the MXFP8 operator's byte
+// (qkvp::dev::ue8m0_byte_up); thread i < 256 also writes the MXFP8 inverse
+// scale of byte i.
+__global__ __launch_bounds__(256) void ue8m0_probe(const float *in, int64_t n, uint8_t *op_byte, uint8_t *mx_byte,
+                                                   float *mx_inverse)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (mx_inverse && i < 256)
+        mx_inverse[i] = qkvp::dev::ue8m0_inverse_scale((uint32_t)i);
+    if (i >= n)
+        return;
+    const float v = in[i];
+    if (op_byte)
+        op_byte[i] = (uint8_t)(qkvp::dev::ue8m0_exponent(__float_as_uint(v)) + 127);
+    if (mx_byte)
+        mx_byte[i] = (uint8_t)qkvp::dev::ue8m0_byte_up(v);
+}
+
 }  // namespace
 
 extern "C" int qkv_prep_probe_convert(const float *in, int64_t n, void *e4m3_out, void *bf16_out, int32_t convert,
@@ -135,5 +157,23 @@ extern "C" int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, vo
     hipLaunchKernelGGL(stream_copy, dim3((uint32_t)blocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<u32x4 *>(dst),
                        static_cast<const u32x4 *>(src), n);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+extern "C" int qkv_prep_probe_ue8m0(const float *in, int64_t n, void *op_byte_out, void *mx_byte_out,
+                                    void *mx_inverse_out, void *stream)
+{
+    if (n < 0 || n >= ((int64_t)1 << 38) || (n > 0 && !in) || (reinterpret_cast<uintptr_t>(in) & 3) ||
+        (reinterpret_cast<uintptr_t>(mx_inverse_out) & 3))
+        return 1;
+    const int64_t threads = n > 256 ? n : 256;
+    const int64_t blocks = mx_inverse_out ? (threads + 255) / 256 : (n + 255) / 256;
+    if (blocks == 0)
+        return 0;
+    if (blocks >= ((int64_t)1 << 31))
+        return 1;
+    hipLaunchKernelGGL(ue8m0_probe, dim3((uint32_t)blocks), dim3(256), 0, static_cast<hipStream_t>(stream), in, n,
+                       static_cast<uint8_t *>(op_byte_out), static_cast<uint8_t *>(mx_byte_out),
+                       static_cast<float *>(mx_inverse_out));
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }

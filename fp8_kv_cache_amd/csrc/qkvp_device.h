@@ -130,6 +130,27 @@ __device__ __forceinline__ int ue8m0_exponent(uint32_t amax_bits)
     return e < -127 ? -127 : e;
 }
 
+// The MXFP8 scale byte of v: the least b >= 0 with v <= 2^(b - 127), at most
+// 254; 0 for v <= 0 (v finite).  Positive floats order like their bit
+// patterns, and 2^(b - 127) has the pattern b << 23 for b >= 1, so the least
+// b >= 1 is the pattern divided by 2^23, rounded up.  Patterns up to
+// 0x00400000 (2^-127, a subnormal) give b = 0; as a signed integer, every
+// negative value and -0 fall in that case too.
+__device__ __forceinline__ uint32_t ue8m0_byte_up(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    if ((int32_t)u <= 0x00400000)
+        return 0u;
+    return min((u + 0x7fffffu) >> 23, 254u);
+}
+
+// The inverse of a scale byte: 2^(127 - byte) for bytes 1..253; 0 for byte 0
+// (a zero block) and for 254, whose power 2^-127 is below the normal range.
+__device__ __forceinline__ float ue8m0_inverse_scale(uint32_t byte)
+{
+    return byte - 1u < 253u ? __builtin_ldexpf(1.0f, 127 - (int)byte) : 0.0f;
+}
+
 // ------------------------------------------------------------------ cross-lane
 
 constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }

@@ -1,0 +1,64 @@
+"""Python binding of the probe library, libqkv_prep_probe.so
+(include/qkv_prep_probe.h): bandwidth ceilings (a streaming copy, an in-place
+streaming update) and the operators' number-format code run on arrays.  Used
+by the tests and the benchmark; the operators never load it.  Argument
+marshalling only, with the C names."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from fp8_kv_cache_amd.qkv_prep import OK, QkvPrepError
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqkv_prep_probe.so")
+
+EXPORTED = ("qkv_prep_probe_copy", "qkv_prep_probe_update", "qkv_prep_probe_convert", "qkv_prep_probe_ue8m0")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libqkv_prep_probe.so is not built (%s); run `python -m fp8_kv_cache_amd.build`"
+                          % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.qkv_prep_probe_copy.argtypes = [vp, vp, i64, vp]
+    L.qkv_prep_probe_update.argtypes = [vp, i64, vp]
+    L.qkv_prep_probe_convert.argtypes = [vp, i64, vp, vp, ctypes.c_int32, vp]
+    L.qkv_prep_probe_ue8m0.argtypes = [vp, i64, vp, vp, vp, vp]
+    for name in EXPORTED:
+        getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+_lib = _load()
+
+
+def library():
+    return _lib
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise QkvPrepError(rc, what)
+
+
+def qkv_prep_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:
+    """The streaming-copy probe (a bandwidth ceiling)."""
+    _check(_lib.qkv_prep_probe_copy(dst_ptr, src_ptr, nbytes, stream), "qkv_prep_probe_copy")
+
+
+def qkv_prep_probe_update(buf_ptr: int, nbytes: int, stream=None) -> None:
+    """The in-place streaming-update probe (a bandwidth ceiling)."""
+    _check(_lib.qkv_prep_probe_update(buf_ptr, nbytes, stream), "qkv_prep_probe_update")
+
+
+def qkv_prep_probe_convert(in_ptr: int, n: int, e4m3_ptr, bf16_ptr, convert: int, stream=None) -> None:
+    """The operator's E4M3 and bf16 conversions on an array (device pointers)."""
+    _check(_lib.qkv_prep_probe_convert(in_ptr, n, e4m3_ptr, bf16_ptr, convert, stream), "qkv_prep_probe_convert")
+
+
+def qkv_prep_probe_ue8m0(in_ptr, n: int, op_byte_ptr, mx_byte_ptr, mx_inverse_ptr, stream=None) -> None:
+    """The operators' two UE8M0 rules on an array (device pointers)."""
+    _check(_lib.qkv_prep_probe_ue8m0(in_ptr, n, op_byte_ptr, mx_byte_ptr, mx_inverse_ptr, stream),
+           "qkv_prep_probe_ue8m0")

@@ -41,9 +41,7 @@ OUT_BF16 = 1
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("qkv_prep_create", "qkv_prep_run", "qkv_prep_destroy", "qkv_prep_supported",
             "qkv_prep_launch_shape", "qkv_prep_validate", "qkv_prep_strerror",
-            "qkv_prep_gather", "qkv_prep_probe_copy", "qkv_prep_probe_update", "qkv_prep_probe_convert",
-            "qkv_prep_mxfp8_norm_quant",
-            "qkv_prep_mxfp8_scale_bytes")
+            "qkv_prep_gather", "qkv_prep_mxfp8_norm_quant", "qkv_prep_mxfp8_scale_bytes")
 
 
 class QkvPrepConfig(ctypes.Structure):
@@ -110,18 +108,10 @@ def _load():
     L.qkv_prep_strerror.restype = ctypes.c_char_p
     L.qkv_prep_gather.argtypes = [ctypes.c_void_p, P(QkvPrepGatherArgs), ctypes.c_void_p]
     L.qkv_prep_gather.restype = ctypes.c_int
-    L.qkv_prep_mxfp8_norm_quant.argtypes = [P(QkvPrepMxfp8Args), ctypes.c_void_p]
+    L.qkv_prep_mxfp8_norm_quant.argtypes = [P(QkvPrepMxfp8Args), ctypes.c_int, ctypes.c_void_p]
     L.qkv_prep_mxfp8_norm_quant.restype = ctypes.c_int
     L.qkv_prep_mxfp8_scale_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32]
     L.qkv_prep_mxfp8_scale_bytes.restype = ctypes.c_int64
-    L.qkv_prep_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                      ctypes.c_void_p]
-    L.qkv_prep_probe_copy.restype = ctypes.c_int
-    L.qkv_prep_probe_update.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    L.qkv_prep_probe_update.restype = ctypes.c_int
-    L.qkv_prep_probe_convert.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                                         ctypes.c_int32, ctypes.c_void_p]
-    L.qkv_prep_probe_convert.restype = ctypes.c_int
     return L
 
 
@@ -188,8 +178,8 @@ def qkv_prep_mxfp8_scale_bytes(m: int, hidden: int) -> int:
     return _lib.qkv_prep_mxfp8_scale_bytes(m, hidden)
 
 
-def qkv_prep_mxfp8_norm_quant(args: QkvPrepMxfp8Args, stream=None) -> None:
-    rc = _lib.qkv_prep_mxfp8_norm_quant(ctypes.byref(args), stream)
+def qkv_prep_mxfp8_norm_quant(args: QkvPrepMxfp8Args, device: int = 0, stream=None) -> None:
+    rc = _lib.qkv_prep_mxfp8_norm_quant(ctypes.byref(args), device, stream)
     if rc != OK:
         raise QkvPrepError(rc, "qkv_prep_mxfp8_norm_quant")
 
@@ -212,33 +202,11 @@ def mxfp8_norm_quant(x, gamma, eps, *, residual=None, residual_out=None, quant_o
     check_mxfp8_tensors(x, gamma, residual, residual_out, quant_out, scale_out)
     args = QkvPrepMxfp8Args(x.data_ptr(), _ptr(residual), _ptr(residual_out), gamma.data_ptr(),
                             quant_out.data_ptr(), scale_out.data_ptr(), m, hidden, eps)
-    # The C call launches on the current device: make it x's.
-    with torch.cuda.device(x.device):
-        if stream is None:
-            stream = torch.cuda.current_stream(x.device).cuda_stream
-        qkv_prep_mxfp8_norm_quant(args, stream)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    qkv_prep_mxfp8_norm_quant(args, x.device.index if x.device.index is not None else torch.cuda.current_device(),
+                              stream)
     return quant_out, scale_out
-
-
-def qkv_prep_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:
-    """The streaming-copy probe of include/qkv_prep_probe.h (a bandwidth ceiling)."""
-    rc = _lib.qkv_prep_probe_copy(dst_ptr, src_ptr, nbytes, stream)
-    if rc != OK:
-        raise QkvPrepError(rc, "qkv_prep_probe_copy")
-
-
-def qkv_prep_probe_convert(in_ptr: int, n: int, e4m3_ptr, bf16_ptr, convert: int, stream=None) -> None:
-    """The conversion probe of include/qkv_prep_probe.h (device pointers)."""
-    rc = _lib.qkv_prep_probe_convert(in_ptr, n, e4m3_ptr, bf16_ptr, convert, stream)
-    if rc != OK:
-        raise QkvPrepError(rc, "qkv_prep_probe_convert")
-
-
-def qkv_prep_probe_update(buf_ptr: int, nbytes: int, stream=None) -> None:
-    """The in-place streaming-update probe of include/qkv_prep_probe.h."""
-    rc = _lib.qkv_prep_probe_update(buf_ptr, nbytes, stream)
-    if rc != OK:
-        raise QkvPrepError(rc, "qkv_prep_probe_update")
 
 
 # ------------------------------------------------------------ torch wrapper

@@ -187,9 +187,11 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *args, void *stream);
 /* Read slots back out of an FP8 + UE8M0 cache (the reader of this cache; the
  * 1Cat-vLLM PR 1280 page, change 5, names it dequantize_and_gather_k_cache).
  * Enqueue on `stream` and return.  Row i of out: dims 0..447 are
- * code * 2^(scale byte - 127) of their 64-dim block (exact in fp32; the bf16
- * output is that value rounded to nearest even), dims 448..511 the stored bf16
- * rope values.  Uses the handle's device and block_size; the handle must have
+ * code * 2^(scale byte - 127) of their 64-dim block, for any scale byte 0..255
+ * (exact in fp32, except that values of 2^128 and above, which only byte 255
+ * reaches, are +-infinity; E4M3 NaN codes give NaN; the bf16 output is the fp32
+ * value rounded to nearest even), dims 448..511 the stored bf16 rope values.
+ * The operator itself never writes byte 255 (its exponents stop at 127).  Uses the handle's device and block_size; the handle must have
  * been created with kv_store = QKV_PREP_KV_FP8 (else QKV_PREP_ERR_UNSUPPORTED).
  * Limits: n < 2^26 and num_blocks * B < 2^31 (else QKV_PREP_ERR_UNSUPPORTED).
  * Argument errors are reported as for qkv_prep_run, with nothing launched.

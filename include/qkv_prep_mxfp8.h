@@ -16,10 +16,11 @@
  *          approximate rsqrt)
  *   n_j  = bf16((p_j * inv) * (gamma_j + 1))
  *   per block of 32: v = RN(amax * RN(1/448)); byte = the biased exponent of v
- *          rounded up (0 for v <= 0, +1 if the mantissa is non-zero unless v is
- *          a subnormal <= 2^-127, at most 254); inverse = 2^(127 - byte), 0 for
- *          byte 0 or 254; code_j = E4M3(clamp(RN(n_j * inverse), +-448)),
- *          round to nearest even
+ *          rounded up: the least b >= 0 with v <= 2^(b - 127), at most 254,
+ *          and 0 for v <= 0 (so every v <= 2^-127 gives 0); inverse =
+ *          2^(127 - byte) for bytes 1..253, 0 for byte 0 and for 254 (whose
+ *          2^-127 is below the normal range); code_j =
+ *          E4M3(clamp(RN(n_j * inverse), +-448)), round to nearest even
  *   codes: uint8 [m][hidden], row-major
  *   scales: the 128x4 swizzled layout, byte (row, col) at
  *          col%4 + (col/4)*512 + (row%32)*16 + ((row%128)/32)*4 + (row/128)*128*cols
@@ -40,9 +41,9 @@ typedef struct {
     void *residual_out;     /* bf16 [m][hidden] or NULL; receives p; 16-B aligned */
     const void *gamma;      /* bf16 [hidden]; 16-B aligned */
     void *quant_out;        /* uint8 [m][hidden]; 16-B aligned */
-    void *scale_out;        /* uint8 [qkv_prep_mxfp8_scale_bytes(m, hidden)] */
+    void *scale_out;        /* uint8 [qkv_prep_mxfp8_scale_bytes(m, hidden)]; 4-B aligned */
     int64_t m;              /* rows >= 0; 0 is a no-op */
-    int32_t hidden;         /* a multiple of 512, at most 8192 */
+    int32_t hidden;         /* a multiple of 128, at most 16384 */
     float eps;              /* >= 0, finite */
 } qkv_prep_mxfp8_args;
 
@@ -51,16 +52,20 @@ typedef struct {
  * not fit in int64_t. */
 int64_t qkv_prep_mxfp8_scale_bytes(int64_t m, int32_t hidden);
 
-/* Enqueue on `stream` (a hipStream_t; NULL = the null stream) of the current
- * HIP device and return.  Return codes are those of qkv_prep.h:
+/* Enqueue on `stream` (a hipStream_t of HIP device `device`; NULL = that
+ * device's null stream) and return.  The device is made current for the call
+ * and the caller's current device is restored, as qkv_prep_run does with its
+ * handle's device.  Return codes are those of qkv_prep.h:
  * QKV_PREP_ERR_INVALID_ARG (NULL pointer, negative m, bad eps),
  * QKV_PREP_ERR_MISALIGNED, QKV_PREP_ERR_UNSUPPORTED (hidden not a multiple of
- * 512 or above 8192, m > 2^31 - 128, or round_up(m, 128) * hidden >= 2^35:
+ * 128 or above 16384, m > 2^31 - 128, or round_up(m, 128) * hidden >= 2^35:
  * the dispatch indexes rows and 16-byte chunks in 32 bits),
- * QKV_PREP_ERR_LAUNCH.
+ * QKV_PREP_ERR_NO_DEVICE (no such device), QKV_PREP_ERR_LAUNCH, and, with
+ * QKV_PREP_SYNC=1 in the environment (the call then waits for the stream),
+ * QKV_PREP_ERR_DEVICE for an asynchronous device error.
  * On an argument error nothing is launched.  No device memory is allocated
  * and only the one kernel is enqueued, so the call can be graph-captured. */
-int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *args, void *stream);
+int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *args, int device, void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,19 +1,26 @@
 /*
- * qkv_prep_probe.h -- probes shipped in libqkv_prep.so next to the operator:
- * a plain streaming device-to-device copy and a streaming in-place update
- * (read and write the same bytes, as the operator does with q), used as
- * bandwidth ceilings; and the operator's fp32 -> E4M3 / bf16 conversions on
- * an array, for exhaustive checks of the conversion instructions.
+ * qkv_prep_probe.h -- the measurement and verification probes, shipped in
+ * their own library, libqkv_prep_probe.so, next to libqkv_prep.so.  None of
+ * them is part of the operators; an application links libqkv_prep.so alone.
  *
- * The pages measure the operator against a warm device-to-device copy of the
- * same card ("achievable bandwidth", FlagGems-vllm PR 684, section
+ * Bandwidth ceilings.  The pages measure the operator against a warm
+ * device-to-device copy of the same card (FlagGems-vllm PR 684, section
  * "Performance against achievable bandwidth").  The runtime's own copy
- * (hipMemcpyAsync) is one such ceiling; this hand-written copy, built with
- * the same load/store idioms as the operator (16-byte non-temporal vector
- * accesses), is a second, usually stricter one.  The in-place update is the
+ * (hipMemcpyAsync) is one such ceiling; qkv_prep_probe_copy, written with the
+ * same load/store idioms as the operator (16-byte non-temporal vector
+ * accesses), is a second, usually stricter one; qkv_prep_probe_update is the
  * third: the operator rewrites q in place, and on MI355X in-place streaming
- * reaches a different rate from a copy between two buffers.  None of them is
- * part of the operator.
+ * reaches a different rate from a copy between two buffers.
+ *
+ * Number-format probes.  qkv_prep_probe_convert and qkv_prep_probe_ue8m0 run
+ * the operators' own device code for the E4M3, bf16 and UE8M0 rules on an
+ * array, so a test can compare it with the oracle on every input pattern.
+ *
+ * All pointers are device pointers owned by the caller.  Return codes are
+ * those of qkv_prep.h: 0 (QKV_PREP_OK), 1 (QKV_PREP_ERR_INVALID_ARG: NULL,
+ * negative, out-of-range or misaligned argument; nothing is launched) and 5
+ * (QKV_PREP_ERR_LAUNCH).  Each call enqueues one kernel on `stream` (a
+ * hipStream_t; NULL = the null stream) of the current HIP device and returns.
  */
 #ifndef QKV_PREP_PROBE_H
 #define QKV_PREP_PROBE_H
@@ -24,35 +31,41 @@
 extern "C" {
 #endif
 
-/* Copy `bytes` bytes from device pointer src to device pointer dst on
- * `stream` (a hipStream_t; NULL = null stream) and return.  Both pointers
- * 16-byte aligned, bytes a multiple of 16, the ranges must not overlap.
- * Returns 0 (QKV_PREP_OK), 1 (invalid argument: NULL, negative or unaligned),
- * or 5 (launch failed).  bytes == 0 is a no-op. */
+/* Copy `bytes` bytes from src to dst.  Both pointers 16-byte aligned, bytes a
+ * multiple of 16, the ranges must not overlap.  bytes == 0 is a no-op. */
 int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, void *stream);
 
-/* In-place streaming update of `bytes` bytes at device pointer buf on
- * `stream`: every 16-byte chunk is read, its first 32-bit word (little-endian
- * unsigned) is incremented by 1 with wrap-around, and the chunk is written
- * back to the same address.  The traffic is bytes read + bytes written.
- * buf 16-byte aligned, bytes a multiple of 16.  Returns 0, 1 (invalid
- * argument: NULL, negative or unaligned) or 5 (launch failed); bytes == 0 is a
- * no-op. */
+/* In-place streaming update of `bytes` bytes at buf: every 16-byte chunk is
+ * read, its first 32-bit word (little-endian unsigned) is incremented by 1
+ * with wrap-around, and the chunk is written back to the same address.  The
+ * traffic is bytes read + bytes written.  buf 16-byte aligned, bytes a
+ * multiple of 16; bytes == 0 is a no-op. */
 int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream);
 
-/* Run the operator's own fp32 conversions on n values of `in`, on `stream`:
+/* The operator's fp32 conversions on n values of `in`:
  * e4m3_out[i] = the E4M3 code of in[i] (OCP e4m3fn, round to nearest even;
  * defined for |in[i]| <= 448, the range the operator converts) and
  * bf16_out[i] = the bf16 of in[i] (round to nearest even; defined for finite
  * values).  convert selects the path as in qkv_prep_config: 1 = integer
  * rounding, 2 = the gfx950 conversion instructions.  Either output may be
  * NULL.  in 16-byte aligned, e4m3_out 4-byte aligned, bf16_out 8-byte
- * aligned, n >= 0 a multiple of 4 and below 2^33.  Returns 0, 1 (invalid or
- * misaligned argument) or 5 (launch failed).  A verification probe: it lets a
- * test compare the device conversions with a reference on every input
- * pattern. */
+ * aligned, n >= 0 a multiple of 4 and below 2^33. */
 int qkv_prep_probe_convert(const float *in, int64_t n, void *e4m3_out, void *bf16_out, int32_t convert,
                            void *stream);
+
+/* The two UE8M0 rules on n values of `in` (fp32, 4-byte aligned, n < 2^38):
+ *   op_byte_out[i]  (uint8) the main operator's scale byte e + 127 of a block
+ *                   whose amax is in[i]: e is the least integer with
+ *                   amax <= 448 * 2^e, clamped to [-127, 127] (defined for
+ *                   finite in[i] >= 0);
+ *   mx_byte_out[i]  (uint8) the MXFP8 operator's scale byte of v = in[i]: the
+ *                   least b >= 0 with v <= 2^(b - 127), at most 254, and 0
+ *                   for v <= 0 (defined for finite v);
+ *   mx_inverse_out  (fp32 [256], 4-byte aligned) the MXFP8 inverse scale of
+ *                   every byte 0..255: 2^(127 - byte) for 1..253, else 0.
+ * Any output may be NULL; with n == 0 only mx_inverse_out is written. */
+int qkv_prep_probe_ue8m0(const float *in, int64_t n, void *op_byte_out, void *mx_byte_out,
+                         void *mx_inverse_out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -94,6 +94,7 @@ def configure(L):
         L.orc_f32_to_bf16_array.argtypes = [vp, vp, i64]
         L.orc_f32_to_e4m3_array.argtypes = [vp, vp, i64]
         L.orc_ue8m0_exponent_array.argtypes = [vp, vp, i64]
+        L.orc_ue8m0_ceil_byte_array.argtypes = [vp, vp, i64]
         L.orc_rows.argtypes = [i64, vp, vp, f32, vp, vp, vp, vp]
         L.orc_quant_rows.argtypes = [i64, vp, vp, vp]
     return L
@@ -263,6 +264,14 @@ def mxfp8_scale_offset(row, col, padded_cols):
 
 def ue8m0_ceil_byte(v):
     return int(lib().orc_ue8m0_ceil_byte(float(v)))
+
+
+def ue8m0_ceil_bytes(v) -> np.ndarray:
+    """The MXFP8 scale byte of every value of a float32 array (uint8)."""
+    v = _c(np.asarray(v, dtype=np.float32), np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_ue8m0_ceil_byte_array(_p(v), _p(out), v.size)
+    return out
 
 
 def ue8m0_inverse(byte):

@@ -481,10 +481,14 @@ void orc_quant_rows(int64_t n, const float *y, uint8_t *codes, uint8_t *scales)
  *   M4 normed = bf16((prenorm * inv) * (gamma + 1)), each product and the
  *      gamma + 1 rounded in fp32 (Gemma weight, the page's order).
  *   M5 per 32-element block: v = RN(amax * RN(1/448)); the scale byte is the
- *      page's rounded-up biased exponent of v (0 for v <= 0; +1 when the
- *      mantissa is non-zero, except a subnormal v at or below 2^-127; at most
- *      254); inverse = 2^(127 - byte), 0 for byte 0 (and for 254, where the
- *      page's exponent arithmetic reaches 0).
+ *      biased exponent of v rounded up (the page's _ue8m0_ceil docstring),
+ *      read as a definition: the least b >= 0 with v <= 2^(b - 127), at most
+ *      254; 0 for v <= 0.  A power of two keeps its own exponent, anything
+ *      else takes the next one up, and every v at or below 2^-127 gives 0.
+ *      The inverse scale is 2^(127 - byte) (the page's _ue8m0_inverse
+ *      docstring) while that power is a normal binary32 number, byte 1..253;
+ *      byte 0 (a zero block) gives 0, and so does 254, whose power 2^-127
+ *      lies below the normal range: the page's helper returns 0 there too.
  *   M6 code = E4M3 of RN(normed * inverse) clamped to +-448 first (satfinite).
  *   M7 codes row-major [m][hidden]; scale byte (row, col = block) at the
  *      128x4 swizzled offset col%4 + (col/4)*512 + (row%32)*16 +
@@ -520,30 +524,32 @@ float orc_sum_squares_n(const uint16_t *x, int64_t n)
     return s;
 }
 
-/* M5: the page's rounded-up UE8M0 byte of v. */
+/* M5: the scale byte of v, from its defining inequality v <= 2^(b - 127),
+ * compared exactly in double.  v is never NaN here (finite rows give a finite
+ * amax); a NaN would read as "not positive". */
 uint32_t orc_ue8m0_ceil_byte(float v)
 {
     if (!(v > 0.0f))
         return 0;
-    uint32_t bits = float_to_bits(v);
-    uint32_t e = (bits >> 23) & 0xffu;
-    uint32_t mant = bits & 0x7fffffu;
-    uint32_t bump = mant != 0;
-    if (e == 0 && mant <= 0x400000u)
-        bump = 0;
-    uint32_t r = e + bump;
-    return r > 254 ? 254 : r;
+    if (isinf(v))
+        return 254;
+    double a = (double)v;
+    int b;
+    frexp(a, &b);                                  /* 2^(b-1) <= a < 2^b */
+    b += 127;                                      /* so a <= 2^(b - 127) holds */
+    while (b > 0 && a <= ldexp(1.0, b - 1 - 127))  /* the least such b, not below 0 */
+        b -= 1;
+    if (b < 0)
+        b = 0;
+    return b > 254 ? 254u : (uint32_t)b;
 }
 
-/* M6: inverse scale 2^(127 - byte), computed as the page does. */
+/* M5: the inverse scale of a byte. */
 float orc_ue8m0_inverse(uint32_t byte)
 {
-    if (byte == 0)
+    if (byte == 0 || byte >= 254)
         return 0.0f;
-    int32_t ne = 254 - (int32_t)byte;
-    if (ne < 0)
-        ne = 0;
-    return bits_to_float((uint32_t)ne << 23);
+    return (float)ldexp(1.0, 127 - (int)byte);
 }
 
 /* M7 */
@@ -609,4 +615,11 @@ int orc_mxfp8_norm_quant(int64_t m, int64_t hidden, const uint16_t *x, const uin
     free(pre);
     free(normed);
     return 0;
+}
+
+/* The MXFP8 scale byte of n values (an array helper for the tests). */
+void orc_ue8m0_ceil_byte_array(const float *v, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (uint8_t)orc_ue8m0_ceil_byte(v[i]);
 }

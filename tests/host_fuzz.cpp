@@ -12,8 +12,9 @@
 //    valid and non-empty, the launch's arguments and grid must be consistent,
 //    and the caller's current device must be restored after every call.
 //  * qkv_prep_mxfp8_scale_bytes and qkv_prep_mxfp8_norm_quant on extreme and
-//    random shapes and pointers: sizes against a 128-bit reference, a launch
-//    exactly when valid, the launch's rows and scale layout.
+//    random shapes, pointers and device indices: sizes against a 128-bit
+//    reference, a launch exactly when valid, on the requested device with the
+//    caller's device restored, the launch's rows and scale layout.
 // Any undefined operation aborts the run; contract violations are counted.
 #include <cmath>
 #include <cstdint>
@@ -53,10 +54,12 @@ hipError_t launch_gather(const GatherArgs &a, int, hipStream_t)
 }
 int mx_launches = 0;
 MxArgs last_mx;
+int mx_device_at_launch = -1;
 hipError_t launch_mxfp8(const MxArgs &a, hipStream_t)
 {
     ++mx_launches;
     last_mx = a;
+    mx_device_at_launch = fake_current;
     return hipSuccess;
 }
 }  // namespace qkvp
@@ -308,7 +311,7 @@ int main()
     long long mx_ok = 0;
     for (long long i = 0; i < 200000; ++i) {
         const int64_t m = next() % 2 ? (int64_t)(next() % 100000) : pick64();
-        const int32_t hidden = next() % 2 ? (int32_t)(512 * (next() % 18)) : pick32();
+        const int32_t hidden = next() % 2 ? (int32_t)(128 * (next() % 140)) : pick32();
         const int64_t sb = qkv_prep_mxfp8_scale_bytes(m, hidden);
         if (m < 0 || hidden <= 0 || hidden % 128) {
             expect(sb == -1, "scale bytes -1 for bad shapes", i);
@@ -328,21 +331,31 @@ int main()
         a.hidden = hidden;
         a.eps = next() % 4 ? 1e-6f : pick_eps();
         const int before = qkvp::mx_launches;
-        const int rc = qkv_prep_mxfp8_norm_quant(&a, nullptr);
-        expect(rc >= 0 && rc <= 6 && rc != QKV_PREP_ERR_NO_DEVICE && rc != QKV_PREP_ERR_DEVICE, "mxfp8 code", i);
+        static const int devices[] = {0, 1, 1, 0, -1, 2, std::numeric_limits<int>::min()};
+        const int device = devices[next() % (sizeof(devices) / sizeof(devices[0]))];
+        fake_current = (int)(next() % 2);
+        const int caller_device = fake_current;
+        const int rc = qkv_prep_mxfp8_norm_quant(&a, device, nullptr);
+        expect(rc >= 0 && rc <= 6 && rc != QKV_PREP_ERR_DEVICE, "mxfp8 code", i);
+        expect(fake_current == caller_device, "mxfp8 restores the caller's device", i);
         const bool launched = qkvp::mx_launches != before;
         expect(launched == (rc == QKV_PREP_OK && m > 0), "mxfp8 launch iff valid and non-empty", i);
+        if (rc == QKV_PREP_ERR_NO_DEVICE)
+            expect(device < 0 || device > 1, "mxfp8 no-device only for a missing device", i);
         if (launched) {
             ++mx_ok;
+            expect(qkvp::mx_device_at_launch == device, "mxfp8 launches on the requested device", i);
             const qkvp::MxArgs &k = qkvp::last_mx;
-            expect(hidden >= 512 && hidden <= 8192 && hidden % 512 == 0, "hidden supported", i);
+            expect(hidden >= 128 && hidden <= 16384 && hidden % 128 == 0, "hidden supported", i);
+            expect(k.chunks == hidden / 8, "chunks", i);
+            expect((reinterpret_cast<uintptr_t>(k.scale_out) & 3) == 0, "scale words aligned", i);
             expect(k.rows_padded == (m + 127) / 128 * 128 && k.rows_padded < ((int64_t)1 << 31), "rows", i);
             expect(k.rows_padded * hidden / 8 < ((int64_t)1 << 32), "chunk indices fit", i);
             expect(k.padded_cols == hidden / 32 && (int64_t)k.rows_padded * k.padded_cols == sb, "scale layout", i);
             expect(std::isfinite(k.eps) && k.eps >= 0.0f, "eps", i);
         }
     }
-    expect(qkv_prep_mxfp8_norm_quant(nullptr, nullptr) == QKV_PREP_ERR_INVALID_ARG, "mxfp8 NULL", 0);
+    expect(qkv_prep_mxfp8_norm_quant(nullptr, 0, nullptr) == QKV_PREP_ERR_INVALID_ARG, "mxfp8 NULL", 0);
 
     std::printf("cases %lld, valid argument sets %lld, launch shapes %lld, runs launched %lld, gathers launched "
                 "%lld, mxfp8 launched %lld, contract failures %d\n", cases, ok_validate, ok_shape, runs_ok,

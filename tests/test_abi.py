@@ -8,6 +8,7 @@ import re
 import pytest
 import torch
 
+from fp8_kv_cache_amd import probe
 from fp8_kv_cache_amd import qkv_prep as qp
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -15,22 +16,41 @@ HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.j
            if h.endswith(".h")]
 
 
-def declared_functions():
+PROBE_HEADER = os.path.join(ROOT, "include", "qkv_prep_probe.h")
+
+
+def declared_functions(headers):
     names = set()
-    for h in HEADERS:
+    for h in headers:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
         names |= set(re.findall(r"\b(qkv_prep_[a-z0-9_]+)\s*\(", text))
     return sorted(names)
 
 
+def operator_headers():
+    return [h for h in HEADERS if h != PROBE_HEADER]
+
+
 def test_header_and_binding_agree():
-    assert declared_functions() == sorted(qp.EXPORTED)
+    assert declared_functions(operator_headers()) == sorted(qp.EXPORTED)
+    assert declared_functions([PROBE_HEADER]) == sorted(probe.EXPORTED)
 
 
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(qp.LIB_PATH)
-    for name in declared_functions():
+    for name in declared_functions(operator_headers()):
         assert hasattr(lib, name), name
+    plib = ctypes.CDLL(probe.LIB_PATH)
+    for name in declared_functions([PROBE_HEADER]):
+        assert hasattr(plib, name), name
+
+
+def test_operator_library_exports_no_probe():
+    # The measurement probes live in their own library: an application that
+    # links libqkv_prep.so gets the operators only.
+    lib = ctypes.CDLL(qp.LIB_PATH)
+    for name in probe.EXPORTED:
+        assert not hasattr(lib, name), name
 
 
 def test_struct_sizes_match_the_header_layout():
@@ -200,7 +220,7 @@ def test_fast_division_used_by_the_kernel():
 
 
 def test_probes_reject_bad_arguments_without_launching():
-    lib = qp.library()
+    lib = probe.library()
     assert lib.qkv_prep_probe_copy(None, None, 0, None) == qp.OK
     assert lib.qkv_prep_probe_copy(None, None, 16, None) == qp.ERR_INVALID_ARG
     assert lib.qkv_prep_probe_copy(1 << 20, 2 << 20, 15, None) == qp.ERR_INVALID_ARG
@@ -220,6 +240,13 @@ def test_probes_reject_bad_arguments_without_launching():
     assert conv(1 << 20, 4, (2 << 20) + 2, None, 1, None) == qp.ERR_INVALID_ARG
     assert conv(1 << 20, 4, None, (3 << 20) + 4, 1, None) == qp.ERR_INVALID_ARG
     assert conv(1 << 20, 1 << 33, None, None, 1, None) == qp.ERR_INVALID_ARG
+    ue = lib.qkv_prep_probe_ue8m0
+    assert ue(None, 0, None, None, None, None) == qp.OK                        # nothing to do
+    assert ue(None, 4, None, None, None, None) == qp.ERR_INVALID_ARG           # NULL input
+    assert ue(1 << 20, -4, None, None, None, None) == qp.ERR_INVALID_ARG
+    assert ue((1 << 20) + 2, 4, None, None, None, None) == qp.ERR_INVALID_ARG  # input misaligned
+    assert ue(1 << 20, 4, None, None, (2 << 20) + 1, None) == qp.ERR_INVALID_ARG
+    assert ue(1 << 20, 1 << 38, None, None, None, None) == qp.ERR_INVALID_ARG
 
 
 def test_gather_without_handle_is_rejected():
@@ -286,19 +313,25 @@ def test_mxfp8_scale_bytes_and_argument_checks():
         d.update(kw)
         a = qp.QkvPrepMxfp8Args(d["x"], d["residual"], d["residual_out"], d["gamma"],
                                 d["quant_out"], d["scale_out"], d["m"], d["hidden"], d["eps"])
-        return qp.library().qkv_prep_mxfp8_norm_quant(ctypes.byref(a), None)
+        return qp.library().qkv_prep_mxfp8_norm_quant(ctypes.byref(a), d.get("device", 0), None)
     assert code(m=0) == qp.OK
     assert code(m=-1) == qp.ERR_INVALID_ARG
     assert code(eps=-1.0) == qp.ERR_INVALID_ARG
     assert code(x=None) == qp.ERR_INVALID_ARG
     assert code(gamma=None) == qp.ERR_INVALID_ARG
     assert code(scale_out=None) == qp.ERR_INVALID_ARG
-    assert code(hidden=768) == qp.ERR_UNSUPPORTED
-    assert code(hidden=8704) == qp.ERR_UNSUPPORTED
+    assert code(hidden=96) == qp.ERR_UNSUPPORTED             # not a multiple of 128
+    assert code(hidden=200) == qp.ERR_UNSUPPORTED
+    assert code(hidden=16512) == qp.ERR_UNSUPPORTED          # above 16384
+    assert code(hidden=-128) == qp.ERR_UNSUPPORTED
+    assert code(scale_out=(4 << 20) + 2) == qp.ERR_MISALIGNED
     assert code(x=(1 << 20) + 2) == qp.ERR_MISALIGNED
     assert code(residual=(5 << 20) + 4) == qp.ERR_MISALIGNED
     assert code(residual_out=(6 << 20) + 8) == qp.ERR_MISALIGNED
     assert code(m=1 << 26) == qp.ERR_UNSUPPORTED
+    # Good arguments on a device that does not exist: rejected before any launch.
+    assert code(device=-1) == qp.ERR_NO_DEVICE
+    assert code(device=1 << 20) == qp.ERR_NO_DEVICE
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path):

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import oracle
+from fp8_kv_cache_amd import probe
 from fp8_kv_cache_amd import qkv_prep as qp
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +48,7 @@ def run_probe(x, convert, e4m3=True, bf16=True):
     n = x.numel()
     e = torch.empty(n, dtype=torch.uint8, device=DEV) if e4m3 else None
     b = torch.empty(n, dtype=torch.int16, device=DEV) if bf16 else None
-    qp.qkv_prep_probe_convert(x.data_ptr(), n, None if e is None else e.data_ptr(),
+    probe.qkv_prep_probe_convert(x.data_ptr(), n, None if e is None else e.data_ptr(),
                               None if b is None else b.data_ptr(), convert,
                               torch.cuda.current_stream().cuda_stream)
     return e, b
@@ -93,3 +94,42 @@ def test_bf16_on_strided_patterns_and_every_tie():
         bad = np.nonzero(got != want)[0]
         assert bad.size == 0, "convert=%d first bad input %#x: got %#x want %#x" % (
             convert, x[bad[0]].view(np.uint32), got[bad[0]], want[bad[0]])
+
+
+def test_ue8m0_rules_on_every_non_negative_pattern():
+    # Both UE8M0 rules as the operators' device code computes them
+    # (qkv_prep_probe_ue8m0), against the oracle, on every finite
+    # non-negative fp32 pattern (about 2.1e9 values): the main operator's
+    # scale byte e + 127 of a block amax, and the MXFP8 operator's byte.  Then
+    # the MXFP8 inverse scale of every byte.
+    stop_all = 0x7F800000
+    jobs = [(s, min(s + CHUNK, stop_all)) for s in range(0, stop_all, CHUNK)]
+    note("UE8M0: %d chunks of up to %d patterns" % (len(jobs), CHUNK))
+
+    def want(j):
+        x = host_bits(j[0], j[1], False)
+        return (oracle.ue8m0_exponent(x) + 127).astype(np.uint8), oracle.ue8m0_ceil_bytes(x)
+
+    st = torch.cuda.current_stream().cuda_stream
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        for k in range(0, len(jobs), 8):
+            batch = jobs[k:k + 8]
+            futs = [pool.submit(want, j) for j in batch]
+            for (start, stop), fut in zip(batch, futs):
+                n = stop - start
+                x = device_bits(start, stop, False)
+                op = torch.empty(n, dtype=torch.uint8, device=DEV)
+                mx = torch.empty(n, dtype=torch.uint8, device=DEV)
+                probe.qkv_prep_probe_ue8m0(x.data_ptr(), n, op.data_ptr(), mx.data_ptr(), None, st)
+                want_op, want_mx = fut.result()
+                for what, got, ref in (("operator byte", op, want_op), ("mxfp8 byte", mx, want_mx)):
+                    got = got.cpu().numpy()
+                    bad = np.nonzero(got != ref)[0]
+                    assert bad.size == 0, "%s: first bad pattern %#x: got %d want %d" % (
+                        what, start + int(bad[0]), got[bad[0]], ref[bad[0]])
+            note("  chunks %d..%d bit-exact" % (k, k + len(batch) - 1))
+    inv = torch.empty(256, dtype=torch.float32, device=DEV)
+    probe.qkv_prep_probe_ue8m0(None, 0, None, None, inv.data_ptr(), st)
+    got = inv.cpu().numpy()
+    ref = np.array([oracle.ue8m0_inverse(b) for b in range(256)], np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))

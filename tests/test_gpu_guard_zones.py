@@ -8,6 +8,7 @@ range would show here as a changed guard byte."""
 import pytest
 import torch
 
+from fp8_kv_cache_amd import probe
 from fp8_kv_cache_amd import qkv_prep as qp
 from fp8_kv_cache_amd import workloads as W
 
@@ -132,15 +133,83 @@ def test_probes_write_only_their_buffers(nbytes):
     gd = Guarded(nbytes, 1601)
     dst = gd.view(torch.uint8, (nbytes,))
     gd.arm()
-    qp.qkv_prep_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st)
+    probe.qkv_prep_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st)
     gd.assert_intact("probe copy")
     assert torch.equal(dst, src)
     gu = Guarded(nbytes, 1602)
     buf = gu.view(torch.uint8, (nbytes,))
     gu.arm()
     start = buf.clone()
-    qp.qkv_prep_probe_update(buf.data_ptr(), nbytes, st)
+    probe.qkv_prep_probe_update(buf.data_ptr(), nbytes, st)
     gu.assert_intact("probe update")
     want = start.view(torch.int32).clone()
     want[0::4] += 1                                  # word 0 of every 16-byte chunk, wrapping
     assert torch.equal(buf.view(torch.int32), want)
+
+
+def _slot_byte_mask(slots, num_blocks, block_size, kv_store):
+    """Host mask of the cache bytes the operator may write for these slots:
+    the data and scale records of every valid slot (FP8 layout), or the
+    1024-byte slot (bf16 layout)."""
+    import numpy as np
+    slot_bytes = qp.SLOT_BYTES if kv_store == qp.KV_FP8 else qp.BF16_SLOT_BYTES
+    mask = np.zeros(num_blocks * block_size * slot_bytes, bool)
+    for s in slots:
+        if not 0 <= s < num_blocks * block_size:
+            continue
+        if kv_store == qp.KV_BF16:
+            mask[s * 1024:(s + 1) * 1024] = True
+            continue
+        b, i = divmod(int(s), block_size)
+        base = b * block_size * qp.SLOT_BYTES
+        mask[base + i * 576: base + (i + 1) * 576] = True
+        mask[base + block_size * 576 + i * 8: base + block_size * 576 + (i + 1) * 8] = True
+    return mask
+
+
+@pytest.mark.parametrize("T,H,kv_store", [(300, 8, qp.KV_FP8), (300, 8, qp.KV_BF16),
+                                          (2051, 64, qp.KV_FP8), (2051, 64, qp.KV_BF16)])
+def test_non_finite_rows_write_only_their_own_spans(T, H, kv_store):
+    # Non-finite inputs are outside the numerics contract, so their values are
+    # not checked; what must still hold is that such rows (whole rows of NaN,
+    # of +-inf, single NaN or inf elements, rows whose sum of squares
+    # overflows) write only their own q row and their own cache slot.  Guard
+    # bands surround q and the cache, and every cache byte outside the valid
+    # slots' records must keep its value.
+    import numpy as np
+    note = "non-finite rows: T=%d H=%d kv_store=%d" % (T, H, kv_store)
+    print(note, flush=True)
+    w = W.custom(T, H, seed=1600 + T + kv_store, num_skip=7)
+    inp = W.make_inputs(w, device=DEV)
+    q_src, kv_src = inp["q"].clone(), inp["kv"].clone()
+    nan, inf = float("nan"), float("inf")
+    q_src[::7, 0, :] = nan
+    q_src[1::7, H - 1, :] = inf
+    q_src[2::7, H // 2, 5] = nan
+    q_src[3::7, 0, 450] = -inf
+    q_src[4::11, :, :] = 3.0e38                      # finite, but the squares overflow
+    kv_src[::5, :] = nan
+    kv_src[1::5, 100] = inf
+    kv_src[2::5, 460] = nan
+    kv_src[3::5, :] = -inf
+    rest = (kv_src, inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"], inp["slot_mapping"])
+    slot_bytes = qp.SLOT_BYTES if kv_store == qp.KV_FP8 else qp.BF16_SLOT_BYTES
+    g = torch.Generator(device=DEV).manual_seed(w.seed + 5)
+    cache0 = torch.randint(0, 256, (w.num_blocks, w.block_size * slot_bytes), dtype=torch.uint8,
+                           device=DEV, generator=g)
+    op = qp.QkvPrep(H, block_size=w.block_size, eps=w.eps, kv_store=kv_store)
+    gq = Guarded(T * H * 1024, seed=w.seed + 1)
+    q = gq.view(torch.bfloat16, (T, H, 512))
+    q.copy_(q_src)
+    gq.arm()
+    gc = Guarded(cache0.numel(), seed=w.seed + 2)
+    cache = gc.view(torch.uint8, tuple(cache0.shape))
+    cache.copy_(cache0)
+    gc.arm()
+    op(q, *rest, cache)
+    gq.assert_intact("q")
+    gc.assert_intact("cache")
+    mask = _slot_byte_mask(inp["slot_mapping"].cpu().numpy(), w.num_blocks, w.block_size, kv_store)
+    after = cache.cpu().numpy().reshape(-1)
+    before = cache0.cpu().numpy().reshape(-1)
+    assert np.array_equal(after[~mask], before[~mask]), "bytes outside the valid slots changed"

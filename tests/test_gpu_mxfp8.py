@@ -26,7 +26,13 @@ def draw(m, hidden, seed, scale=1.0):
 @pytest.mark.parametrize("m,hidden,with_res,with_out", [
     (1, 512, False, False), (5, 1024, True, True), (127, 1536, True, False),
     (128, 4096, False, True), (300, 7168, True, True), (129, 8192, True, True),
-    (64, 2560, False, False), (1000, 3072, True, True)])
+    (64, 2560, False, False), (1000, 3072, True, True),
+    # hidden a multiple of 128 but not of 512 (a partial last group of 16, 32
+    # or 48 chunks), and past 8192 (an odd group count above 16 is launched
+    # with one empty group more)
+    (3, 128, True, True), (130, 384, True, False), (17, 640, False, True), (64, 1152, True, True),
+    (257, 3200, True, True), (40, 8704, True, True), (33, 12288, False, True), (129, 16384, True, True),
+    (5, 16256, True, True)])
 def test_mxfp8_matches_the_oracle(m, hidden, with_res, with_out):
     x, r, gamma = draw(m, hidden, 900 + m + hidden)
     eps = 1e-6
@@ -111,3 +117,19 @@ def test_mxfp8_subnormal_inputs(eps, with_res):
         assert np.array_equal(W.as_u16(res_out), wp)
     if eps == 1e-6:
         assert set(np.unique(ws).tolist()) <= {0, 1, 2, 3, 4}       # the bottom of the scale range
+
+
+def test_mxfp8_partial_group_decides_the_sum_order():
+    # hidden 640: one full group of 64 chunks and a partial one of 16.  Large
+    # values in the partial group and tiny ones elsewhere make the sum depend
+    # on where the partial group's sum joins the tree, so a kernel that added
+    # it anywhere else than the oracle's odd-carry position would differ.
+    m, hidden = 64, 640
+    x, r, gamma = draw(m, hidden, 970)
+    x[:, 512:] *= 4096.0
+    x[:, :8] = 1.0
+    codes, scales = qp.mxfp8_norm_quant(x, gamma, 1e-6)
+    torch.cuda.synchronize()
+    wc, ws, _ = oracle.mxfp8_norm_quant(W.as_u16(x), W.as_u16(gamma), 1e-6)
+    assert np.array_equal(codes.cpu().numpy(), wc)
+    assert np.array_equal(scales.cpu().numpy(), ws)

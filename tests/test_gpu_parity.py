@@ -363,11 +363,11 @@ def test_bad_arguments_touch_nothing():
 
 
 def test_probe_copy_copies():
-    from fp8_kv_cache_amd import qkv_prep as qp
+    from fp8_kv_cache_amd import probe
     for n in (16, 4096 * 16 + 48, 3 << 20):
         src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)
         dst = torch.zeros_like(src)
-        qp.qkv_prep_probe_copy(dst.data_ptr(), src.data_ptr(), n,
+        probe.qkv_prep_probe_copy(dst.data_ptr(), src.data_ptr(), n,
                                torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         assert torch.equal(src, dst)
@@ -375,13 +375,13 @@ def test_probe_copy_copies():
 
 
 def test_probe_update_increments_every_chunk_once():
-    from fp8_kv_cache_amd import qkv_prep as qp
+    from fp8_kv_cache_amd import probe
     rng = np.random.default_rng(420)
     for n in (16, 64 * 16 + 48, 3 << 20):
         host = rng.integers(0, 2 ** 32, n // 4, dtype=np.uint64).astype(np.uint32)
         host[0:12:4] = 0xFFFFFFFF                             # wraps to 0
         buf = torch.from_numpy(host.view(np.int32).copy()).to(DEV)
-        qp.qkv_prep_probe_update(buf.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+        probe.qkv_prep_probe_update(buf.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         got = buf.cpu().numpy().view(np.uint32).reshape(-1, 4)
         want = host.reshape(-1, 4).copy()

@@ -126,12 +126,18 @@ def _nan_aware_equal(got_bits, want_bits, nan_mask_got, nan_mask_want):
 @pytest.mark.parametrize("bs,nb", [(64, 96), (7, 300)])
 def test_gather_arbitrary_cache_bytes(bs, nb):
     # Every byte of the cache random: all 256 codes (NaN codes 0x7f/0xff
-    # included), every scale byte 0..254 and random rope bf16.  Every slot is
-    # read once in a random order, plus invalid slots.
+    # included), every scale byte 0..255 and random rope bf16.  Every slot is
+    # read once in a random order, plus invalid slots.  Byte 255 (scale 2^128)
+    # is also forced on some blocks whose codes include 0x00 and 0x80, which
+    # must read back as +0 and -0.
     note("gather arbitrary bytes: block_size %d, %d blocks" % (bs, nb))
     rng = np.random.default_rng(720 + bs)
     host = rng.integers(0, 256, (nb, bs * W.SLOT_BYTES), dtype=np.uint8)
-    host[:, bs * 576:] = rng.integers(0, 255, (nb, bs * 8), dtype=np.uint8)   # scale bytes <= 254
+    rec = host[:, bs * 576:].reshape(nb, bs, 8)
+    rec[::5, :, 0] = 255
+    data = host[:, : bs * 576].reshape(nb, bs, 576)
+    data[::5, :, 0] = 0x00
+    data[::5, :, 1] = 0x80
     cap = nb * bs
     probe = np.concatenate([rng.permutation(cap), [-1, cap, -5, cap + 1]]).astype(np.int64)
     want = oracle.gather_dequant(host, nb, bs, probe)
@@ -145,6 +151,10 @@ def test_gather_arbitrary_cache_bytes(bs, nb):
     torch.cuda.synchronize()
     got32 = out32.cpu().numpy()
     assert np.isnan(want).any() and np.isinf(want).any()        # the odd values are exercised
+    cases = np.arange(cap)[np.argsort(probe[:cap])]             # row of each slot
+    zero_rows = cases.reshape(nb, bs)[::5].reshape(-1)
+    assert np.all(want[zero_rows, 0] == 0) and not np.signbit(want[zero_rows, 0]).any()
+    assert np.all(want[zero_rows, 1] == 0) and np.signbit(want[zero_rows, 1]).all()
     assert _nan_aware_equal(got32.view(np.uint32), want.view(np.uint32), np.isnan(got32), np.isnan(want))
     got16 = W.as_u16(out16)
     want16 = oracle.f32_to_bf16(want)

@@ -27,7 +27,8 @@ SLOW = {"test_bf16_matches_torch_cast_on_strided_patterns"}
 # The exhaustive sweeps (billions of patterns) run once, directly, in
 # test_oracle_formats.py; the battery leaves them out.
 EXHAUSTIVE = {"test_e4m3_matches_torch_cast_on_every_in_range_pattern",
-              "test_ue8m0_definition_on_every_positive_pattern"}
+              "test_ue8m0_definition_on_every_positive_pattern",
+              "test_ue8m0_byte_on_every_pattern"}
 
 
 def _expand(name, fn):
@@ -113,7 +114,13 @@ MUTANTS = [
      "scale[b] = orc_quant_block(y + (b ^ 1) * ORC_QBLOCK, data + b * ORC_QBLOCK);"),
     ("bf16 store unrotated", "insert_bf16_slot(z, cache, slot_mapping[t]);", "insert_bf16_slot(y, cache, slot_mapping[t]);"),
     ("gather exponent bias", "(int)scale[j / ORC_QBLOCK] - 127", "(int)scale[j / ORC_QBLOCK] - 128"),
-    ("mxfp8 ceil never bumps", "uint32_t bump = mant != 0;", "uint32_t bump = 0;"),
+    ("mxfp8 byte of a power of two bumped", "while (b > 0 && a <= ldexp(1.0, b - 1 - 127))  /* the least such b, not below 0 */\n        b -= 1;",
+     "while (0)\n        b -= 1;"),
+    ("mxfp8 byte rounded down", "b += 127;                                      /* so a <= 2^(b - 127) holds */",
+     "b += 126;"),
+    ("mxfp8 byte capped at 255", "return b > 254 ? 254u : (uint32_t)b;", "return b > 255 ? 255u : (uint32_t)b;"),
+    ("mxfp8 byte negative wraps", "if (b < 0)\n        b = 0;\n    return b > 254", "if (b < -1000)\n        b = 0;\n    return b > 254"),
+    ("mxfp8 inverse of 254 kept", "if (byte == 0 || byte >= 254)", "if (byte == 0 || byte >= 255)"),
     ("mxfp8 plain weight", "float g1 = orc_bf16_to_f32(gamma[j]) + 1.0f;", "float g1 = orc_bf16_to_f32(gamma[j]);"),
     ("mxfp8 no bf16 rounding before quant", "normed[j] = orc_bf16_to_f32(orc_f32_to_bf16(t * g1));",
      "normed[j] = t * g1;"),

@@ -45,7 +45,31 @@ def test_ue8m0_inverse():
     for b in range(1, 254):
         assert oracle.ue8m0_inverse(b) == np.float32(2.0 ** (127 - b))
     assert oracle.ue8m0_inverse(0) == 0.0
-    assert oracle.ue8m0_inverse(254) == 0.0       # the page's exponent arithmetic floors at 0
+    assert oracle.ue8m0_inverse(254) == 0.0       # 2^-127 is below the normal range: 0, as on the page
+    assert oracle.ue8m0_inverse(255) == 0.0
+
+
+def _byte_by_frexp(v):
+    """The scale byte from frexp: v = f * 2^E with f in [0.5, 1), so the
+    smallest power of two at or above v is 2^(E-1) when f is exactly 0.5 and
+    2^E otherwise; its biased exponent, clamped to [0, 254], is the byte.
+    +inf has no power of two above it and takes the cap, 254."""
+    f, e = np.frexp(v.astype(np.float64))
+    up = np.where(np.isinf(v), 254, e.astype(np.int64) - (f == 0.5) + 127)
+    return np.where(v > 0, np.clip(up, 0, 254), 0).astype(np.uint8)
+
+
+def test_ue8m0_byte_on_every_pattern():
+    # Every positive finite fp32 pattern, +inf, both zeros and a stride of the
+    # negative ones, against the frexp form of the definition.
+    from test_oracle_formats import _over_chunks
+
+    def check(start, stop):
+        v = np.arange(start, stop, dtype=np.uint32).view(np.float32)
+        return np.array_equal(oracle.ue8m0_ceil_bytes(v), _byte_by_frexp(v))
+    assert _over_chunks(check, 0, 0x7F800001) == []
+    neg = (np.arange(0x80000000, 0xFF800001, 4093, dtype=np.uint64)).astype(np.uint32).view(np.float32)
+    assert not oracle.ue8m0_ceil_bytes(neg).any()
 
 
 # ------------------------------------------------------------- swizzle
@@ -176,3 +200,19 @@ def test_random_rows_against_float64(hidden):
 def test_hidden_must_be_a_multiple_of_128():
     with pytest.raises(ValueError):
         oracle.mxfp8_norm_quant(np.zeros((1, 96), np.uint16), np.zeros(96, np.uint16), 1e-6)
+
+
+def test_odd_carry_tree_equals_the_zero_padded_tree():
+    # The summation order (chunks of 8 left to right, adjacent pairs level by
+    # level, an odd last value carried up) gives the same bits as the same tree
+    # over the row padded with zero chunks to a power-of-two count, because a
+    # carried x and x + 0 are the same number.  A kernel that splits rows into
+    # whole groups of 64 chunks and pads the last group relies on this.
+    rng = np.random.default_rng(71)
+    for n in (128, 384, 640, 1152, 3200, 8704, 12288, 16256):
+        x = bf16(rng.standard_normal(n) * np.exp(rng.uniform(-8, 8, n)))
+        width = 1 << int(np.ceil(np.log2(n)))
+        padded = np.concatenate([x, np.zeros(width - n, np.uint16)])
+        a = oracle.lib().orc_sum_squares_n(np.ascontiguousarray(x).ctypes.data, n)
+        b = oracle.lib().orc_sum_squares_n(np.ascontiguousarray(padded).ctypes.data, width)
+        assert np.float32(a).view(np.uint32) == np.float32(b).view(np.uint32), n
