@@ -7,6 +7,15 @@ The metric is effective HBM bandwidth: the operator's algorithmic bytes (read
 of the 8 TB/s HBM3E peak and as a fraction of a warm device-to-device copy
 ceiling measured in the same process.
 
+Order of a run: a known-answer check on the Tiny workload; the headline
+workload's inputs drawn on the GPU; the copy ceilings (the "before" set)
+measured right after, so that the operator's warmup and timed steps follow a
+sustained streaming load, as the ceilings themselves do; W warmup steps; the
+K timed steps; then the per-launch, flushed-cache and after-idle passes of the
+same workload, the second operator workload, the other workloads and the
+neighbouring paths, the "after" ceilings, the known-answer check again and the
+CPU baseline.
+
 Prints ONE JSON line.  ``value`` is the Prefill workload (32768 tokens x 64
 heads); the Long workload (131072 x 128) is reported under ``also``.
 
@@ -30,6 +39,7 @@ if ROOT not in sys.path:
 METRIC = "effective HBM GB/s & % of warm copy ceiling, tokens×heads 32768×64 / 131072×128"
 PEAK_HBM_GBPS = 8000.0
 KERNEL_NAME = "qkv_prep_kernel"
+IDLE_S = 1.0
 
 
 def log(msg):
@@ -84,30 +94,27 @@ def copy_rate(torch, copier, size_bytes, reps=20, max_rounds=12):
     return 2.0 * size_bytes / min(medians) / 1e9
 
 
-def copy_ceilings(torch, qp):
+def copy_ceilings(torch, probe):
     """The ceilings at 512 MiB and 2 GiB: the runtime's hipMemcpyAsync, the
-    library's streaming-copy probe and its in-place streaming-update probe (the
+    probe library's streaming copy and its in-place streaming update (the
     operator rewrites q in place; counted as bytes read + bytes written).  The
     largest rate is the denominator."""
     out = {}
-    update = lambda dst, src, nbytes, stream: qp.qkv_prep_probe_update(dst, nbytes, stream)
-    for label, fn in (("hipMemcpyAsync", DeviceCopy()), ("probe_copy", qp.qkv_prep_probe_copy),
+    update = lambda dst, src, nbytes, stream: probe.qkv_prep_probe_update(dst, nbytes, stream)
+    for label, fn in (("hipMemcpyAsync", DeviceCopy()), ("probe_copy", probe.qkv_prep_probe_copy),
                       ("probe_update", update)):
         for size in (512 << 20, 2 << 30):
             out["%s_%dMiB" % (label, size >> 20)] = round(copy_rate(torch, fn, size), 1)
     return out
 
 
-# ----------------------------------------------------------------- one workload
+# ----------------------------------------------------------------- timing
 
-def time_launches(torch, fn, steps):
+def time_region(torch, fn, steps):
     """The timed region: `steps` back-to-back launches bracketed by
     synchronizations, with one HIP event just before the first launch and one
     just after the last, on torch's current stream (the stream the library
-    launches on).  Returns the per-launch durations of a second pass of as many
-    launches, each between two events (for the median, minimum and p90), the
-    wall time of the timed region, and its event time (for the mean launch
-    duration over the timed region)."""
+    launches on).  Returns (wall seconds, event seconds)."""
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -117,16 +124,20 @@ def time_launches(torch, fn, steps):
         fn()
     end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    region = start.elapsed_time(end) * 1e-3
+    return time.perf_counter() - t0, start.elapsed_time(end) * 1e-3
+
+
+def time_each(torch, fn, reps):
+    """Per-launch durations, each launch between two HIP events."""
+    stream = torch.cuda.current_stream()
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+              for _ in range(reps)]
     for e0, e1 in events:
         e0.record(stream)
         fn()
         e1.record(stream)
     torch.cuda.synchronize()
-    return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events], wall, region
+    return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events]
 
 
 def time_cold(torch, fn, reps, scratch):
@@ -150,6 +161,142 @@ def p90(xs):
     return xs[min(len(xs) - 1, int(0.9 * len(xs)))]
 
 
+# ----------------------------------------------------------------- profiles
+
+def profile_record(prefix, kind, label, family):
+    """The machine-readable record of a committed rocprofv3 summary
+    (profiles/<prefix>_<kind>_<label>.txt), or None when the file is missing
+    or was taken on other sources than the current ones of the kernel family."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_%s.txt" % (prefix, kind, label))
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{"):
+                rec = json.loads(line)
+    if not rec:
+        return None
+    from fp8_kv_cache_amd.rocprof_harness import kernel_sha
+    return rec if rec.get("kernel_sha") == kernel_sha(family) else None
+
+
+def profile_fields(t, alg_bytes):
+    """From the current profiles of target t: HBM bytes per launch (FETCH_SIZE
+    and WRITE_SIZE, each scaled by a copy of known size), the mean resident
+    waves per CU, and the trace's average launch duration with the fraction
+    of peak it gives.  Fields whose summary is missing or stale are None."""
+    ctr = profile_record(t.prefix, "counters", t.label, t.family)
+    waves = profile_record(t.prefix, "waves", t.label, t.family)
+    trace = (profile_record(t.prefix, "kernel_trace_bench", t.label, t.family) or
+             profile_record(t.prefix, "kernel_trace", t.label, t.family))
+    out = {"traffic": ctr.get("hbm_bytes_per_dispatch") if ctr else None,
+           "fetch_bytes": ctr.get("op_fetch_bytes") if ctr else None,
+           "write_bytes": ctr.get("op_write_bytes") if ctr else None,
+           "waves_per_cu": waves.get("mean_occupancy_per_cu") if waves else None,
+           "occupancy_percent": waves.get("occupancy_percent") if waves else None,
+           "kernel_us_trace": trace.get("op_avg_us") if trace else None,
+           "frac_trace": None}
+    if trace and trace.get("op_avg_us"):
+        out["frac_trace"] = round(alg_bytes / (trace["op_avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+    return out
+
+
+# ----------------------------------------------------------------- workloads
+
+def bench_workload(torch, W, qp, probe, name, steps, warmup, ceiling_first):
+    """One operator workload: inputs drawn; with ceiling_first, the copy
+    ceilings measured right after; W warmup steps; the K timed steps; then a
+    per-launch pass, a flushed-cache pass, and a K-step region started after
+    the GPU idled for IDLE_S seconds."""
+    w = W.WORKLOADS[name]
+    log("bench: drawing %s inputs on the GPU" % w.label)
+    inp = W.make_inputs(w, device="cuda")
+    valid = int(((inp["slot_mapping"] >= 0) &
+                 (inp["slot_mapping"] < w.num_blocks * w.block_size)).sum())
+    nbytes = W.algorithmic_bytes(w.num_tokens, w.num_heads, valid)
+    op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
+    shape = op.launch_shape(w.num_tokens)
+    args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+            inp["slot_mapping"], inp["cache"])
+    fn = lambda: op(*args)
+    ceilings = None
+    if ceiling_first:
+        ceilings = copy_ceilings(torch, probe)
+        log("bench: copy ceilings before = %s GB/s" % ceilings)
+    log("bench: %s warmup %d" % (w.label, warmup))
+    for _ in range(warmup):
+        fn()
+    log("bench: %s timing %d steps" % (w.label, steps))
+    wall, region = time_region(torch, fn, steps)
+    each = time_each(torch, fn, steps)
+    log("bench: %s cold-cache launches" % w.label)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = time_cold(torch, fn, min(steps, 10), scratch)
+    del scratch
+    log("bench: %s region after %.1f s idle" % (w.label, IDLE_S))
+    torch.cuda.synchronize()
+    time.sleep(IDLE_S)
+    _, region_idle = time_region(torch, fn, steps)
+    res = {
+        "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
+        "label": "%s_%dx%d" % (name, w.num_tokens, w.num_heads),
+        "bytes_per_step": nbytes,
+        "wall_s_per_step": wall / steps,
+        "kernel_s_mean": region / steps,
+        "kernel_s_median": statistics.median(each),
+        "kernel_s_min": min(each),
+        "kernel_s_p90": p90(each),
+        "kernel_s_median_cold": statistics.median(cold),
+        "kernel_s_p90_cold": p90(cold),
+        "kernel_s_mean_after_idle": region_idle / steps,
+        "launch": {"rows_per_wave": shape.rows_per_wave, "waves_per_block": shape.waves_per_block,
+                   "convert": shape.convert, "kv_per_wave": shape.kv_per_wave, "grid": shape.grid},
+        "valid_slots": valid,
+    }
+    res["gbps_wall"] = nbytes / res["wall_s_per_step"] / 1e9
+    res["gbps_kernel_mean"] = nbytes / res["kernel_s_mean"] / 1e9
+    del inp, args, fn
+    torch.cuda.empty_cache()
+    return w, res, ceilings
+
+
+def kernel_us(res):
+    return {k: round(res["kernel_s_" + k] * 1e6, 2)
+            for k in ("median", "min", "p90", "median_cold", "p90_cold", "mean_after_idle")}
+
+
+def bench_configs(torch, qp, names, warmup):
+    """The other workloads, event-timed per launch: median, min and p90 over
+    200 launches for the small ones (Tiny, Decode-like) and 30 for the large
+    ones, plus the median of 10 launches with L2 and the MALL flushed first."""
+    from fp8_kv_cache_amd import variants as V
+    out = {}
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for name in names:
+        t = V.target(name)
+        log("bench: config %s" % t.label)
+        fn = V.setup(t, torch, qp)
+        for _ in range(warmup):
+            fn()
+        reps = 200 if t.alg_bytes < (1 << 30) else 30
+        ks = time_each(torch, fn, reps)
+        cold = time_cold(torch, fn, 10, scratch)
+        del fn
+        torch.cuda.empty_cache()
+        med = statistics.median(ks)
+        prof = profile_fields(t, t.alg_bytes)
+        out[t.label] = {"gbps_median": round(t.alg_bytes / med / 1e9, 1), "reps": reps,
+                        "kernel_us": {"median": round(med * 1e6, 2), "min": round(min(ks) * 1e6, 2),
+                                      "p90": round(p90(ks) * 1e6, 2),
+                                      "median_cold": round(statistics.median(cold) * 1e6, 2)},
+                        "bytes_per_launch": t.alg_bytes, "traffic": prof["traffic"],
+                        "waves_per_cu": prof["waves_per_cu"]}
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_variants(torch, qp, steps, warmup):
     """The neighbouring paths, each timed like the operator: the bf16-store cache
     mode on the Prefill workload (1024-byte slots, no quantization); the cache
@@ -165,92 +312,19 @@ def bench_variants(torch, qp, steps, warmup):
         fn = V.setup(t, torch, qp)
         for _ in range(warmup):
             fn()
-        ks, wall, region = time_launches(torch, fn, steps)
+        wall, region = time_region(torch, fn, steps)
+        ks = time_each(torch, fn, steps)
         del fn
         torch.cuda.empty_cache()
         mean = region / steps
-        out[t.label] = {
-            "gbps": round(t.alg_bytes * steps / wall / 1e9, 1),
-            "kernel_us_mean": round(mean * 1e6, 2),
-            "kernel_us_median": round(statistics.median(ks) * 1e6, 2),
-            "roofline": {"bound": "hbm", "kernel": t.kernel, "achieved": round(t.alg_bytes / mean / 1e9, 1),
-                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": round(t.alg_bytes / mean / 1e9 / PEAK_HBM_GBPS, 4),
-                         "traffic": recorded_traffic(t), "bytes_per_launch": t.alg_bytes},
-        }
+        roof = {"bound": "hbm", "kernel": t.kernel, "achieved": round(t.alg_bytes / mean / 1e9, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(t.alg_bytes / mean / 1e9 / PEAK_HBM_GBPS, 4), "bytes_per_launch": t.alg_bytes}
+        roof.update(profile_fields(t, t.alg_bytes))
+        out[t.label] = {"gbps": round(t.alg_bytes * steps / wall / 1e9, 1),
+                        "kernel_us_mean": round(mean * 1e6, 2),
+                        "kernel_us_median": round(statistics.median(ks) * 1e6, 2), "roofline": roof}
     return out
-
-
-def bench_configs(torch, W, qp, names, warmup):
-    """The other workloads, event-timed per launch: median, min and p90 over
-    200 launches for the small ones (Tiny, Decode-like) and 30 for the large
-    ones, plus the median of 10 launches with L2 and the MALL flushed first."""
-    from fp8_kv_cache_amd import variants as V
-    out = {}
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    for name in names:
-        t = V.target(name)
-        log("bench: config %s" % t.label)
-        fn = V.setup(t, torch, qp)
-        for _ in range(warmup):
-            fn()
-        reps = 200 if t.alg_bytes < (1 << 30) else 30
-        ks, _, _ = time_launches(torch, fn, reps)
-        cold = time_cold(torch, fn, 10, scratch)
-        del fn
-        torch.cuda.empty_cache()
-        med = statistics.median(ks)
-        out[t.label] = {"gbps_median": round(t.alg_bytes / med / 1e9, 1), "reps": reps,
-                        "kernel_us": {"median": round(med * 1e6, 2), "min": round(min(ks) * 1e6, 2),
-                                      "p90": round(p90(ks) * 1e6, 2),
-                                      "median_cold": round(statistics.median(cold) * 1e6, 2)},
-                        "bytes_per_launch": t.alg_bytes}
-    del scratch
-    torch.cuda.empty_cache()
-    return out
-
-
-def bench_workload(torch, W, qp, name, steps, warmup):
-    w = W.WORKLOADS[name]
-    log("bench: drawing %s inputs on the GPU" % w.label)
-    inp = W.make_inputs(w, device="cuda")
-    valid = int(((inp["slot_mapping"] >= 0) &
-                 (inp["slot_mapping"] < w.num_blocks * w.block_size)).sum())
-    nbytes = W.algorithmic_bytes(w.num_tokens, w.num_heads, valid)
-    op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
-    shape = op.launch_shape(w.num_tokens)
-    args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
-            inp["slot_mapping"], inp["cache"])
-    log("bench: %s warmup %d" % (w.label, warmup))
-    for _ in range(warmup):
-        op(*args)
-    torch.cuda.synchronize()
-    log("bench: %s timing %d steps" % (w.label, steps))
-    kernel_s, wall, region = time_launches(torch, lambda: op(*args), steps)
-    log("bench: %s cold-cache launches" % w.label)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    cold_s = time_cold(torch, lambda: op(*args), min(steps, 10), scratch)
-    del scratch
-    res = {
-        "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
-        "bytes_per_step": nbytes,
-        "wall_s_per_step": wall / steps,
-        "kernel_s_mean": region / steps,
-        "kernel_s_median": statistics.median(kernel_s),
-        "kernel_s_min": min(kernel_s),
-        "kernel_s_p90": p90(kernel_s),
-        "kernel_s_median_cold": statistics.median(cold_s),
-        "kernel_s_p90_cold": p90(cold_s),
-        "launch": {"rows_per_wave": shape.rows_per_wave, "waves_per_block": shape.waves_per_block,
-                   "convert": shape.convert, "grid": shape.grid},
-        "valid_slots": valid,
-    }
-    res["gbps_wall"] = nbytes / res["wall_s_per_step"] / 1e9
-    res["gbps_kernel_mean"] = nbytes / res["kernel_s_mean"] / 1e9
-    res["gbps_kernel_median"] = nbytes / res["kernel_s_median"] / 1e9
-    del inp, args
-    torch.cuda.empty_cache()
-    return w, res
 
 
 def known_answer_check(torch, W, qp):
@@ -295,81 +369,69 @@ def host_cpu():
     return model, usable
 
 
-def cpu_baseline(torch, W, name, target_s=12.0, sample_tokens=4096):
-    """The oracle (plain scalar C, OpenMP over tokens) on a bounded sample of
-    the same workload: its first `sample_tokens` tokens, passed over
-    repeatedly until about target_s seconds of CPU work.  Throughput uses the
-    same byte formula as the GPU figure.  The output buffer is allocated and
-    touched once, so the timed passes are the oracle's compute and memory
-    traffic only."""
+def cpu_pass(torch, W, name, threads, chunk_tokens=4096, max_tokens=None):
+    """The oracle (plain scalar C, OpenMP over tokens) over the workload's
+    tokens, chunk by chunk: each chunk's inputs are drawn on the GPU with the
+    workload's seed (the same draw the GPU run takes), copied to the host, and
+    the oracle is timed around its compute only.  Returns (algorithmic bytes
+    of the tokens covered, compute seconds, tokens covered)."""
     import numpy as np
     import oracle
     w = W.WORKLOADS[name]
-    nth = max(1, min(16, host_cpu()[1]))        # at most 16 threads
-    n = min(w.num_tokens, sample_tokens)
-    sub = W.Workload(w.name, n, w.num_heads, w.max_position, w.num_blocks, w.block_size,
-                     w.positions, w.slots, w.seed, num_seqs=max(1, n * w.num_seqs // w.num_tokens),
-                     outlier_frac=w.outlier_frac)
-    inp = W.make_inputs(sub, device="cuda")
-    q = W.as_u16(inp["q"])
-    kv = W.as_u16(inp["kv"])
-    qw, kvw = W.as_u16(inp["q_w"]), W.as_u16(inp["kv_w"])
+    inp = W.make_inputs(w, device="cuda")
+    T = w.num_tokens if max_tokens is None else min(w.num_tokens, max_tokens)
     pos = inp["positions"].cpu().numpy()
-    cs = inp["cos_sin"].cpu().numpy()
     slots = inp["slot_mapping"].cpu().numpy()
+    cs = inp["cos_sin"].cpu().numpy()
     cache = inp["cache"].cpu().numpy()
-    valid = int(((slots >= 0) & (slots < w.num_blocks * w.block_size)).sum())
-    nbytes = W.algorithmic_bytes(n, w.num_heads, valid)
-    out = np.empty_like(q)
-    out.fill(0)                       # touch the pages once, outside the timed passes
+    qw, kvw = W.as_u16(inp["q_w"]), W.as_u16(inp["kv_w"])
+    out = np.zeros((min(chunk_tokens, T), w.num_heads, 512), np.uint16)   # pages touched once
+    compute = 0.0
+    for t0 in range(0, T, chunk_tokens):
+        t1 = min(T, t0 + chunk_tokens)
+        q = W.as_u16(inp["q"][t0:t1])
+        kv = W.as_u16(inp["kv"][t0:t1])
+        o = out[: t1 - t0]
+        c0 = time.perf_counter()
+        oracle.qkv_prep(q, kv, qw, kvw, pos[t0:t1], cs, slots[t0:t1], cache, w.num_blocks, w.block_size,
+                        w.eps, threads, out=o)
+        compute += time.perf_counter() - c0
+    valid = int(((slots[:T] >= 0) & (slots[:T] < w.num_blocks * w.block_size)).sum())
+    del inp
+    torch.cuda.empty_cache()
+    return W.algorithmic_bytes(T, w.num_heads, valid), compute, T
 
-    def passes(threads, budget):
-        done, t0 = 0, time.perf_counter()
-        while True:
-            oracle.qkv_prep(q, kv, qw, kvw, pos, cs, slots, cache, w.num_blocks, w.block_size,
-                            w.eps, threads, out=out)
-            done += 1
-            dt = time.perf_counter() - t0
-            if dt >= budget:
-                return done, dt
 
-    k, dt = passes(nth, target_s)
-    k1, dt1 = passes(1, 2.0)
+def cpu_baseline(torch, W, names):
+    """The oracle over every token of each named workload on the host cores
+    (at most 16 threads), plus a one-thread figure on the first 2048 tokens of
+    the first workload.  Throughput uses the same byte formula as the GPU
+    figure.  The first workload's figure is the baseline's value."""
     model, usable = host_cpu()
-    return {"value": round(nbytes * k / dt / 1e9, 3), "unit": "GB/s", "cores": nth,
-            "kind": "oracle", "cpu_model": model, "host_cpus": usable,
-            "sample": "first %d of %d tokens of %s %dx%d, %d passes in %.1f s" % (
-                n, w.num_tokens, w.name, w.num_tokens, w.num_heads, k, dt),
-            "value_1_core": round(nbytes * k1 / dt1 / 1e9, 3)}
+    nth = max(1, min(16, usable))
+    per = {}
+    for name in names:
+        log("bench: cpu baseline %s (%d threads)" % (name, nth))
+        nbytes, secs, T = cpu_pass(torch, W, name, nth)
+        w = W.WORKLOADS[name]
+        per["%s_%dx%d" % (name, w.num_tokens, w.num_heads)] = {
+            "gbps": round(nbytes / secs / 1e9, 3), "tokens": T, "compute_s": round(secs, 2)}
+    log("bench: cpu baseline, one thread")
+    nb1, s1, T1 = cpu_pass(torch, W, names[0], 1, chunk_tokens=2048, max_tokens=2048)
+    first = next(iter(per.values()))
+    return {"value": first["gbps"], "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": "every token of %s, in 4096-token chunks; compute time only" % " and ".join(per),
+            "cpu_model": model, "host_cpus": usable, "per_workload": per,
+            "value_1_core": round(nb1 / s1 / 1e9, 3),
+            "sample_1_core": "first %d tokens of %s" % (T1, names[0])}
 
 
-# ----------------------------------------------------------------- counters
+# ----------------------------------------------------------------- profile mode
 
-def recorded_traffic(t):
-    """HBM bytes per dispatch of target t from the committed rocprofv3 counter
-    summary, if it was taken on the current source of t's kernel (else None)."""
-    path = os.path.join(ROOT, "profiles", "%s_counters_%s.txt" % (t.prefix, t.label))
-    if not os.path.exists(path):
-        return None
-    rec = None
-    with open(path) as f:
-        for line in f:
-            if line.startswith("{"):
-                rec = json.loads(line)
-    if not rec:
-        return None
-    from fp8_kv_cache_amd.rocprof_harness import kernel_sha
-    if rec.get("kernel_sha") != kernel_sha(t.family):
-        return None
-    return rec.get("hbm_bytes_per_dispatch")
-
-
-# ----------------------------------------------------------------- main
-
-def profile_run(torch, qp, name, launches, copy_bytes=512 << 20, copies=3):
+def profile_run(torch, qp, probe, name, launches, copy_bytes=512 << 20, copies=3):
     """A short program for rocprofv3: a few launches of one target (the
     operator on a workload, or a neighbouring path), then a few launches of the
-    library's streaming-copy probe over a buffer of known size (its
+    probe library's streaming copy over a buffer of known size (its
     FETCH_SIZE/WRITE_SIZE calibrate the counters against bytes that are known
     exactly)."""
     from fp8_kv_cache_amd import variants as V
@@ -386,11 +448,13 @@ def profile_run(torch, qp, name, launches, copy_bytes=512 << 20, copies=3):
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for i in range(copies):
-        qp.qkv_prep_probe_copy(dst.data_ptr(), src.data_ptr(), copy_bytes,
-                               torch.cuda.current_stream().cuda_stream)
+        probe.qkv_prep_probe_copy(dst.data_ptr(), src.data_ptr(), copy_bytes,
+                                  torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
     log("profile: %d copies of %d bytes done" % (copies, copy_bytes))
 
+
+# ----------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser()
@@ -417,6 +481,7 @@ def main():
         sys.exit(2)
 
     import torch
+    from fp8_kv_cache_amd import probe
     from fp8_kv_cache_amd import qkv_prep as qp
     from fp8_kv_cache_amd import variants as V
     from fp8_kv_cache_amd import workloads as W
@@ -425,28 +490,32 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.mode == "profile":
-        profile_run(torch, qp, args.workload, args.launches)
+        profile_run(torch, qp, probe, args.workload, args.launches)
         return
     kat_before = known_answer_check(torch, W, qp)
-    ceil_before = None if args.no_ceiling else copy_ceilings(torch, qp)
-    log("bench: copy ceilings before = %s GB/s" % ceil_before)
-    w, main_res = bench_workload(torch, W, qp, args.workload, args.steps, args.warmup)
+    w, main_res, ceil_before = bench_workload(torch, W, qp, probe, args.workload, args.steps, args.warmup,
+                                              ceiling_first=not args.no_ceiling)
     also = None
     if not args.no_also and args.also and args.also != args.workload:
-        _, also = bench_workload(torch, W, qp, args.also, args.steps, args.warmup)
+        _, also, _ = bench_workload(torch, W, qp, probe, args.also, args.steps, args.warmup, False)
     others = [n for n in W.WORKLOADS if n not in (args.workload, args.also)]
-    configs = None if args.no_variants else bench_configs(torch, W, qp, others, args.warmup)
+    configs = None if args.no_variants else bench_configs(torch, qp, others, args.warmup)
     variants = None if args.no_variants else bench_variants(torch, qp, args.steps, args.warmup)
-    ceil_after = None if args.no_ceiling else copy_ceilings(torch, qp)
+    ceil_after = None if args.no_ceiling else copy_ceilings(torch, probe)
     log("bench: copy ceilings after = %s GB/s" % ceil_after)
     kat_after = known_answer_check(torch, W, qp)
-    ceiling = max(list(ceil_before.values()) + list(ceil_after.values())) if ceil_before else None
+    ceilings = list(ceil_before.values()) + list(ceil_after.values()) if ceil_before else []
+    ceiling = max(ceilings) if ceilings else None
     memcpy_ceiling = max(v for k, v in list(ceil_before.items()) + list(ceil_after.items())
                          if k.startswith("hipMemcpy")) if ceil_before else None
 
     value = main_res["gbps_wall"]
     achieved = main_res["gbps_kernel_mean"]
-    traffic = recorded_traffic(V.target(args.workload))
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "kernel": KERNEL_NAME,
+            "kernel_us_mean": round(main_res["kernel_s_mean"] * 1e6, 2),
+            "bytes_per_launch": main_res["bytes_per_step"]}
+    roof.update(profile_fields(V.target(args.workload), main_res["bytes_per_step"]))
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -469,31 +538,27 @@ def main():
         "copy_ceilings_before_after": [ceil_before, ceil_after],
         "frac_of_copy": round(value / ceiling, 4) if ceiling else None,
         "frac_of_hipmemcpy": round(value / memcpy_ceiling, 4) if memcpy_ceiling else None,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": KERNEL_NAME,
-                     "kernel_us_mean": round(main_res["kernel_s_mean"] * 1e6, 2),
-                     "bytes_per_launch": main_res["bytes_per_step"]},
-        "kernel_us": {k: round(main_res["kernel_s_" + k] * 1e6, 2)
-                      for k in ("median", "min", "p90", "median_cold", "p90_cold")},
+        "roofline": roof,
+        "kernel_us": kernel_us(main_res),
         "known_answer_before_after": [kat_before, kat_after],
     }
     if also:
+        a_roof = profile_fields(V.target(args.also), also["bytes_per_step"])
         out["also"] = {"workload": also["workload"], "value": round(also["gbps_wall"], 1),
                        "kernel_gbps": round(also["gbps_kernel_mean"], 1),
                        "ms_per_step": round(also["wall_s_per_step"] * 1e3, 4),
                        "frac_of_peak": round(also["gbps_wall"] / PEAK_HBM_GBPS, 4),
                        "frac_of_copy": round(also["gbps_wall"] / ceiling, 4) if ceiling else None,
-                       "kernel_us": {k: round(also["kernel_s_" + k] * 1e6, 2)
-                                     for k in ("median", "min", "p90", "median_cold", "p90_cold")},
-                       "launch": also["launch"], "bytes_per_step": also["bytes_per_step"],
-                       "traffic": recorded_traffic(V.target(args.also))}
+                       "kernel_us_mean": round(also["kernel_s_mean"] * 1e6, 2),
+                       "kernel_us": kernel_us(also), "launch": also["launch"],
+                       "bytes_per_step": also["bytes_per_step"], "roofline": a_roof}
     if configs:
         out["configs"] = configs
     if variants:
         out["variants"] = variants
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(torch, W, args.workload)
+        names = [args.workload] + ([args.also] if also else [])
+        out["cpu_baseline"] = cpu_baseline(torch, W, names)
     print(json.dumps(out), flush=True)
 
 

@@ -11,11 +11,13 @@ counter group, each as a child process with its own time limit:
   reqs    --pmc TCC_EA0_RDREQ_{32B,64B,128B}_sum TCC_EA0_RDREQ_sum
                                            read requests by size
   waves   --pmc <wave counters>            occupancy
-  bench   --kernel-trace --stats           over bench.py's own timing run of an
-                                           operator workload (no other workload,
-                                           variant, ceiling or CPU baseline), so
-                                           the trace's average duration can be set
-                                           beside the bench's event-timed mean
+  bench   --kernel-trace --stats           over bench.py's own run of an operator
+                                           workload (its ceilings, warmup and
+                                           timed steps; no other workload, variant
+                                           or CPU baseline), so that the trace's
+                                           durations of exactly the timed steps'
+                                           launches can be set beside the bench's
+                                           event-timed mean
 
 and writes short text summaries (the figures and the exact commands) to the
 output directory.  The copy probe's counters against its known byte count
@@ -106,6 +108,20 @@ def kernel_stats(d):
     return rows
 
 
+def dispatch_durations(d, name):
+    """Durations (us) of every dispatch of the kernel called exactly `name`,
+    in launch order, from the per-dispatch kernel trace."""
+    rows = list(csv.DictReader(open(find_csv(d, "kernel_trace.csv"))))
+    hits = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows if r["Kernel_Name"] == name)
+    return [(e - b) / 1e3 for b, e in hits]
+
+
+def main_instance(rows, kernel):
+    """The stats row of `kernel`'s most-launched template instance."""
+    hits = [r for r in rows if kernel in r["Name"]]
+    return max(hits, key=lambda r: int(r["Calls"])) if hits else None
+
+
 def counter_rows(d):
     return list(csv.DictReader(open(find_csv(d, "counter_collection.csv"))))
 
@@ -139,8 +155,8 @@ def main():
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--passes", default="trace,fetch,write,reqs,waves")
     ap.add_argument("--wave-counters", default="OccupancyPercent,MeanOccupancyPerCU,SQ_WAVES")
-    ap.add_argument("--bench-steps", type=int, default=200)
-    ap.add_argument("--bench-warmup", type=int, default=20)
+    ap.add_argument("--bench-steps", type=int, default=20)
+    ap.add_argument("--bench-warmup", type=int, default=5)
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     from fp8_kv_cache_amd import variants as V
@@ -167,9 +183,13 @@ def main():
             lines.append("%-70s %6s %14.2f %14.2f %14.2f" % (
                 name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3))
-            if op_kernel in r["Name"]:
-                summary["op_avg_us"] = float(r["AverageNs"]) / 1e3
-                summary["op_calls"] = int(r["Calls"])
+        top = main_instance(rows, op_kernel)
+        if top:
+            summary["op_avg_us"] = float(top["AverageNs"]) / 1e3
+            summary["op_calls"] = int(top["Calls"])
+        lines += ["", "# machine-readable:", json.dumps({
+            "workload": label, "kernel": op_kernel, "kernel_sha": summary["kernel_sha"],
+            "op_avg_us": summary.get("op_avg_us"), "op_calls": summary.get("op_calls")})]
         text = "\n".join(lines) + "\n"
         open(os.path.join(out, "%s_kernel_trace_%s.txt" % (prefix, label)), "w").write(text)
         log(text)
@@ -261,13 +281,19 @@ def main():
         rows = counter_rows(d)
         lines = ["# rocprofv3 wave counters, kernel %s, workload %s" % (op_kernel, label),
                  "# command (from the repository root): %s" % " ".join(cmd), ""]
+        means = {}
         for c in ctrs:
             name, vals = pick(per_dispatch(rows, c), op_kernel)
             lines.append("%-20s %s" % (c, vals))
+            means[c] = sum(vals) / len(vals) if vals else None
         lines.append("")
         lines.append("OccupancyPercent = 400 * sum(SQ_WAVE_CYCLES) / GRBM_GUI_ACTIVE / CUs / 32 "
                      "(resident waves as a share of 32 wave slots per CU); MeanOccupancyPerCU = "
                      "mean resident waves per CU (rocprofv3 derived counters)")
+        lines += ["", "# machine-readable (means over the dispatches):", json.dumps({
+            "workload": label, "kernel": op_kernel, "kernel_sha": summary["kernel_sha"],
+            "mean_occupancy_per_cu": means.get("MeanOccupancyPerCU"),
+            "occupancy_percent": means.get("OccupancyPercent")})]
         text = "\n".join(lines) + "\n"
         open(os.path.join(out, "%s_waves_%s.txt" % (prefix, label)), "w").write(text)
         log(text)
@@ -276,28 +302,42 @@ def main():
         if t.family != "op" or args.workload not in W.WORKLOADS:
             raise SystemExit("the bench pass takes an operator workload")
         bench_args = ["--workload", args.workload, "--steps", str(args.bench_steps), "--warmup", str(args.bench_warmup),
-                      "--no-also", "--no-variants", "--no-cpu-baseline", "--no-ceiling"]
-        cmd, d, json_line = run_pass("bench", ["--kernel-trace", "--stats"], args.workload, 0, out, 600,
+                      "--no-also", "--no-variants", "--no-cpu-baseline"]
+        cmd, d, json_line = run_pass("bench", ["--kernel-trace", "--stats"], args.workload, 0, out, 900,
                                      bench_args=bench_args)
         rec = json.loads(json_line)
         rows = kernel_stats(d)
         shape = rec["config"]["launch"]
-        lines = ["# rocprofv3 kernel trace over bench.py's timing run, kernel %s, workload %s" % (op_kernel, label),
+        top = main_instance(rows, op_kernel)
+        durs = dispatch_durations(d, top["Name"])
+        k, wu = args.bench_steps, args.bench_warmup
+        region = durs[wu:wu + k]
+        region_avg = sum(region) / len(region)
+        lines = ["# rocprofv3 kernel trace over bench.py's run, kernel %s, workload %s" % (op_kernel, label),
                  "# command (from the repository root): %s" % " ".join(cmd),
                  "# kernel source sha256[:16] = %s" % summary["kernel_sha"],
-                 "# the workload's launches of %s (rows_per_wave %d): %d warmup + %d in the timed region + %d event-timed"
-                 % (op_kernel, shape["rows_per_wave"], args.bench_warmup, args.bench_steps, args.bench_steps)
-                 + " + 10 after a cache flush; the bench's known-answer checks on the tiny workload use the",
-                 "# small-batch template instance (rows_per_wave 2), listed on its own line", "",
+                 "# the workload's launches of %s (rows_per_wave %d), in order: %d warmup, %d in the timed region,"
+                 % (op_kernel, shape["rows_per_wave"], wu, k)
+                 + " %d event-timed one by one, 10 after a cache flush, %d after the GPU idled;" % (k, k),
+                 "# the bench's known-answer checks on the tiny workload use the small-batch template instance"
+                 " (rows_per_wave 2), listed on its own line", "",
                  "%-70s %6s %14s %14s %14s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
         for r in rows:
             lines.append("%-70s %6s %14.2f %14.2f %14.2f" % (
                 r["Name"][:70], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3))
-        lines += ["", "# the bench's own figures in the same run (HIP events, kernel_us_mean; wall-clock value):",
+        lines += ["", "# the timed region's %d launches in the per-dispatch trace (us):" % len(region),
+                  "region_launch_us        %s" % json.dumps([round(x, 2) for x in region]),
+                  "region_avg_us           %.2f" % region_avg,
+                  "", "# the bench's own figures in the same run (HIP events over the timed region; wall-clock value):",
                   "roofline.kernel_us_mean  %s" % rec["roofline"]["kernel_us_mean"],
                   "kernel_us               %s" % json.dumps(rec["kernel_us"]),
-                  "value_gbps              %s" % rec["value"]]
+                  "value_gbps              %s" % rec["value"],
+                  "", "# machine-readable:", json.dumps({
+                      "workload": label, "kernel": op_kernel, "kernel_sha": summary["kernel_sha"],
+                      "op_avg_us": round(region_avg, 2), "op_avg_us_all_launches": float(top["AverageNs"]) / 1e3,
+                      "op_calls": int(top["Calls"]), "steps": k, "warmup": wu,
+                      "bench_kernel_us_mean": rec["roofline"]["kernel_us_mean"]})]
         text = "\n".join(lines) + "\n"
         open(os.path.join(out, "%s_kernel_trace_bench_%s.txt" % (prefix, label)), "w").write(text)
         log(text)

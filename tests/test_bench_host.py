@@ -1,5 +1,5 @@
 """Host-only checks of bench.py's contract pieces: the one-GPU refusal, the
-traffic lookup (current profile summaries are used, stale ones are not) and
+profile lookup (current rocprofv3 summaries are used, stale ones are not) and
 the p90 helper."""
 import os
 import shutil
@@ -30,13 +30,22 @@ def test_bad_counts_are_refused(flags):
 
 
 def test_committed_profiles_are_current_for_every_target():
+    # Every measured target has a current counter summary whose HBM bytes are
+    # within a few percent of the algorithmic bytes (the shuffled reader order
+    # is the one case with real excess); the headline pair also has current
+    # occupancy and timed-region trace summaries, so the bench line carries
+    # FETCH/WRITE bytes, waves per CU and a trace-derived fraction of peak.
     for name in ["prefill", "long"] + list(V.VARIANTS):
         t = V.target(name)
-        traffic = bench.recorded_traffic(t)
-        assert traffic is not None, t.label
-        # within a few percent of the algorithmic bytes (the shuffled reader
-        # order is the one case with real excess)
-        assert 0.99 * t.alg_bytes < traffic < 1.10 * t.alg_bytes, (t.label, traffic / t.alg_bytes)
+        f = bench.profile_fields(t, t.alg_bytes)
+        assert f["traffic"] is not None, t.label
+        assert 0.99 * t.alg_bytes < f["traffic"] < 1.10 * t.alg_bytes, (t.label, f["traffic"] / t.alg_bytes)
+        assert abs(f["fetch_bytes"] + f["write_bytes"] - f["traffic"]) < 1e-6 * f["traffic"]
+        assert f["waves_per_cu"] is not None and 0 < f["waves_per_cu"] <= 32, t.label
+        assert f["kernel_us_trace"] is not None and 0 < f["frac_trace"] < 1, t.label
+    for name in ("prefill", "long"):
+        t = V.target(name)
+        assert bench.profile_record(t.prefix, "kernel_trace_bench", t.label, t.family) is not None, name
 
 
 def test_stale_profile_is_not_reported(tmp_path, monkeypatch):
@@ -47,10 +56,10 @@ def test_stale_profile_is_not_reported(tmp_path, monkeypatch):
     text = open(src).read()
     (prof / os.path.basename(src)).write_text(text)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.recorded_traffic(t) is not None
+    assert bench.profile_fields(t, t.alg_bytes)["traffic"] is not None
     (prof / os.path.basename(src)).write_text(text.replace('"kernel_sha": "', '"kernel_sha": "0'))
-    assert bench.recorded_traffic(t) is None
-    assert bench.recorded_traffic(V.target("tiny")) is None      # no summary at all
+    assert bench.profile_fields(t, t.alg_bytes)["traffic"] is None
+    assert bench.profile_fields(V.target("tiny"), 1)["traffic"] is None      # no summary at all
 
 
 def test_p90():
