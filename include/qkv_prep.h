@@ -43,7 +43,14 @@ extern "C" {
 #define QKV_PREP_SLOT_BYTES 584
 
 /* Return codes.  On any code other than QKV_PREP_OK from an argument check,
- * nothing was launched and no output was touched. */
+ * nothing was launched and no output was touched.  The launch itself is
+ * checked with hipGetLastError right after it, so a refused launch is reported
+ * by the call that made it; an error of the running kernel is asynchronous,
+ * and QKV_PREP_SYNC=1 in the environment makes every call wait for its stream
+ * and report such an error as QKV_PREP_ERR_DEVICE.  The FlagGems-vllm PR 684
+ * page ("The seven test and benchmark fixes") describes a backend where a failed
+ * launch surfaced only at the next launch, several frames from its cause: these
+ * two checks keep the error with the call that caused it. */
 enum {
     QKV_PREP_OK = 0,
     QKV_PREP_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, bad field */
@@ -202,7 +209,10 @@ int qkv_prep_gather(qkv_prep_t h, const qkv_prep_gather_args *args, void *stream
 int qkv_prep_destroy(qkv_prep_t h);
 
 /* 1 if the kernel implements this shape (head_dim 512, rope_dim 64, H >= 1),
- * else 0.  Lets a caller route other shapes elsewhere instead of failing. */
+ * else 0.  A support gate in the manner of the rocm-aiter PR 1 page ("Technical
+ * Details": a fixed-shape kernel exposes is_supported so that a caller serving
+ * other shapes routes them to another kernel instead of tripping a check).
+ * Pure host code; needs no device. */
 int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
 
 /* The launch qkv_prep_run would use for num_tokens tokens with config cfg on
