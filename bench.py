@@ -267,9 +267,12 @@ def kernel_us(res):
 
 
 def bench_configs(torch, qp, names, warmup):
-    """The other workloads, event-timed per launch: median, min and p90 over
-    200 launches for the small ones (Tiny, Decode-like) and 30 for the large
-    ones, plus the median of 10 launches with L2 and the MALL flushed first."""
+    """The other workloads: the mean launch time over a region of back-to-back
+    launches (as for the headline), then per-launch event timings (median,
+    min and p90) over as many launches, 200 for the small workloads (Tiny,
+    Decode-like) and 30 for the large ones, and the median of 10 launches with
+    L2 and the MALL flushed first.  For short kernels the two events around
+    each launch add a microsecond or two, which the region does not pay."""
     from fp8_kv_cache_amd import variants as V
     out = {}
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -280,14 +283,17 @@ def bench_configs(torch, qp, names, warmup):
         for _ in range(warmup):
             fn()
         reps = 200 if t.alg_bytes < (1 << 30) else 30
+        _, region = time_region(torch, fn, reps)
         ks = time_each(torch, fn, reps)
         cold = time_cold(torch, fn, 10, scratch)
         del fn
         torch.cuda.empty_cache()
         med = statistics.median(ks)
         prof = profile_fields(t, t.alg_bytes)
-        out[t.label] = {"gbps_median": round(t.alg_bytes / med / 1e9, 1), "reps": reps,
-                        "kernel_us": {"median": round(med * 1e6, 2), "min": round(min(ks) * 1e6, 2),
+        out[t.label] = {"gbps_region": round(t.alg_bytes * reps / region / 1e9, 1),
+                        "gbps_median": round(t.alg_bytes / med / 1e9, 1), "reps": reps,
+                        "kernel_us": {"region_mean": round(region / reps * 1e6, 2),
+                                      "median": round(med * 1e6, 2), "min": round(min(ks) * 1e6, 2),
                                       "p90": round(p90(ks) * 1e6, 2),
                                       "median_cold": round(statistics.median(cold) * 1e6, 2)},
                         "bytes_per_launch": t.alg_bytes, "traffic": prof["traffic"],
@@ -454,6 +460,75 @@ def profile_run(torch, qp, probe, name, launches, copy_bytes=512 << 20, copies=3
     log("profile: %d copies of %d bytes done" % (copies, copy_bytes))
 
 
+# ----------------------------------------------------------------- sweep mode
+
+def warm_chip(torch, probe, seconds=0.5, nbytes=2 << 30):
+    """Sustained in-place streaming for about `seconds`, so that what follows
+    runs in the chip's warm power state (the transient after a lull is
+    described in the design notes)."""
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            probe.qkv_prep_probe_update(buf.data_ptr(), nbytes, stream)
+        torch.cuda.synchronize()
+    del buf
+
+
+def sweep_workload(W, name, size):
+    """A named workload, or for size "TxH" a decode-like one of that size:
+    positions uniform in [0, 131072), random distinct slots of a cache twice
+    the token count."""
+    if not size:
+        return W.WORKLOADS[name]
+    T, H = (int(v) for v in size.lower().split("x"))
+    return W.custom(T, H, seed=11 + T + H, max_position=131072)
+
+
+def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3):
+    """Every forced launch shape of the operator on one workload (rows per
+    wavefront 1/2/4 x wavefronts per workgroup 1/2/4/8 x kv tokens per
+    wavefront 1/2/4), plus both conversion paths at the heuristic's shape:
+    the region time of `launches` back-to-back launches, best of `rounds`
+    interleaved rounds, with the chip warmed first.  Every shape computes the
+    same bits (the GPU parity tests check each one); this measures only their
+    speed, so the heuristic's choice can be re-checked on any machine."""
+    from fp8_kv_cache_amd import probe
+    w = sweep_workload(W, name, size)
+    name = w.name
+    inp = W.make_inputs(w, device="cuda")
+    valid = int(((inp["slot_mapping"] >= 0) & (inp["slot_mapping"] < w.num_blocks * w.block_size)).sum())
+    nbytes = W.algorithmic_bytes(w.num_tokens, w.num_heads, valid)
+    args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+            inp["slot_mapping"], inp["cache"])
+    heur = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps).launch_shape(w.num_tokens)
+    shapes = [dict(rows_per_wave=r, waves_per_block=b, kv_per_wave=k)
+              for r in (1, 2, 4) for b in (1, 2, 4, 8) for k in (1, 2, 4)]
+    shapes += [dict(rows_per_wave=heur.rows_per_wave, waves_per_block=heur.waves_per_block,
+                    kv_per_wave=heur.kv_per_wave, convert=c) for c in (1, 2)]
+    ops = [qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps, **sh) for sh in shapes]
+    warm_chip(torch, probe)
+    best = [float("inf")] * len(shapes)
+    for rnd in range(rounds):
+        order = range(len(shapes)) if rnd % 2 == 0 else reversed(range(len(shapes)))
+        for i in order:
+            fn = lambda op=ops[i]: op(*args)
+            for _ in range(3):
+                fn()
+            _, region = time_region(torch, fn, launches)
+            best[i] = min(best[i], region / launches)
+    rows = sorted(({"shape": sh, "us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1)}
+                   for sh, t in zip(shapes, best)), key=lambda r: r["us"])
+    del inp, args, ops
+    torch.cuda.empty_cache()
+    return {"mode": "sweep", "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
+            "bytes_per_launch": nbytes, "launches": launches, "rounds": rounds,
+            "heuristic": {"rows_per_wave": heur.rows_per_wave, "waves_per_block": heur.waves_per_block,
+                          "kv_per_wave": heur.kv_per_wave, "convert": heur.convert},
+            "shapes": rows}
+
+
 # ----------------------------------------------------------------- main
 
 def main():
@@ -469,9 +544,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "profile"], default="bench",
-                    help="profile: a short fixed program for rocprofv3 (no JSON line)")
+    ap.add_argument("--mode", choices=["bench", "profile", "sweep"], default="bench",
+                    help="profile: a short fixed program for rocprofv3 (no JSON line); sweep: every "
+                         "forced launch shape of the operator on --workload (one JSON line)")
     ap.add_argument("--launches", type=int, default=5)
+    ap.add_argument("--sizes", default="",
+                    help="sweep mode: comma-separated TxH sizes (decode-like inputs) instead of --workload")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0 or args.launches < 1:
         ap.error("--steps and --launches must be at least 1, --warmup at least 0")
@@ -491,6 +569,10 @@ def main():
         sys.exit(1)
     if args.mode == "profile":
         profile_run(torch, qp, probe, args.workload, args.launches)
+        return
+    if args.mode == "sweep":
+        for size in (args.sizes.split(",") if args.sizes else [None]):
+            print(json.dumps(sweep_shapes(torch, W, qp, args.workload, size)), flush=True)
         return
     kat_before = known_answer_check(torch, W, qp)
     w, main_res, ceil_before = bench_workload(torch, W, qp, probe, args.workload, args.steps, args.warmup,

@@ -39,32 +39,29 @@ int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)
     return QKV_PREP_OK;
 }
 
-// Launch shape for T tokens.
-//  * rows_per_wave: 1 (one q row per wavefront), or U = 2, 4 consecutive heads
-//    of one token per wavefront, processed one after another with the token's
-//    position, cos/sin row and the q weight loaded once.  Measured on MI355X
-//    (T = 64..16384, H = 64 and 128, two interleaved rounds, back-to-back and
-//    with L2 and the MALL flushed before each launch): up to 2^17 q rows
-//    (256 MiB of q, about the MALL's size) two heads per wavefront are up to
-//    10% faster back to back, where q stays cache-resident as it does right after
-//    the kernel that produced it; above 2^17 rows one row per wavefront, with
-//    its system-scope stores, ties or wins in both regimes (by 0.4-5.5%
-//    flushed).
-//    Four heads per wavefront never win; they are used only when fewer
-//    wavefronts would need 2^32 or more work-items in the dispatch.
-//  * waves_per_block: 1 (64-lane workgroups).  Measured on MI355X with four
-//    interleaved rounds per shape: 1 wave per workgroup beats 2, 4 and 8 on
-//    2048x64, 32768x64, 32768x128 and 131072x128 (by 1-5%).
+// Launch shape for T tokens.  Chosen from the committed sweep (bench.py
+// --mode sweep: every forced shape, 30 back-to-back launches, best of three
+// interleaved rounds, after warming the chip), run on MI355X over 28 sizes
+// from 512x64 to 131072x8 (H = 8 to 128) twice, rounds agreeing within 1%:
+//  * rows_per_wave: two consecutive heads of one token per wavefront (the
+//    token's position, cos/sin row and q weight loaded once for both rows,
+//    processed one after the other) below 2^16 q rows, and, with at most 16
+//    heads, from 2^14 tokens: there it is 2-7% faster (32768x8: 94.6 against
+//    101.1 us; 65536x16: 356.6 against 361.4).  Otherwise one q row per
+//    wavefront, with system-scope stores: 1-6% faster from 2^16 q rows with
+//    32 heads or more, or with fewer tokens (2048x64: 41.7 against 42.5 us;
+//    4096x16: 23.0 against 24.3).  Below 2^16 rows the shapes are within ~2%
+//    of each other and two heads stay.  Four heads per wavefront never win;
+//    they are used only when fewer wavefronts would need 2^32 or more
+//    work-items in the dispatch.
+//  * kv_per_wave: four consecutive tokens' kv rows per kv wavefront, their
+//    loads issued together, from 2^16 q rows (the kv wavefronts run first, as
+//    a latency-bound burst; 2048x32: 22.3 against 23.3 us); one below, where
+//    four per wavefront lose up to 12% (512x64: 14.1 against 12.6 us).
+//  * waves_per_block: 1.  More wavefronts per workgroup gain at most ~1% at a
+//    few small-head shapes and lose up to 3% on the large ones.
 //  * convert: the gfx950 conversion instructions (bit-identical to the integer
 //    rounding, which the tests check on every workload).
-//  * kv_per_wave: 4 consecutive tokens' kv rows per kv wavefront, their loads
-//    issued together, from 2^17 q rows; 1 below.  The kv wavefronts are
-//    dispatched first and form a latency-bound burst.  Measured on MI355X (two
-//    to four alternating rounds): from 2^17 q rows four tokens are 0.8-2.9%
-//    faster (32768x64 +1.3%, 2048x64 +1.9%, 16384x8 +2.9%, 131072x128 even);
-//    below, where the kernel lasts as long as its slowest wavefront, they are
-//    up to 14% slower (256x64 and 512x64), even at 2^16 rows.  Two per
-//    wavefront gain less; eight no more than four.
 qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
 {
     (void)num_cus;
@@ -72,14 +69,16 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     const int64_t q_rows = T * c.num_heads;
     s.waves_per_block = c.waves_per_block ? c.waves_per_block : 1;
     s.convert = c.convert ? c.convert : 2;
-    s.kv_per_wave = c.kv_per_wave ? c.kv_per_wave : (q_rows >= ((int64_t)1 << 17) ? 4 : 1);
+    s.kv_per_wave = c.kv_per_wave ? c.kv_per_wave : (q_rows >= ((int64_t)1 << 16) ? 4 : 1);
     s.kv_blocks = ceil_div(T, (int64_t)s.kv_per_wave * s.waves_per_block);
     // q wavefronts: T * ceil(H / U) (U heads of one token per wavefront)
     auto q_waves = [&](int u) { return T * ceil_div(c.num_heads, u); };
     if (c.rows_per_wave) {
         s.rows_per_wave = c.rows_per_wave;
     } else {
-        s.rows_per_wave = q_rows <= ((int64_t)1 << 17) && c.num_heads > 1 ? 2 : 1;
+        const bool few_rows = q_rows < ((int64_t)1 << 16);
+        const bool many_tokens_few_heads = c.num_heads <= 16 && T >= ((int64_t)1 << 14);
+        s.rows_per_wave = (few_rows || many_tokens_few_heads) && c.num_heads > 1 ? 2 : 1;
         while (s.rows_per_wave < 4 &&
                (s.kv_blocks + ceil_div(q_waves(s.rows_per_wave), s.waves_per_block)) * 64 *
                        s.waves_per_block >= ((int64_t)1 << 32))

@@ -35,16 +35,16 @@
 //  * q rows and kv rows go to different workgroups of one launch (the FlagGems
 //    page merges the Q and KV launches); kv workgroups come first in dispatch
 //    order, so their quantization overlaps the q stream instead of trailing it.
-//    From 2^17 q rows a kv wavefront takes four consecutive tokens, all their
-//    loads issued together: the kv wavefronts form a latency-bound burst at
-//    the start, and more loads in flight per wavefront shorten it.
-//  * Decode-sized batches (up to 2^17 q rows) take two heads of one token per
-//    wavefront, one after the other, so the token's position, cos/sin row and
-//    the q weight are loaded once per two rows (up to 10% faster there while q
-//    is cache-resident; the launch heuristic picks it).  Issuing several q
-//    rows' loads at once (the sglang page's "K tokens per block" load-level
-//    parallelism) was slower at every size measured; the kv burst above is
-//    the one place where it pays.
+//    For larger batches a kv wavefront takes four consecutive tokens, all
+//    their loads issued together: the kv wavefronts form a latency-bound
+//    burst at the start, and more loads in flight per wavefront shorten it.
+//  * Small batches, and batches of many tokens with few heads, take two heads
+//    of one token per wavefront, one after the other, so the token's
+//    position, cos/sin row and the q weight are loaded once per two rows (the
+//    launch heuristic in qkv_prep_api.cpp says when, with its measurements).
+//    Issuing several q rows' loads at once (the sglang page's "K tokens per
+//    block" load-level parallelism) was slower at every size measured; the kv
+//    burst above is the one place where it pays.
 #include "qkv_prep_launch.h"
 #include "qkvp_device.h"
 
@@ -125,9 +125,7 @@ __device__ __forceinline__ void q_row(const KernelArgs &a, int64_t row, uint32_t
 // row after another: the token's position, its cos/sin row and the q weight
 // are loaded once for the chunk, then each row is loaded, normalized, rotated
 // and stored in turn (one row's load in flight, as with one row per
-// wavefront).  Measured on MI355X, two heads per wavefront beat one by up to
-// 10% up to 2^17 q rows (decode-sized batches) when q is cache-resident, and
-// tie or lose above.
+// wavefront).
 template <int U, bool HAS_W, bool HW>
 __device__ __forceinline__ void q_chunk(const KernelArgs &a, uint32_t wv, uint32_t lane)
 {

@@ -157,21 +157,29 @@ def test_launch_shape_heuristic():
     small = qp.qkv_prep_launch_shape(cfg, 256, 16)
     # decode-sized: two heads of a token per wavefront, up to 2^17 q rows
     assert small.rows_per_wave == 2 and small.waves_per_block == 1 and small.convert == 2
-    # kv rows: one token per wavefront below 2^17 q rows
+    # kv rows: one token per wavefront below 2^16 q rows
     assert small.kv_per_wave == 1
     assert small.kv_blocks == 16 and small.q_blocks == 16 * 32 and small.grid == 16 * 33
-    # four consecutive tokens per kv wavefront from 2^17 q rows
-    assert qp.qkv_prep_launch_shape(cfg, 256, 2047).kv_per_wave == 1
-    at = qp.qkv_prep_launch_shape(cfg, 256, 2048)
-    assert at.kv_per_wave == 4 and at.kv_blocks == 2048 // 4
-    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 16384).kv_per_wave == 4
+    # four consecutive tokens per kv wavefront from 2^16 q rows
+    assert qp.qkv_prep_launch_shape(cfg, 256, 1023).kv_per_wave == 1
+    at = qp.qkv_prep_launch_shape(cfg, 256, 1024)
+    assert at.kv_per_wave == 4 and at.kv_blocks == 1024 // 4
+    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 8192).kv_per_wave == 4
     assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 4096).kv_per_wave == 1
     ragged = qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=4), 256, 17)
     assert ragged.kv_per_wave == 4 and ragged.kv_blocks == 5                  # ceil(17 / 4)
     assert qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=2, waves_per_block=2),
                                     256, 9).kv_blocks == 3                    # ceil(9 / (2 * 2))
-    assert qp.qkv_prep_launch_shape(cfg, 256, 2048).rows_per_wave == 2        # 2^17 rows
-    assert qp.qkv_prep_launch_shape(cfg, 256, 2049).rows_per_wave == 1
+    # two heads per wavefront below 2^16 q rows ...
+    assert qp.qkv_prep_launch_shape(cfg, 256, 1023).rows_per_wave == 2
+    assert qp.qkv_prep_launch_shape(cfg, 256, 1024).rows_per_wave == 1        # 2^16 rows
+    assert qp.qkv_prep_launch_shape(cfg, 256, 2048).rows_per_wave == 1
+    # ... and with at most 16 heads from 2^14 tokens
+    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 8192).rows_per_wave == 1
+    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 16384).rows_per_wave == 2
+    assert qp.qkv_prep_launch_shape(qp.make_config(16), 256, 16384).rows_per_wave == 2
+    assert qp.qkv_prep_launch_shape(qp.make_config(17), 256, 16384).rows_per_wave == 1
+    assert qp.qkv_prep_launch_shape(qp.make_config(32), 256, 65536).rows_per_wave == 1
     one_head = qp.qkv_prep_launch_shape(qp.make_config(1), 256, 100)
     assert one_head.rows_per_wave == 1 and one_head.q_blocks == 100
     odd_heads = qp.qkv_prep_launch_shape(qp.make_config(5), 256, 10)

@@ -104,14 +104,18 @@ def test_kv_rows_per_wavefront_with_wider_workgroups(T, kv_per_wave, wpb):
         check(w, kv_per_wave=kv_per_wave, waves_per_block=wpb, rows_per_wave=rpw)
 
 
-@pytest.mark.parametrize("T,H", [(2048, 64), (2049, 64), (1024, 128), (1025, 128)])
-def test_both_sides_of_the_launch_threshold(T, H):
-    # The heuristic takes two heads per wavefront up to 2^17 q rows and one
-    # row per wavefront above; default launch on each side of the boundary.
+@pytest.mark.parametrize("T,H", [(1023, 64), (1024, 64), (511, 128), (512, 128), (8192, 8), (16384, 8),
+                                 (16383, 16), (16384, 16)])
+def test_both_sides_of_the_launch_thresholds(T, H):
+    # The heuristic takes two heads per wavefront below 2^16 q rows, and with
+    # at most 16 heads from 2^14 tokens, one row per wavefront otherwise; four
+    # kv tokens per kv wavefront from 2^16 q rows.  Default launch on each
+    # side of each boundary.
     from fp8_kv_cache_amd.qkv_prep import QkvPrep
     shape = QkvPrep(H).launch_shape(T)
-    assert shape.rows_per_wave == (2 if T * H <= 1 << 17 else 1)
-    assert shape.kv_per_wave == (4 if T * H >= 1 << 17 else 1)
+    two = T * H < 1 << 16 or (H <= 16 and T >= 1 << 14)
+    assert shape.rows_per_wave == (2 if two else 1)
+    assert shape.kv_per_wave == (4 if T * H >= 1 << 16 else 1)
     check(W.custom(T, H, seed=330 + T + H, num_skip=5))
 
 
