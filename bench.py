@@ -267,12 +267,14 @@ def kernel_us(res):
 
 
 def bench_configs(torch, qp, names, warmup):
-    """The other workloads: the mean launch time over a region of back-to-back
-    launches (as for the headline), then per-launch event timings (median,
+    """The other workloads, each after a short sustained streaming load (like
+    the headline, which follows its ceiling measurement): the mean launch
+    time over a region of back-to-back launches, then per-launch event timings (median,
     min and p90) over as many launches, 200 for the small workloads (Tiny,
     Decode-like) and 30 for the large ones, and the median of 10 launches with
     L2 and the MALL flushed first.  For short kernels the two events around
     each launch add a microsecond or two, which the region does not pay."""
+    from fp8_kv_cache_amd import probe
     from fp8_kv_cache_amd import variants as V
     out = {}
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -280,6 +282,7 @@ def bench_configs(torch, qp, names, warmup):
         t = V.target(name)
         log("bench: config %s" % t.label)
         fn = V.setup(t, torch, qp)
+        warm_chip(torch, probe)
         for _ in range(warmup):
             fn()
         reps = 200 if t.alg_bytes < (1 << 30) else 30
@@ -304,18 +307,21 @@ def bench_configs(torch, qp, names, warmup):
 
 
 def bench_variants(torch, qp, steps, warmup):
-    """The neighbouring paths, each timed like the operator: the bf16-store cache
+    """The neighbouring paths, each timed like the operator (after a short
+    sustained streaming load, then W warmups and K steps): the bf16-store cache
     mode on the Prefill workload (1024-byte slots, no quantization); the cache
     reader gathering every slot of a 4096 x 64-slot cache (262144 rows) to bf16
     and to fp32 as a block-table walk, and to fp32 in a fully random slot order;
     and the MXFP8 norm-quant operator on 16384 x 7168 with the residual add and
     the residual output."""
+    from fp8_kv_cache_amd import probe
     from fp8_kv_cache_amd import variants as V
     out = {}
     for name in V.VARIANTS:
         t = V.target(name)
         log("bench: variant %s" % t.label)
         fn = V.setup(t, torch, qp)
+        warm_chip(torch, probe)
         for _ in range(warmup):
             fn()
         wall, region = time_region(torch, fn, steps)
