@@ -18,7 +18,8 @@ struct GatherArgs {
     uint32_t xcd_chunk;        // rows per XCD chunk (0: workgroup b takes row b)
 };
 
-// Enqueue the cache reader: one wavefront per row, `waves_per_block` per workgroup.
+// Enqueue the cache reader: one wavefront per fp32 row or per two bf16 rows,
+// `waves_per_block` wavefronts per workgroup.
 hipError_t launch_gather(const GatherArgs &a, int waves_per_block, hipStream_t stream);
 
 }  // namespace qkvp

@@ -1,8 +1,9 @@
 // Cache reader for the FP8 + UE8M0 paged cache written by qkv_prep_kernel:
 // dequantize and gather slots back into fp32 or bf16 rows (the cache layout is
 // the one stated in include/qkv_prep.h).  HBM bound: 584 bytes read and 1 or
-// 2 KiB written per row, one wavefront per row, non-temporal system-scope
-// stores (plain loads: a slot's lines are shared with its neighbours).
+// 2 KiB written per row; one wavefront per fp32 row or per two bf16 rows;
+// non-temporal system-scope stores (plain loads: a slot's lines are shared
+// with its neighbours).
 #include "qkv_prep_gather.h"
 #include "qkvp_device.h"
 
@@ -28,39 +29,66 @@ __device__ __forceinline__ u32x4 dequant4(uint32_t codes, uint32_t b)
                  __float_as_uint(__builtin_ldexpf(hi[0], e)), __float_as_uint(__builtin_ldexpf(hi[1], e))};
 }
 
-// bf16 rows: one wavefront per output row.  Lane l < 56 reads the 8 codes of
-// dims 8l..8l+7 and the scale byte of their block; lanes 56..63 read 16 bytes
-// of rope bf16; each lane stores its 16 output bytes, so the wavefront's one
-// store covers the 1 KiB row.
-__device__ __forceinline__ void gather_row_bf16(const GatherArgs &a, int64_t i, uint32_t lane)
+// bf16 rows: R consecutive rows per wavefront.  Lane l < 56 reads the 8
+// codes of dims 8l..8l+7 and the scale byte of their block; lanes 56..63 read
+// 16 bytes of rope bf16; each lane stores its 16 output bytes, so one store
+// covers a 1 KiB row.  All R rows' slot and data loads are issued before the
+// first row is finished: the wavefront's two dependent round trips (slot,
+// then data) are then shared by R rows.  Measured on MI355X over a
+// 262144-slot block walk by graph replay: two rows per wavefront 59.6 us
+// against 63.9 us for one (6.6 -> 7.1 TB/s); four or eight gain less.  fp32
+// rows lose with the same change (92.3 -> 97.5 us at two rows), so they keep
+// one row per wavefront.
+template <int R>
+__device__ __forceinline__ void gather_rows_bf16(const GatherArgs &a, int64_t i0, uint32_t lane)
 {
-    const int64_t slot = a.slots[i];
-    float v[8];
-    if (slot < 0 || slot >= a.num_slots) {
+    int64_t slot[R];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = 0.0f;
-    } else {
-        const uint32_t s32 = (uint32_t)slot;
-        const uint32_t blk = fastdiv(s32, a.blocks);
-        const uint32_t sib = s32 - blk * a.block_size;
-        const uint8_t *base = a.cache + (int64_t)blk * a.block_size * kSlotBytes;
-        const uint8_t *data = base + (int64_t)sib * kSlotData;
-        if (lane < kRopeLane) {
-            const u32x2 codes = *(reinterpret_cast<const u32x2 *>(data) + lane);
-            const uint32_t b = base[(int64_t)a.block_size * kSlotData + (int64_t)sib * kSlotScale + lane / 8];
+    for (int u = 0; u < R; ++u)
+        slot[u] = i0 + u < a.n ? a.slots[i0 + u] : -1;
+    u32x4 d[R];
+    uint32_t b[R];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4 d = dequant4(codes[h], b);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[4 * h + e] = __uint_as_float(d[e]);
+    for (int u = 0; u < R; ++u) {
+        d[u] = u32x4{0u, 0u, 0u, 0u};
+        b[u] = 0u;
+        if (slot[u] >= 0 && slot[u] < a.num_slots) {
+            const uint32_t s32 = (uint32_t)slot[u];
+            const uint32_t blk = fastdiv(s32, a.blocks);
+            const uint32_t sib = s32 - blk * a.block_size;
+            const uint8_t *base = a.cache + (int64_t)blk * a.block_size * kSlotBytes;
+            const uint8_t *data = base + (int64_t)sib * kSlotData;
+            if (lane < kRopeLane) {
+                const u32x2 codes = *(reinterpret_cast<const u32x2 *>(data) + lane);
+                d[u] = u32x4{codes[0], codes[1], 0u, 0u};
+                b[u] = base[(int64_t)a.block_size * kSlotData + (int64_t)sib * kSlotScale + lane / 8];
+            } else {
+                d[u] = *(reinterpret_cast<const u32x4 *>(data + kNopeDim) + (lane - kRopeLane));
             }
-        } else {
-            unpack_bf16x8(*(reinterpret_cast<const u32x4 *>(data + kNopeDim) + (lane - kRopeLane)), v);
         }
     }
-    store_sys(static_cast<uint8_t *>(a.out) + i * 1024, 1024u, lane * 16u, pack_bf16x8<true>(v));
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        if (i0 + u >= a.n)
+            break;
+        float v[8];
+        if (slot[u] < 0 || slot[u] >= a.num_slots) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = 0.0f;
+        } else if (lane < kRopeLane) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 q = dequant4(d[u][h], b[u]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[4 * h + e] = __uint_as_float(q[e]);
+            }
+        } else {
+            unpack_bf16x8(d[u], v);
+        }
+        store_sys(static_cast<uint8_t *>(a.out) + (i0 + u) * 1024, 1024u, lane * 16u, pack_bf16x8<true>(v));
+    }
 }
 
 // fp32 rows (2 KiB): lane l owns dims 4l..4l+3 and 256+4l..256+4l+3, so each
@@ -109,17 +137,23 @@ __device__ __forceinline__ uint32_t xcd_row_block(uint32_t b, uint32_t chunk)
     return w * win + (r & 7u) * chunk + (r >> 3);
 }
 
+// Rows per wavefront of each output type.
+constexpr int kBf16Rows = 2;
+constexpr int kF32Rows = 1;
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a)
 {
+    constexpr int R = OUT_BF16 ? kBf16Rows : kF32Rows;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t i = (int64_t)xcd_row_block(blockIdx.x, a.xcd_chunk) * (blockDim.x >> 6) + wave;
-    if (i < a.n) {
+    const int64_t unit = (int64_t)xcd_row_block(blockIdx.x, a.xcd_chunk) * (blockDim.x >> 6) + wave;
+    const int64_t i0 = unit * R;
+    if (i0 < a.n) {
         if constexpr (OUT_BF16)
-            gather_row_bf16(a, i, lane);
+            gather_rows_bf16<R>(a, i0, lane);
         else
-            gather_row_f32(a, i, lane);
+            gather_row_f32(a, i0, lane);
     }
 }
 
@@ -128,12 +162,16 @@ __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a)
 hipError_t launch_gather(const GatherArgs &a, int waves_per_block, hipStream_t stream)
 {
     GatherArgs g = a;
-    int64_t blocks = (a.n + waves_per_block - 1) / waves_per_block;
+    const int rows = a.out_bf16 ? kBf16Rows : kF32Rows;
+    const int64_t waves = (a.n + rows - 1) / rows;
+    int64_t blocks = (waves + waves_per_block - 1) / waves_per_block;
     // 64 rows per XCD chunk (a cache block's worth of slots at the usual block
-    // size).  Measured on MI355X over a 262144-slot block-table walk: fp32 rows
-    // 6.5 -> 7.1 TB/s, bf16 rows 6.0 -> 6.3 TB/s; every slot in a random order:
-    // +2.5%.  Small grids keep the plain order (the padding would cost more).
-    g.xcd_chunk = blocks >= 4096 ? 64u : 0u;
+    // size), counted in workgroups of `rows * waves_per_block` rows.  Measured
+    // on MI355X over a 262144-slot block-table walk: fp32 rows 6.5 -> 7.1 TB/s,
+    // bf16 rows 6.0 -> 6.3 TB/s; every slot in a random order: +2.5%.  Small
+    // grids keep the plain order (the padding would cost more).
+    const int64_t rows_per_block = (int64_t)rows * waves_per_block;
+    g.xcd_chunk = blocks * rows_per_block >= 4096 ? (uint32_t)(64 / rows_per_block) : 0u;
     if (g.xcd_chunk)
         blocks = (blocks + 8 * g.xcd_chunk - 1) / (8 * g.xcd_chunk) * (8 * g.xcd_chunk);
     const dim3 grid((uint32_t)blocks), block(64u * (uint32_t)waves_per_block);

@@ -82,14 +82,17 @@ def test_operator_writes_only_q_and_the_cache(T, H, rpw, kv_store):
     assert same_bytes(cache, cache_ref)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_gather_writes_only_its_rows(dtype):
+@pytest.mark.parametrize("dtype,drop", [(torch.float32, 0), (torch.bfloat16, 0), (torch.float32, 1),
+                                        (torch.bfloat16, 1), (torch.bfloat16, 999)])
+def test_gather_writes_only_its_rows(dtype, drop):
+    # drop = 1 leaves an odd row count, so the last two-row bf16 wavefront has
+    # one row to write; drop = 999 leaves a single row.
     w = W.custom(1000, 4, seed=1400, num_skip=7)
     inp = W.make_inputs(w, device=DEV)
     op = qp.QkvPrep(4, block_size=w.block_size, eps=w.eps)
     op(inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"], inp["slot_mapping"],
        inp["cache"])
-    slots = inp["slot_mapping"].flip(0).contiguous()          # includes the skipped (negative) slots
+    slots = inp["slot_mapping"].flip(0)[drop:].contiguous()   # includes the skipped (negative) slots
     n = slots.numel()
     ref = torch.empty((n, 512), dtype=dtype, device=DEV)
     op.gather(inp["cache"], slots, ref)
