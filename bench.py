@@ -217,9 +217,9 @@ def bench_workload(torch, W, qp, probe, name, steps, warmup, ceiling_first):
     nbytes = W.algorithmic_bytes(w.num_tokens, w.num_heads, valid)
     op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
     shape = op.launch_shape(w.num_tokens)
-    args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
-            inp["slot_mapping"], inp["cache"])
-    fn = lambda: op(*args)
+    # checked once; each step is then one C call (qkv_prep_run)
+    fn = op.prepare(inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
+                    inp["slot_mapping"], inp["cache"])
     ceilings = None
     if ceiling_first:
         ceilings = copy_ceilings(torch, probe)
@@ -256,7 +256,7 @@ def bench_workload(torch, W, qp, probe, name, steps, warmup, ceiling_first):
     }
     res["gbps_wall"] = nbytes / res["wall_s_per_step"] / 1e9
     res["gbps_kernel_mean"] = nbytes / res["kernel_s_mean"] / 1e9
-    del inp, args, fn
+    del inp, fn
     torch.cuda.empty_cache()
     return w, res, ceilings
 
@@ -514,19 +514,20 @@ def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3):
     shapes += [dict(rows_per_wave=heur.rows_per_wave, waves_per_block=heur.waves_per_block,
                     kv_per_wave=heur.kv_per_wave, convert=c) for c in (1, 2)]
     ops = [qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps, **sh) for sh in shapes]
+    launches_of = [op.prepare(*args) for op in ops]
     warm_chip(torch, probe)
     best = [float("inf")] * len(shapes)
     for rnd in range(rounds):
         order = range(len(shapes)) if rnd % 2 == 0 else reversed(range(len(shapes)))
         for i in order:
-            fn = lambda op=ops[i]: op(*args)
+            fn = launches_of[i]
             for _ in range(3):
                 fn()
             _, region = time_region(torch, fn, launches)
             best[i] = min(best[i], region / launches)
     rows = sorted(({"shape": sh, "us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1)}
                    for sh, t in zip(shapes, best)), key=lambda r: r["us"])
-    del inp, args, ops
+    del inp, args, ops, launches_of
     torch.cuda.empty_cache()
     return {"mode": "sweep", "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
             "bytes_per_launch": nbytes, "launches": launches, "rounds": rounds,

@@ -188,25 +188,10 @@ def mxfp8_norm_quant(x, gamma, eps, *, residual=None, residual_out=None, quant_o
                      scale_out=None, stream=None):
     """Torch wrapper of qkv_prep_mxfp8_norm_quant: x [m, hidden] bf16.  Returns
     (codes uint8 [m, hidden], swizzled scales uint8 [...])."""
-    import torch
-    if x.dim() != 2:
-        raise ValueError("x must be [m, hidden]")
-    if x.device.type != "cuda":
-        raise ValueError("x must be on a HIP device, got %s" % x.device)
-    m, hidden = x.shape
-    if quant_out is None:
-        quant_out = torch.empty((m, hidden), dtype=torch.uint8, device=x.device)
-    if scale_out is None:
-        n = qkv_prep_mxfp8_scale_bytes(m, hidden)
-        scale_out = torch.empty(max(n, 0), dtype=torch.uint8, device=x.device)
-    check_mxfp8_tensors(x, gamma, residual, residual_out, quant_out, scale_out)
-    args = QkvPrepMxfp8Args(x.data_ptr(), _ptr(residual), _ptr(residual_out), gamma.data_ptr(),
-                            quant_out.data_ptr(), scale_out.data_ptr(), m, hidden, eps)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    qkv_prep_mxfp8_norm_quant(args, x.device.index if x.device.index is not None else torch.cuda.current_device(),
-                              stream)
-    return quant_out, scale_out
+    launch = prepare_mxfp8_norm_quant(x, gamma, eps, residual=residual, residual_out=residual_out,
+                                      quant_out=quant_out, scale_out=scale_out, stream=stream)
+    launch()
+    return launch.outputs
 
 
 # ------------------------------------------------------------ torch wrapper
@@ -304,11 +289,81 @@ def make_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_c
                        num_blocks, T)
 
 
+def _stream_of(stream, device):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Launch:
+    """One launch whose tensors were checked and whose argument struct was
+    built once, for callers that repeat the same call (a serving loop over
+    fixed buffers, a benchmark).  Calling it only calls the C entry point and
+    checks the return code, so its host cost is one ctypes call.
+
+    It keeps references to the tensors and to the owning object, so the
+    pointers it holds stay valid while it lives; the tensors must not be
+    resized or re-strided in place meanwhile.  The stream is fixed when the
+    launch is prepared."""
+
+    __slots__ = ("_fn", "_cargs", "_what", "_keep")
+
+    def __init__(self, fn, cargs, what, keep):
+        self._fn = fn
+        self._cargs = cargs
+        self._what = what
+        self._keep = keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._cargs)
+        if rc != OK:
+            raise QkvPrepError(rc, self._what)
+
+
+class _MxLaunch(Launch):
+    __slots__ = ()
+
+    @property
+    def outputs(self):
+        return self._keep[4], self._keep[5]
+
+
+def prepare_mxfp8_norm_quant(x, gamma, eps, *, residual=None, residual_out=None, quant_out=None,
+                             scale_out=None, stream=None) -> Launch:
+    """mxfp8_norm_quant with every check done now: returns a Launch that
+    enqueues the operator on ``stream`` (default: the current torch stream
+    at this call).  Outputs are allocated here when not given; the Launch's
+    ``outputs`` are (quant_out, scale_out)."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [m, hidden]")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device, got %s" % x.device)
+    m, hidden = x.shape
+    if quant_out is None:
+        quant_out = torch.empty((m, hidden), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty(max(qkv_prep_mxfp8_scale_bytes(m, hidden), 0), dtype=torch.uint8,
+                                device=x.device)
+    check_mxfp8_tensors(x, gamma, residual, residual_out, quant_out, scale_out)
+    args = QkvPrepMxfp8Args(x.data_ptr(), _ptr(residual), _ptr(residual_out), gamma.data_ptr(),
+                            quant_out.data_ptr(), scale_out.data_ptr(), m, hidden, eps)
+    device = x.device.index if x.device.index is not None else torch.cuda.current_device()
+    keep = (x, gamma, residual, residual_out, quant_out, scale_out, args)
+    return _MxLaunch(_lib.qkv_prep_mxfp8_norm_quant,
+                     (ctypes.byref(args), device, _stream_of(stream, x.device)),
+                     "qkv_prep_mxfp8_norm_quant", keep)
+
+
 class QkvPrep:
     """A qkv_prep handle bound to one device.
 
     ``op(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache)``
-    enqueues the operator on the current torch stream (or ``stream``)."""
+    enqueues the operator on the current torch stream (or ``stream``).
+    ``op.prepare(...)`` and ``op.prepare_gather(...)`` check the same tensors
+    once and return a Launch that repeats the call at the cost of one ctypes
+    call."""
 
     def __init__(self, num_heads, *, device=0, block_size=64, eps=1e-6, rows_per_wave=0,
                  waves_per_block=0, convert=0, kv_store=KV_FP8, kv_per_wave=0):
@@ -321,25 +376,53 @@ class QkvPrep:
 
     def __call__(self, q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
                  stream=None):
+        args = self._op_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache)
+        qkv_prep_run(self.handle, args, _stream_of(stream, q.device))
+        return q
+
+    def _op_args(self, q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache):
         import torch
         check_op_tensors(self.cfg.num_heads, self.cfg.block_size, self.slot_bytes,
                          torch.device("cuda", self.device), q, kv, q_norm_w, kv_norm_w, positions,
                          cos_sin, slot_mapping, kv_cache)
         per_block = self.cfg.block_size * self.slot_bytes
-        args = make_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
+        return make_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
                          None if kv_cache is None else kv_cache.numel() // per_block)
-        if stream is None:
-            stream = torch.cuda.current_stream(q.device).cuda_stream
-        qkv_prep_run(self.handle, args, stream)
-        return q
+
+    def prepare(self, q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache,
+                stream=None) -> Launch:
+        """The operator call of ``__call__``, checked and marshalled now.  The
+        returned Launch enqueues it on ``stream`` (default: the current torch
+        stream at this call) each time it is called."""
+        args = self._op_args(q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache)
+        rc = qkv_prep_validate(self.cfg, args)
+        if rc != OK:
+            raise QkvPrepError(rc, "qkv_prep_validate")
+        keep = (self, q, kv, q_norm_w, kv_norm_w, positions, cos_sin, slot_mapping, kv_cache, args)
+        return Launch(_lib.qkv_prep_run, (self.handle, ctypes.byref(args), _stream_of(stream, q.device)),
+                      "qkv_prep_run", keep)
+
+    def prepare_gather(self, kv_cache, slots, out, stream=None) -> Launch:
+        """``gather`` checked and marshalled now; the Launch enqueues it on
+        ``stream`` (default: the current torch stream at this call)."""
+        import torch
+        check_gather_tensors(self.cfg.block_size, torch.device("cuda", self.device), kv_cache, slots, out)
+        args = self._gather_args(kv_cache, slots, out)
+        keep = (self, kv_cache, slots, out, args)
+        return Launch(_lib.qkv_prep_gather, (self.handle, ctypes.byref(args), _stream_of(stream, out.device)),
+                      "qkv_prep_gather", keep)
+
+    def _gather_args(self, kv_cache, slots, out):
+        import torch
+        return QkvPrepGatherArgs(kv_cache.data_ptr(), kv_cache.numel() // (self.cfg.block_size * SLOT_BYTES),
+                                 slots.data_ptr(), slots.numel(), out.data_ptr(),
+                                 OUT_F32 if out.dtype == torch.float32 else OUT_BF16)
 
     def gather(self, kv_cache, slots, out, stream=None):
         """Read `slots` back out of an FP8 cache into `out` ([n, 512] fp32 or bf16)."""
         import torch
         check_gather_tensors(self.cfg.block_size, torch.device("cuda", self.device), kv_cache, slots, out)
-        args = QkvPrepGatherArgs(kv_cache.data_ptr(), kv_cache.numel() // (self.cfg.block_size * SLOT_BYTES),
-                                 slots.data_ptr(), slots.numel(), out.data_ptr(),
-                                 OUT_F32 if out.dtype == torch.float32 else OUT_BF16)
+        args = self._gather_args(kv_cache, slots, out)
         if stream is None:
             stream = torch.cuda.current_stream(out.device).cuda_stream
         qkv_prep_gather(self.handle, args, stream)
@@ -349,9 +432,13 @@ class QkvPrep:
         return qkv_prep_launch_shape(self.cfg, num_cus, num_tokens)
 
     def close(self):
-        if self.handle:
-            qkv_prep_destroy(self.handle)
-            self.handle = None
+        """Destroy the handle.  A Launch prepared from this object shares the
+        handle's ctypes cell, which is cleared here, so calling it afterwards
+        raises (invalid argument) instead of using a freed handle."""
+        h, self.handle = self.handle, None
+        if h:
+            qkv_prep_destroy(h)
+            h.value = None
 
     def __del__(self):
         try:

@@ -93,8 +93,9 @@ def target(name: str) -> Target:
 
 def setup(t: Target, torch, qp) -> Callable[[], None]:
     """Allocate and draw the target's inputs on the current GPU; return a
-    zero-argument callable that enqueues one launch on the current stream.
-    The callable holds the tensors; drop it to free them."""
+    prepared launch (a zero-argument callable, checked once) that enqueues
+    one launch on the current stream.  It holds the tensors; drop it to free
+    them."""
     if t.family == "op":
         w = W.WORKLOADS["prefill" if t.name == "bf16store_prefill" else t.name]
         inp = W.make_inputs(w, device="cuda")
@@ -104,9 +105,8 @@ def setup(t: Target, torch, qp) -> Callable[[], None]:
         else:
             cache = inp["cache"]
             op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
-        args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
-                inp["slot_mapping"], cache)
-        return lambda: op(*args)
+        return op.prepare(inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"],
+                          inp["cos_sin"], inp["slot_mapping"], cache)
     if t.family == "gather":
         w = W.WORKLOADS[GATHER_WORKLOAD]
         cap = w.num_blocks * w.block_size
@@ -125,7 +125,7 @@ def setup(t: Target, torch, qp) -> Callable[[], None]:
         dtype = torch.bfloat16 if t.name.startswith("gather_bf16") else torch.float32
         rows = torch.empty((cap, 512), dtype=dtype, device="cuda")
         op = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps)
-        return lambda: op.gather(cache, slots, rows)
+        return op.prepare_gather(cache, slots, rows)
     if t.family == "mxfp8":
         m, h = MX_ROWS, MX_HIDDEN
         gen = torch.Generator(device="cuda").manual_seed(77)
@@ -135,6 +135,6 @@ def setup(t: Target, torch, qp) -> Callable[[], None]:
         res_out = torch.empty_like(x)
         codes = torch.empty((m, h), dtype=torch.uint8, device="cuda")
         scales = torch.empty(mxfp8_scale_bytes(m, h), dtype=torch.uint8, device="cuda")
-        return lambda: qp.mxfp8_norm_quant(x, gamma, 1e-6, residual=r, residual_out=res_out,
+        return qp.prepare_mxfp8_norm_quant(x, gamma, 1e-6, residual=r, residual_out=res_out,
                                            quant_out=codes, scale_out=scales)
     raise KeyError(t.family)

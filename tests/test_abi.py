@@ -267,6 +267,26 @@ def test_run_without_handle_is_rejected():
     assert qp.library().qkv_prep_destroy(None) == qp.OK
 
 
+def test_prepared_launch_reports_the_c_code_and_keeps_its_arguments_alive():
+    """A Launch is one C call plus the return-code check.  With a cleared
+    handle cell (what QkvPrep.close leaves behind) the run is refused with
+    ERR_INVALID_ARG, before any device work."""
+    args = _good_args()
+    cell = ctypes.c_void_p(None)
+    launch = qp.Launch(qp.library().qkv_prep_run, (cell, ctypes.byref(args), None), "qkv_prep_run",
+                       (args,))
+    del args
+    with pytest.raises(qp.QkvPrepError) as e:
+        launch()
+    assert e.value.code == qp.ERR_INVALID_ARG
+    assert "qkv_prep_run" in str(e.value)
+    calls = []
+    ok = qp.Launch(lambda *a: calls.append(a) or qp.OK, (1, 2, 3), "x", ())
+    ok()
+    ok()
+    assert calls == [(1, 2, 3), (1, 2, 3)]
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
 def test_create_without_a_device_reports_no_device():
     with pytest.raises(qp.QkvPrepError) as e:
