@@ -119,6 +119,50 @@ def test_both_sides_of_the_launch_thresholds(T, H):
     check(W.custom(T, H, seed=330 + T + H, num_skip=5))
 
 
+def _random_cases(n, seed):
+    """n seeded configurations that mix every knob at once: ragged token and
+    head counts (up to 2^18 q rows), block sizes, table lengths, skipped
+    slots, outlier rows, eps, a weightless q, both cache modes, and every
+    forced launch setting (0 = the heuristic)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        T = int(rng.integers(1, 4) if len(cases) < 3 else rng.integers(1, 6001))
+        H = int(rng.integers(1, 161))
+        if T * H > 1 << 18:
+            continue
+        cases.append(dict(
+            T=T, H=H, seed=int(rng.integers(1 << 30)),
+            block_size=int(rng.choice([1, 3, 16, 64, 100, 256])),
+            max_position=int(rng.choice([1, 7, 4096, 200000])),
+            num_skip=int(rng.integers(0, min(T, 9) + 1)),
+            outlier_frac=float(rng.choice([0.0, 0.01])),
+            eps=float(rng.choice([0.0, 1e-6, 1e-2])),
+            q_weight=bool(rng.integers(2)),
+            kv_store=int(rng.integers(2)),
+            rows_per_wave=int(rng.choice([0, 1, 2, 4])),
+            waves_per_block=int(rng.choice([0, 1, 2, 4, 8])),
+            kv_per_wave=int(rng.choice([0, 1, 2, 4])),
+            convert=int(rng.integers(3))))
+    return cases
+
+
+RANDOM_CASES = _random_cases(24, 20261202)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=["%dx%d" % (c["T"], c["H"]) for c in RANDOM_CASES])
+def test_seeded_random_configurations(case):
+    c = dict(case)
+    w = W.custom(c.pop("T"), c.pop("H"), seed=c.pop("seed"), max_position=c.pop("max_position"),
+                 block_size=c.pop("block_size"), num_skip=c.pop("num_skip"),
+                 outlier_frac=c.pop("outlier_frac"), eps=c.pop("eps"))
+    note("case %s %s" % (w.label, case))
+    inp = W.make_inputs(w, device=DEV)
+    res = run_and_compare(w, inp, **c)
+    note("  -> %s" % res)
+    assert_bit_exact(res)
+
+
 @pytest.mark.parametrize("rpw", [0, 1])
 def test_exponent_clamp_and_subnormal_outputs(rpw):
     # Tiny weights: every kv block sits at the exponent clamp (scale byte 0)
