@@ -305,7 +305,8 @@ class Launch:
     It keeps references to the tensors and to the owning object, so the
     pointers it holds stay valid while it lives; the tensors must not be
     resized or re-strided in place meanwhile.  The stream is fixed when the
-    launch is prepared."""
+    launch is prepared, so a launch meant for a HIP graph is prepared inside
+    the capture (where the current stream is the capturing one)."""
 
     __slots__ = ("_fn", "_cargs", "_what", "_keep")
 

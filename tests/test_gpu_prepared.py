@@ -126,3 +126,35 @@ def test_prepared_mxfp8_matches_wrapper(m, hidden, residual):
     assert torch.equal(scales_p, scales_d)
     if residual:
         assert torch.equal(ro_p.view(torch.int16), ro_d.view(torch.int16))
+
+
+def test_prepared_op_captured_in_a_graph():
+    """A launch prepared inside the capture runs on the capturing stream; the
+    graph (two launches) replays to the bytes of two direct calls, four times,
+    with eager work and synchronizations between replays."""
+    print("prepared op in a graph", flush=True)
+    w, q0, rest, cache0 = _op_case(300, 16, 990)
+    op = qp.QkvPrep(16, block_size=w.block_size, eps=w.eps)
+    q_d, c_d = q0.clone(), cache0.clone()
+    op(q_d, *rest, c_d)
+    op(q_d, *rest, c_d)
+    q_g, c_g = q0.clone(), cache0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        op(q_g, *rest, c_g)                      # warm-up launch outside the graph
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch = op.prepare(q_g, *rest, c_g)
+        launch()
+        launch()
+    for _ in range(4):
+        q_g.copy_(q0)
+        c_g.copy_(cache0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q_g.view(torch.int16), q_d.view(torch.int16))
+        assert torch.equal(c_g, c_d)
