@@ -4,8 +4,11 @@
  * heads, 16-slot blocks, skipped and out-of-range slots, a poisoned cache) and
  * compares q, the whole cache and the gathered rows with the oracle's C
  * entry points (test infrastructure, compiled into this test program) byte
- * for byte.  Exit status 0 = bit-exact; the last line printed says which part
- * differed otherwise. */
+ * for byte.  Then it captures the same two calls into a HIP graph on a stream
+ * of its own and replays the graph three times over freshly uploaded inputs,
+ * each replay compared the same way: the calls allocate nothing and issue no
+ * memset, so a C caller can capture them.  Exit status 0 = bit-exact; the
+ * last line printed says which part differed otherwise. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -49,6 +52,25 @@ static uint16_t rand_bf16(void)
             return 2;                                                                    \
         }                                                                                \
     } while (0)
+
+/* Nonzero (after printing which part) when a result differs from the oracle. */
+static int compare(const char *what, const void *q_out, const void *q_ref, size_t qn, const void *cache_out,
+                   const void *cache_ref, size_t cn, const void *rows, const void *rows_ref, size_t rn)
+{
+    if (memcmp(q_out, q_ref, qn) != 0) {
+        printf("c consumer (%s): q differs from the oracle\n", what);
+        return 1;
+    }
+    if (memcmp(cache_out, cache_ref, cn) != 0) {
+        printf("c consumer (%s): cache differs from the oracle\n", what);
+        return 1;
+    }
+    if (memcmp(rows, rows_ref, rn) != 0) {
+        printf("c consumer (%s): gathered rows differ from the oracle\n", what);
+        return 1;
+    }
+    return 0;
+}
 
 int main(void)
 {
@@ -148,9 +170,6 @@ int main(void)
     CHECK_HIP(hipMemcpy(q_out, dq, qn, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(cache_out, dcache, cn, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(rows, drows, sizeof(rows), hipMemcpyDeviceToHost));
-    qkv_prep_destroy(h);
-    hipFree(dq); hipFree(dkv); hipFree(dqw); hipFree(dkvw); hipFree(dpos);
-    hipFree(dcs); hipFree(dslots); hipFree(dcache); hipFree(drows);
 
     memcpy(cache_ref, cache, cn);
     if (orc_qkv_prep(T, H, q, q_ref, kv, qw, kvw, pos, cs, P, slots, cache_ref, NB, B, 1e-6f, 1) != 0) {
@@ -158,18 +177,43 @@ int main(void)
         return 2;
     }
     orc_gather_dequant(cache_ref, NB, B, slots, T + 2, rows_ref);
-    if (memcmp(q_out, q_ref, qn) != 0) {
-        printf("c consumer: q differs from the oracle\n");
+    if (compare("eager", q_out, q_ref, qn, cache_out, cache_ref, cn, rows, rows_ref, sizeof(rows)))
         return 1;
+
+    /* The same two calls captured into a graph, replayed over fresh inputs. */
+    hipStream_t st;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+    CHECK_HIP(hipStreamCreate(&st));
+    CHECK_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeGlobal));
+    const int rc_run = qkv_prep_run(h, &a, st);
+    const int rc_gather = qkv_prep_gather(h, &g, st);
+    CHECK_HIP(hipStreamEndCapture(st, &graph));
+    if (rc_run != QKV_PREP_OK || rc_gather != QKV_PREP_OK) {
+        printf("capture: %s / %s\n", qkv_prep_strerror(rc_run), qkv_prep_strerror(rc_gather));
+        return 2;
     }
-    if (memcmp(cache_out, cache_ref, cn) != 0) {
-        printf("c consumer: cache differs from the oracle\n");
-        return 1;
+    CHECK_HIP(hipGraphInstantiate(&exec, graph, NULL, NULL, 0));
+    for (i = 0; i < 3; ++i) {
+        CHECK_HIP(hipMemcpy(dq, q, qn, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(dcache, cache, cn, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemset(drows, 0x7f, sizeof(rows)));
+        CHECK_HIP(hipDeviceSynchronize());
+        CHECK_HIP(hipGraphLaunch(exec, st));
+        CHECK_HIP(hipStreamSynchronize(st));
+        CHECK_HIP(hipMemcpy(q_out, dq, qn, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(cache_out, dcache, cn, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(rows, drows, sizeof(rows), hipMemcpyDeviceToHost));
+        if (compare("graph replay", q_out, q_ref, qn, cache_out, cache_ref, cn, rows, rows_ref, sizeof(rows)))
+            return 1;
     }
-    if (memcmp(rows, rows_ref, sizeof(rows)) != 0) {
-        printf("c consumer: gathered rows differ from the oracle\n");
-        return 1;
-    }
-    printf("c consumer: q, cache and gathered rows bit-exact (%d tokens x %d heads)\n", T, H);
+    CHECK_HIP(hipGraphExecDestroy(exec));
+    CHECK_HIP(hipGraphDestroy(graph));
+    CHECK_HIP(hipStreamDestroy(st));
+    qkv_prep_destroy(h);
+    hipFree(dq); hipFree(dkv); hipFree(dqw); hipFree(dkvw); hipFree(dpos);
+    hipFree(dcs); hipFree(dslots); hipFree(dcache); hipFree(drows);
+    printf("c consumer: q, cache and gathered rows bit-exact, eager and 3 graph replays (%d tokens x %d heads)\n",
+           T, H);
     return 0;
 }

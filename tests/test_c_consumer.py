@@ -2,7 +2,8 @@
 (C11; the public header and the HIP runtime's C API only) is compiled with gcc
 and linked against libqkv_prep.so and the oracle's source.  On the CPU the
 test checks that it builds without warnings; on the GPU it runs and must report
-q, the cache and the gathered rows bit-exact against the oracle."""
+q, the cache and the gathered rows bit-exact against the oracle, eagerly and
+over three replays of a HIP graph captured from C."""
 import os
 import shutil
 import subprocess
