@@ -441,19 +441,22 @@ def cpu_baseline(torch, W, names):
 # ----------------------------------------------------------------- profile mode
 
 def profile_run(torch, qp, probe, name, launches, copy_bytes=512 << 20, copies=3):
-    """A short program for rocprofv3: a few launches of one target (the
-    operator on a workload, or a neighbouring path), then a few launches of the
-    probe library's streaming copy over a buffer of known size (its
-    FETCH_SIZE/WRITE_SIZE calibrate the counters against bytes that are known
-    exactly)."""
+    """A short program for rocprofv3: half a second of sustained streaming
+    (the probe's in-place update, so the launches that follow run in the
+    chip's warm power state, as the bench's do), then `launches` back-to-back
+    launches of one target (the operator on a workload, or a neighbouring
+    path), then a few launches of the probe library's streaming copy over a
+    buffer of known size (its FETCH_SIZE/WRITE_SIZE calibrate the counters
+    against bytes that are known exactly)."""
     from fp8_kv_cache_amd import variants as V
     t = V.target(name)
     fn = V.setup(t, torch, qp)
     torch.cuda.synchronize()
-    for i in range(launches):
+    warm_chip(torch, probe)
+    for _ in range(launches):
         fn()
-        torch.cuda.synchronize()
-        log("profile: %s launch %d done" % (t.label, i))
+    torch.cuda.synchronize()
+    log("profile: %s, %d launches done" % (t.label, launches))
     del fn
     torch.cuda.empty_cache()
     src = torch.ones(copy_bytes, dtype=torch.uint8, device="cuda")
