@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -18,7 +19,10 @@ struct qkv_prep {
     int device;
     int num_cus;
     bool sync;  // QKV_PREP_SYNC=1: wait for the stream inside run
-    bool log;   // QKV_PREP_LOG=1: print each launch shape to stderr
+    bool log;   // QKV_PREP_LOG=1: print a launch shape to stderr when it changes
+    // The last launch shape printed (a packed key; ~0 = none yet).  Atomic so
+    // that concurrent calls on one handle stay safe.
+    std::atomic<uint64_t> logged{~0ull};
 };
 
 namespace {
@@ -294,10 +298,16 @@ int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
     DeviceScope dev(h->device);
     if (!dev.ok())
         return QKV_PREP_ERR_NO_DEVICE;
-    if (h->log)
-        std::fprintf(stderr, "qkv_prep: T=%lld H=%lld rows/wave=%d kv/wave=%d waves/block=%d convert=%d grid=%lld+%lld\n",
-                     (long long)T, (long long)H, s.rows_per_wave, s.kv_per_wave, s.waves_per_block, s.convert,
-                     (long long)s.kv_blocks, (long long)s.q_blocks);
+    if (h->log) {
+        const uint64_t key = (uint64_t)s.rows_per_wave | (uint64_t)s.kv_per_wave << 8 |
+                             (uint64_t)s.waves_per_block << 16 | (uint64_t)s.convert << 24;
+        if (h->logged.exchange(key, std::memory_order_relaxed) != key)
+            std::fprintf(stderr,
+                         "qkv_prep: launch shape rows/wave=%d kv/wave=%d waves/block=%d convert=%d "
+                         "(first at T=%lld H=%lld, grid %lld+%lld workgroups)\n",
+                         s.rows_per_wave, s.kv_per_wave, s.waves_per_block, s.convert, (long long)T,
+                         (long long)H, (long long)s.kv_blocks, (long long)s.q_blocks);
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     return finish(h, qkvp::launch_qkv_prep(k, s, st), st);
 }

@@ -172,9 +172,12 @@ int qkv_prep_create(const qkv_prep_config *cfg, int device, qkv_prep_t *out);
  * out-of-range position is clamped into the table, so memory stays in bounds,
  * but that token's output is unspecified), distinct valid slots, finite
  * inputs.  With QKV_PREP_SYNC=1 in the environment the call also waits for
- * the stream and reports a device error as QKV_PREP_ERR_DEVICE.
- * The handle is read only here, so concurrent calls on different streams
- * are safe.  The call allocates no device memory and enqueues nothing but
+ * the stream and reports a device error as QKV_PREP_ERR_DEVICE.  With
+ * QKV_PREP_LOG=1 the handle prints its launch shape to stderr whenever it
+ * differs from the last one it printed (once per shape in a steady run).
+ * Both variables are read by qkv_prep_create.
+ * The handle's configuration is read only here (the log's last-shape record
+ * is atomic), so concurrent calls on different streams are safe.  The call allocates no device memory and enqueues nothing but
  * the one kernel (no memset, no copy), so it can be captured in a HIP graph.
  *
  * Numerics (all fp32, each step rounded to nearest even):
