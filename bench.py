@@ -140,6 +140,29 @@ def time_each(torch, fn, reps):
     return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in events]
 
 
+def time_graph(torch, launch, per_graph=100, replays=5):
+    """Mean time per launch with the host out of the loop: `per_graph`
+    launches captured in one HIP graph (each a prepared call on the capturing
+    stream), the graph replayed `replays` times between two HIP events on
+    torch's current stream, after one untimed replay."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = launch.on_stream(torch.cuda.current_stream().cuda_stream)
+        for _ in range(per_graph):
+            captured()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e-3 / (per_graph * replays)
+
+
 def time_cold(torch, fn, reps, scratch):
     """Per-launch HIP-event durations with L2 and the MALL flushed before each
     launch: a 1 GiB scratch write, on the same stream and outside the events."""
@@ -273,7 +296,9 @@ def bench_configs(torch, qp, names, warmup):
     min and p90) over as many launches, 200 for the small workloads (Tiny,
     Decode-like) and 30 for the large ones, and the median of 10 launches with
     L2 and the MALL flushed first.  For short kernels the two events around
-    each launch add a microsecond or two, which the region does not pay."""
+    each launch add a microsecond or two, which the region does not pay.  The
+    small workloads also get a graph-replay mean (100 launches per graph), the
+    launch-bound loop with the host taken out."""
     from fp8_kv_cache_amd import probe
     from fp8_kv_cache_amd import variants as V
     out = {}
@@ -289,6 +314,7 @@ def bench_configs(torch, qp, names, warmup):
         _, region = time_region(torch, fn, reps)
         ks = time_each(torch, fn, reps)
         cold = time_cold(torch, fn, 10, scratch)
+        graph = time_graph(torch, fn) if reps == 200 else None
         del fn
         torch.cuda.empty_cache()
         med = statistics.median(ks)
@@ -298,7 +324,8 @@ def bench_configs(torch, qp, names, warmup):
                         "kernel_us": {"region_mean": round(region / reps * 1e6, 2),
                                       "median": round(med * 1e6, 2), "min": round(min(ks) * 1e6, 2),
                                       "p90": round(p90(ks) * 1e6, 2),
-                                      "median_cold": round(statistics.median(cold) * 1e6, 2)},
+                                      "median_cold": round(statistics.median(cold) * 1e6, 2),
+                                      "graph_replay_mean": None if graph is None else round(graph * 1e6, 2)},
                         "bytes_per_launch": t.alg_bytes, "traffic": prof["traffic"],
                         "waves_per_cu": prof["waves_per_cu"]}
     del scratch

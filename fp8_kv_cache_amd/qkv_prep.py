@@ -321,6 +321,11 @@ class Launch:
         if rc != OK:
             raise QkvPrepError(rc, self._what)
 
+    def on_stream(self, stream) -> "Launch":
+        """The same launch on another stream (the stream is the C call's last
+        argument), e.g. on the capturing stream inside a HIP graph capture."""
+        return type(self)(self._fn, self._cargs[:-1] + (stream,), self._what, self._keep)
+
 
 class _MxLaunch(Launch):
     __slots__ = ()

@@ -285,6 +285,10 @@ def test_prepared_launch_reports_the_c_code_and_keeps_its_arguments_alive():
     ok()
     ok()
     assert calls == [(1, 2, 3), (1, 2, 3)]
+    # on_stream replaces only the last argument (the stream)
+    moved = ok.on_stream(9)
+    moved()
+    assert calls[-1] == (1, 2, 9) and type(moved) is qp.Launch
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")

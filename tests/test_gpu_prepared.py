@@ -158,3 +158,29 @@ def test_prepared_op_captured_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(q_g.view(torch.int16), q_d.view(torch.int16))
         assert torch.equal(c_g, c_d)
+
+
+def test_launch_moved_onto_the_capturing_stream():
+    """A launch prepared outside a capture, moved with on_stream onto the
+    capturing stream, records into the graph; replays equal the direct call."""
+    print("prepared gather moved into a graph", flush=True)
+    nb, bs = 24, 64
+    gen = torch.Generator(device=DEV).manual_seed(995)
+    cache = torch.randint(0, 256, (nb, bs * qp.SLOT_BYTES), dtype=torch.uint8, device=DEV, generator=gen)
+    slots = torch.randperm(nb * bs, device=DEV, generator=gen).to(torch.int64)
+    op = qp.QkvPrep(64, block_size=bs)
+    want = torch.empty((slots.numel(), 512), dtype=torch.float32, device=DEV)
+    op.gather(cache, slots, want)
+    out = torch.empty_like(want)
+    launch = op.prepare_gather(cache, slots, out)
+    launch()                                   # warm-up outside the graph
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch.on_stream(torch.cuda.current_stream().cuda_stream)()
+    for k in range(4):
+        out.fill_(float(k))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), want.view(torch.int32))
