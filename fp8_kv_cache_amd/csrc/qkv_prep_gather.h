@@ -15,7 +15,7 @@ struct GatherArgs {
     uint32_t block_size;
     FastDiv blocks;
     int32_t out_bf16;          // 0: fp32 rows, 1: bf16 rows
-    uint32_t xcd_chunk;        // rows per XCD chunk (0: workgroup b takes row b)
+    uint32_t xcd_chunk;        // consecutive workgroups per XCD chunk (0: plain order)
 };
 
 // Enqueue the cache reader: one wavefront per fp32 row or per two bf16 rows,

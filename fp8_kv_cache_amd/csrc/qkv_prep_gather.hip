@@ -126,9 +126,10 @@ __device__ __forceinline__ void gather_row_f32(const GatherArgs &a, int64_t i, u
 // own L2.  Rows next to each other in the slot list usually read neighbouring
 // slots (a block-table walk reads a block's slots in order), which share cache
 // lines: 8 scale records per 64-byte segment, and the 128-byte line where one
-// slot's data ends and the next begins.  So workgroup b takes a row such that
-// every XCD gets `chunk` consecutive rows out of each window of 8 * chunk
-// (a bijection of [0, grid) when grid is a multiple of 8 * chunk).
+// slot's data ends and the next begins.  So workgroup b takes the rows of
+// workgroup slot xcd_row_block(b, chunk): every XCD gets `chunk` consecutive
+// workgroups' rows out of each window of 8 * chunk (a bijection of [0, grid)
+// when grid is a multiple of 8 * chunk).
 __device__ __forceinline__ uint32_t xcd_row_block(uint32_t b, uint32_t chunk)
 {
     if (chunk == 0)

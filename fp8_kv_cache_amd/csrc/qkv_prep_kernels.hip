@@ -14,13 +14,13 @@
 //    Measured on MI355X, this shape streams at the copy ceiling at every
 //    footprint (~6.5 TB/s with non-temporal stores), while shapes with several
 //    loads per lane in flight (4 rows per wave, or several rows per wave) lose
-//    6-15% once the footprint passes a few GiB.  One-wavefront workgroups (the measured optimum), non-temporal
-//    loads.
-//  * Stores: with one row per wavefront (the large-batch shape) every store
-//    carries the non-temporal system-scope policy (nt sc1), 1-2.5% faster than
-//    plain non-temporal stores from 32768x64 up (about 2% at 32768x128 and
-//    131072x128).  The decode-sized shape keeps plain non-temporal stores:
-//    there nt sc1 was ~2% slower (a footprint near the size of the MALL).
+//    6-15% once the footprint passes a few GiB.  Workgroups of one wavefront
+//    (the measured optimum); non-temporal loads.
+//  * Stores: with one row per wavefront every store carries the non-temporal
+//    system-scope policy (nt sc1), 1-2.5% faster than plain non-temporal
+//    stores from 32768x64 up (about 2% at 32768x128 and 131072x128).  The
+//    two-heads shape of small batches keeps plain non-temporal stores: there
+//    nt sc1 was ~2% slower (a footprint near the size of the MALL).
 //  * The sum of squares follows the fixed order of the numerics contract: each
 //    chunk sequentially, then adjacent chunk pairs.  Levels 1-4 are DPP adds
 //    inside a 16-lane row (quad_perm xor1, xor2, row_half_mirror, row_mirror);
