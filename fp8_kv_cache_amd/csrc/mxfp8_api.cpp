@@ -47,7 +47,8 @@ extern "C" int qkv_prep_mxfp8_norm_quant(const qkv_prep_mxfp8_args *a, int devic
     if (a->m > kMaxRows)
         return QKV_PREP_ERR_UNSUPPORTED;
     const int64_t rows_padded = (a->m + 127) / 128 * 128;
-    if (rows_padded * a->hidden / 8 >= ((int64_t)1 << 32))     // 16-byte chunk indices are 32-bit
+    // One workgroup per padded row; the dispatch counts work-items in 32 bits.
+    if (rows_padded * qkvp::mx_threads_per_row(a->hidden) >= ((int64_t)1 << 32))
         return QKV_PREP_ERR_UNSUPPORTED;
     qkvp::MxArgs k;
     k.x = static_cast<const uint16_t *>(a->x);

@@ -28,6 +28,28 @@ struct MxArgs {
 // Rows of up to kMxMaxGroups groups of 512 values (hidden <= 16384).
 constexpr int kMxMaxGroups = 32;
 
+// Groups of 64 chunks per wavefront for a row of K groups.  Measured on
+// MI355X at hidden 1024-8192 (two interleaved rounds): two groups per
+// wavefront (K/2 wavefronts per row) is the fastest or tied everywhere; one
+// group per wavefront is within 2%; one wavefront per row loses up to 60% at
+// large K (VGPR pressure).  Odd K up to 15 uses one group per wavefront; an
+// odd K above 16 is launched as K + 1 groups (the last one empty, which adds
+// zeros to the sum) so that a workgroup stays within 16 wavefronts.
+constexpr int mx_groups_per_wave(int K) { return K % 2 == 0 ? 2 : 1; }
+constexpr bool mx_launchable(int K) { return K <= 16 || K % 2 == 0; }
+
+// The groups a row of `hidden` values is launched with (hidden a positive
+// multiple of 128, at most 512 * kMxMaxGroups), and the workgroup size: one
+// workgroup per row, 64 lanes per wavefront.
+constexpr int mx_launch_groups(int hidden)
+{
+    return mx_launchable((hidden + 511) / 512) ? (hidden + 511) / 512 : (hidden + 511) / 512 + 1;
+}
+constexpr int mx_threads_per_row(int hidden)
+{
+    return 64 * (mx_launch_groups(hidden) / mx_groups_per_wave(mx_launch_groups(hidden)));
+}
+
 // Enqueue the kernel for hidden a multiple of 128, 128 <= hidden <= 512 *
 // kMxMaxGroups (checked by the caller).
 hipError_t launch_mxfp8(const MxArgs &a, hipStream_t stream);

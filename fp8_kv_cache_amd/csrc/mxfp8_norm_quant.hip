@@ -162,23 +162,15 @@ __global__ __launch_bounds__(1024) void mxfp8_kernel(MxArgs a)
     }
 }
 
-// Groups of 64 chunks per wavefront for a row of K groups.  Measured on
-// MI355X at hidden 1024-8192 (two interleaved rounds): two groups per
-// wavefront (K/2 wavefronts per row) is the fastest or tied everywhere; one
-// group per wavefront is within 2%; one wavefront per row loses up to 60% at
-// large K (VGPR pressure).  Odd K up to 15 uses one group per wavefront; an
-// odd K above 16 is launched as K + 1 groups (the last one empty, which adds
-// zeros to the sum) so that a workgroup stays within 16 wavefronts.
-constexpr int groups_per_wave(int K) { return K % 2 == 0 ? 2 : 1; }
-constexpr bool launchable(int K) { return K <= 16 || K % 2 == 0; }
-
+// K groups of 64 chunks per row, mx_groups_per_wave(K) of them per
+// wavefront (mxfp8_launch.h has the choice and its measurements).
 template <int K>
 hipError_t launch_k(const MxArgs &a, hipStream_t st)
 {
-    if constexpr (!launchable(K)) {
+    if constexpr (!mx_launchable(K)) {
         return hipErrorInvalidValue;
     } else {
-        constexpr int G = groups_per_wave(K);
+        constexpr int G = mx_groups_per_wave(K);
         static_assert(K / G <= 16, "at most 1024 lanes per workgroup");
         const dim3 grid((uint32_t)a.rows_padded), block(64u * (K / G));
         const bool partial = a.chunks != K * 64;
@@ -209,10 +201,7 @@ hipError_t launch_table(const MxArgs &a, hipStream_t st, int k, std::integer_seq
 
 hipError_t launch_mxfp8(const MxArgs &a, hipStream_t st)
 {
-    int k = (a.hidden + 511) / 512;
-    if (!launchable(k))
-        k += 1;
-    return launch_table(a, st, k, std::make_integer_sequence<int, kMxMaxGroups>{});
+    return launch_table(a, st, mx_launch_groups(a.hidden), std::make_integer_sequence<int, kMxMaxGroups>{});
 }
 
 }  // namespace qkvp

@@ -138,10 +138,6 @@ __device__ __forceinline__ uint32_t xcd_row_block(uint32_t b, uint32_t chunk)
     return w * win + (r & 7u) * chunk + (r >> 3);
 }
 
-// Rows per wavefront of each output type.
-constexpr int kBf16Rows = 2;
-constexpr int kF32Rows = 1;
-
 template <bool OUT_BF16>
 __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a)
 {
@@ -163,19 +159,9 @@ __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a)
 hipError_t launch_gather(const GatherArgs &a, int waves_per_block, hipStream_t stream)
 {
     GatherArgs g = a;
-    const int rows = a.out_bf16 ? kBf16Rows : kF32Rows;
-    const int64_t waves = (a.n + rows - 1) / rows;
-    int64_t blocks = (waves + waves_per_block - 1) / waves_per_block;
-    // 64 rows per XCD chunk (a cache block's worth of slots at the usual block
-    // size), counted in workgroups of `rows * waves_per_block` rows.  Measured
-    // on MI355X over a 262144-slot block-table walk: fp32 rows 6.5 -> 7.1 TB/s,
-    // bf16 rows 6.0 -> 6.3 TB/s; every slot in a random order: +2.5%.  Small
-    // grids keep the plain order (the padding would cost more).
-    const int64_t rows_per_block = (int64_t)rows * waves_per_block;
-    g.xcd_chunk = blocks * rows_per_block >= 4096 ? (uint32_t)(64 / rows_per_block) : 0u;
-    if (g.xcd_chunk)
-        blocks = (blocks + 8 * g.xcd_chunk - 1) / (8 * g.xcd_chunk) * (8 * g.xcd_chunk);
-    const dim3 grid((uint32_t)blocks), block(64u * (uint32_t)waves_per_block);
+    const GatherGrid gg = gather_grid(a.n, a.out_bf16 != 0, waves_per_block);
+    g.xcd_chunk = gg.xcd_chunk;
+    const dim3 grid((uint32_t)gg.blocks), block(64u * (uint32_t)waves_per_block);
     if (a.out_bf16)
         hipLaunchKernelGGL(gather_kernel<true>, grid, block, 0, stream, g);
     else

@@ -58,8 +58,10 @@ int64_t qkv_prep_mxfp8_scale_bytes(int64_t m, int32_t hidden);
  * handle's device.  Return codes are those of qkv_prep.h:
  * QKV_PREP_ERR_INVALID_ARG (NULL pointer, negative m, bad eps),
  * QKV_PREP_ERR_MISALIGNED, QKV_PREP_ERR_UNSUPPORTED (hidden not a multiple of
- * 128 or above 16384, m > 2^31 - 128, or round_up(m, 128) * hidden >= 2^35:
- * the dispatch indexes rows and 16-byte chunks in 32 bits),
+ * 128 or above 16384, m > 2^31 - 128, or round_up(m, 128) * W >= 2^32: one
+ * workgroup of W lanes per padded row, and the dispatch counts work-items in
+ * 32 bits; W = 64 * ceil(hidden / 512) when that count K is odd and at most
+ * 15, 32 * K when K is even, 32 * (K + 1) when K is odd and above 16),
  * QKV_PREP_ERR_NO_DEVICE (no such device), QKV_PREP_ERR_LAUNCH, and, with
  * QKV_PREP_SYNC=1 in the environment (the call then waits for the stream),
  * QKV_PREP_ERR_DEVICE for an asynchronous device error.

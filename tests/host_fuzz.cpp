@@ -296,6 +296,13 @@ int main()
             if (glaunched) {
                 ++gathers_ok;
                 expect(last_g.n == g.n && g.n < ((int64_t)1 << 26), "gather rows", i);
+                for (int wpb : {1, 2, 4, 8})
+                    for (int bf : {0, 1}) {
+                        const qkvp::GatherGrid gg = qkvp::gather_grid(g.n, bf != 0, wpb);
+                        const int rows = bf ? qkvp::kBf16Rows : qkvp::kF32Rows;
+                        expect(gg.blocks * 64 * wpb < ((int64_t)1 << 32), "gather grid fits", i);
+                        expect(gg.blocks * wpb * rows >= g.n, "gather grid covers every row", i);
+                    }
                 expect(last_g.num_slots == g.num_blocks * c.block_size && last_g.num_slots < ((int64_t)1 << 31),
                        "gather slots", i);
                 expect(last_g.out_bf16 == (g.out_dtype == QKV_PREP_OUT_BF16), "gather dtype", i);
@@ -350,12 +357,46 @@ int main()
             expect(k.chunks == hidden / 8, "chunks", i);
             expect((reinterpret_cast<uintptr_t>(k.scale_out) & 3) == 0, "scale words aligned", i);
             expect(k.rows_padded == (m + 127) / 128 * 128 && k.rows_padded < ((int64_t)1 << 31), "rows", i);
-            expect(k.rows_padded * hidden / 8 < ((int64_t)1 << 32), "chunk indices fit", i);
+            expect(k.rows_padded * qkvp::mx_threads_per_row(hidden) < ((int64_t)1 << 32), "grid fits", i);
             expect(k.padded_cols == hidden / 32 && (int64_t)k.rows_padded * k.padded_cols == sb, "scale layout", i);
             expect(std::isfinite(k.eps) && k.eps >= 0.0f, "eps", i);
         }
     }
     expect(qkv_prep_mxfp8_norm_quant(nullptr, 0, nullptr) == QKV_PREP_ERR_INVALID_ARG, "mxfp8 NULL", 0);
+
+    // The work-item limit at its edge, for workgroups of 64 (hidden 128),
+    // 192 (hidden 1152: three groups, one per wavefront) and 1024 lanes
+    // (hidden 16384): the largest padded row count that fits launches, one
+    // more tile is refused.
+    {
+        static const struct { int32_t hidden; int64_t lanes; } edges[] = {{128, 64}, {1152, 192}, {16384, 1024}};
+        for (const auto &e : edges) {
+            expect(qkvp::mx_threads_per_row(e.hidden) == e.lanes, "workgroup size", e.hidden);
+            const int64_t max_rows = (((int64_t)1 << 32) - 1) / e.lanes / 128 * 128;
+            for (int64_t m : {max_rows, max_rows - 127, max_rows + 1}) {
+                qkv_prep_mxfp8_args a;
+                std::memset(&a, 0, sizeof(a));
+                a.x = a.gamma = reinterpret_cast<const void *>(0x100000);
+                a.quant_out = a.scale_out = reinterpret_cast<void *>(0x200000);
+                a.m = m;
+                a.hidden = e.hidden;
+                a.eps = 1e-6f;
+                const int rc = qkv_prep_mxfp8_norm_quant(&a, 0, nullptr);
+                expect(rc == (m <= max_rows ? QKV_PREP_OK : QKV_PREP_ERR_UNSUPPORTED), "mxfp8 grid edge", m);
+            }
+        }
+    }
+    // The reader's grid at its row limit: the XCD padding would reach 2^32
+    // work-items, so the plain order is kept; a little below it, it pads.
+    {
+        const qkvp::GatherGrid top = qkvp::gather_grid(((int64_t)1 << 26) - 1, false, 1);
+        expect(top.xcd_chunk == 0 && top.blocks == ((int64_t)1 << 26) - 1, "reader grid at the limit", 0);
+        const qkvp::GatherGrid below = qkvp::gather_grid(((int64_t)1 << 26) - 512, false, 1);
+        expect(below.xcd_chunk == 64 && below.blocks == ((int64_t)1 << 26) - 512, "reader grid below the limit", 0);
+        const qkvp::GatherGrid bf = qkvp::gather_grid(((int64_t)1 << 26) - 1, true, 1);
+        expect(bf.xcd_chunk == 32 && bf.blocks * 2 >= ((int64_t)1 << 26) - 1 && bf.blocks * 64 < ((int64_t)1 << 32),
+               "bf16 reader grid at the limit", 0);
+    }
 
     std::printf("cases %lld, valid argument sets %lld, launch shapes %lld, runs launched %lld, gathers launched "
                 "%lld, mxfp8 launched %lld, contract failures %d\n", cases, ok_validate, ok_shape, runs_ok,

@@ -361,6 +361,13 @@ def test_mxfp8_scale_bytes_and_argument_checks():
     assert code(residual=(5 << 20) + 4) == qp.ERR_MISALIGNED
     assert code(residual_out=(6 << 20) + 8) == qp.ERR_MISALIGNED
     assert code(m=1 << 26) == qp.ERR_UNSUPPORTED
+    # The grid limit: round_up(m, 128) workgroups of W lanes must stay below
+    # 2^32 work-items (W = 64 at hidden 128, 192 at 1152, 1024 at 16384).
+    # Sizes that fit reach the device check (device -1: nothing is launched).
+    for hidden, lanes in ((128, 64), (1152, 192), (16384, 1024)):
+        top = (2 ** 32 - 1) // lanes // 128 * 128
+        assert code(hidden=hidden, m=top, device=-1) == qp.ERR_NO_DEVICE
+        assert code(hidden=hidden, m=top + 1) == qp.ERR_UNSUPPORTED
     # Good arguments on a device that does not exist: rejected before any launch.
     assert code(device=-1) == qp.ERR_NO_DEVICE
     assert code(device=1 << 20) == qp.ERR_NO_DEVICE
