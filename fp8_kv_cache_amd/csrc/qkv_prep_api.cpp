@@ -55,9 +55,12 @@ int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)
 //    wavefront, with system-scope stores: 1-6% faster from 2^16 q rows with
 //    32 heads or more, or with fewer tokens (2048x64: 41.7 against 42.5 us;
 //    4096x16: 23.0 against 24.3).  Below 2^16 rows the shapes are within ~2%
-//    of each other and two heads stay.  Four heads per wavefront never win;
-//    they are used only when fewer wavefronts would need 2^32 or more
-//    work-items in the dispatch.
+//    of each other and two heads stay.  Four heads per wavefront never win.
+//    A grid past what one dispatch takes (2^32 work-items, from about 2^26 q
+//    rows) is split into consecutive dispatches rather than narrowed to more
+//    heads per wavefront: at 600000x128 one row per wavefront over two
+//    dispatches keeps the large-batch rate, where two heads per wavefront
+//    ran at 6.30 TB/s (and four, at 1100000x128, at 6.16).
 //  * kv_per_wave: four consecutive tokens' kv rows per kv wavefront, their
 //    loads issued together, from 2^16 q rows (the kv wavefronts run first, as
 //    a latency-bound burst; 2048x32: 22.3 against 23.3 us); one below, where
@@ -75,20 +78,15 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     s.convert = c.convert ? c.convert : 2;
     s.kv_per_wave = c.kv_per_wave ? c.kv_per_wave : (q_rows >= ((int64_t)1 << 16) ? 4 : 1);
     s.kv_blocks = ceil_div(T, (int64_t)s.kv_per_wave * s.waves_per_block);
-    // q wavefronts: T * ceil(H / U) (U heads of one token per wavefront)
-    auto q_waves = [&](int u) { return T * ceil_div(c.num_heads, u); };
     if (c.rows_per_wave) {
         s.rows_per_wave = c.rows_per_wave;
     } else {
         const bool few_rows = q_rows < ((int64_t)1 << 16);
         const bool many_tokens_few_heads = c.num_heads <= 16 && T >= ((int64_t)1 << 14);
         s.rows_per_wave = (few_rows || many_tokens_few_heads) && c.num_heads > 1 ? 2 : 1;
-        while (s.rows_per_wave < 4 &&
-               (s.kv_blocks + ceil_div(q_waves(s.rows_per_wave), s.waves_per_block)) * 64 *
-                       s.waves_per_block >= ((int64_t)1 << 32))
-            s.rows_per_wave *= 2;
     }
-    s.q_blocks = ceil_div(q_waves(s.rows_per_wave), s.waves_per_block);
+    // q wavefronts: T * ceil(H / U) (U heads of one token per wavefront)
+    s.q_blocks = ceil_div(T * ceil_div(c.num_heads, s.rows_per_wave), s.waves_per_block);
     return s;
 }
 
@@ -123,7 +121,7 @@ int check_config(const qkv_prep_config *cfg)
 }
 
 // Everything qkv_prep_run checks before it touches the device.
-int check_args(const qkv_prep_config &c, int num_cus, const qkv_prep_args *a)
+int check_args(const qkv_prep_config &c, const qkv_prep_args *a)
 {
     if (!a)
         return QKV_PREP_ERR_INVALID_ARG;
@@ -145,11 +143,7 @@ int check_args(const qkv_prep_config &c, int num_cus, const qkv_prep_args *a)
     if (!rows_fit(c, T) || a->num_blocks > (int64_t)0x7fffffff / B ||
         a->max_position > ((int64_t)1 << 40))
         return QKV_PREP_ERR_UNSUPPORTED;
-    // The dispatch counts work-items in 32 bits.
-    const qkvp::LaunchShape s = choose_shape(c, num_cus, T);
-    if ((s.kv_blocks + s.q_blocks) * 64 * s.waves_per_block >= ((int64_t)1 << 32))
-        return QKV_PREP_ERR_UNSUPPORTED;
-    return QKV_PREP_OK;
+    return QKV_PREP_OK;    // any grid: one past what a dispatch takes is split (launch_qkv_prep)
 }
 
 int check_gather(const qkv_prep_config &c, const qkv_prep_gather_args *a)
@@ -256,14 +250,14 @@ int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t n
 int qkv_prep_validate(const qkv_prep_config *cfg, const qkv_prep_args *args)
 {
     const int rc = check_config(cfg);
-    return rc != QKV_PREP_OK ? rc : check_args(*cfg, 0, args);
+    return rc != QKV_PREP_OK ? rc : check_args(*cfg, args);
 }
 
 int qkv_prep_run(qkv_prep_t h, const qkv_prep_args *a, void *stream)
 {
     if (!h)
         return QKV_PREP_ERR_INVALID_ARG;
-    const int rc_args = check_args(h->cfg, h->num_cus, a);
+    const int rc_args = check_args(h->cfg, a);
     if (rc_args != QKV_PREP_OK || a->num_tokens == 0)
         return rc_args;
     const int64_t T = a->num_tokens;

@@ -29,6 +29,7 @@ struct KernelArgs {
     FastDiv chunk_div;         // divides a q wavefront index by `chunks`
     float eps;
     int32_t bf16_store;        // 1: kv slots are 1024 bytes of bf16, no quantization
+    int64_t block_base;        // workgroup index of this dispatch's first workgroup
 };
 
 // The most consecutive tokens whose kv rows one wavefront takes.
@@ -43,7 +44,24 @@ struct LaunchShape {
     int64_t q_blocks;
 };
 
-// Enqueue the kernel.  Returns the hipError_t of the launch.
+// The most workgroups of `waves_per_block` wavefronts one dispatch takes: the
+// dispatch counts work-items in 32 bits.  A larger grid is enqueued as
+// consecutive dispatches of the same kernel, each covering the next range of
+// workgroup indices (KernelArgs::block_base).
+inline int64_t max_blocks_per_launch(int waves_per_block)
+{
+    return (((int64_t)1 << 32) - 1) / (64 * (int64_t)waves_per_block);
+}
+
+// Dispatches for a grid of `blocks` workgroups.
+inline int64_t launches_for(int64_t blocks, int waves_per_block)
+{
+    const int64_t per = max_blocks_per_launch(waves_per_block);
+    return (blocks + per - 1) / per;
+}
+
+// Enqueue the kernel (launches_for(...) dispatches, in order, on `stream`).
+// Returns the hipError_t of the first launch that fails, else hipSuccess.
 hipError_t launch_qkv_prep(const KernelArgs &a, const LaunchShape &s, hipStream_t stream);
 
 }  // namespace qkvp

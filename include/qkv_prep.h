@@ -135,7 +135,11 @@ typedef struct {
     int32_t kv_per_wave;      /* tokens' kv rows per kv wavefront (1, 2 or 4) */
     int64_t kv_blocks;        /* workgroups that handle kv rows (dispatched first) */
     int64_t q_blocks;         /* workgroups that handle q rows */
-    int64_t grid;             /* kv_blocks + q_blocks */
+    int64_t grid;             /* kv_blocks + q_blocks; a grid of more than
+                                 (2^32 - 1) / (64 * waves_per_block) workgroups
+                                 (a dispatch counts work-items in 32 bits) is
+                                 enqueued as consecutive dispatches of that
+                                 many workgroups, in order */
 } qkv_prep_launch;
 
 /* Arguments of the cache reader (qkv_prep_gather).
@@ -177,8 +181,11 @@ int qkv_prep_create(const qkv_prep_config *cfg, int device, qkv_prep_t *out);
  * differs from the last one it printed (once per shape in a steady run).
  * Both variables are read by qkv_prep_create.
  * The handle's configuration is read only here (the log's last-shape record
- * is atomic), so concurrent calls on different streams are safe.  The call allocates no device memory and enqueues nothing but
- * the one kernel (no memset, no copy), so it can be captured in a HIP graph.
+ * is atomic), so concurrent calls on different streams are safe.  The call
+ * allocates no device memory and enqueues nothing but the kernel (no memset,
+ * no copy; one dispatch, or consecutive dispatches of the same kernel for a
+ * grid past 2^32 work-items, from about 2^26 q rows), so it can be captured
+ * in a HIP graph.
  *
  * Numerics (all fp32, each step rounded to nearest even):
  *   S     = sum of x_j^2: chunk l (8 consecutive dims) summed left to right,

@@ -200,8 +200,8 @@ int main()
         if (rv == QKV_PREP_OK && T > 0) {
             ++ok_validate;
             expect(rs == QKV_PREP_OK, "valid args have a launch shape", i);
-            expect((sh.kv_blocks + sh.q_blocks) * 64 * sh.waves_per_block < ((int64_t)1 << 32),
-                   "dispatch fits 32-bit work-item count", i);
+            expect(sh.grid < ((int64_t)1 << 32) && sh.kv_blocks < ((int64_t)1 << 32),
+                   "workgroup indices fit 32 bits", i);
             expect(T * (int64_t)c.num_heads <= 0x7fffffff, "row indices fit 31 bits", i);
             expect(std::isfinite(c.eps) && c.eps >= 0.0f, "eps finite and >= 0", i);
         }
@@ -263,11 +263,18 @@ int main()
                 expect(k.num_tokens == a.num_tokens && k.q_rows == a.num_tokens * c.num_heads, "sizes", i);
                 expect(k.num_slots == a.num_blocks * c.block_size && k.num_slots < ((int64_t)1 << 31), "slots", i);
                 expect(k.kv_blocks == (uint32_t)last_s.kv_blocks, "kv blocks", i);
-                expect(k.chunks == (uint32_t)((c.num_heads + last_s.rows_per_wave - 1) / last_s.rows_per_wave),
+                expect(k.chunks == (uint32_t)(((int64_t)c.num_heads + last_s.rows_per_wave - 1) / last_s.rows_per_wave),
                        "chunks per token", i);
                 expect((int64_t)k.chunks * a.num_tokens < ((int64_t)1 << 31), "q wavefront index fits", i);
-                expect((last_s.kv_blocks + last_s.q_blocks) * 64 * last_s.waves_per_block < ((int64_t)1 << 32),
-                       "grid fits", i);
+                {
+                    const int64_t grid = last_s.kv_blocks + last_s.q_blocks;
+                    const int64_t per = qkvp::max_blocks_per_launch(last_s.waves_per_block);
+                    const int64_t n = qkvp::launches_for(grid, last_s.waves_per_block);
+                    expect(per * 64 * last_s.waves_per_block < ((int64_t)1 << 32) &&
+                               (per + 1) * 64 * last_s.waves_per_block >= ((int64_t)1 << 32),
+                           "a dispatch holds as many workgroups as fit", i);
+                    expect(n >= 1 && (n - 1) * per < grid && n * per >= grid, "dispatches cover the grid", i);
+                }
                 expect(last_s.q_blocks * last_s.waves_per_block >= a.num_tokens * (int64_t)k.chunks,
                        "every q wavefront has a slot in the grid", i);
                 expect(last_s.kv_blocks * last_s.waves_per_block * last_s.kv_per_wave >= a.num_tokens,

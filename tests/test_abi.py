@@ -188,10 +188,11 @@ def test_launch_shape_heuristic():
     big = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 131072)
     assert big.rows_per_wave == 1 and big.waves_per_block == 1
     assert big.q_blocks == 131072 * 128 and big.kv_blocks == 131072 // 4
-    # a batch whose one-row-per-wavefront grid would pass 2^32 work-items
+    # a batch whose grid passes 2^32 work-items keeps one row per wavefront
+    # (qkv_prep_run splits the grid into consecutive dispatches)
     huge = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 600000)
-    assert huge.rows_per_wave == 2
-    assert (huge.kv_blocks + huge.q_blocks) * 64 * huge.waves_per_block < 2 ** 32
+    assert huge.rows_per_wave == 1 and huge.q_blocks == 600000 * 128
+    assert huge.grid * 64 * huge.waves_per_block >= 2 ** 32
     forced = qp.qkv_prep_launch_shape(qp.make_config(64, rows_per_wave=2, waves_per_block=8,
                                                      convert=1), 256, 1000)
     assert (forced.rows_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)

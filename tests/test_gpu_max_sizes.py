@@ -1,7 +1,8 @@
-"""The largest batches one MI355X holds, at the sizes where the launch
-heuristic's grid-size fallbacks take over: from 2^26 q rows a wavefront per
-row would pass 2^32 work-items, so two heads share a wavefront, and from about
-1.3e8 rows four do.  q alone is 78 GB and 144 GB here.  Every token cannot be
+"""The largest batches one MI355X holds.  From about 2^26 q rows the
+operator's grid passes the 2^32 work-items one dispatch takes, so it is
+enqueued as consecutive dispatches of the same kernel (two at 600000 x 128,
+three at 1100000 x 128), each starting at its own workgroup index.  q alone
+is 79 GB and 144 GB here.  Every token cannot be
 checked on the host at this size, so a seeded sample of tokens (the first, the
 last, skipped ones and random ones) is checked one by one against the oracle:
 each sampled token's q rows bit for bit, and its cache slot byte for byte (the
@@ -26,8 +27,8 @@ def note(msg):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("T,H,rows_per_wave", [(600000, 128, 2), (1100000, 128, 4)])
-def test_largest_batches_on_sampled_tokens(T, H, rows_per_wave):
+@pytest.mark.parametrize("T,H,dispatches", [(600000, 128, 2), (1100000, 128, 3)])
+def test_largest_batches_on_sampled_tokens(T, H, dispatches):
     w = W.custom(T, H, seed=T // 1000 + H, num_skip=7)
     need = T * H * 1024 + T * 1024 + w.num_blocks * w.block_size * qp.SLOT_BYTES + (2 << 30)
     torch.cuda.empty_cache()
@@ -36,8 +37,9 @@ def test_largest_batches_on_sampled_tokens(T, H, rows_per_wave):
         pytest.skip("needs %.0f GB of free device memory, %.0f GB free" % (need / 1e9, free / 1e9))
     op = qp.QkvPrep(H, block_size=w.block_size, eps=w.eps)
     shape = op.launch_shape(T)
-    assert shape.rows_per_wave == rows_per_wave
-    assert (shape.kv_blocks + shape.q_blocks) * 64 < 2 ** 32
+    assert shape.rows_per_wave == 1 and shape.waves_per_block == 1
+    per = (2 ** 32 - 1) // 64                       # workgroups one dispatch takes
+    assert -(-shape.grid // per) == dispatches
     note("case %s: drawing inputs (q %.0f GB), launch %s" % (
         w.label, T * H * 1024 / 1e9, (shape.rows_per_wave, shape.kv_per_wave, shape.grid)))
     inp = W.make_inputs(w, device=DEV)
