@@ -522,14 +522,27 @@ def sweep_workload(W, name, size):
     return W.custom(T, H, seed=11 + T + H, max_position=131072)
 
 
-def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3):
+def parse_shapes(text):
+    """'r:b:k,...' (q rows per wavefront, wavefronts per workgroup, kv tokens
+    per wavefront) -> a list of forced shapes; '' -> None (every shape)."""
+    if not text:
+        return None
+    out = []
+    for item in text.split(","):
+        r, b, k = (int(v) for v in item.split(":"))
+        out.append(dict(rows_per_wave=r, waves_per_block=b, kv_per_wave=k))
+    return out
+
+
+def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3, only=None):
     """Every forced launch shape of the operator on one workload (rows per
     wavefront 1/2/4 x wavefronts per workgroup 1/2/4/8 x kv tokens per
-    wavefront 1/2/4), plus both conversion paths at the heuristic's shape:
-    the region time of `launches` back-to-back launches, best of `rounds`
-    interleaved rounds, with the chip warmed first.  Every shape computes the
-    same bits (the GPU parity tests check each one); this measures only their
-    speed, so the heuristic's choice can be re-checked on any machine."""
+    wavefront 1/2/4), plus both conversion paths at the heuristic's shape, or
+    only the shapes in `only`: the region time of `launches` back-to-back
+    launches, best of `rounds` interleaved rounds, with the chip warmed first.
+    Every shape computes the same bits (the GPU parity tests check each one);
+    this measures only their speed, so the heuristic's choice can be
+    re-checked on any machine."""
     from fp8_kv_cache_amd import probe
     w = sweep_workload(W, name, size)
     name = w.name
@@ -539,10 +552,13 @@ def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3):
     args = (inp["q"], inp["kv"], inp["q_w"], inp["kv_w"], inp["positions"], inp["cos_sin"],
             inp["slot_mapping"], inp["cache"])
     heur = qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps).launch_shape(w.num_tokens)
-    shapes = [dict(rows_per_wave=r, waves_per_block=b, kv_per_wave=k)
-              for r in (1, 2, 4) for b in (1, 2, 4, 8) for k in (1, 2, 4)]
-    shapes += [dict(rows_per_wave=heur.rows_per_wave, waves_per_block=heur.waves_per_block,
-                    kv_per_wave=heur.kv_per_wave, convert=c) for c in (1, 2)]
+    if only is None:
+        shapes = [dict(rows_per_wave=r, waves_per_block=b, kv_per_wave=k)
+                  for r in (1, 2, 4) for b in (1, 2, 4, 8) for k in (1, 2, 4)]
+        shapes += [dict(rows_per_wave=heur.rows_per_wave, waves_per_block=heur.waves_per_block,
+                        kv_per_wave=heur.kv_per_wave, convert=c) for c in (1, 2)]
+    else:
+        shapes = list(only)
     ops = [qp.QkvPrep(w.num_heads, block_size=w.block_size, eps=w.eps, **sh) for sh in shapes]
     launches_of = [op.prepare(*args) for op in ops]
     warm_chip(torch, probe)
@@ -587,6 +603,8 @@ def main():
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--sizes", default="",
                     help="sweep mode: comma-separated TxH sizes (decode-like inputs) instead of --workload")
+    ap.add_argument("--shapes", default="",
+                    help="sweep mode: only these shapes, as rows_per_wave:waves_per_block:kv_per_wave,...")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0 or args.launches < 1:
         ap.error("--steps and --launches must be at least 1, --warmup at least 0")
@@ -609,7 +627,8 @@ def main():
         return
     if args.mode == "sweep":
         for size in (args.sizes.split(",") if args.sizes else [None]):
-            print(json.dumps(sweep_shapes(torch, W, qp, args.workload, size)), flush=True)
+            print(json.dumps(sweep_shapes(torch, W, qp, args.workload, size, only=parse_shapes(args.shapes))),
+                  flush=True)
         return
     kat_before = known_answer_check(torch, W, qp)
     w, main_res, ceil_before = bench_workload(torch, W, qp, probe, args.workload, args.steps, args.warmup,

@@ -72,3 +72,11 @@ def test_host_cpu():
     model, usable = bench.host_cpu()
     assert isinstance(model, str) and model
     assert usable >= 1
+
+
+def test_sweep_shape_list():
+    assert bench.parse_shapes("") is None
+    assert bench.parse_shapes("1:1:4,2:8:1") == [dict(rows_per_wave=1, waves_per_block=1, kv_per_wave=4),
+                                                  dict(rows_per_wave=2, waves_per_block=8, kv_per_wave=1)]
+    with pytest.raises(ValueError):
+        bench.parse_shapes("1:1")
