@@ -117,6 +117,20 @@ def test_gather_empty_and_bad_arguments():
     assert torch.all(out == 0)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gather_from_an_empty_cache_reads_zero_rows(dtype):
+    # num_blocks 0 and no cache at all: every slot is out of range, so every
+    # row reads as zeros and the (absent) cache is never touched.
+    slots = torch.tensor([0, 1, -1, 5, 100, 2 ** 40], dtype=torch.int64, device=DEV)
+    out = torch.full((slots.numel(), 512), 7.0, dtype=dtype, device=DEV)
+    op = qp.QkvPrep(8, block_size=64)
+    args = qp.QkvPrepGatherArgs(None, 0, slots.data_ptr(), slots.numel(), out.data_ptr(),
+                                qp.OUT_F32 if dtype == torch.float32 else qp.OUT_BF16)
+    qp.qkv_prep_gather(op.handle, args, None)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and not torch.any(torch.signbit(out))
+
+
 def _nan_aware_equal(got_bits, want_bits, nan_mask_got, nan_mask_want):
     """Equal bit patterns, except that a NaN may carry any payload."""
     return np.array_equal(nan_mask_got, nan_mask_want) and \
