@@ -9,6 +9,9 @@ import inspect
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
 
 import pytest
 
@@ -176,9 +179,32 @@ def test_unmodified_oracle_passes_the_battery(tmp_path):
     assert first_failure_in_child(build_variant(tmp_path, open(SRC).read())) is None
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_planted_mistake_is_caught(tmp_path, name, old, new):
-    text = open(SRC).read()
-    assert text.count(old) == 1, "mutation site not found exactly once: %s" % name
-    caught = first_failure_in_child(build_variant(tmp_path, text.replace(old, new)))
-    assert caught is not None, "no pin catches: %s" % name
+def _run_mutant(i):
+    """Build mutant i in a directory of its own and run the battery on it."""
+    name, old, new = MUTANTS[i]
+    with tempfile.TemporaryDirectory(prefix="mutant%02d_" % i) as d:
+        return first_failure_in_child(build_variant(Path(d), open(SRC).read().replace(old, new)))
+
+
+_FUTURES = []
+
+
+def _mutant_result(i):
+    """The battery's first failure on mutant i.  Each mutant is a gcc build
+    and a child process, so on the first request every mutant is started, a
+    few at a time, and each test then waits for its own; under pytest-xdist,
+    which already spreads the cases over workers, each case runs alone."""
+    if os.environ.get("PYTEST_XDIST_WORKER"):
+        return _run_mutant(i)
+    if not _FUTURES:
+        pool = ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1)))
+        _FUTURES.extend(pool.submit(_run_mutant, k) for k in range(len(MUTANTS)))
+        pool.shutdown(wait=False)
+    return _FUTURES[i].result()
+
+
+@pytest.mark.parametrize("i", range(len(MUTANTS)), ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(i):
+    name, old, new = MUTANTS[i]
+    assert open(SRC).read().count(old) == 1, "mutation site not found exactly once: %s" % name
+    assert _mutant_result(i) is not None, "no pin catches: %s" % name
