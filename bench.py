@@ -500,8 +500,8 @@ def profile_run(torch, qp, probe, name, launches, copy_bytes=512 << 20, copies=3
 
 def warm_chip(torch, probe, seconds=0.5, nbytes=2 << 30):
     """Sustained in-place streaming for about `seconds`, so that what follows
-    runs in the chip's warm power state (the transient after a lull is
-    described in the design notes)."""
+    runs in the chip's warm power state: after a lull, the first ~15 ms of
+    sustained streaming run up to 25% slow."""
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     t0 = time.perf_counter()
@@ -610,7 +610,8 @@ def main():
         ap.error("--steps and --launches must be at least 1, --warmup at least 0")
     if args.gpus != 1:
         print("bench.py measures one GPU: this operator is per token and needs no collective; "
-              "run with --gpus 1 (see the design notes for how it would shard).", file=sys.stderr)
+              "run with --gpus 1 (over N GPUs each would run this kernel on its own share of the "
+              "tokens, or of the heads with the kv row replicated).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -31,8 +31,7 @@
  * rounded); the file is compiled with -ffp-contract=off so that no product is
  * silently fused into an addition.
  *
- * Readings of points the pages leave open (each is also listed in the design
- * notes):
+ * Readings of points the pages leave open:
  *   R1 sum of squares: chunk l (l = 0..63) of 8 consecutive elements is summed
  *      left to right; the 64 chunk sums are then added pairwise, adjacent
  *      pairs first, in six levels.  [SG] Modifications says the reduction tree
