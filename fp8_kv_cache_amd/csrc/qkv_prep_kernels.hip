@@ -262,9 +262,21 @@ __device__ __forceinline__ void kv_rows(const KernelArgs &a, int64_t t0, uint32_
 {
     int64_t slot[N];
     u32x4 d[N];
+    // All N slot loads are issued before any is used: an index past the batch
+    // is clamped to its last token (in bounds) and masked afterwards.  Loaded
+    // under the per-token conditions instead, the compiler waited for each
+    // slot before issuing the next (four round trips).  Issuing them together
+    // is 0.2% faster at 32768x64 and 0.5-0.8% at 32768x8 and 8192x16, and
+    // 0.3% slower at 2048x64 (41.35 -> 41.46 us), measured on MI355X.
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const int64_t t = t0 + u < a.num_tokens ? t0 + u : a.num_tokens - 1;
+        slot[u] = a.slot_mapping[t];
+    }
 #pragma unroll
     for (int u = 0; u < N; ++u)
-        slot[u] = (uint32_t)u < a.kv_per_wave && t0 + u < a.num_tokens ? a.slot_mapping[t0 + u] : -1;
+        if ((uint32_t)u >= a.kv_per_wave || t0 + u >= a.num_tokens)
+            slot[u] = -1;
 #pragma unroll
     for (int u = 0; u < N; ++u)
         if (slot[u] >= 0 && slot[u] < a.num_slots)
