@@ -63,10 +63,18 @@ int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)
 //    ran at 6.30 TB/s (and four, at 1100000x128, at 6.16).
 //  * kv_per_wave: four consecutive tokens' kv rows per kv wavefront, their
 //    loads issued together, from 2^16 q rows (the kv wavefronts run first, as
-//    a latency-bound burst; 2048x32: 22.3 against 23.3 us); one below, where
-//    four per wavefront lose up to 12% (512x64: 14.1 against 12.6 us).
-//  * waves_per_block: 1.  More wavefronts per workgroup gain at most ~1% at a
-//    few small-head shapes and lose up to 3% on the large ones.
+//    a latency-bound burst; 2048x32: 22.3 against 23.3 us); two from 2^15 q
+//    rows with at least 2048 tokens, where the kv rows are a larger share
+//    (with two wavefronts per workgroup, below: 1.2-5.3% faster at seven
+//    sizes from 2048x24 to 16384x2, in two repeated sweeps); one below, where
+//    more per wavefront lose up to 17% (512x8: 5.42 against 4.68 us).
+//  * waves_per_block: 2 with two heads per wavefront wherever the kv
+//    wavefronts take several tokens (from 2^16 q rows, which with two heads
+//    means many tokens and at most 16 heads: 0.8-2.6% faster than 1 at all
+//    eight sizes from 16384x8 to 65536x16 in two repeated sweeps, 32768x8:
+//    94.3 against 95.9 us; and the mid range above).  Otherwise 1: more
+//    wavefronts per workgroup lose up to 6% with one row per wavefront and up
+//    to 14% for small batches.
 //  * convert: the gfx950 conversion instructions (bit-identical to the integer
 //    rounding, which the tests check on every workload).
 qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
@@ -74,10 +82,10 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     (void)num_cus;
     qkvp::LaunchShape s;
     const int64_t q_rows = T * c.num_heads;
-    s.waves_per_block = c.waves_per_block ? c.waves_per_block : 1;
     s.convert = c.convert ? c.convert : 2;
-    s.kv_per_wave = c.kv_per_wave ? c.kv_per_wave : (q_rows >= ((int64_t)1 << 16) ? 4 : 1);
-    s.kv_blocks = ceil_div(T, (int64_t)s.kv_per_wave * s.waves_per_block);
+    const bool large = q_rows >= ((int64_t)1 << 16);
+    const bool mid = !large && q_rows >= ((int64_t)1 << 15) && T >= 2048;
+    s.kv_per_wave = c.kv_per_wave ? c.kv_per_wave : (large ? 4 : mid ? 2 : 1);
     if (c.rows_per_wave) {
         s.rows_per_wave = c.rows_per_wave;
     } else {
@@ -85,6 +93,11 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
         const bool many_tokens_few_heads = c.num_heads <= 16 && T >= ((int64_t)1 << 14);
         s.rows_per_wave = (few_rows || many_tokens_few_heads) && c.num_heads > 1 ? 2 : 1;
     }
+    if (c.waves_per_block)
+        s.waves_per_block = c.waves_per_block;
+    else
+        s.waves_per_block = s.rows_per_wave == 2 && (large || mid) ? 2 : 1;
+    s.kv_blocks = ceil_div(T, (int64_t)s.kv_per_wave * s.waves_per_block);
     // q wavefronts: T * ceil(H / U) (U heads of one token per wavefront)
     s.q_blocks = ceil_div(T * ceil_div(c.num_heads, s.rows_per_wave), s.waves_per_block);
     return s;

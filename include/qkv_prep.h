@@ -75,7 +75,10 @@ typedef struct {
                                  token per wavefront, one after another (the
                                  heuristic takes 2 below 2^16 q rows and, with
                                  at most 16 heads, from 2^14 tokens; else 1) */
-    int32_t waves_per_block;  /* 0 = launch heuristic; 1, 2, 4 or 8 forces it */
+    int32_t waves_per_block;  /* 0 = launch heuristic; 1, 2, 4 or 8 forces it (the
+                                 heuristic takes 2 with two heads per wavefront
+                                 from 2^16 q rows, and from 2^15 q rows with at
+                                 least 2048 tokens; else 1) */
     int32_t convert;          /* 0 = heuristic, 1 = integer bf16/E4M3 rounding,
                                  2 = gfx950 conversion instructions; both give
                                  the same bits (tests check this) */
@@ -89,7 +92,8 @@ typedef struct {
     int32_t kv_per_wave;      /* 0 = launch heuristic; 1, 2 or 4 = that many
                                  consecutive tokens' kv rows per wavefront, all
                                  their loads issued together (the heuristic
-                                 takes 4 from 2^16 q rows, else 1) */
+                                 takes 4 from 2^16 q rows, 2 from 2^15 q rows
+                                 with at least 2048 tokens, else 1) */
 } qkv_prep_config;
 
 #define QKV_PREP_KV_FP8 0
@@ -229,10 +233,12 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
 /* The launch qkv_prep_run would use for num_tokens tokens with config cfg on
  * a device with num_cus compute units (256 on MI355X).  Pure host code: needs
  * no device, so the launch heuristic can be inspected anywhere.  The current
- * heuristic (one wavefront per workgroup; two heads of a token per wavefront
- * below 2^16 q rows, and with at most 16 heads from 2^14 tokens, one q row per
- * wavefront otherwise; four tokens' kv rows per kv wavefront from 2^16 q rows,
- * one below) does not depend on num_cus; the argument keeps the signature
+ * heuristic (two heads of a token per wavefront below 2^16 q rows, and with at
+ * most 16 heads from 2^14 tokens, one q row per wavefront otherwise; four
+ * tokens' kv rows per kv wavefront from 2^16 q rows, two from 2^15 q rows
+ * with at least 2048 tokens, one below; two wavefronts per workgroup with two
+ * heads per wavefront where the kv wavefronts take two or four tokens, one
+ * otherwise) does not depend on num_cus; the argument keeps the signature
  * stable for a device-dependent one.  Returns QKV_PREP_ERR_INVALID_ARG for a NULL out or num_tokens < 0, and
  * QKV_PREP_ERR_UNSUPPORTED when num_tokens * num_heads >= 2^31 (the limit of
  * qkv_prep_run). */

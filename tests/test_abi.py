@@ -165,7 +165,8 @@ def test_launch_shape_heuristic():
     at = qp.qkv_prep_launch_shape(cfg, 256, 1024)
     assert at.kv_per_wave == 4 and at.kv_blocks == 1024 // 4
     assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 8192).kv_per_wave == 4
-    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 4096).kv_per_wave == 1
+    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 4096).kv_per_wave == 2    # 2^15 rows, 4096 tokens
+    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 2047).kv_per_wave == 1
     ragged = qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=4), 256, 17)
     assert ragged.kv_per_wave == 4 and ragged.kv_blocks == 5                  # ceil(17 / 4)
     assert qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=2, waves_per_block=2),
@@ -174,9 +175,25 @@ def test_launch_shape_heuristic():
     assert qp.qkv_prep_launch_shape(cfg, 256, 1023).rows_per_wave == 2
     assert qp.qkv_prep_launch_shape(cfg, 256, 1024).rows_per_wave == 1        # 2^16 rows
     assert qp.qkv_prep_launch_shape(cfg, 256, 2048).rows_per_wave == 1
-    # ... and with at most 16 heads from 2^14 tokens
-    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 8192).rows_per_wave == 1
-    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 16384).rows_per_wave == 2
+    # ... and with at most 16 heads from 2^14 tokens, two wavefronts per
+    # workgroup when the kv wavefronts also take four tokens
+    few = qp.qkv_prep_launch_shape(qp.make_config(8), 256, 8192)
+    assert (few.rows_per_wave, few.waves_per_block, few.kv_per_wave) == (1, 1, 4)
+    few = qp.qkv_prep_launch_shape(qp.make_config(8), 256, 16384)
+    assert (few.rows_per_wave, few.waves_per_block, few.kv_per_wave) == (2, 2, 4)
+    assert few.kv_blocks == 16384 // 8 and few.q_blocks == 16384 * 4 // 2
+    # 2^15 to 2^16 q rows with at least 2048 tokens: two kv tokens per
+    # wavefront, two wavefronts per workgroup with the two-heads shape
+    mid = qp.qkv_prep_launch_shape(qp.make_config(2), 256, 16384)           # 2^15 rows
+    assert (mid.rows_per_wave, mid.waves_per_block, mid.kv_per_wave) == (2, 2, 2)
+    assert mid.kv_blocks == 16384 // 4 and mid.q_blocks == 16384 // 2
+    mid = qp.qkv_prep_launch_shape(qp.make_config(16), 256, 2048)
+    assert (mid.rows_per_wave, mid.waves_per_block, mid.kv_per_wave) == (2, 2, 2)
+    for H, T in ((32, 1024), (8, 2048), (64, 511)):                         # T < 2048, or < 2^15 rows
+        small = qp.qkv_prep_launch_shape(qp.make_config(H), 256, T)
+        assert (small.rows_per_wave, small.waves_per_block, small.kv_per_wave) == (2, 1, 1)
+    assert qp.qkv_prep_launch_shape(qp.make_config(64), 256, 1023).waves_per_block == 1
+    assert qp.qkv_prep_launch_shape(qp.make_config(8, waves_per_block=1), 256, 16384).waves_per_block == 1
     assert qp.qkv_prep_launch_shape(qp.make_config(16), 256, 16384).rows_per_wave == 2
     assert qp.qkv_prep_launch_shape(qp.make_config(17), 256, 16384).rows_per_wave == 1
     assert qp.qkv_prep_launch_shape(qp.make_config(32), 256, 65536).rows_per_wave == 1

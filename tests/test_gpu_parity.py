@@ -105,17 +105,22 @@ def test_kv_rows_per_wavefront_with_wider_workgroups(T, kv_per_wave, wpb):
 
 
 @pytest.mark.parametrize("T,H", [(1023, 64), (1024, 64), (511, 128), (512, 128), (8192, 8), (16384, 8),
-                                 (16383, 16), (16384, 16)])
+                                 (16383, 16), (16384, 16), (2047, 16), (2048, 16), (4096, 8), (1024, 32)])
 def test_both_sides_of_the_launch_thresholds(T, H):
     # The heuristic takes two heads per wavefront below 2^16 q rows, and with
     # at most 16 heads from 2^14 tokens, one row per wavefront otherwise; four
-    # kv tokens per kv wavefront from 2^16 q rows.  Default launch on each
-    # side of each boundary.
+    # kv tokens per kv wavefront from 2^16 q rows, two from 2^15 q rows with
+    # at least 2048 tokens, one below; two wavefronts per workgroup with two
+    # heads per wavefront where the kv wavefronts take several tokens.
+    # Default launch on each side of each boundary.
     from fp8_kv_cache_amd.qkv_prep import QkvPrep
     shape = QkvPrep(H).launch_shape(T)
     two = T * H < 1 << 16 or (H <= 16 and T >= 1 << 14)
+    large = T * H >= 1 << 16
+    mid = not large and T * H >= 1 << 15 and T >= 2048
     assert shape.rows_per_wave == (2 if two else 1)
-    assert shape.kv_per_wave == (4 if T * H >= 1 << 16 else 1)
+    assert shape.kv_per_wave == (4 if large else 2 if mid else 1)
+    assert shape.waves_per_block == (2 if two and (large or mid) else 1)
     check(W.custom(T, H, seed=330 + T + H, num_skip=5))
 
 
