@@ -43,60 +43,86 @@ int finish(const qkv_prep *h, hipError_t launched, hipStream_t st)
     return QKV_PREP_OK;
 }
 
-// Launch shape for T tokens.  Chosen from the committed sweep (bench.py
-// --mode sweep: every forced shape, 30 back-to-back launches, best of three
-// interleaved rounds, after warming the chip), run on MI355X over 28 sizes
-// from 512x64 to 131072x8 (H = 8 to 128) twice, rounds agreeing within 1%:
-//  * rows_per_wave: two consecutive heads of one token per wavefront (the
-//    token's position, cos/sin row and q weight loaded once for both rows,
-//    processed one after the other) below 2^16 q rows, and, with at most 16
-//    heads, from 2^14 tokens: there it is 2-7% faster (32768x8: 94.6 against
-//    101.1 us; 65536x16: 356.6 against 361.4).  Otherwise one q row per
-//    wavefront, with system-scope stores: 1-6% faster from 2^16 q rows with
-//    32 heads or more, or with fewer tokens (2048x64: 41.7 against 42.5 us;
-//    4096x16: 23.0 against 24.3).  Below 2^16 rows the shapes are within ~2%
-//    of each other and two heads stay.  Four heads per wavefront never win.
-//    A grid past what one dispatch takes (2^32 work-items, from about 2^26 q
+// Launch shape for T tokens of H heads (q_rows = T * H).  Chosen from the
+// committed sweep (bench.py --mode sweep: each forced shape, 30 back-to-back
+// launches, best of three interleaved rounds, after warming the chip), run on
+// MI355X over a grid of 92 sizes (T 512 to 131072, H 1 to 128, 2^12 to 2^17
+// q rows) twice, and checked on 46 sizes the rule was not fitted on.
+//
+// From 2^16 q rows:
+//  * one q row per wavefront, with system-scope stores (2048x64: 41.7
+//    against 42.5 us for two heads), except with at most 16 heads from 2^14
+//    tokens, where two consecutive heads of one token per wavefront (the
+//    token's position, cos/sin row and q weight loaded once for both rows)
+//    are 2-7% faster (32768x8: 94.6 against 101.1 us);
+//  * four consecutive tokens' kv rows per kv wavefront, their loads issued
+//    together (the kv wavefronts run first, as a latency-bound burst;
+//    2048x32: 22.3 against 23.3 us);
+//  * two wavefronts per workgroup with the two-heads shape (0.8-2.6% faster
+//    at all eight sizes from 16384x8 to 65536x16; 32768x8: 94.3 against
+//    95.9 us);
+//  * a grid past what one dispatch takes (2^32 work-items, from about 2^26 q
 //    rows) is split into consecutive dispatches rather than narrowed to more
 //    heads per wavefront: at 600000x128 one row per wavefront over two
 //    dispatches keeps the large-batch rate, where two heads per wavefront
 //    ran at 6.30 TB/s (and four, at 1100000x128, at 6.16).
-//  * kv_per_wave: four consecutive tokens' kv rows per kv wavefront, their
-//    loads issued together, from 2^16 q rows (the kv wavefronts run first, as
-//    a latency-bound burst; 2048x32: 22.3 against 23.3 us); two from 2^15 q
-//    rows with at least 2048 tokens, where the kv rows are a larger share
-//    (with two wavefronts per workgroup, below: 1.2-5.3% faster at seven
-//    sizes from 2048x24 to 16384x2, in two repeated sweeps); one below, where
-//    more per wavefront lose up to 17% (512x8: 5.42 against 4.68 us).
-//  * waves_per_block: 2 with two heads per wavefront wherever the kv
-//    wavefronts take several tokens (from 2^16 q rows, which with two heads
-//    means many tokens and at most 16 heads: 0.8-2.6% faster than 1 at all
-//    eight sizes from 16384x8 to 65536x16 in two repeated sweeps, 32768x8:
-//    94.3 against 95.9 us; and the mid range above).  Otherwise 1: more
-//    wavefronts per workgroup lose up to 6% with one row per wavefront and up
-//    to 14% for small batches.
+// Below 2^16 q rows the kv rows are a large share of the work when heads
+// are few, and the shape follows the token count as much as the row count:
+//  * one row and four kv tokens per wavefront from 49152 q rows, from 2^15
+//    with more than 4096 tokens, and from 24576 with more than 8192
+//    (16384x3: 22.5 against 24.9 us for two heads and two kv tokens;
+//    24576x1: 18.8 against 22.1 for one kv token);
+//  * else, from 2^15 q rows with at least 2048 tokens: two heads per
+//    wavefront, two kv tokens, two wavefronts per workgroup (4096x8: 13.5
+//    against 14.2 us for one row and four kv tokens);
+//  * else, from 3072 tokens, or from 2048 with an odd head count (where the
+//    last of a token's two-heads wavefronts is half empty): one row per
+//    wavefront, and two kv tokens from 2^14 q rows or above 8192 tokens, one
+//    below (8192x3: 12.6 against 15.3 us for two heads; 2048x7: 8.1
+//    against 8.8);
+//  * else two heads per wavefront and one kv token (1024x16: 7.2 against
+//    8.1 us for one row).
+// Over both grid runs and the held-out sizes the rule averages 0.5-0.9%
+// above the fastest shape per size and 6.2% at most; the rule it replaced
+// averaged 3.2-5.6% above, and up to 22%.  Four heads per wavefront never
+// won in the sweeps over every shape, and four wavefronts per workgroup win
+// by 1.6% at most.
 //  * convert: the gfx950 conversion instructions (bit-identical to the integer
 //    rounding, which the tests check on every workload).
+// A forced field (non-zero in the config) overrides its part; the workgroup
+// width then still follows the q rows per wavefront in use.
 qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
 {
     (void)num_cus;
     qkvp::LaunchShape s;
-    const int64_t q_rows = T * c.num_heads;
+    const int64_t H = c.num_heads;
+    const int64_t q_rows = T * H;
     s.convert = c.convert ? c.convert : 2;
-    const bool large = q_rows >= ((int64_t)1 << 16);
-    const bool mid = !large && q_rows >= ((int64_t)1 << 15) && T >= 2048;
-    s.kv_per_wave = c.kv_per_wave ? c.kv_per_wave : (large ? 4 : mid ? 2 : 1);
-    if (c.rows_per_wave) {
-        s.rows_per_wave = c.rows_per_wave;
+    int rows, kv;
+    if (q_rows >= ((int64_t)1 << 16)) {
+        rows = H > 1 && H <= 16 && T >= ((int64_t)1 << 14) ? 2 : 1;
+        kv = 4;
     } else {
-        const bool few_rows = q_rows < ((int64_t)1 << 16);
-        const bool many_tokens_few_heads = c.num_heads <= 16 && T >= ((int64_t)1 << 14);
-        s.rows_per_wave = (few_rows || many_tokens_few_heads) && c.num_heads > 1 ? 2 : 1;
+        const int64_t one_row_four_kv = T > 8192 ? 3 << 13 : T > 4096 ? 1 << 15 : 3 << 14;
+        if (q_rows >= one_row_four_kv) {
+            rows = 1;
+            kv = 4;
+        } else if (q_rows >= ((int64_t)1 << 15) && T >= 2048) {
+            rows = H > 1 ? 2 : 1;
+            kv = 2;
+        } else if (T >= 3072 || (T >= 2048 && H % 2 == 1)) {
+            rows = 1;
+            kv = q_rows >= ((int64_t)1 << 14) || T > 8192 ? 2 : 1;
+        } else {
+            rows = H > 1 ? 2 : 1;
+            kv = 1;
+        }
     }
-    if (c.waves_per_block)
-        s.waves_per_block = c.waves_per_block;
-    else
-        s.waves_per_block = s.rows_per_wave == 2 && (large || mid) ? 2 : 1;
+    s.rows_per_wave = c.rows_per_wave ? c.rows_per_wave : rows;
+    s.kv_per_wave = c.kv_per_wave ? c.kv_per_wave : kv;
+    // two wavefronts per workgroup with the two-heads shape wherever the
+    // rule takes several kv tokens per wavefront
+    s.waves_per_block = c.waves_per_block ? c.waves_per_block : s.rows_per_wave == 2 && kv >= 2 ? 2 : 1;
     s.kv_blocks = ceil_div(T, (int64_t)s.kv_per_wave * s.waves_per_block);
     // q wavefronts: T * ceil(H / U) (U heads of one token per wavefront)
     s.q_blocks = ceil_div(T * ceil_div(c.num_heads, s.rows_per_wave), s.waves_per_block);

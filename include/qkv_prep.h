@@ -73,12 +73,12 @@ typedef struct {
     int32_t rows_per_wave;    /* 0 = launch heuristic; 1 = one q row per wavefront;
                                  2 or 4 = that many consecutive heads of one
                                  token per wavefront, one after another (the
-                                 heuristic takes 2 below 2^16 q rows and, with
-                                 at most 16 heads, from 2^14 tokens; else 1) */
+                                 heuristic's choice is described at
+                                 qkv_prep_launch_shape) */
     int32_t waves_per_block;  /* 0 = launch heuristic; 1, 2, 4 or 8 forces it (the
                                  heuristic takes 2 with two heads per wavefront
-                                 from 2^16 q rows, and from 2^15 q rows with at
-                                 least 2048 tokens; else 1) */
+                                 where it takes several kv tokens per kv
+                                 wavefront; else 1) */
     int32_t convert;          /* 0 = heuristic, 1 = integer bf16/E4M3 rounding,
                                  2 = gfx950 conversion instructions; both give
                                  the same bits (tests check this) */
@@ -91,9 +91,8 @@ typedef struct {
                                  rotated); slot s at byte s * 1024 */
     int32_t kv_per_wave;      /* 0 = launch heuristic; 1, 2 or 4 = that many
                                  consecutive tokens' kv rows per wavefront, all
-                                 their loads issued together (the heuristic
-                                 takes 4 from 2^16 q rows, 2 from 2^15 q rows
-                                 with at least 2048 tokens, else 1) */
+                                 their loads issued together (the heuristic's
+                                 choice is described at qkv_prep_launch_shape) */
 } qkv_prep_config;
 
 #define QKV_PREP_KV_FP8 0
@@ -233,13 +232,19 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
 /* The launch qkv_prep_run would use for num_tokens tokens with config cfg on
  * a device with num_cus compute units (256 on MI355X).  Pure host code: needs
  * no device, so the launch heuristic can be inspected anywhere.  The current
- * heuristic (two heads of a token per wavefront below 2^16 q rows, and with at
- * most 16 heads from 2^14 tokens, one q row per wavefront otherwise; four
- * tokens' kv rows per kv wavefront from 2^16 q rows, two from 2^15 q rows
- * with at least 2048 tokens, one below; two wavefronts per workgroup with two
- * heads per wavefront where the kv wavefronts take two or four tokens, one
- * otherwise) does not depend on num_cus; the argument keeps the signature
- * stable for a device-dependent one.  Returns QKV_PREP_ERR_INVALID_ARG for a NULL out or num_tokens < 0, and
+ * heuristic, for T tokens of H heads and q = T * H rows, as (q rows per
+ * wavefront, wavefronts per workgroup, kv tokens per kv wavefront):
+ *   q >= 2^16:  (2, 2, 4) with 2 <= H <= 16 and T >= 2^14, else (1, 1, 4);
+ *   else q >= 49152, or q >= 2^15 with T > 4096, or q >= 24576 with
+ *               T > 8192:  (1, 1, 4);
+ *   else q >= 2^15 with T >= 2048:  (2, 2, 2);
+ *   else T >= 3072, or T >= 2048 with H odd:  (1, 1, 2) when q >= 2^14 or
+ *               T > 8192, else (1, 1, 1);
+ *   else (2, 1, 1), and (1, 1, 1) for H = 1.
+ * A field forced in cfg replaces its part; the workgroup width then follows
+ * the q rows per wavefront in use.  The heuristic does not depend on num_cus;
+ * the argument keeps the signature stable for a device-dependent one.
+ * Returns QKV_PREP_ERR_INVALID_ARG for a NULL out or num_tokens < 0, and
  * QKV_PREP_ERR_UNSUPPORTED when num_tokens * num_heads >= 2^31 (the limit of
  * qkv_prep_run). */
 int qkv_prep_launch_shape(const qkv_prep_config *cfg, int32_t num_cus, int64_t num_tokens,

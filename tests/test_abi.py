@@ -152,51 +152,53 @@ def test_unsupported_head_dim():
     assert qp.qkv_prep_validate(cfg, _good_args()) == qp.ERR_UNSUPPORTED
 
 
+def _shape(H, T, **forced):
+    s = qp.qkv_prep_launch_shape(qp.make_config(H, **forced), 256, T)
+    return (s.rows_per_wave, s.waves_per_block, s.kv_per_wave)
+
+
 def test_launch_shape_heuristic():
     cfg = qp.make_config(64)
     small = qp.qkv_prep_launch_shape(cfg, 256, 16)
-    # decode-sized: two heads of a token per wavefront, up to 2^17 q rows
+    # decode-sized: two heads of a token per wavefront, one kv token
     assert small.rows_per_wave == 2 and small.waves_per_block == 1 and small.convert == 2
-    # kv rows: one token per wavefront below 2^16 q rows
     assert small.kv_per_wave == 1
     assert small.kv_blocks == 16 and small.q_blocks == 16 * 32 and small.grid == 16 * 33
-    # four consecutive tokens per kv wavefront from 2^16 q rows
-    assert qp.qkv_prep_launch_shape(cfg, 256, 1023).kv_per_wave == 1
+    # from 2^16 q rows: four consecutive tokens per kv wavefront, one q row
+    # per wavefront (two heads, two wavefronts per workgroup with at most 16
+    # heads from 2^14 tokens)
     at = qp.qkv_prep_launch_shape(cfg, 256, 1024)
-    assert at.kv_per_wave == 4 and at.kv_blocks == 1024 // 4
-    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 8192).kv_per_wave == 4
-    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 4096).kv_per_wave == 2    # 2^15 rows, 4096 tokens
-    assert qp.qkv_prep_launch_shape(qp.make_config(8), 256, 2047).kv_per_wave == 1
-    ragged = qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=4), 256, 17)
-    assert ragged.kv_per_wave == 4 and ragged.kv_blocks == 5                  # ceil(17 / 4)
-    assert qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=2, waves_per_block=2),
-                                    256, 9).kv_blocks == 3                    # ceil(9 / (2 * 2))
-    # two heads per wavefront below 2^16 q rows ...
-    assert qp.qkv_prep_launch_shape(cfg, 256, 1023).rows_per_wave == 2
-    assert qp.qkv_prep_launch_shape(cfg, 256, 1024).rows_per_wave == 1        # 2^16 rows
-    assert qp.qkv_prep_launch_shape(cfg, 256, 2048).rows_per_wave == 1
-    # ... and with at most 16 heads from 2^14 tokens, two wavefronts per
-    # workgroup when the kv wavefronts also take four tokens
-    few = qp.qkv_prep_launch_shape(qp.make_config(8), 256, 8192)
-    assert (few.rows_per_wave, few.waves_per_block, few.kv_per_wave) == (1, 1, 4)
+    assert at.kv_per_wave == 4 and at.kv_blocks == 1024 // 4 and at.rows_per_wave == 1
+    assert _shape(64, 2048) == (1, 1, 4)
+    assert _shape(8, 8192) == (1, 1, 4)
     few = qp.qkv_prep_launch_shape(qp.make_config(8), 256, 16384)
     assert (few.rows_per_wave, few.waves_per_block, few.kv_per_wave) == (2, 2, 4)
     assert few.kv_blocks == 16384 // 8 and few.q_blocks == 16384 * 4 // 2
-    # 2^15 to 2^16 q rows with at least 2048 tokens: two kv tokens per
-    # wavefront, two wavefronts per workgroup with the two-heads shape
-    mid = qp.qkv_prep_launch_shape(qp.make_config(2), 256, 16384)           # 2^15 rows
-    assert (mid.rows_per_wave, mid.waves_per_block, mid.kv_per_wave) == (2, 2, 2)
-    assert mid.kv_blocks == 16384 // 4 and mid.q_blocks == 16384 // 2
+    assert _shape(16, 16384)[0] == 2 and _shape(17, 16384)[0] == 1 and _shape(32, 65536)[0] == 1
+    # below 2^16: one row and four kv tokens from 49152 q rows, from 2^15
+    # with more than 4096 tokens, from 24576 with more than 8192
+    assert _shape(64, 1023) == (1, 1, 4)                                     # 65472 rows
+    assert _shape(12, 4096) == (1, 1, 4) and _shape(11, 4096) == (2, 2, 2)   # 49152 / 45056 rows
+    assert _shape(8, 4097) == (1, 1, 4) and _shape(8, 4096) == (2, 2, 2)     # 2^15 rows, > 4096 tokens
+    assert _shape(2, 16384) == (1, 1, 4)
+    assert _shape(3, 8193) == (1, 1, 4) and _shape(3, 8192) == (1, 1, 2)     # 24579 / 24576 rows
+    assert _shape(1, 24576) == (1, 1, 4) and _shape(1, 32768) == (1, 1, 4)
+    # else from 2^15 q rows with at least 2048 tokens: two heads, two kv
+    # tokens, two wavefronts per workgroup
     mid = qp.qkv_prep_launch_shape(qp.make_config(16), 256, 2048)
     assert (mid.rows_per_wave, mid.waves_per_block, mid.kv_per_wave) == (2, 2, 2)
-    for H, T in ((32, 1024), (8, 2048), (64, 511)):                         # T < 2048, or < 2^15 rows
-        small = qp.qkv_prep_launch_shape(qp.make_config(H), 256, T)
-        assert (small.rows_per_wave, small.waves_per_block, small.kv_per_wave) == (2, 1, 1)
-    assert qp.qkv_prep_launch_shape(qp.make_config(64), 256, 1023).waves_per_block == 1
-    assert qp.qkv_prep_launch_shape(qp.make_config(8, waves_per_block=1), 256, 16384).waves_per_block == 1
-    assert qp.qkv_prep_launch_shape(qp.make_config(16), 256, 16384).rows_per_wave == 2
-    assert qp.qkv_prep_launch_shape(qp.make_config(17), 256, 16384).rows_per_wave == 1
-    assert qp.qkv_prep_launch_shape(qp.make_config(32), 256, 65536).rows_per_wave == 1
+    assert mid.kv_blocks == 2048 // 4 and mid.q_blocks == 2048 * 8 // 2
+    # else from 3072 tokens, or 2048 with an odd head count: one row per
+    # wavefront, two kv tokens from 2^14 q rows or above 8192 tokens
+    assert _shape(2, 3072) == (1, 1, 1) and _shape(2, 3071) == (2, 1, 1)
+    assert _shape(7, 2048) == (1, 1, 1) and _shape(7, 2047) == (2, 1, 1) and _shape(8, 2048) == (2, 1, 1)
+    assert _shape(11, 2048) == (1, 1, 2)                                     # 22528 rows
+    assert _shape(4, 4096) == (1, 1, 2) and _shape(4, 4095) == (1, 1, 1)     # 2^14 rows
+    assert _shape(1, 8193) == (1, 1, 2) and _shape(1, 8192) == (1, 1, 1)
+    assert _shape(6, 4096) == (1, 1, 2)
+    # else two heads per wavefront, one kv token
+    for H, T in ((32, 1024), (8, 2047), (64, 511), (16, 1024)):
+        assert _shape(H, T) == (2, 1, 1)
     one_head = qp.qkv_prep_launch_shape(qp.make_config(1), 256, 100)
     assert one_head.rows_per_wave == 1 and one_head.q_blocks == 100
     odd_heads = qp.qkv_prep_launch_shape(qp.make_config(5), 256, 10)
@@ -210,11 +212,22 @@ def test_launch_shape_heuristic():
     huge = qp.qkv_prep_launch_shape(qp.make_config(128), 256, 600000)
     assert huge.rows_per_wave == 1 and huge.q_blocks == 600000 * 128
     assert huge.grid * 64 * huge.waves_per_block >= 2 ** 32
+    # forced fields: each overrides its part; the workgroup width follows the
+    # q rows per wavefront in use (two with two heads where the rule takes
+    # several kv tokens)
+    ragged = qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=4), 256, 17)
+    assert ragged.kv_per_wave == 4 and ragged.kv_blocks == 5                  # ceil(17 / 4)
+    assert qp.qkv_prep_launch_shape(qp.make_config(64, kv_per_wave=2, waves_per_block=2),
+                                    256, 9).kv_blocks == 3                    # ceil(9 / (2 * 2))
+    assert _shape(6, 8192, rows_per_wave=2) == (2, 2, 4)
+    assert _shape(8, 4096, rows_per_wave=1) == (1, 1, 2)
+    assert _shape(8, 16384, waves_per_block=1) == (2, 1, 4)
     forced = qp.qkv_prep_launch_shape(qp.make_config(64, rows_per_wave=2, waves_per_block=8,
                                                      convert=1), 256, 1000)
     assert (forced.rows_per_wave, forced.waves_per_block, forced.convert) == (2, 8, 1)
+    assert forced.kv_per_wave == 4                                            # 64000 rows
     assert forced.q_blocks == -(-(1000 * 32) // 8)
-    assert forced.kv_blocks == -(-1000 // 8)
+    assert forced.kv_blocks == -(-1000 // (4 * 8))
     # the row limit of qkv_prep_run also bounds the shape query (no overflow)
     for T in (2 ** 31 // 64, 2 ** 62, 2 ** 63 - 1):
         with pytest.raises(qp.QkvPrepError) as e:

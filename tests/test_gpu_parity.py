@@ -104,23 +104,36 @@ def test_kv_rows_per_wavefront_with_wider_workgroups(T, kv_per_wave, wpb):
         check(w, kv_per_wave=kv_per_wave, waves_per_block=wpb, rows_per_wave=rpw)
 
 
+def _expected_shape(T, H):
+    """The launch heuristic, restated: (q rows per wavefront, wavefronts per
+    workgroup, kv tokens per wavefront)."""
+    q = T * H
+    if q >= 1 << 16:
+        two = 1 < H <= 16 and T >= 1 << 14
+        return (2, 2, 4) if two else (1, 1, 4)
+    if q >= (3 << 13 if T > 8192 else 1 << 15 if T > 4096 else 3 << 14):
+        return (1, 1, 4)
+    if q >= 1 << 15 and T >= 2048:
+        return (2, 2, 2)
+    if T >= 3072 or (T >= 2048 and H % 2 == 1):
+        return (1, 1, 2 if q >= 1 << 14 or T > 8192 else 1)
+    return (2 if H > 1 else 1, 1, 1)
+
+
 @pytest.mark.parametrize("T,H", [(1023, 64), (1024, 64), (511, 128), (512, 128), (8192, 8), (16384, 8),
-                                 (16383, 16), (16384, 16), (2047, 16), (2048, 16), (4096, 8), (1024, 32)])
+                                 (16383, 16), (16384, 16), (2047, 16), (2048, 16), (4096, 8), (1024, 32),
+                                 (4096, 12), (4096, 11), (4097, 8), (8193, 3), (8192, 3), (24576, 1),
+                                 (3072, 2), (3071, 2), (2048, 7), (2047, 7), (2048, 11), (4096, 4),
+                                 (4095, 4), (8193, 1), (8192, 1)])
 def test_both_sides_of_the_launch_thresholds(T, H):
-    # The heuristic takes two heads per wavefront below 2^16 q rows, and with
-    # at most 16 heads from 2^14 tokens, one row per wavefront otherwise; four
-    # kv tokens per kv wavefront from 2^16 q rows, two from 2^15 q rows with
-    # at least 2048 tokens, one below; two wavefronts per workgroup with two
-    # heads per wavefront where the kv wavefronts take several tokens.
-    # Default launch on each side of each boundary.
+    # Default launch on each side of each boundary of the heuristic: 2^16 q
+    # rows; one row and four kv tokens from 49152, 2^15 (above 4096 tokens)
+    # or 24576 (above 8192 tokens) q rows; the two-heads band from 2^15 q
+    # rows and 2048 tokens; one row from 3072 tokens (2048 with an odd head
+    # count); two kv tokens from 2^14 q rows or above 8192 tokens.
     from fp8_kv_cache_amd.qkv_prep import QkvPrep
     shape = QkvPrep(H).launch_shape(T)
-    two = T * H < 1 << 16 or (H <= 16 and T >= 1 << 14)
-    large = T * H >= 1 << 16
-    mid = not large and T * H >= 1 << 15 and T >= 2048
-    assert shape.rows_per_wave == (2 if two else 1)
-    assert shape.kv_per_wave == (4 if large else 2 if mid else 1)
-    assert shape.waves_per_block == (2 if two and (large or mid) else 1)
+    assert (shape.rows_per_wave, shape.waves_per_block, shape.kv_per_wave) == _expected_shape(T, H)
     check(W.custom(T, H, seed=330 + T + H, num_skip=5))
 
 
