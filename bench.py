@@ -575,11 +575,44 @@ def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3, only=None
                    for sh, t in zip(shapes, best)), key=lambda r: r["us"])
     del inp, args, ops, launches_of
     torch.cuda.empty_cache()
-    return {"mode": "sweep", "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
-            "bytes_per_launch": nbytes, "launches": launches, "rounds": rounds,
-            "heuristic": {"rows_per_wave": heur.rows_per_wave, "waves_per_block": heur.waves_per_block,
-                          "kv_per_wave": heur.kv_per_wave, "convert": heur.convert},
-            "shapes": rows}
+    res = {"mode": "sweep", "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
+           "bytes_per_launch": nbytes, "launches": launches, "rounds": rounds,
+           "heuristic": {"rows_per_wave": heur.rows_per_wave, "waves_per_block": heur.waves_per_block,
+                         "kv_per_wave": heur.kv_per_wave, "convert": heur.convert},
+           "shapes": rows}
+    res.update(heuristic_standing(res))
+    return res
+
+
+def heuristic_standing(res):
+    """How the heuristic's shape compares with the fastest shape of one sweep
+    result: {"heuristic_us", "best_us", "heuristic_over_best"} (the last as
+    a fraction, 0 when the heuristic is the fastest), with None for the
+    heuristic's time when its shape was not among those swept.  A swept shape
+    without a conversion field runs the default conversion path, the one
+    the heuristic takes."""
+    h = res["heuristic"]
+    key = (h["rows_per_wave"], h["waves_per_block"], h["kv_per_wave"])
+    best = min(r["us"] for r in res["shapes"])
+    mine = [r["us"] for r in res["shapes"]
+            if (r["shape"]["rows_per_wave"], r["shape"]["waves_per_block"], r["shape"]["kv_per_wave"]) == key
+            and r["shape"].get("convert", h["convert"]) == h["convert"]]
+    if not mine:
+        return {"heuristic_us": None, "best_us": best, "heuristic_over_best": None}
+    return {"heuristic_us": min(mine), "best_us": best, "heuristic_over_best": round(min(mine) / best - 1, 4)}
+
+
+def sweep_summary(results):
+    """One line over a sweep of several sizes: the mean and largest excess
+    of the heuristic's shape over the fastest shape, and where the largest
+    one falls (sizes whose heuristic shape was not swept are left out)."""
+    got = [(r["heuristic_over_best"], r["workload"]) for r in results if r["heuristic_over_best"] is not None]
+    if not got:
+        return {"mode": "sweep_summary", "sizes": 0}
+    worst = max(got)
+    return {"mode": "sweep_summary", "sizes": len(got),
+            "mean_heuristic_over_best": round(sum(g for g, _ in got) / len(got), 4),
+            "max_heuristic_over_best": worst[0], "worst": worst[1]}
 
 
 # ----------------------------------------------------------------- main
@@ -627,9 +660,12 @@ def main():
         profile_run(torch, qp, probe, args.workload, args.launches)
         return
     if args.mode == "sweep":
+        results = []
         for size in (args.sizes.split(",") if args.sizes else [None]):
-            print(json.dumps(sweep_shapes(torch, W, qp, args.workload, size, only=parse_shapes(args.shapes))),
-                  flush=True)
+            results.append(sweep_shapes(torch, W, qp, args.workload, size, only=parse_shapes(args.shapes)))
+            print(json.dumps(results[-1]), flush=True)
+        if len(results) > 1:
+            print(json.dumps(sweep_summary(results)), flush=True)
         return
     kat_before = known_answer_check(torch, W, qp)
     w, main_res, ceil_before = bench_workload(torch, W, qp, probe, args.workload, args.steps, args.warmup,

@@ -1,6 +1,7 @@
 """Host-only checks of bench.py's contract pieces: the one-GPU refusal, the
-profile lookup (current rocprofv3 summaries are used, stale ones are not) and
-the p90 helper."""
+profile lookup (current rocprofv3 summaries are used, stale ones are not), the
+p90 helper, and the sweep mode's shape list and heuristic-against-best
+report."""
 import os
 import shutil
 import subprocess
@@ -80,3 +81,29 @@ def test_sweep_shape_list():
                                                   dict(rows_per_wave=2, waves_per_block=8, kv_per_wave=1)]
     with pytest.raises(ValueError):
         bench.parse_shapes("1:1")
+
+
+def _sweep_result(workload, heur, times):
+    rows = [{"shape": dict(zip(("rows_per_wave", "waves_per_block", "kv_per_wave"), k), **extra), "us": us}
+            for (k, extra), us in times]
+    return {"workload": workload, "heuristic": dict(zip(("rows_per_wave", "waves_per_block", "kv_per_wave"), heur),
+                                                   convert=2), "shapes": rows}
+
+
+def test_sweep_reports_the_heuristic_against_the_fastest_shape():
+    r = _sweep_result("custom 8192x3", (1, 1, 2), [(((1, 1, 2), {}), 12.6), (((2, 1, 1), {}), 15.3),
+                                                   (((1, 1, 2), {"convert": 1}), 12.0)])
+    # the conversion-1 run of the same shape is not the heuristic's launch
+    assert bench.heuristic_standing(r) == {"heuristic_us": 12.6, "best_us": 12.0,
+                                           "heuristic_over_best": round(12.6 / 12.0 - 1, 4)}
+    r2 = _sweep_result("custom 4096x8", (2, 2, 2), [(((2, 2, 2), {"convert": 2}), 13.5), (((1, 1, 4), {}), 14.2)])
+    assert bench.heuristic_standing(r2)["heuristic_over_best"] == 0
+    r3 = _sweep_result("custom 16x8", (2, 1, 1), [(((1, 1, 4), {}), 5.0)])
+    assert bench.heuristic_standing(r3) == {"heuristic_us": None, "best_us": 5.0, "heuristic_over_best": None}
+    for x in (r, r2, r3):
+        x.update(bench.heuristic_standing(x))
+    s = bench.sweep_summary([r, r2, r3])
+    assert s["sizes"] == 2 and s["worst"] == "custom 8192x3"
+    assert s["max_heuristic_over_best"] == r["heuristic_over_best"]
+    assert s["mean_heuristic_over_best"] == round(r["heuristic_over_best"] / 2, 4)
+    assert bench.sweep_summary([r3]) == {"mode": "sweep_summary", "sizes": 0}
