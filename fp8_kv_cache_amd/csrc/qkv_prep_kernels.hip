@@ -14,13 +14,15 @@
 //    Measured on MI355X, this shape streams at the copy ceiling at every
 //    footprint (~6.5 TB/s with non-temporal stores), while shapes with several
 //    loads per lane in flight (4 rows per wave, or several rows per wave) lose
-//    6-15% once the footprint passes a few GiB.  Workgroups of one wavefront
-//    (the measured optimum); non-temporal loads.
+//    6-15% once the footprint passes a few GiB.  Workgroups of one wavefront,
+//    or two where the launch heuristic pairs the two-heads shape with several
+//    kv tokens per wavefront; non-temporal loads.
 //  * Stores: with one row per wavefront every store carries the non-temporal
 //    system-scope policy (nt sc1), 1-2.5% faster than plain non-temporal
 //    stores from 32768x64 up (about 2% at 32768x128 and 131072x128).  The
-//    two-heads shape of small batches keeps plain non-temporal stores: there
-//    nt sc1 was ~2% slower (a footprint near the size of the MALL).
+//    two-heads shape keeps plain non-temporal stores: with nt sc1 it was
+//    3-18% slower on small batches (footprints within the MALL) and within
+//    noise on large few-head ones.
 //  * The sum of squares follows the fixed order of the numerics contract: each
 //    chunk sequentially, then adjacent chunk pairs.  Levels 1-4 are DPP adds
 //    inside a 16-lane row (quad_perm xor1, xor2, row_half_mirror, row_mirror);
@@ -35,13 +37,14 @@
 //  * q rows and kv rows go to different workgroups of one launch (the FlagGems
 //    page merges the Q and KV launches); kv workgroups come first in dispatch
 //    order, so their quantization overlaps the q stream instead of trailing it.
-//    For larger batches a kv wavefront takes four consecutive tokens, all
-//    their loads issued together: the kv wavefronts form a latency-bound
-//    burst at the start, and more loads in flight per wavefront shorten it.
-//  * Small batches, and batches of many tokens with few heads, take two heads
-//    of one token per wavefront, one after the other, so the token's
-//    position, cos/sin row and the q weight are loaded once per two rows (the
-//    launch heuristic in qkv_prep_api.cpp says when, with its measurements).
+//    Where the launch heuristic says so, a kv wavefront takes two or four
+//    consecutive tokens, all their loads issued together: the kv wavefronts
+//    form a latency-bound burst at the start, and more loads in flight per
+//    wavefront shorten it.
+//  * Depending on the token and head counts, a wavefront takes two heads of
+//    one token, one after the other, so the token's position, cos/sin row and
+//    the q weight are loaded once per two rows (the launch heuristic in
+//    qkv_prep_api.cpp says when, with its measurements).
 //    Issuing several q rows' loads at once (the sglang page's "K tokens per
 //    block" load-level parallelism) was slower at every size measured; the kv
 //    burst above is the one place where it pays.
