@@ -137,18 +137,24 @@ def test_both_sides_of_the_launch_thresholds(T, H):
     check(W.custom(T, H, seed=330 + T + H, num_skip=5))
 
 
-def _random_cases(n, seed):
+def _random_cases(n, seed, few_heads=False):
     """n seeded configurations that mix every knob at once: ragged token and
     head counts (up to 2^18 q rows), block sizes, table lengths, skipped
     slots, outlier rows, eps, a weightless q, both cache modes, and every
-    forced launch setting (0 = the heuristic)."""
+    forced launch setting (0 = the heuristic).  With few_heads: 2048 to 65536
+    tokens of 1 to 8 heads (the launch shapes that follow the token count),
+    three cases in four at the heuristic's shape."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
-        T = int(rng.integers(1, 4) if len(cases) < 3 else rng.integers(1, 6001))
-        H = int(rng.integers(1, 161))
-        if T * H > 1 << 18:
+        if few_heads:
+            T, H = int(rng.integers(2048, 65537)), int(rng.integers(1, 9))
+        else:
+            T = int(rng.integers(1, 4) if len(cases) < 3 else rng.integers(1, 6001))
+            H = int(rng.integers(1, 161))
+        if T * H > 1 << 18 and not few_heads:
             continue
+        forced = not few_heads or rng.integers(4) == 0
         cases.append(dict(
             T=T, H=H, seed=int(rng.integers(1 << 30)),
             block_size=int(rng.choice([1, 3, 16, 64, 100, 256])),
@@ -158,14 +164,14 @@ def _random_cases(n, seed):
             eps=float(rng.choice([0.0, 1e-6, 1e-2])),
             q_weight=bool(rng.integers(2)),
             kv_store=int(rng.integers(2)),
-            rows_per_wave=int(rng.choice([0, 1, 2, 4])),
-            waves_per_block=int(rng.choice([0, 1, 2, 4, 8])),
-            kv_per_wave=int(rng.choice([0, 1, 2, 4])),
+            rows_per_wave=int(rng.choice([0, 1, 2, 4])) if forced else 0,
+            waves_per_block=int(rng.choice([0, 1, 2, 4, 8])) if forced else 0,
+            kv_per_wave=int(rng.choice([0, 1, 2, 4])) if forced else 0,
             convert=int(rng.integers(3))))
     return cases
 
 
-RANDOM_CASES = _random_cases(24, 20261202)
+RANDOM_CASES = _random_cases(24, 20261202) + _random_cases(8, 20261203, few_heads=True)
 
 
 @pytest.mark.parametrize("case", RANDOM_CASES, ids=["%dx%d" % (c["T"], c["H"]) for c in RANDOM_CASES])
