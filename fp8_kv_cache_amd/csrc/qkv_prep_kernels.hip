@@ -36,7 +36,9 @@
 //    page removes a per-head re-gather).
 //  * q rows and kv rows go to different workgroups of one launch (the FlagGems
 //    page merges the Q and KV launches); kv workgroups come first in dispatch
-//    order, so their quantization overlaps the q stream instead of trailing it.
+//    order, so their quantization overlaps the q stream instead of trailing it
+//    (for large two-heads batches they are spread over the first 55-75% of
+//    the grid instead; the launch heuristic says when).
 //    Where the launch heuristic says so, a kv wavefront takes two or four
 //    consecutive tokens, all their loads issued together: the kv wavefronts
 //    form a latency-bound burst at the start, and more loads in flight per
@@ -294,6 +296,33 @@ __device__ __forceinline__ void kv_rows(const KernelArgs &a, int64_t t0, uint32_
 
 // ------------------------------------------------------------------ kernel
 
+// kv workgroup `b` (its index among the kv workgroups): its wavefront takes
+// a.kv_per_wave consecutive tokens' kv rows.
+template <int U, bool HW>
+__device__ __forceinline__ void kv_workgroup(const KernelArgs &a, int64_t b, uint32_t wave,
+                                             uint32_t waves_per_block, uint32_t lane)
+{
+    const int64_t t = (b * waves_per_block + wave) * a.kv_per_wave;
+    if (t < a.num_tokens)
+        kv_rows<HW, U == 1, kMaxKvPerWave>(a, t, lane);
+}
+
+// q workgroup `b` (its index among the q workgroups): its wavefront takes one
+// q row, or U heads of one token.
+template <int U, bool HAS_W, bool HW>
+__device__ __forceinline__ void q_workgroup(const KernelArgs &a, int64_t b, uint32_t wave,
+                                            uint32_t waves_per_block, uint32_t lane)
+{
+    const int64_t wv = b * waves_per_block + wave;
+    if constexpr (U == 1) {
+        if (wv < a.q_rows)
+            q_row<HAS_W, HW>(a, wv, lane);
+    } else {
+        if (wv < a.num_tokens * (int64_t)a.chunks)
+            q_chunk<U, HAS_W, HW>(a, (uint32_t)wv, lane);
+    }
+}
+
 // SPLIT: this dispatch is one of several covering a grid past 2^32
 // work-items, so its workgroup indices start at a.block_base.  Single
 // dispatches (every grid below about 2^26 q rows) use the instance without
@@ -306,19 +335,28 @@ __global__ __launch_bounds__(512) void qkv_prep_kernel(KernelArgs a)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t waves_per_block = blockDim.x >> 6;
     const int64_t blk = SPLIT ? (int64_t)blockIdx.x + a.block_base : (int64_t)blockIdx.x;
-    if (blk < a.kv_blocks) {
-        const int64_t t = (blk * waves_per_block + wave) * a.kv_per_wave;
-        if (t < a.num_tokens)
-            kv_rows<HW, U == 1, kMaxKvPerWave>(a, t, lane);
-    } else {
-        const int64_t wv = (blk - a.kv_blocks) * waves_per_block + wave;
-        if constexpr (U == 1) {
-            if (wv < a.q_rows)
-                q_row<HAS_W, HW>(a, wv, lane);
-        } else {
-            if (wv < a.num_tokens * (int64_t)a.chunks)
-                q_chunk<U, HAS_W, HW>(a, (uint32_t)wv, lane);
+    if constexpr (U == 2) {
+        // Grid index -> kv or q workgroup and its index among those: kv first,
+        // or kv workgroup j at index j * kv_period with the q workgroups in
+        // the gaps and after (the grid has fewer than 2^31 workgroups there,
+        // so the fixed-point division is exact).  One call site per body
+        // keeps the instance's code size.
+        bool kv = blk < a.kv_blocks;
+        int64_t idx = kv ? blk : blk - a.kv_blocks;
+        if (a.kv_period != 0) {
+            const uint32_t j = fastdiv((uint32_t)blk, a.period_div);
+            kv = j < a.kv_blocks && (uint32_t)blk == j * a.kv_period;
+            idx = kv ? (int64_t)j : blk - (j < a.kv_blocks ? (int64_t)j + 1 : (int64_t)a.kv_blocks);
         }
+        if (kv)
+            kv_workgroup<U, HW>(a, idx, wave, waves_per_block, lane);
+        else
+            q_workgroup<U, HAS_W, HW>(a, idx, wave, waves_per_block, lane);
+    } else {
+        if (blk < a.kv_blocks)
+            kv_workgroup<U, HW>(a, blk, wave, waves_per_block, lane);
+        else
+            q_workgroup<U, HAS_W, HW>(a, blk - a.kv_blocks, wave, waves_per_block, lane);
     }
 }
 

@@ -30,6 +30,9 @@ struct KernelArgs {
     float eps;
     int32_t bf16_store;        // 1: kv slots are 1024 bytes of bf16, no quantization
     int64_t block_base;        // workgroup index of this dispatch's first workgroup
+    uint32_t kv_period;        // 0: the kv workgroups come first; else kv workgroup j sits at
+                               // grid index j * kv_period (two-heads instance only)
+    FastDiv period_div;        // divides a grid index by kv_period
 };
 
 // The most consecutive tokens whose kv rows one wavefront takes.
@@ -42,6 +45,7 @@ struct LaunchShape {
     int kv_per_wave;      // tokens' kv rows per kv wavefront (1, 2, 4)
     int64_t kv_blocks;
     int64_t q_blocks;
+    int64_t kv_period;    // 0, or the spacing of the kv workgroups in the grid (odd, >= 3)
 };
 
 // The most workgroups of `waves_per_block` wavefronts one dispatch takes: the

@@ -76,7 +76,7 @@ class QkvPrepMxfp8Args(ctypes.Structure):
 class QkvPrepLaunch(ctypes.Structure):
     _fields_ = [("rows_per_wave", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
                 ("convert", ctypes.c_int32), ("kv_per_wave", ctypes.c_int32), ("kv_blocks", ctypes.c_int64),
-                ("q_blocks", ctypes.c_int64), ("grid", ctypes.c_int64)]
+                ("q_blocks", ctypes.c_int64), ("grid", ctypes.c_int64), ("kv_period", ctypes.c_int64)]
 
 
 class QkvPrepError(RuntimeError):

@@ -136,13 +136,19 @@ typedef struct {
     int32_t waves_per_block;
     int32_t convert;          /* 1 integer, 2 instructions */
     int32_t kv_per_wave;      /* tokens' kv rows per kv wavefront (1, 2 or 4) */
-    int64_t kv_blocks;        /* workgroups that handle kv rows (dispatched first) */
+    int64_t kv_blocks;        /* workgroups that handle kv rows */
     int64_t q_blocks;         /* workgroups that handle q rows */
     int64_t grid;             /* kv_blocks + q_blocks; a grid of more than
                                  (2^32 - 1) / (64 * waves_per_block) workgroups
                                  (a dispatch counts work-items in 32 bits) is
                                  enqueued as consecutive dispatches of that
                                  many workgroups, in order */
+    int64_t kv_period;        /* 0: the kv workgroups come first in the grid;
+                                 else (two heads and four kv tokens per
+                                 wavefront, from 2^18 q rows) kv workgroup j
+                                 is grid index j * kv_period, an odd spacing
+                                 >= 3 that spreads them over the first 55-75%
+                                 of the grid */
 } qkv_prep_launch;
 
 /* Arguments of the cache reader (qkv_prep_gather).
@@ -241,6 +247,9 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
  *   else T >= 3072, or T >= 2048 with H odd:  (1, 1, 2) when q >= 2^14 or
  *               T > 8192, else (1, 1, 1);
  *   else (2, 1, 1), and (1, 1, 1) for H = 1.
+ * The kv workgroups come first in the grid, except with two heads and four kv
+ * tokens per wavefront from 2^18 q rows, where they are spread over the first
+ * 55-75% of it (out->kv_period).
  * A field forced in cfg replaces its part; the workgroup width then follows
  * the q rows per wavefront in use.  The heuristic does not depend on num_cus;
  * the argument keeps the signature stable for a device-dependent one.

@@ -214,7 +214,7 @@ int main()
     }
 
     // Handles on the fake devices: run and gather against the contract.
-    long long runs_ok = 0, gathers_ok = 0;
+    long long runs_ok = 0, gathers_ok = 0, spread_runs = 0;
     for (long long i = 0; i < 100000; ++i) {
         qkv_prep_config c;
         std::memset(&c, 0, sizeof(c));
@@ -281,6 +281,32 @@ int main()
                        "every kv row covered", i);
                 expect(k.kv_per_wave == (uint32_t)last_s.kv_per_wave, "kv rows per wavefront", i);
                 expect(k.bf16_store == (c.kv_store == QKV_PREP_KV_BF16), "store mode", i);
+                expect(k.kv_period == (uint32_t)last_s.kv_period, "kv period passed through", i);
+                if (last_s.kv_period != 0) {
+                    // kv workgroup j at grid index j * P: only for two heads and
+                    // four kv tokens per wavefront from 2^18 q rows; P odd (the kv
+                    // workgroups fall on every XCD in turn) and >= 3; every kv
+                    // workgroup inside a grid of fewer than 2^31 workgroups, where
+                    // the kernel's fixed-point division by P is exact.
+                    const int64_t p = last_s.kv_period;
+                    const int64_t grid = last_s.kv_blocks + last_s.q_blocks;
+                    ++spread_runs;
+                    expect(last_s.rows_per_wave == 2 && last_s.kv_per_wave == 4 && k.q_rows >= ((int64_t)1 << 18),
+                           "kv spread only for the large two-heads shape", i);
+                    expect(p % 2 == 1 && p >= 3, "kv period odd and >= 3", i);
+                    expect((last_s.kv_blocks - 1) * p < grid && grid < ((int64_t)1 << 31),
+                           "kv workgroups inside the grid", i);
+                    for (int64_t n : {(int64_t)0, p - 1, p, (last_s.kv_blocks - 1) * p, grid - 1,
+                                      (int64_t)(next() % (uint64_t)grid)}) {
+                        const uint32_t q32 = (uint32_t)((((uint64_t)(uint32_t)n * k.period_div.mul) >> 32) + (uint64_t)n)
+                                             >> k.period_div.shift;
+                        expect((int64_t)q32 == n / p, "fixed-point division by the kv period", i);
+                    }
+                } else {
+                    expect(!(last_s.rows_per_wave == 2 && last_s.kv_per_wave == 4 && k.q_rows >= ((int64_t)1 << 18) &&
+                             3 * (last_s.kv_blocks + last_s.q_blocks) / (4 * last_s.kv_blocks) >= 3),
+                           "large two-heads batches spread their kv workgroups", i);
+                }
             }
 
             qkv_prep_gather_args g;
@@ -405,8 +431,9 @@ int main()
                "bf16 reader grid at the limit", 0);
     }
 
-    std::printf("cases %lld, valid argument sets %lld, launch shapes %lld, runs launched %lld, gathers launched "
-                "%lld, mxfp8 launched %lld, contract failures %d\n", cases, ok_validate, ok_shape, runs_ok,
-                gathers_ok, mx_ok, failures);
+    expect(spread_runs > 0, "some runs spread their kv workgroups", 0);
+    std::printf("cases %lld, valid argument sets %lld, launch shapes %lld, runs launched %lld (kv spread %lld), "
+                "gathers launched %lld, mxfp8 launched %lld, contract failures %d\n", cases, ok_validate, ok_shape,
+                runs_ok, spread_runs, gathers_ok, mx_ok, failures);
     return failures ? 1 : 0;
 }

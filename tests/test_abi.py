@@ -56,7 +56,7 @@ def test_operator_library_exports_no_probe():
 def test_struct_sizes_match_the_header_layout():
     assert ctypes.sizeof(qp.QkvPrepConfig) == 40
     assert ctypes.sizeof(qp.QkvPrepArgs) == 88
-    assert ctypes.sizeof(qp.QkvPrepLaunch) == 40
+    assert ctypes.sizeof(qp.QkvPrepLaunch) == 48
     assert ctypes.sizeof(qp.QkvPrepGatherArgs) == 48
     assert ctypes.sizeof(qp.QkvPrepMxfp8Args) == 64
 
@@ -236,6 +236,59 @@ def test_launch_shape_heuristic():
     assert qp.qkv_prep_launch_shape(cfg, 256, 2 ** 31 // 64 - 1).grid > 0
     odd = qp.qkv_prep_launch_shape(qp.make_config(3, waves_per_block=4), 256, 5)
     assert odd.rows_per_wave == 2 and odd.q_blocks == 3 and odd.kv_blocks == 2   # 5 * 2 wavefronts / 4
+
+
+def _grid_roles(s):
+    """The kernel's grid-index mapping, restated: for every workgroup of a
+    launch, ("kv", j) or ("q", j) with j its index among its kind."""
+    K, Q, P = s.kv_blocks, s.q_blocks, s.kv_period
+    roles = []
+    for b in range(K + Q):
+        if P:
+            j = b // P
+            if j < K and b == j * P:
+                roles.append(("kv", j))
+            else:
+                roles.append(("q", b - min(j + 1, K)))
+        else:
+            roles.append(("kv", b) if b < K else ("q", b - K))
+    return roles
+
+
+def test_kv_workgroups_spread_over_large_two_heads_grids():
+    # kv first, except with two heads and four kv tokens per wavefront from
+    # 2^18 q rows: kv workgroup j at grid index j * P, P = floor(3N / 4K)
+    # made odd by rounding down, so the kv workgroups cover the first 55-75%
+    # of the grid and fall on every XCD (index mod 8) in turn.
+    for H, T, P in ((16, 16384, 23), (8, 32768, 11), (2, 131072, 3), (16, 131072, 23), (4, 65536, 5)):
+        s = qp.qkv_prep_launch_shape(qp.make_config(H), 256, T)
+        assert (s.rows_per_wave, s.kv_per_wave) == (2, 4) and s.kv_period == P
+        assert P % 2 == 1 and P == (3 * s.grid // (4 * s.kv_blocks)) - (3 * s.grid // (4 * s.kv_blocks) + 1) % 2
+        last = (s.kv_blocks - 1) * P
+        assert 0.55 * s.grid <= last < 0.75 * s.grid
+        assert len({(j * P) % 8 for j in range(min(s.kv_blocks, 8))}) == min(s.kv_blocks, 8)
+    for H, T in ((8, 16384), (16, 16383), (64, 65536), (32, 16384), (2, 65535), (17, 32768)):
+        assert qp.qkv_prep_launch_shape(qp.make_config(H), 256, T).kv_period == 0      # below 2^18 rows, or one row
+    forced = qp.qkv_prep_launch_shape(qp.make_config(64, rows_per_wave=2, kv_per_wave=4), 256, 8192)
+    assert forced.kv_period > 0 and forced.waves_per_block == 2                            # the shape in use decides
+    assert qp.qkv_prep_launch_shape(qp.make_config(16, kv_per_wave=2), 256, 16384).kv_period == 0
+    assert qp.qkv_prep_launch_shape(qp.make_config(16), 256, 0).kv_period == 0
+
+
+def test_grid_mapping_covers_every_workgroup_once():
+    # Every kv and q workgroup index appears exactly once, with and without
+    # the spread, on ragged sizes around the threshold and the forced shapes.
+    cases = [(9, 29127, {}), (9, 29128, {}), (3, 87382, {}), (16, 16385, {}), (5, 60000, {"waves_per_block": 1}),
+             (12, 40000, {"waves_per_block": 4}), (64, 4099, {"rows_per_wave": 2, "kv_per_wave": 4}), (8, 1000, {})]
+    seen_spread = 0
+    for H, T, forced in cases:
+        s = qp.qkv_prep_launch_shape(qp.make_config(H, **forced), 256, T)
+        seen_spread += s.kv_period > 0
+        roles = _grid_roles(s)
+        kv = sorted(j for r, j in roles if r == "kv")
+        q = sorted(j for r, j in roles if r == "q")
+        assert kv == list(range(s.kv_blocks)) and q == list(range(s.q_blocks)), (H, T, forced)
+    assert seen_spread >= 5
 
 
 def test_fast_division_used_by_the_kernel():

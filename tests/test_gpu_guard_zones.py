@@ -51,7 +51,8 @@ def same_bytes(a, b):
 @pytest.mark.parametrize("T,H,rpw,kv_store", [
     (1, 1, 0, qp.KV_FP8), (777, 5, 1, qp.KV_FP8), (777, 5, 2, qp.KV_FP8), (300, 64, 0, qp.KV_FP8),
     (4096, 64, 1, qp.KV_FP8), (300, 8, 1, qp.KV_BF16), (300, 8, 2, qp.KV_BF16),
-    (2051, 64, 0, qp.KV_FP8), (2051, 64, 0, qp.KV_BF16)])   # four tokens per kv wavefront, ragged
+    (2051, 64, 0, qp.KV_FP8), (2051, 64, 0, qp.KV_BF16),    # four tokens per kv wavefront, ragged
+    (29131, 9, 0, qp.KV_FP8)])                              # kv workgroups spread through the grid
 def test_operator_writes_only_q_and_the_cache(T, H, rpw, kv_store):
     w = W.custom(T, H, seed=1300 + T + H, num_skip=min(T // 4, 5))
     inp = W.make_inputs(w, device=DEV)

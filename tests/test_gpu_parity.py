@@ -137,6 +137,25 @@ def test_both_sides_of_the_launch_thresholds(T, H):
     check(W.custom(T, H, seed=330 + T + H, num_skip=5))
 
 
+@pytest.mark.parametrize("T,H,cfg", [
+    (29127, 9, {}), (29128, 9, {}), (131075, 2, {}), (65537, 5, {}), (40000, 16, {}),
+    (29128, 9, {"kv_store": 1}), (50000, 7, {"waves_per_block": 1}), (60001, 12, {"waves_per_block": 4}),
+    (8192, 64, {"rows_per_wave": 2, "kv_per_wave": 4}), (40000, 16, {"kv_per_wave": 2})])
+def test_kv_workgroups_spread_through_the_grid(T, H, cfg):
+    # Two heads and four kv tokens per wavefront from 2^18 q rows: the kv
+    # workgroups sit every kv_period workgroups through the first 55-75% of
+    # the grid instead of first.  Both sides of the threshold (29127 x 9 =
+    # 2^18 - 1 rows), ragged and odd sizes, both cache modes, forced
+    # workgroup widths and a forced two-heads shape at 64 heads; with two kv
+    # tokens per wavefront the kv workgroups come first.
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    shape_cfg = {k: v for k, v in cfg.items() if k != "kv_store"}
+    shape = QkvPrep(H, **shape_cfg).launch_shape(T)
+    spread = shape.rows_per_wave == 2 and shape.kv_per_wave == 4 and T * H >= 1 << 18
+    assert (shape.kv_period > 0) == spread
+    check(W.custom(T, H, seed=360 + T + H, num_skip=7), **cfg)
+
+
 def _random_cases(n, seed, few_heads=False):
     """n seeded configurations that mix every knob at once: ragged token and
     head counts (up to 2^18 q rows), block sizes, table lengths, skipped
