@@ -77,10 +77,15 @@ int64_t kv_spread(const qkvp::LaunchShape &s, int64_t q_rows)
 //
 // From 2^16 q rows:
 //  * one q row per wavefront, with system-scope stores (2048x64: 41.7
-//    against 42.5 us for two heads), except with at most 16 heads from 2^14
+//    against 42.5 us for two heads), except with at most 56 heads from 2^14
 //    tokens, where two consecutive heads of one token per wavefront (the
 //    token's position, cos/sin row and q weight loaded once for both rows)
-//    are 2-7% faster (32768x8: 94.6 against 101.1 us);
+//    are faster: 2-7% with at most 16 heads (32768x8: 94.6 against 101.1
+//    us), and 0.8-4.4% with 17-56 heads, where the q rows pass 2^18 and the
+//    kv workgroups are spread (kv_spread; 32768x20: 210.5 against 220.1 us,
+//    65536x24: 497.6 against 516.8).  With 57-63 heads the two tie or one
+//    row wins (16384x63: 2% for one row), and from 64 heads one row wins or
+//    ties (32768x64: 0.5%);
 //  * four consecutive tokens' kv rows per kv wavefront, their loads issued
 //    together (the kv wavefronts run first, as a latency-bound burst;
 //    2048x32: 22.3 against 23.3 us);
@@ -127,7 +132,7 @@ qkvp::LaunchShape choose_shape(const qkv_prep_config &c, int num_cus, int64_t T)
     s.convert = c.convert ? c.convert : 2;
     int rows, kv;
     if (q_rows >= ((int64_t)1 << 16)) {
-        rows = H > 1 && H <= 16 && T >= ((int64_t)1 << 14) ? 2 : 1;
+        rows = H > 1 && H <= 56 && T >= ((int64_t)1 << 14) ? 2 : 1;
         kv = 4;
     } else {
         const int64_t one_row_four_kv = T > 8192 ? 3 << 13 : T > 4096 ? 1 << 15 : 3 << 14;

@@ -240,7 +240,7 @@ int qkv_prep_supported(int32_t num_heads, int32_t head_dim, int32_t rope_dim);
  * no device, so the launch heuristic can be inspected anywhere.  The current
  * heuristic, for T tokens of H heads and q = T * H rows, as (q rows per
  * wavefront, wavefronts per workgroup, kv tokens per kv wavefront):
- *   q >= 2^16:  (2, 2, 4) with 2 <= H <= 16 and T >= 2^14, else (1, 1, 4);
+ *   q >= 2^16:  (2, 2, 4) with 2 <= H <= 56 and T >= 2^14, else (1, 1, 4);
  *   else q >= 49152, or q >= 2^15 with T > 4096, or q >= 24576 with
  *               T > 8192:  (1, 1, 4);
  *   else q >= 2^15 with T >= 2048:  (2, 2, 2);

@@ -165,7 +165,7 @@ def test_launch_shape_heuristic():
     assert small.kv_per_wave == 1
     assert small.kv_blocks == 16 and small.q_blocks == 16 * 32 and small.grid == 16 * 33
     # from 2^16 q rows: four consecutive tokens per kv wavefront, one q row
-    # per wavefront (two heads, two wavefronts per workgroup with at most 16
+    # per wavefront (two heads, two wavefronts per workgroup with at most 56
     # heads from 2^14 tokens)
     at = qp.qkv_prep_launch_shape(cfg, 256, 1024)
     assert at.kv_per_wave == 4 and at.kv_blocks == 1024 // 4 and at.rows_per_wave == 1
@@ -174,7 +174,8 @@ def test_launch_shape_heuristic():
     few = qp.qkv_prep_launch_shape(qp.make_config(8), 256, 16384)
     assert (few.rows_per_wave, few.waves_per_block, few.kv_per_wave) == (2, 2, 4)
     assert few.kv_blocks == 16384 // 8 and few.q_blocks == 16384 * 4 // 2
-    assert _shape(16, 16384)[0] == 2 and _shape(17, 16384)[0] == 1 and _shape(32, 65536)[0] == 1
+    assert _shape(16, 16384)[0] == 2 and _shape(17, 16384)[0] == 2 and _shape(56, 16384)[0] == 2
+    assert _shape(57, 16384)[0] == 1 and _shape(40, 16383)[0] == 1 and _shape(64, 65536)[0] == 1
     # below 2^16: one row and four kv tokens from 49152 q rows, from 2^15
     # with more than 4096 tokens, from 24576 with more than 8192
     assert _shape(64, 1023) == (1, 1, 4)                                     # 65472 rows
@@ -267,7 +268,7 @@ def test_kv_workgroups_spread_over_large_two_heads_grids():
         last = (s.kv_blocks - 1) * P
         assert 0.55 * s.grid <= last < 0.75 * s.grid
         assert len({(j * P) % 8 for j in range(min(s.kv_blocks, 8))}) == min(s.kv_blocks, 8)
-    for H, T in ((8, 16384), (16, 16383), (64, 65536), (32, 16384), (2, 65535), (17, 32768)):
+    for H, T in ((8, 16384), (16, 16383), (64, 65536), (32, 16383), (2, 65535), (57, 32768)):
         assert qp.qkv_prep_launch_shape(qp.make_config(H), 256, T).kv_period == 0      # below 2^18 rows, or one row
     forced = qp.qkv_prep_launch_shape(qp.make_config(64, rows_per_wave=2, kv_per_wave=4), 256, 8192)
     assert forced.kv_period > 0 and forced.waves_per_block == 2                            # the shape in use decides

@@ -109,7 +109,7 @@ def _expected_shape(T, H):
     workgroup, kv tokens per wavefront)."""
     q = T * H
     if q >= 1 << 16:
-        two = 1 < H <= 16 and T >= 1 << 14
+        two = 1 < H <= 56 and T >= 1 << 14
         return (2, 2, 4) if two else (1, 1, 4)
     if q >= (3 << 13 if T > 8192 else 1 << 15 if T > 4096 else 3 << 14):
         return (1, 1, 4)
@@ -124,7 +124,7 @@ def _expected_shape(T, H):
                                  (16383, 16), (16384, 16), (2047, 16), (2048, 16), (4096, 8), (1024, 32),
                                  (4096, 12), (4096, 11), (4097, 8), (8193, 3), (8192, 3), (24576, 1),
                                  (3072, 2), (3071, 2), (2048, 7), (2047, 7), (2048, 11), (4096, 4),
-                                 (4095, 4), (8193, 1), (8192, 1)])
+                                 (4095, 4), (8193, 1), (8192, 1), (16384, 56), (16384, 57), (16383, 40)])
 def test_both_sides_of_the_launch_thresholds(T, H):
     # Default launch on each side of each boundary of the heuristic: 2^16 q
     # rows; one row and four kv tokens from 49152, 2^15 (above 4096 tokens)
