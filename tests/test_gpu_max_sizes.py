@@ -1,8 +1,9 @@
 """The largest batches one MI355X holds.  From about 2^26 q rows the
 operator's grid passes the 2^32 work-items one dispatch takes, so it is
 enqueued as consecutive dispatches of the same kernel (two at 600000 x 128,
-three at 1100000 x 128), each starting at its own workgroup index.  q alone
-is 79 GB and 144 GB here.  Every token cannot be
+three at 1100000 x 128, two at 2400000 x 56 with two heads per wavefront and
+the kv workgroups spread), each starting at its own workgroup index.  q
+alone is 79, 144 and 138 GB here.  Every token cannot be
 checked on the host at this size, so a seeded sample of tokens (the first, the
 last, skipped ones and random ones) is checked one by one against the oracle:
 each sampled token's q rows bit for bit, and its cache slot byte for byte (the
@@ -27,8 +28,10 @@ def note(msg):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("T,H,dispatches", [(600000, 128, 2), (1100000, 128, 3)])
+@pytest.mark.parametrize("T,H,dispatches", [(600000, 128, 2), (1100000, 128, 3), (2400000, 56, 2)])
 def test_largest_batches_on_sampled_tokens(T, H, dispatches):
+    # 2400000 x 56: two heads per wavefront, two wavefronts per workgroup,
+    # and the kv workgroups spread through the grid, over two dispatches.
     w = W.custom(T, H, seed=T // 1000 + H, num_skip=7)
     need = T * H * 1024 + T * 1024 + w.num_blocks * w.block_size * qp.SLOT_BYTES + (2 << 30)
     torch.cuda.empty_cache()
@@ -37,11 +40,14 @@ def test_largest_batches_on_sampled_tokens(T, H, dispatches):
         pytest.skip("needs %.0f GB of free device memory, %.0f GB free" % (need / 1e9, free / 1e9))
     op = qp.QkvPrep(H, block_size=w.block_size, eps=w.eps)
     shape = op.launch_shape(T)
-    assert shape.rows_per_wave == 1 and shape.waves_per_block == 1
-    per = (2 ** 32 - 1) // 64                       # workgroups one dispatch takes
+    if H > 56:
+        assert shape.rows_per_wave == 1 and shape.waves_per_block == 1 and shape.kv_period == 0
+    else:
+        assert shape.rows_per_wave == 2 and shape.waves_per_block == 2 and shape.kv_period > 0
+    per = (2 ** 32 - 1) // (64 * shape.waves_per_block)     # workgroups one dispatch takes
     assert -(-shape.grid // per) == dispatches
     note("case %s: drawing inputs (q %.0f GB), launch %s" % (
-        w.label, T * H * 1024 / 1e9, (shape.rows_per_wave, shape.kv_per_wave, shape.grid)))
+        w.label, T * H * 1024 / 1e9, (shape.rows_per_wave, shape.kv_per_wave, shape.grid, shape.kv_period)))
     inp = W.make_inputs(w, device=DEV)
     try:
         slots_all = inp["slot_mapping"]
