@@ -615,6 +615,85 @@ def sweep_summary(results):
             "max_heuristic_over_best": worst[0], "worst": worst[1]}
 
 
+# ----------------------------------------------------------------- streams mode
+
+def stream_table(probe):
+    """The streams timed by --mode streams: (label, kind, load policy, store
+    policy, sleep, lanes per workgroup).  Reads, writes, copies and in-place
+    updates with the cache-policy bits the kernels choose between, the pause
+    before the store that the in-place update needs, and the workgroup sizes
+    of the copy and the update."""
+    R, Wr, C, U = probe.READ, probe.WRITE, probe.COPY, probe.UPDATE
+    NT, SC1, SC0 = probe.NT, probe.SC1, probe.SC0
+    return [
+        ("read plain", R, 0, 0, 0, 256),
+        ("read nt", R, NT, 0, 0, 256),
+        ("read nt sc1", R, NT | SC1, 0, 0, 256),
+        ("write plain", Wr, 0, 0, 0, 256),
+        ("write nt", Wr, 0, NT, 0, 256),
+        ("write sc1", Wr, 0, SC1, 0, 256),
+        ("write nt sc1", Wr, 0, NT | SC1, 0, 256),
+        ("write sc0 nt sc1", Wr, 0, SC0 | NT | SC1, 0, 256),
+        ("copy plain -> plain", C, 0, 0, 0, 256),
+        ("copy nt -> nt", C, NT, NT, 0, 256),
+        ("copy nt -> nt sc1", C, NT, NT | SC1, 0, 256),
+        ("copy nt sc1 -> nt sc1", C, NT | SC1, NT | SC1, 0, 256),
+        ("copy nt -> nt sc1, sleep", C, NT, NT | SC1, 1, 256),
+        ("copy nt -> nt sc1, 64 lanes", C, NT, NT | SC1, 0, 64),
+        ("copy nt -> nt sc1, 1024 lanes", C, NT, NT | SC1, 0, 1024),
+        ("update nt -> nt", U, NT, NT, 0, 64),
+        ("update nt -> nt, sleep", U, NT, NT, 1, 64),
+        ("update nt -> nt sc1", U, NT, NT | SC1, 0, 64),
+        ("update nt -> nt sc1, sleep", U, NT, NT | SC1, 1, 64),
+        ("update plain -> plain, sleep", U, 0, 0, 1, 64),
+        ("update nt -> nt sc1, sleep, 256 lanes", U, NT, NT | SC1, 1, 256),
+    ]
+
+
+def sweep_streams(torch, probe, nbytes, launches=20, rounds=4):
+    """Every stream of stream_table over `nbytes`-byte buffers: the region
+    time of `launches` back-to-back launches, best of `rounds` interleaved
+    rounds (alternate rounds in reverse order), after warming the chip.
+    Counted traffic: nbytes for a read or a write, 2 * nbytes for a copy or an
+    update."""
+    table = stream_table(probe)
+    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")   # chunks XOR to 0, never the key
+    dst = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    key = 0x9E3779B9
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launcher(kind, lp, sp, sleep, lanes):
+        if kind == probe.READ:
+            d, s_ = sink.data_ptr(), src.data_ptr()
+        elif kind == probe.COPY:
+            d, s_ = dst.data_ptr(), src.data_ptr()
+        else:
+            d, s_ = dst.data_ptr(), None
+        return lambda: probe.qkv_prep_probe_stream(kind, lp, sp, sleep, lanes, d, s_, nbytes, key, stream)
+
+    fns = [launcher(*row[1:]) for row in table]
+    warm_chip(torch, probe)
+    best = [float("inf")] * len(table)
+    for rnd in range(rounds):
+        order = range(len(table)) if rnd % 2 == 0 else reversed(range(len(table)))
+        for i in order:
+            for _ in range(3):
+                fns[i]()
+            _, region = time_region(torch, fns[i], launches)
+            best[i] = min(best[i], region / launches)
+    if int(sink[0].item()) != 0:
+        raise RuntimeError("read stream sink was written: the source did not hold zeros")
+    rows = []
+    for (label, kind, lp, sp, sleep, lanes), t in zip(table, best):
+        traffic = nbytes * (2 if kind in (probe.COPY, probe.UPDATE) else 1)
+        rows.append({"stream": label, "kind": kind, "load_policy": lp, "store_policy": sp, "sleep": sleep,
+                     "lanes": lanes, "us": round(t * 1e6, 2), "gbps": round(traffic / t / 1e9, 1)})
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"mode": "streams", "bytes": nbytes, "launches": launches, "rounds": rounds, "streams": rows}
+
+
 # ----------------------------------------------------------------- main
 
 def main():
@@ -630,12 +709,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "profile", "sweep"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "profile", "sweep", "streams"], default="bench",
                     help="profile: a short fixed program for rocprofv3 (no JSON line); sweep: every "
-                         "forced launch shape of the operator on --workload (one JSON line)")
+                         "forced launch shape of the operator on --workload (one JSON line); streams: "
+                         "read/write/copy/update streams by cache policy (one JSON line per size)")
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--sizes", default="",
-                    help="sweep mode: comma-separated TxH sizes (decode-like inputs) instead of --workload")
+                    help="sweep mode: comma-separated TxH sizes (decode-like inputs) instead of --workload; "
+                         "streams mode: comma-separated buffer sizes in MiB (default 512,2048)")
     ap.add_argument("--shapes", default="",
                     help="sweep mode: only these shapes, as rows_per_wave:waves_per_block:kv_per_wave,...")
     args = ap.parse_args()
@@ -658,6 +739,10 @@ def main():
         sys.exit(1)
     if args.mode == "profile":
         profile_run(torch, qp, probe, args.workload, args.launches)
+        return
+    if args.mode == "streams":
+        for mib in (args.sizes or "512,2048").split(","):
+            print(json.dumps(sweep_streams(torch, probe, int(mib) << 20)), flush=True)
         return
     if args.mode == "sweep":
         results = []

@@ -1,7 +1,9 @@
 // The measurement and verification probes of libqkv_prep_probe.so (see
-// include/qkv_prep_probe.h): a streaming copy and an in-place streaming update
-// used as bandwidth ceilings, and the operators' own number-format code run on
-// arrays so that tests can compare it with a reference on every input pattern.
+// include/qkv_prep_probe.h): policy-selectable read, write, copy and in-place
+// update streams, two of which (a copy and an in-place update at their fastest
+// settings) serve as bandwidth ceilings, and the operators' own number-format
+// code run on arrays so that tests can compare it with a reference on every
+// input pattern.
 // None of this is part of the operators; it is built into its own library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -11,59 +13,159 @@
 
 namespace {
 
-using qkvp::dev::store_sys;
 using qkvp::dev::u32x2;
 using qkvp::dev::u32x4;
-// One 16-byte non-temporal load and one 16-byte store per lane, 256-lane
-// blocks: the fastest of the copy shapes measured on MI355X (1, 2, 4, 8 and 16
-// loads per lane; 256, 512 and 1024 lanes per block; plain or non-temporal;
-// natural or XCD-contiguous block order), about 6.4-6.5 TB/s at 0.5-4 GiB with
-// non-temporal stores.  A sweep of the load and store cache-policy bits (sc0,
-// sc1, nt) then found the non-temporal system-scope store (nt sc1) best, at
-// ~6.7 TB/s; every load policy with nt set is within noise of the others.
-constexpr int kUnroll = 1;
-constexpr int kThreads = 256;
 
-// Block b copies kUnroll * kThreads consecutive 16-byte units; all loads are
-// issued before the first store.
-__global__ __launch_bounds__(kThreads) void stream_copy(u32x4 *dst, const u32x4 *src, int64_t n)
+// Policy-selectable streams (qkv_prep_probe_stream): one 16-byte access per
+// lane, blockDim.x lanes per workgroup, every access through a buffer
+// descriptor whose base is the workgroup's first chunk, so any combination of
+// the cache-policy bits can be put on the loads and on the stores.  These are
+// the streams behind the read / write / copy / update rates and the
+// cache-policy comparison quoted in the kernels' comments.
+constexpr int kSc0 = 1, kNt = 2, kSc1 = 16;
+enum StreamKind { kRead = 0, kWrite = 1, kCopy = 2, kUpdate = 3 };
+
+template <int P>
+__device__ __forceinline__ u32x4 load_policy(const u32x4 *base, uint32_t bytes, uint32_t off)
 {
-    const int64_t first = (int64_t)blockIdx.x * (kThreads * kUnroll);
-    const int64_t base = first + threadIdx.x;
-    u32x4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t i = base + (int64_t)u * kThreads;
-        if (i < n)
-            v[u] = __builtin_nontemporal_load(src + i);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t i = base + (int64_t)u * kThreads;
-        if (i < n)
-            store_sys(dst + first, kThreads * kUnroll * 16u, (uint32_t)(i - first) * 16u, v[u]);
+    return __builtin_amdgcn_raw_buffer_load_b128(qkvp::dev::stream_rsrc(const_cast<u32x4 *>(base), bytes),
+                                                  (int)off, 0, P);
+}
+
+template <int P>
+__device__ __forceinline__ void store_policy(u32x4 *base, uint32_t bytes, uint32_t off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, qkvp::dev::stream_rsrc(base, bytes), (int)off, 0, P);
+}
+
+// LP / SP: the load / store policy bits.  SLEEP: the wavefront pauses
+// (s_sleep 2, about 128 cycles) between its load's arrival and its store.
+// A read keeps its data live by comparing the XOR of each chunk's four words
+// with `key` and writing the key to the sink word dst[0] on a match.
+template <int KIND, int LP, int SP, bool SLEEP>
+__device__ __forceinline__ void stream_body(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
+{
+    const int64_t first = (int64_t)blockIdx.x * blockDim.x;
+    const int64_t i = first + threadIdx.x;
+    if (i >= n)
+        return;
+    const int64_t left = n - first;
+    const uint32_t span = (uint32_t)(left < (int64_t)blockDim.x ? left : (int64_t)blockDim.x) * 16u;
+    const uint32_t off = threadIdx.x * 16u;
+    if constexpr (KIND == kRead) {
+        const u32x4 v = load_policy<LP>(src + first, span, off);
+        if ((v[0] ^ v[1] ^ v[2] ^ v[3]) == key)
+            *reinterpret_cast<uint32_t *>(dst) = key;
+    } else if constexpr (KIND == kWrite) {
+        store_policy<SP>(dst + first, span, off, u32x4{(uint32_t)i, (uint32_t)(i >> 32), key, ~key});
+    } else {
+        u32x4 v = load_policy<LP>(KIND == kCopy ? src + first : dst + first, span, off);
+        if constexpr (KIND == kUpdate)
+            v[0] += 1u;
+        if constexpr (SLEEP)
+            __builtin_amdgcn_s_sleep(2);
+        store_policy<SP>(dst + first, span, off, v);
     }
 }
 
-// In-place update, one 16-byte chunk per lane, one wavefront per workgroup.
-// Measured on MI355X at 4 GiB: a store issued right after its load's data
-// arrives streams at only ~4.5 TB/s; pausing the wavefront for a moment
-// (s_sleep 2, ~128 cycles) between the load and the store gives ~6.7 TB/s,
-// above the two-buffer copy.  A wave-wide reduction in the same place does not
-// help (~4.5 TB/s); sleeps of 2 to 32 units are the same.  The nt sc1 store
-// policy adds ~1.5% (~6.8 TB/s at 2 GiB).
-constexpr int kUpdateThreads = 64;
-
-__global__ __launch_bounds__(kUpdateThreads) void stream_update(u32x4 *buf, int64_t n)
+template <int KIND, int LP, int SP, bool SLEEP>
+__global__ __launch_bounds__(1024) void policy_stream(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
 {
-    const int64_t first = (int64_t)blockIdx.x * kUpdateThreads;
-    const int64_t i = first + threadIdx.x;
-    if (i < n) {
-        u32x4 v = __builtin_nontemporal_load(buf + i);
-        v[0] += 1u;
-        __builtin_amdgcn_s_sleep(2);
-        store_sys(buf + first, kUpdateThreads * 16u, threadIdx.x * 16u, v);
+    stream_body<KIND, LP, SP, SLEEP>(dst, src, n, key);
+}
+
+// The two ceilings are the policy streams at their fastest settings in the
+// streams sweep (bench.py --mode streams, 512 MiB and 2 GiB buffers on
+// MI355X): one wavefront per workgroup, non-temporal loads, nt sc1 stores.
+// Copy: 6.80 TB/s with 64 lanes per workgroup, 6.67 with 256 and 6.29-6.49
+// with 1024.  In-place update: 6.83-6.88 TB/s, the same with or without a
+// pause before the store; 6.64-6.67 with 256 lanes.  They keep kernels of
+// their own so that a profile can tell them apart.
+constexpr int kCeilingLanes = 64;
+
+__global__ __launch_bounds__(kCeilingLanes) void stream_copy(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
+{
+    stream_body<kCopy, kNt, kNt | kSc1, false>(dst, src, n, key);
+}
+
+__global__ __launch_bounds__(kCeilingLanes) void stream_update(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
+{
+    stream_body<kUpdate, kNt, kNt | kSc1, false>(dst, src, n, key);
+}
+
+struct StreamLaunch {
+    dim3 grid, block;
+    hipStream_t stream;
+    u32x4 *dst;
+    const u32x4 *src;
+    int64_t n;
+    uint32_t key;
+};
+
+template <int KIND, int LP, int SP, bool SLEEP>
+bool launch_stream(const StreamLaunch &L)
+{
+    hipLaunchKernelGGL((policy_stream<KIND, LP, SP, SLEEP>), L.grid, L.block, 0, L.stream, L.dst, L.src, L.n, L.key);
+    return true;
+}
+
+// The accepted policies: loads plain, nt or nt sc1; stores plain, nt, sc1,
+// nt sc1 or sc0 nt sc1.  Anything else returns false (nothing launched).
+template <int KIND, int LP, bool SLEEP>
+bool launch_by_store(const StreamLaunch &L, int sp)
+{
+    switch (sp) {
+    case 0: return launch_stream<KIND, LP, 0, SLEEP>(L);
+    case kNt: return launch_stream<KIND, LP, kNt, SLEEP>(L);
+    case kSc1: return launch_stream<KIND, LP, kSc1, SLEEP>(L);
+    case kNt | kSc1: return launch_stream<KIND, LP, kNt | kSc1, SLEEP>(L);
+    case kSc0 | kNt | kSc1: return launch_stream<KIND, LP, kSc0 | kNt | kSc1, SLEEP>(L);
+    default: return false;
     }
+}
+
+template <int KIND, bool SLEEP>
+bool launch_by_load(const StreamLaunch &L, int lp, int sp)
+{
+    switch (lp) {
+    case 0: return launch_by_store<KIND, 0, SLEEP>(L, sp);
+    case kNt: return launch_by_store<KIND, kNt, SLEEP>(L, sp);
+    case kNt | kSc1: return launch_by_store<KIND, kNt | kSc1, SLEEP>(L, sp);
+    default: return false;
+    }
+}
+
+bool launch_policy_stream(int kind, int lp, int sp, bool sleep, const StreamLaunch &L)
+{
+    switch (kind) {
+    case kRead:
+        switch (lp) {
+        case 0: return launch_stream<kRead, 0, 0, false>(L);
+        case kNt: return launch_stream<kRead, kNt, 0, false>(L);
+        case kNt | kSc1: return launch_stream<kRead, kNt | kSc1, 0, false>(L);
+        default: return false;
+        }
+    case kWrite:
+        switch (sp) {
+        case 0: return launch_stream<kWrite, 0, 0, false>(L);
+        case kNt: return launch_stream<kWrite, 0, kNt, false>(L);
+        case kSc1: return launch_stream<kWrite, 0, kSc1, false>(L);
+        case kNt | kSc1: return launch_stream<kWrite, 0, kNt | kSc1, false>(L);
+        case kSc0 | kNt | kSc1: return launch_stream<kWrite, 0, kSc0 | kNt | kSc1, false>(L);
+        default: return false;
+        }
+    case kCopy:
+        return sleep ? launch_by_load<kCopy, true>(L, lp, sp) : launch_by_load<kCopy, false>(L, lp, sp);
+    case kUpdate:
+        return sleep ? launch_by_load<kUpdate, true>(L, lp, sp) : launch_by_load<kUpdate, false>(L, lp, sp);
+    default: return false;
+    }
+}
+
+bool valid_load_policy(int p) { return p == 0 || p == kNt || p == (kNt | kSc1); }
+bool valid_store_policy(int p)
+{
+    return p == 0 || p == kNt || p == kSc1 || p == (kNt | kSc1) || p == (kSc0 | kNt | kSc1);
 }
 
 // The operator's conversions (qkvp::dev::pack_e4m3 / pack_bf16) on four
@@ -127,19 +229,29 @@ extern "C" int qkv_prep_probe_convert(const float *in, int64_t n, void *e4m3_out
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
+static int ceiling_stream(int kind, void *dst, const void *src, int64_t bytes, hipStream_t stream)
+{
+    const int64_t n = bytes / 16;
+    const int64_t blocks = (n + kCeilingLanes - 1) / kCeilingLanes;
+    if (blocks >= ((int64_t)1 << 31))
+        return 1;
+    const dim3 grid((uint32_t)blocks), block(kCeilingLanes);
+    u32x4 *d = static_cast<u32x4 *>(dst);
+    const u32x4 *s = static_cast<const u32x4 *>(src);
+    if (kind == kCopy)
+        hipLaunchKernelGGL(stream_copy, grid, block, 0, stream, d, s, n, 0u);
+    else
+        hipLaunchKernelGGL(stream_update, grid, block, 0, stream, d, s, n, 0u);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
 extern "C" int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream)
 {
     if (bytes < 0 || (bytes > 0 && !buf) || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15))
         return 1;
     if (bytes == 0)
         return 0;
-    const int64_t n = bytes / 16;
-    const int64_t blocks = (n + kUpdateThreads - 1) / kUpdateThreads;
-    if (blocks >= ((int64_t)1 << 31))
-        return 1;
-    hipLaunchKernelGGL(stream_update, dim3((uint32_t)blocks), dim3(kUpdateThreads), 0,
-                       static_cast<hipStream_t>(stream), static_cast<u32x4 *>(buf), n);
-    return hipGetLastError() == hipSuccess ? 0 : 5;
+    return ceiling_stream(kUpdate, buf, nullptr, bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, void *stream)
@@ -149,15 +261,7 @@ extern "C" int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, vo
         return 1;
     if (bytes == 0)
         return 0;
-    const int64_t n = bytes / 16;
-    const int64_t per_block = (int64_t)kThreads * kUnroll;
-    const int64_t blocks = (n + per_block - 1) / per_block;
-    if (blocks >= ((int64_t)1 << 31))
-        return 1;
-    hipLaunchKernelGGL(stream_copy, dim3((uint32_t)blocks), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), static_cast<u32x4 *>(dst),
-                       static_cast<const u32x4 *>(src), n);
-    return hipGetLastError() == hipSuccess ? 0 : 5;
+    return ceiling_stream(kCopy, dst, src, bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int qkv_prep_probe_ue8m0(const float *in, int64_t n, void *op_byte_out, void *mx_byte_out,
@@ -175,5 +279,49 @@ extern "C" int qkv_prep_probe_ue8m0(const float *in, int64_t n, void *op_byte_ou
     hipLaunchKernelGGL(ue8m0_probe, dim3((uint32_t)blocks), dim3(256), 0, static_cast<hipStream_t>(stream), in, n,
                        static_cast<uint8_t *>(op_byte_out), static_cast<uint8_t *>(mx_byte_out),
                        static_cast<float *>(mx_inverse_out));
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t store_policy, int32_t sleep,
+                                     int32_t lanes_per_block, void *dst, const void *src, int64_t bytes,
+                                     uint32_t key, void *stream)
+{
+    const uintptr_t pd = reinterpret_cast<uintptr_t>(dst), ps = reinterpret_cast<uintptr_t>(src);
+    const bool reads = kind == kRead || kind == kCopy || kind == kUpdate;
+    const bool writes = kind == kWrite || kind == kCopy || kind == kUpdate;
+    if (kind < kRead || kind > kUpdate || bytes < 0 || (bytes & 15) || (sleep != 0 && sleep != 1))
+        return 1;
+    if (lanes_per_block != 64 && lanes_per_block != 128 && lanes_per_block != 256 && lanes_per_block != 512 &&
+        lanes_per_block != 1024)
+        return 1;
+    if (reads ? !valid_load_policy(load_policy) : load_policy != 0)
+        return 1;
+    if (writes ? !valid_store_policy(store_policy) : store_policy != 0)
+        return 1;
+    if (sleep && kind != kCopy && kind != kUpdate)
+        return 1;
+    // dst: the sink word of a read (4-byte aligned), else the written range
+    // (16-byte aligned); src: the range a read or copy loads, NULL otherwise.
+    const bool needs_src = kind == kRead || kind == kCopy;
+    if (!dst || (pd & (kind == kRead ? 3 : 15)) || (needs_src ? (!src || (ps & 15)) : src != nullptr))
+        return 1;
+    if (kind == kCopy && bytes > 0 && pd < ps + (uint64_t)bytes && ps < pd + (uint64_t)bytes)
+        return 1;
+    if (bytes == 0)
+        return 0;
+    const int64_t n = bytes / 16;
+    const int64_t blocks = (n + lanes_per_block - 1) / lanes_per_block;
+    if (blocks >= ((int64_t)1 << 31))
+        return 1;
+    StreamLaunch L;
+    L.grid = dim3((uint32_t)blocks);
+    L.block = dim3((uint32_t)lanes_per_block);
+    L.stream = static_cast<hipStream_t>(stream);
+    L.dst = static_cast<u32x4 *>(dst);
+    L.src = static_cast<const u32x4 *>(src);
+    L.n = n;
+    L.key = key;
+    if (!launch_policy_stream(kind, load_policy, store_policy, sleep != 0, L))
+        return 1;
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }

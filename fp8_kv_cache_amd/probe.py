@@ -1,8 +1,8 @@
 """Python binding of the probe library, libqkv_prep_probe.so
 (include/qkv_prep_probe.h): bandwidth ceilings (a streaming copy, an in-place
-streaming update) and the operators' number-format code run on arrays.  Used
-by the tests and the benchmark; the operators never load it.  Argument
-marshalling only, with the C names."""
+streaming update), policy-selectable streams, and the operators' number-format
+code run on arrays.  Used by the tests and the benchmark; the operators never
+load it.  Argument marshalling only, with the C names."""
 from __future__ import annotations
 
 import ctypes
@@ -13,7 +13,12 @@ from fp8_kv_cache_amd.qkv_prep import OK, QkvPrepError
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqkv_prep_probe.so")
 
-EXPORTED = ("qkv_prep_probe_copy", "qkv_prep_probe_update", "qkv_prep_probe_convert", "qkv_prep_probe_ue8m0")
+EXPORTED = ("qkv_prep_probe_copy", "qkv_prep_probe_update", "qkv_prep_probe_stream", "qkv_prep_probe_convert",
+            "qkv_prep_probe_ue8m0")
+
+# qkv_prep_probe_stream kinds and cache-policy bits.
+READ, WRITE, COPY, UPDATE = 0, 1, 2, 3
+SC0, NT, SC1 = 1, 2, 16
 
 
 def _load():
@@ -24,6 +29,8 @@ def _load():
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.qkv_prep_probe_copy.argtypes = [vp, vp, i64, vp]
     L.qkv_prep_probe_update.argtypes = [vp, i64, vp]
+    i32 = ctypes.c_int32
+    L.qkv_prep_probe_stream.argtypes = [i32, i32, i32, i32, i32, vp, vp, i64, ctypes.c_uint32, vp]
     L.qkv_prep_probe_convert.argtypes = [vp, i64, vp, vp, ctypes.c_int32, vp]
     L.qkv_prep_probe_ue8m0.argtypes = [vp, i64, vp, vp, vp, vp]
     for name in EXPORTED:
@@ -51,6 +58,13 @@ def qkv_prep_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) ->
 def qkv_prep_probe_update(buf_ptr: int, nbytes: int, stream=None) -> None:
     """The in-place streaming-update probe (a bandwidth ceiling)."""
     _check(_lib.qkv_prep_probe_update(buf_ptr, nbytes, stream), "qkv_prep_probe_update")
+
+
+def qkv_prep_probe_stream(kind: int, load_policy: int, store_policy: int, sleep: int, lanes_per_block: int,
+                          dst_ptr, src_ptr, nbytes: int, key: int = 0, stream=None) -> None:
+    """A policy-selectable read, write, copy or in-place update stream."""
+    _check(_lib.qkv_prep_probe_stream(kind, load_policy, store_policy, sleep, lanes_per_block, dst_ptr, src_ptr,
+                                      nbytes, key, stream), "qkv_prep_probe_stream")
 
 
 def qkv_prep_probe_convert(in_ptr: int, n: int, e4m3_ptr, bf16_ptr, convert: int, stream=None) -> None:

@@ -32,15 +32,48 @@ extern "C" {
 #endif
 
 /* Copy `bytes` bytes from src to dst.  Both pointers 16-byte aligned, bytes a
- * multiple of 16, the ranges must not overlap.  bytes == 0 is a no-op. */
+ * multiple of 16, the ranges must not overlap.  bytes == 0 is a no-op.  The
+ * same stream as qkv_prep_probe_stream(QKV_PREP_PROBE_COPY, NT, NT|SC1, 0, 64,
+ * ...): the fastest copy of that probe's sweep. */
 int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, void *stream);
 
 /* In-place streaming update of `bytes` bytes at buf: every 16-byte chunk is
  * read, its first 32-bit word (little-endian unsigned) is incremented by 1
  * with wrap-around, and the chunk is written back to the same address.  The
  * traffic is bytes read + bytes written.  buf 16-byte aligned, bytes a
- * multiple of 16; bytes == 0 is a no-op. */
+ * multiple of 16; bytes == 0 is a no-op.  The same stream as
+ * qkv_prep_probe_stream(QKV_PREP_PROBE_UPDATE, NT, NT|SC1, 0, 64, ...). */
 int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream);
+
+/* Policy-selectable streams over `bytes` bytes (a multiple of 16), one
+ * 16-byte access per lane and `lanes_per_block` lanes (64, 128, 256, 512 or
+ * 1024) per workgroup, for comparing stream kinds, cache policies and shapes
+ * on the device (the pages' own method of judging a kernel against what its
+ * card can stream: FlagGems-vllm PR 684, "Performance against achievable
+ * bandwidth").  kind:
+ *   QKV_PREP_PROBE_READ (0)    reads src; dst is a 4-byte sink word (4-byte
+ *                              aligned) that receives `key` only if some
+ *                              chunk's four 32-bit words XOR to `key`;
+ *   QKV_PREP_PROBE_WRITE (1)   writes dst: chunk i = {i mod 2^32, i >> 32,
+ *                              key, ~key}; src must be NULL;
+ *   QKV_PREP_PROBE_COPY (2)    copies src to dst (ranges must not overlap);
+ *   QKV_PREP_PROBE_UPDATE (3)  in place at dst: the first 32-bit word of
+ *                              every chunk is incremented with wrap-around;
+ *                              src must be NULL.
+ * load_policy / store_policy: the cache-policy bits of the loads / stores, a
+ * combination of QKV_PREP_PROBE_SC0 (1), QKV_PREP_PROBE_NT (2) and
+ * QKV_PREP_PROBE_SC1 (16).  Loads accept 0, NT or NT|SC1; stores accept 0,
+ * NT, SC1, NT|SC1 or SC0|NT|SC1; the policy of an access the kind does not
+ * make must be 0.  sleep = 1 (copy and update only) pauses each wavefront for
+ * about 128 cycles between its load's arrival and its store; else 0.
+ * Written and read ranges 16-byte aligned.  Traffic: `bytes` for a read or a
+ * write, 2 * bytes for a copy or an update.  bytes == 0 is a no-op after the
+ * checks. */
+enum { QKV_PREP_PROBE_READ = 0, QKV_PREP_PROBE_WRITE = 1, QKV_PREP_PROBE_COPY = 2, QKV_PREP_PROBE_UPDATE = 3 };
+enum { QKV_PREP_PROBE_SC0 = 1, QKV_PREP_PROBE_NT = 2, QKV_PREP_PROBE_SC1 = 16 };
+int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t store_policy, int32_t sleep,
+                          int32_t lanes_per_block, void *dst, const void *src, int64_t bytes, uint32_t key,
+                          void *stream);
 
 /* The operator's fp32 conversions on n values of `in`:
  * e4m3_out[i] = the E4M3 code of in[i] (OCP e4m3fn, round to nearest even;

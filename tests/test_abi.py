@@ -324,6 +324,47 @@ def test_probes_reject_bad_arguments_without_launching():
     assert lib.qkv_prep_probe_update(1 << 20, 15, None) == qp.ERR_INVALID_ARG
     assert lib.qkv_prep_probe_update((1 << 20) + 8, 16, None) == qp.ERR_INVALID_ARG
     assert lib.qkv_prep_probe_update(1 << 20, -16, None) == qp.ERR_INVALID_ARG
+    st = lib.qkv_prep_probe_stream
+    A, B = 1 << 20, 1 << 30                     # aligned, non-overlapping stand-in addresses
+    R, Wr, C, U = probe.READ, probe.WRITE, probe.COPY, probe.UPDATE
+    NT, SC1, SC0 = probe.NT, probe.SC1, probe.SC0
+    # Good arguments with nothing to do return OK without launching.
+    assert st(R, NT, 0, 0, 256, A, B, 0, 0, None) == qp.OK
+    assert st(Wr, 0, NT | SC1, 0, 64, A, None, 0, 0, None) == qp.OK
+    assert st(C, NT, NT | SC1, 1, 1024, A, B, 0, 0, None) == qp.OK
+    assert st(U, NT, SC0 | NT | SC1, 1, 64, A, None, 0, 0, None) == qp.OK
+    assert st(R, 0, 0, 0, 256, A + 4, B, 0, 0, None) == qp.OK           # a read's sink is a word
+    bad = [
+        (4, NT, 0, 0, 256, A, B, 16),            # no such kind
+        (-1, NT, 0, 0, 256, A, B, 16),
+        (R, NT, 0, 0, 256, A, B, 15),            # not whole chunks
+        (R, NT, 0, 0, 256, A, B, -16),
+        (R, NT, 0, 0, 32, A, B, 16),             # lanes per block
+        (R, NT, 0, 0, 2048, A, B, 16),
+        (R, NT, 0, 0, 96, A, B, 16),
+        (R, SC1, 0, 0, 256, A, B, 16),           # load policy outside the accepted set
+        (R, SC0 | NT, 0, 0, 256, A, B, 16),
+        (R, NT, NT, 0, 256, A, B, 16),           # a read makes no store
+        (Wr, NT, NT, 0, 256, A, None, 16),       # a write makes no load
+        (Wr, 0, SC0, 0, 256, A, None, 16),       # store policy outside the accepted set
+        (Wr, 0, NT | SC0, 0, 256, A, None, 16),
+        (R, NT, 0, 1, 256, A, B, 16),            # sleep only in a copy or an update
+        (Wr, 0, NT, 1, 256, A, None, 16),
+        (C, NT, NT, 2, 256, A, B, 16),           # sleep is 0 or 1
+        (R, NT, 0, 0, 256, None, B, 16),         # NULL sink
+        (R, NT, 0, 0, 256, A + 2, B, 16),        # misaligned sink
+        (R, NT, 0, 0, 256, A, None, 16),         # NULL source
+        (R, NT, 0, 0, 256, A, B + 8, 16),        # misaligned source
+        (Wr, 0, NT, 0, 256, A + 4, None, 16),    # misaligned destination
+        (Wr, 0, NT, 0, 256, A, B, 16),           # a write takes no source
+        (U, NT, NT, 0, 256, A, B, 16),           # an update takes no source
+        (C, NT, NT, 0, 256, A, A + 16, 32),      # overlapping copy
+        (C, NT, NT, 0, 256, A + 16, A, 32),
+        (C, NT, NT, 0, 256, A, None, 16),
+        (Wr, 0, NT, 0, 64, A, None, (1 << 31) * 64 * 16),  # 2^31 workgroups
+    ]
+    for a in bad:
+        assert st(*a, 0, None) == qp.ERR_INVALID_ARG, a
     conv = lib.qkv_prep_probe_convert
     assert conv(None, 0, None, None, 2, None) == qp.OK
     assert conv(None, 4, None, None, 2, None) == qp.ERR_INVALID_ARG            # NULL input

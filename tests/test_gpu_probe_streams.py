@@ -1,0 +1,117 @@
+"""GPU checks of the policy-selectable stream probe (qkv_prep_probe_stream):
+for every stream kind, accepted cache policy, pause and workgroup size, on
+ragged sizes, the probe computes what its header states and writes nothing
+outside its range (seeded guard bands around every written buffer).  The
+cache-policy bits change where lines are kept, never the bytes written, so
+every policy must give the same result."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_kv_cache_amd import probe
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+GUARD = 4096
+LANES = (64, 128, 256, 512, 1024)
+LOADS = (0, probe.NT, probe.NT | probe.SC1)
+STORES = (0, probe.NT, probe.SC1, probe.NT | probe.SC1, probe.SC0 | probe.NT | probe.SC1)
+# Chunk counts: below one workgroup, ragged over several, and exact multiples.
+CHUNKS = (1, 63, 1000, 4096, 70001)
+
+
+def guarded(nbytes, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return torch.randint(0, 256, (GUARD + nbytes + GUARD,), dtype=torch.uint8, device=DEV, generator=g)
+
+
+def check_guards(buf, before, nbytes, what):
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:GUARD], before[:GUARD]), "%s: bytes before the range changed" % what
+    assert torch.equal(buf[GUARD + nbytes:], before[GUARD + nbytes:]), "%s: bytes after the range changed" % what
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+@pytest.mark.parametrize("chunks", CHUNKS)
+def test_write_stream_pattern_every_policy(chunks):
+    nbytes = chunks * 16
+    key = 0x1234ABCD
+    i = np.arange(chunks, dtype=np.uint64)
+    want = np.stack([(i & 0xFFFFFFFF).astype(np.uint32), (i >> np.uint64(32)).astype(np.uint32),
+                     np.full(chunks, key, np.uint32), np.full(chunks, ~np.uint32(key), np.uint32)], axis=1)
+    for n, (sp, lanes) in enumerate(itertools.product(STORES, LANES)):
+        buf = guarded(nbytes, 100 + n)
+        before = buf.clone()
+        probe.qkv_prep_probe_stream(probe.WRITE, 0, sp, 0, lanes, buf[GUARD:].data_ptr(), None, nbytes, key,
+                                    stream())
+        what = "write chunks=%d store=%d lanes=%d" % (chunks, sp, lanes)
+        check_guards(buf, before, nbytes, what)
+        got = buf[GUARD:GUARD + nbytes].cpu().numpy().view(np.uint32).reshape(chunks, 4)
+        assert np.array_equal(got, want), what
+
+
+@pytest.mark.parametrize("chunks", CHUNKS)
+def test_copy_stream_every_policy(chunks):
+    nbytes = chunks * 16
+    g = torch.Generator(device=DEV).manual_seed(chunks)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV, generator=g)
+    for n, (lp, sp, sleep, lanes) in enumerate(itertools.product(LOADS, STORES, (0, 1), LANES)):
+        if lanes not in (64, 256, 1024) and (lp, sp) != (probe.NT, probe.NT | probe.SC1):
+            continue
+        buf = guarded(nbytes, 200 + n)
+        before = buf.clone()
+        probe.qkv_prep_probe_stream(probe.COPY, lp, sp, sleep, lanes, buf[GUARD:].data_ptr(), src.data_ptr(),
+                                    nbytes, 0, stream())
+        what = "copy chunks=%d load=%d store=%d sleep=%d lanes=%d" % (chunks, lp, sp, sleep, lanes)
+        check_guards(buf, before, nbytes, what)
+        assert torch.equal(buf[GUARD:GUARD + nbytes], src), what
+
+
+@pytest.mark.parametrize("chunks", CHUNKS)
+def test_update_stream_every_policy(chunks):
+    nbytes = chunks * 16
+    for n, (lp, sp, sleep, lanes) in enumerate(itertools.product(LOADS, STORES, (0, 1), LANES)):
+        if lanes not in (64, 256, 1024) and (lp, sp) != (probe.NT, probe.NT | probe.SC1):
+            continue
+        buf = guarded(nbytes, 300 + n)
+        words = buf[GUARD:GUARD + nbytes].view(torch.int32).view(chunks, 4)
+        words[::5, 0] = -1                         # 0xFFFFFFFF wraps to 0
+        before = buf.clone()
+        probe.qkv_prep_probe_stream(probe.UPDATE, lp, sp, sleep, lanes, buf[GUARD:].data_ptr(), None, nbytes, 0,
+                                    stream())
+        what = "update chunks=%d load=%d store=%d sleep=%d lanes=%d" % (chunks, lp, sp, sleep, lanes)
+        check_guards(buf, before, nbytes, what)
+        old = before[GUARD:GUARD + nbytes].cpu().numpy().view(np.uint32).reshape(chunks, 4)
+        got = buf[GUARD:GUARD + nbytes].cpu().numpy().view(np.uint32).reshape(chunks, 4)
+        assert np.array_equal(got[:, 0], old[:, 0] + np.uint32(1)), what
+        assert np.array_equal(got[:, 1:], old[:, 1:]), what
+
+
+@pytest.mark.parametrize("chunks", CHUNKS)
+def test_read_stream_writes_the_key_only_on_a_match(chunks):
+    nbytes = chunks * 16
+    key = 0x0BADF00D
+    g = torch.Generator(device=DEV).manual_seed(7 + chunks)
+    src = torch.randint(0, 1 << 30, (chunks, 4), dtype=torch.int32, device=DEV, generator=g)
+    # Make no chunk XOR to the key, then plant the key in one chunk (the last
+    # one: the ragged tail of the last workgroup).
+    x = src[:, 0] ^ src[:, 1] ^ src[:, 2] ^ src[:, 3]
+    src[x == key, 0] ^= 1
+    for lp, lanes in itertools.product(LOADS, LANES):
+        sink = torch.full((4,), 77, dtype=torch.int32, device=DEV)
+        probe.qkv_prep_probe_stream(probe.READ, lp, 0, 0, lanes, sink.data_ptr(), src.data_ptr(), nbytes, key,
+                                    stream())
+        assert sink.tolist() == [77] * 4, "read without a match wrote the sink (load=%d lanes=%d)" % (lp, lanes)
+    planted = src.clone()
+    planted[-1, 3] = planted[-1, 0] ^ planted[-1, 1] ^ planted[-1, 2] ^ key
+    for lp, lanes in itertools.product(LOADS, LANES):
+        sink = torch.full((4,), 77, dtype=torch.int32, device=DEV)
+        probe.qkv_prep_probe_stream(probe.READ, lp, 0, 0, lanes, sink.data_ptr(), planted.data_ptr(), nbytes, key,
+                                    stream())
+        assert sink.tolist() == [key, 77, 77, 77], "read with a match (load=%d lanes=%d)" % (lp, lanes)
