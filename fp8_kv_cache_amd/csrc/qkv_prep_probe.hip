@@ -39,39 +39,66 @@ __device__ __forceinline__ void store_policy(u32x4 *base, uint32_t bytes, uint32
 }
 
 // LP / SP: the load / store policy bits.  SLEEP: the wavefront pauses
-// (s_sleep 2, about 128 cycles) between its load's arrival and its store.
-// A read keeps its data live by comparing the XOR of each chunk's four words
-// with `key` and writing the key to the sink word dst[0] on a match.
-template <int KIND, int LP, int SP, bool SLEEP>
+// (s_sleep 2, about 128 cycles) between its loads' arrival and its stores.
+// DEPTH: each lane takes DEPTH chunks, blockDim.x chunks apart (with one
+// wavefront per workgroup, DEPTH consecutive 1 KiB rows per wavefront), and
+// issues all their loads before its first store.  The grid has exactly
+// ceil(n / (blockDim.x * DEPTH)) workgroups, so every workgroup starts inside
+// the range; the descriptor of each workgroup covers only its own chunks
+// below n, so in the ragged last workgroup a load past n reads zeros and a
+// store past n is dropped, with no memory access either way.  No access is
+// guarded by a branch: guarded loads made the compiler wait for each load
+// before issuing the next.  A read keeps its data live by comparing the XOR of
+// each in-range chunk's four words with `key` and writing the key to the sink
+// word dst[0] on a match.
+template <int KIND, int LP, int SP, bool SLEEP, int DEPTH>
 __device__ __forceinline__ void stream_body(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
 {
-    const int64_t first = (int64_t)blockIdx.x * blockDim.x;
-    const int64_t i = first + threadIdx.x;
-    if (i >= n)
-        return;
+    const int64_t per = (int64_t)blockDim.x * DEPTH;
+    const int64_t first = (int64_t)blockIdx.x * per;
     const int64_t left = n - first;
-    const uint32_t span = (uint32_t)(left < (int64_t)blockDim.x ? left : (int64_t)blockDim.x) * 16u;
-    const uint32_t off = threadIdx.x * 16u;
-    if constexpr (KIND == kRead) {
-        const u32x4 v = load_policy<LP>(src + first, span, off);
-        if ((v[0] ^ v[1] ^ v[2] ^ v[3]) == key)
-            *reinterpret_cast<uint32_t *>(dst) = key;
-    } else if constexpr (KIND == kWrite) {
-        store_policy<SP>(dst + first, span, off, u32x4{(uint32_t)i, (uint32_t)(i >> 32), key, ~key});
+    const uint32_t span = (uint32_t)(left < per ? left : per) * 16u;
+    uint32_t off[DEPTH];
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+        off[u] = (u * blockDim.x + threadIdx.x) * 16u;
+    if constexpr (KIND == kWrite) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) {
+            const int64_t i = first + off[u] / 16u;
+            store_policy<SP>(dst + first, span, off[u], u32x4{(uint32_t)i, (uint32_t)(i >> 32), key, ~key});
+        }
     } else {
-        u32x4 v = load_policy<LP>(KIND == kCopy ? src + first : dst + first, span, off);
-        if constexpr (KIND == kUpdate)
-            v[0] += 1u;
-        if constexpr (SLEEP)
-            __builtin_amdgcn_s_sleep(2);
-        store_policy<SP>(dst + first, span, off, v);
+        u32x4 v[DEPTH];
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u)
+            v[u] = load_policy<LP>(KIND == kUpdate ? dst + first : src + first, span, off[u]);
+        if constexpr (KIND == kRead) {
+            bool hit = false;
+#pragma unroll
+            for (int u = 0; u < DEPTH; ++u)
+                hit |= (off[u] < span) & ((v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3]) == key);
+            if (hit)
+                *reinterpret_cast<uint32_t *>(dst) = key;
+        } else {
+            if constexpr (KIND == kUpdate) {
+#pragma unroll
+                for (int u = 0; u < DEPTH; ++u)
+                    v[u][0] += 1u;
+            }
+            if constexpr (SLEEP)
+                __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+            for (int u = 0; u < DEPTH; ++u)
+                store_policy<SP>(dst + first, span, off[u], v[u]);
+        }
     }
 }
 
-template <int KIND, int LP, int SP, bool SLEEP>
+template <int KIND, int LP, int SP, bool SLEEP, int DEPTH>
 __global__ __launch_bounds__(1024) void policy_stream(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
 {
-    stream_body<KIND, LP, SP, SLEEP>(dst, src, n, key);
+    stream_body<KIND, LP, SP, SLEEP, DEPTH>(dst, src, n, key);
 }
 
 // The two ceilings are the policy streams at their fastest settings in the
@@ -85,12 +112,12 @@ constexpr int kCeilingLanes = 64;
 
 __global__ __launch_bounds__(kCeilingLanes) void stream_copy(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
 {
-    stream_body<kCopy, kNt, kNt | kSc1, false>(dst, src, n, key);
+    stream_body<kCopy, kNt, kNt | kSc1, false, 1>(dst, src, n, key);
 }
 
 __global__ __launch_bounds__(kCeilingLanes) void stream_update(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
 {
-    stream_body<kUpdate, kNt, kNt | kSc1, false>(dst, src, n, key);
+    stream_body<kUpdate, kNt, kNt | kSc1, false, 1>(dst, src, n, key);
 }
 
 struct StreamLaunch {
@@ -102,11 +129,26 @@ struct StreamLaunch {
     uint32_t key;
 };
 
-template <int KIND, int LP, int SP, bool SLEEP>
+template <int KIND, int LP, int SP, bool SLEEP, int DEPTH = 1>
 bool launch_stream(const StreamLaunch &L)
 {
-    hipLaunchKernelGGL((policy_stream<KIND, LP, SP, SLEEP>), L.grid, L.block, 0, L.stream, L.dst, L.src, L.n, L.key);
+    hipLaunchKernelGGL((policy_stream<KIND, LP, SP, SLEEP, DEPTH>), L.grid, L.block, 0, L.stream, L.dst, L.src,
+                       L.n, L.key);
     return true;
+}
+
+// Several chunks per lane: only with the fastest policies (nt loads, nt sc1
+// stores) and no pause.
+template <int DEPTH>
+bool launch_deep(int kind, const StreamLaunch &L)
+{
+    switch (kind) {
+    case kRead: return launch_stream<kRead, kNt, 0, false, DEPTH>(L);
+    case kWrite: return launch_stream<kWrite, 0, kNt | kSc1, false, DEPTH>(L);
+    case kCopy: return launch_stream<kCopy, kNt, kNt | kSc1, false, DEPTH>(L);
+    case kUpdate: return launch_stream<kUpdate, kNt, kNt | kSc1, false, DEPTH>(L);
+    default: return false;
+    }
 }
 
 // The accepted policies: loads plain, nt or nt sc1; stores plain, nt, sc1,
@@ -283,8 +325,8 @@ extern "C" int qkv_prep_probe_ue8m0(const float *in, int64_t n, void *op_byte_ou
 }
 
 extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t store_policy, int32_t sleep,
-                                     int32_t lanes_per_block, void *dst, const void *src, int64_t bytes,
-                                     uint32_t key, void *stream)
+                                     int32_t lanes_per_block, int32_t depth, void *dst, const void *src,
+                                     int64_t bytes, uint32_t key, void *stream)
 {
     const uintptr_t pd = reinterpret_cast<uintptr_t>(dst), ps = reinterpret_cast<uintptr_t>(src);
     const bool reads = kind == kRead || kind == kCopy || kind == kUpdate;
@@ -300,6 +342,10 @@ extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t 
         return 1;
     if (sleep && kind != kCopy && kind != kUpdate)
         return 1;
+    if (depth != 1 && depth != 2 && depth != 4 && depth != 8 && depth != 16)
+        return 1;
+    if (depth > 1 && (sleep || load_policy != (reads ? kNt : 0) || store_policy != (writes ? (kNt | kSc1) : 0)))
+        return 1;
     // dst: the sink word of a read (4-byte aligned), else the written range
     // (16-byte aligned); src: the range a read or copy loads, NULL otherwise.
     const bool needs_src = kind == kRead || kind == kCopy;
@@ -310,7 +356,8 @@ extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t 
     if (bytes == 0)
         return 0;
     const int64_t n = bytes / 16;
-    const int64_t blocks = (n + lanes_per_block - 1) / lanes_per_block;
+    const int64_t per = (int64_t)lanes_per_block * depth;
+    const int64_t blocks = (n + per - 1) / per;
     if (blocks >= ((int64_t)1 << 31))
         return 1;
     StreamLaunch L;
@@ -321,7 +368,15 @@ extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t 
     L.src = static_cast<const u32x4 *>(src);
     L.n = n;
     L.key = key;
-    if (!launch_policy_stream(kind, load_policy, store_policy, sleep != 0, L))
+    bool launched;
+    switch (depth) {
+    case 2: launched = launch_deep<2>(kind, L); break;
+    case 4: launched = launch_deep<4>(kind, L); break;
+    case 8: launched = launch_deep<8>(kind, L); break;
+    case 16: launched = launch_deep<16>(kind, L); break;
+    default: launched = launch_policy_stream(kind, load_policy, store_policy, sleep != 0, L);
+    }
+    if (!launched)
         return 1;
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }

@@ -45,9 +45,11 @@ int qkv_prep_probe_copy(void *dst, const void *src, int64_t bytes, void *stream)
  * qkv_prep_probe_stream(QKV_PREP_PROBE_UPDATE, NT, NT|SC1, 0, 64, ...). */
 int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream);
 
-/* Policy-selectable streams over `bytes` bytes (a multiple of 16), one
- * 16-byte access per lane and `lanes_per_block` lanes (64, 128, 256, 512 or
- * 1024) per workgroup, for comparing stream kinds, cache policies and shapes
+/* Policy-selectable streams over `bytes` bytes (a multiple of 16), 16-byte
+ * accesses, `lanes_per_block` lanes (64, 128, 256, 512 or 1024) per
+ * workgroup and `depth` (1, 2, 4, 8 or 16) chunks per lane, lanes_per_block
+ * chunks apart, whose loads are all issued before the lane's first store, for
+ * comparing stream kinds, cache policies and shapes
  * on the device (the pages' own method of judging a kernel against what its
  * card can stream: FlagGems-vllm PR 684, "Performance against achievable
  * bandwidth").  kind:
@@ -65,15 +67,16 @@ int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream);
  * QKV_PREP_PROBE_SC1 (16).  Loads accept 0, NT or NT|SC1; stores accept 0,
  * NT, SC1, NT|SC1 or SC0|NT|SC1; the policy of an access the kind does not
  * make must be 0.  sleep = 1 (copy and update only) pauses each wavefront for
- * about 128 cycles between its load's arrival and its store; else 0.
+ * about 128 cycles between its loads' arrival and its stores; else 0.  With
+ * depth > 1 the policies must be NT loads and NT|SC1 stores, and sleep 0.
  * Written and read ranges 16-byte aligned.  Traffic: `bytes` for a read or a
  * write, 2 * bytes for a copy or an update.  bytes == 0 is a no-op after the
  * checks. */
 enum { QKV_PREP_PROBE_READ = 0, QKV_PREP_PROBE_WRITE = 1, QKV_PREP_PROBE_COPY = 2, QKV_PREP_PROBE_UPDATE = 3 };
 enum { QKV_PREP_PROBE_SC0 = 1, QKV_PREP_PROBE_NT = 2, QKV_PREP_PROBE_SC1 = 16 };
 int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t store_policy, int32_t sleep,
-                          int32_t lanes_per_block, void *dst, const void *src, int64_t bytes, uint32_t key,
-                          void *stream);
+                          int32_t lanes_per_block, int32_t depth, void *dst, const void *src, int64_t bytes,
+                          uint32_t key, void *stream);
 
 /* The operator's fp32 conversions on n values of `in`:
  * e4m3_out[i] = the E4M3 code of in[i] (OCP e4m3fn, round to nearest even;
