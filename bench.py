@@ -705,6 +705,68 @@ def sweep_streams(torch, probe, nbytes, launches=20, rounds=4):
     return {"mode": "streams", "bytes": nbytes, "launches": launches, "rounds": rounds, "streams": rows}
 
 
+# ----------------------------------------------------------------- MXFP8 pattern mode
+
+def mxfp8_pattern(torch, probe, qp, m=None, hidden=None, launches=50, rounds=5):
+    """The MXFP8 operator against its own memory access pattern with no
+    arithmetic (qkv_prep_probe_mxfp8_pattern) at m x hidden (with the
+    residual): the product's prepared launch and the pattern with every
+    stream, without the barrier, without the scale words, without the codes,
+    and with the two inputs and the residual output only.  Region time of
+    `launches` back-to-back launches, best of `rounds` interleaved rounds,
+    after warming the chip; each rate counts that variant's own bytes."""
+    from fp8_kv_cache_amd import variants as V
+    m = m or V.MX_ROWS
+    hidden = hidden or V.MX_HIDDEN
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    x = torch.randn((m, hidden), generator=gen, device="cuda").to(torch.bfloat16)
+    r = torch.randn((m, hidden), generator=gen, device="cuda").to(torch.bfloat16)
+    gamma = (0.1 * torch.randn(hidden, generator=gen, device="cuda")).to(torch.bfloat16)
+    res_out = torch.empty_like(x)
+    codes = torch.empty((m, hidden), dtype=torch.uint8, device="cuda")
+    nscale = V.mxfp8_scale_bytes(m, hidden)
+    scales = torch.empty(nscale, dtype=torch.uint8, device="cuda")
+    product = qp.prepare_mxfp8_norm_quant(x, gamma, 1e-6, residual=r, residual_out=res_out, quant_out=codes,
+                                          scale_out=scales)
+    stream = torch.cuda.current_stream().cuda_stream
+    RES, COD, SCA, BAR = probe.MX_RESIDUAL, probe.MX_CODES, probe.MX_SCALES, probe.MX_BARRIER
+    mh = m * hidden
+
+    def own_bytes(streams):
+        return (2 * mh + (4 * mh if streams & RES else 0) + (mh if streams & COD else 0) +
+                (nscale if streams & SCA else 0))
+
+    def pattern(streams):
+        return lambda: probe.qkv_prep_probe_mxfp8_pattern(x.data_ptr(), r.data_ptr(), gamma.data_ptr(),
+                                                          res_out.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                                                          m, hidden, streams, stream)
+
+    table = [("product kernel", product, own_bytes(RES | COD | SCA) + 2 * hidden)]
+    for label, st in (("pattern: every stream, barrier", RES | COD | SCA | BAR),
+                      ("pattern: every stream, no barrier", RES | COD | SCA),
+                      ("pattern: no scale words", RES | COD | BAR),
+                      ("pattern: no codes", RES | SCA | BAR),
+                      ("pattern: inputs and residual output only", RES | BAR)):
+        table.append((label, pattern(st), own_bytes(st)))
+    warm_chip(torch, probe)
+    best = [float("inf")] * len(table)
+    for rnd in range(rounds):
+        order = range(len(table)) if rnd % 2 == 0 else reversed(range(len(table)))
+        for i in order:
+            fn = table[i][1]
+            for _ in range(3):
+                fn()
+            _, region = time_region(torch, fn, launches)
+            best[i] = min(best[i], region / launches)
+    rows = [{"variant": label, "us": round(t * 1e6, 2), "bytes": nb, "gbps": round(nb / t / 1e9, 1)}
+            for (label, _, nb), t in zip(table, best)]
+    out = {"mode": "mxfp8_pattern", "m": m, "hidden": hidden, "launches": launches, "rounds": rounds,
+           "rows": rows, "product_rate_over_pattern": round(best[1] / best[0], 4)}
+    del product, x, r, gamma, res_out, codes, scales
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------- main
 
 def main():
@@ -720,10 +782,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "profile", "sweep", "streams"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "profile", "sweep", "streams", "mxfp8-pattern"], default="bench",
                     help="profile: a short fixed program for rocprofv3 (no JSON line); sweep: every "
                          "forced launch shape of the operator on --workload (one JSON line); streams: "
-                         "read/write/copy/update streams by cache policy (one JSON line per size)")
+                         "read/write/copy/update streams by cache policy (one JSON line per size); "
+                         "mxfp8-pattern: the MXFP8 operator against its own access pattern (--sizes MxH)")
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--sizes", default="",
                     help="sweep mode: comma-separated TxH sizes (decode-like inputs) instead of --workload; "
@@ -750,6 +813,11 @@ def main():
         sys.exit(1)
     if args.mode == "profile":
         profile_run(torch, qp, probe, args.workload, args.launches)
+        return
+    if args.mode == "mxfp8-pattern":
+        for size in (args.sizes.split(",") if args.sizes else [""]):
+            m, h = (int(v) for v in size.lower().split("x")) if size else (None, None)
+            print(json.dumps(mxfp8_pattern(torch, probe, qp, m, h)), flush=True)
         return
     if args.mode == "streams":
         for mib in (args.sizes or "512,2048").split(","):

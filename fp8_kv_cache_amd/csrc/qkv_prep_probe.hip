@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mxfp8_launch.h"
 #include "qkv_prep_probe.h"
 #include "qkvp_device.h"
 
@@ -210,6 +211,113 @@ bool valid_store_policy(int p)
     return p == 0 || p == kNt || p == kSc1 || p == (kNt | kSc1) || p == (kSc0 | kNt | kSc1);
 }
 
+// The MXFP8 operator's memory access pattern with no arithmetic
+// (qkv_prep_probe_mxfp8_pattern): its grid (one workgroup per row padded to
+// 128 rows, G groups of 64 16-byte chunks per wavefront), its non-temporal
+// loads of x and the residual, its nt sc1 stores of the residual output (16
+// bytes per lane), its one LDS barrier where a row spans several wavefronts,
+// then per group a 16-byte load of gamma (cache-resident) followed by that
+// group's nt sc1 code store (8 bytes per lane) and 4-byte scale word from the
+// first lane of each 16-lane row into the 128x4 swizzled layout, and the zero
+// words of the padding rows.  The stored values are XORs of the loaded words,
+// which keeps every load live and orders each group's stores after its gamma
+// load, as in the operator.
+struct MxPattern {
+    const u32x4 *x;
+    const u32x4 *residual;
+    const u32x4 *gamma;
+    uint8_t *residual_out;
+    uint8_t *codes;
+    uint8_t *scales;
+    int64_t m;
+    int32_t hidden;
+    int32_t padded_cols;
+};
+
+// The scale byte of (row, col) in the 128x4 swizzled layout (the MXFP8
+// operator's output format): 128-row tiles of padded_cols columns.
+__device__ __forceinline__ int64_t mx_swizzled(int64_t row, int64_t col, int64_t padded_cols)
+{
+    return (col & 3) + (col >> 2) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (row >> 7) * 128 * padded_cols;
+}
+
+template <int G, bool RES, bool CODES, bool SCALES, bool BARRIER>
+__global__ __launch_bounds__(1024) void mxfp8_pattern(MxPattern a)
+{
+    __shared__ uint32_t wave_word[16];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row = blockIdx.x;
+    if (row >= a.m) {
+        if constexpr (SCALES)
+            for (int c = threadIdx.x * 4; c < a.padded_cols; c += blockDim.x * 4)
+                *reinterpret_cast<uint32_t *>(a.scales + mx_swizzled(row, c, a.padded_cols)) = 0u;
+        return;
+    }
+    const int64_t chunks_per_row = a.hidden / 8;
+    u32x4 p[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int64_t chunk = (int64_t)(w * G + j) * 64 + lane;
+        p[j] = qkvp::dev::load_stream(a.x + row * chunks_per_row + chunk);
+        if constexpr (RES)
+            p[j] ^= qkvp::dev::load_stream(a.residual + row * chunks_per_row + chunk);
+    }
+    if constexpr (RES) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const uint32_t chunk = (w * G + j) * 64 + lane;
+            qkvp::dev::store_sys(a.residual_out + row * a.hidden * 2, (uint32_t)a.hidden * 2u, chunk * 16u, p[j]);
+        }
+    }
+    uint32_t extra = 0;
+    if constexpr (BARRIER) {
+        if (lane == 0)
+            wave_word[w] = p[0][0];
+        __syncthreads();
+        extra = wave_word[0];
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const uint32_t chunk = (w * G + j) * 64 + lane;
+        if constexpr (CODES || SCALES) {
+            const u32x4 gm = a.gamma[chunk];
+            if constexpr (CODES)
+                qkvp::dev::store_sys2(a.codes + row * a.hidden, (uint32_t)a.hidden, chunk * 8u,
+                                      u32x2{p[j][0] ^ p[j][1] ^ gm[0] ^ extra, p[j][2] ^ p[j][3] ^ gm[1]});
+            if constexpr (SCALES) {
+                if ((lane & 15) == 0)
+                    *reinterpret_cast<uint32_t *>(a.scales + mx_swizzled(row, chunk >> 2, a.padded_cols)) =
+                        p[j][0] ^ p[j][3] ^ gm[3] ^ extra;
+            }
+        }
+    }
+}
+
+template <int G, bool RES, bool CODES, bool SCALES>
+void launch_mx_pattern_b(const MxPattern &a, bool barrier, dim3 grid, dim3 block, hipStream_t st)
+{
+    if (barrier)
+        hipLaunchKernelGGL((mxfp8_pattern<G, RES, CODES, SCALES, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((mxfp8_pattern<G, RES, CODES, SCALES, false>), grid, block, 0, st, a);
+}
+
+template <int G>
+void launch_mx_pattern(const MxPattern &a, int streams, dim3 grid, dim3 block, hipStream_t st)
+{
+    const bool barrier = (streams & 8) != 0;
+    switch (streams & 7) {
+    case 1: launch_mx_pattern_b<G, true, false, false>(a, barrier, grid, block, st); break;
+    case 2: launch_mx_pattern_b<G, false, true, false>(a, barrier, grid, block, st); break;
+    case 3: launch_mx_pattern_b<G, true, true, false>(a, barrier, grid, block, st); break;
+    case 4: launch_mx_pattern_b<G, false, false, true>(a, barrier, grid, block, st); break;
+    case 5: launch_mx_pattern_b<G, true, false, true>(a, barrier, grid, block, st); break;
+    case 6: launch_mx_pattern_b<G, false, true, true>(a, barrier, grid, block, st); break;
+    default: launch_mx_pattern_b<G, true, true, true>(a, barrier, grid, block, st); break;
+    }
+}
+
 // The operator's conversions (qkvp::dev::pack_e4m3 / pack_bf16) on four
 // values per thread.
 template <bool HW>
@@ -378,5 +486,48 @@ extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t 
     }
     if (!launched)
         return 1;
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+extern "C" int qkv_prep_probe_mxfp8_pattern(const void *x, const void *residual, const void *gamma,
+                                            void *residual_out, void *codes, void *scales, int64_t m,
+                                            int32_t hidden, int32_t streams, void *stream)
+{
+    const bool res = streams & 1, cod = streams & 2, sca = streams & 4;
+    if (streams < 1 || streams > 15 || !(streams & 7) || m < 0 || hidden < 512 || hidden % 512 ||
+        hidden > 512 * qkvp::kMxMaxGroups)
+        return 1;
+    const int k = hidden / 512;
+    if (!qkvp::mx_launchable(k))
+        return 1;
+    auto misaligned = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+    if (!x || misaligned(x, 16) || (res && (!residual || !residual_out || misaligned(residual, 16) ||
+                                           misaligned(residual_out, 16))) ||
+        (cod && (!codes || misaligned(codes, 8))) || (sca && (!scales || misaligned(scales, 4))) ||
+        ((cod || sca) && (!gamma || misaligned(gamma, 16))))
+        return 1;
+    const int64_t rows_padded = (m + 127) / 128 * 128;
+    const int g = qkvp::mx_groups_per_wave(k);
+    const int64_t threads = 64 * (k / g);
+    if (rows_padded * threads >= ((int64_t)1 << 32))
+        return 1;
+    if (rows_padded == 0)
+        return 0;
+    MxPattern a;
+    a.x = static_cast<const u32x4 *>(x);
+    a.residual = static_cast<const u32x4 *>(residual);
+    a.gamma = static_cast<const u32x4 *>(gamma);
+    a.residual_out = static_cast<uint8_t *>(residual_out);
+    a.codes = static_cast<uint8_t *>(codes);
+    a.scales = static_cast<uint8_t *>(scales);
+    a.m = m;
+    a.hidden = hidden;
+    a.padded_cols = hidden / 32;
+    const dim3 grid((uint32_t)rows_padded), block((uint32_t)threads);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (g == 2)
+        launch_mx_pattern<2>(a, streams, grid, block, st);
+    else
+        launch_mx_pattern<1>(a, streams, grid, block, st);
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }

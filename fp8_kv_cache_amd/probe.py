@@ -13,12 +13,14 @@ from fp8_kv_cache_amd.qkv_prep import OK, QkvPrepError
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqkv_prep_probe.so")
 
-EXPORTED = ("qkv_prep_probe_copy", "qkv_prep_probe_update", "qkv_prep_probe_stream", "qkv_prep_probe_convert",
-            "qkv_prep_probe_ue8m0")
+EXPORTED = ("qkv_prep_probe_copy", "qkv_prep_probe_update", "qkv_prep_probe_stream",
+            "qkv_prep_probe_mxfp8_pattern", "qkv_prep_probe_convert", "qkv_prep_probe_ue8m0")
 
 # qkv_prep_probe_stream kinds and cache-policy bits.
 READ, WRITE, COPY, UPDATE = 0, 1, 2, 3
 SC0, NT, SC1 = 1, 2, 16
+# qkv_prep_probe_mxfp8_pattern streams.
+MX_RESIDUAL, MX_CODES, MX_SCALES, MX_BARRIER = 1, 2, 4, 8
 
 
 def _load():
@@ -31,6 +33,7 @@ def _load():
     L.qkv_prep_probe_update.argtypes = [vp, i64, vp]
     i32 = ctypes.c_int32
     L.qkv_prep_probe_stream.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, ctypes.c_uint32, vp]
+    L.qkv_prep_probe_mxfp8_pattern.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, vp]
     L.qkv_prep_probe_convert.argtypes = [vp, i64, vp, vp, ctypes.c_int32, vp]
     L.qkv_prep_probe_ue8m0.argtypes = [vp, i64, vp, vp, vp, vp]
     for name in EXPORTED:
@@ -65,6 +68,13 @@ def qkv_prep_probe_stream(kind: int, load_policy: int, store_policy: int, sleep:
     """A policy-selectable read, write, copy or in-place update stream."""
     _check(_lib.qkv_prep_probe_stream(kind, load_policy, store_policy, sleep, lanes_per_block, depth, dst_ptr,
                                       src_ptr, nbytes, key, stream), "qkv_prep_probe_stream")
+
+
+def qkv_prep_probe_mxfp8_pattern(x_ptr, residual_ptr, gamma_ptr, residual_out_ptr, codes_ptr, scales_ptr, m: int,
+                                 hidden: int, streams: int, stream=None) -> None:
+    """The MXFP8 operator's access pattern with no arithmetic."""
+    _check(_lib.qkv_prep_probe_mxfp8_pattern(x_ptr, residual_ptr, gamma_ptr, residual_out_ptr, codes_ptr,
+                                             scales_ptr, m, hidden, streams, stream), "qkv_prep_probe_mxfp8_pattern")
 
 
 def qkv_prep_probe_convert(in_ptr: int, n: int, e4m3_ptr, bf16_ptr, convert: int, stream=None) -> None:

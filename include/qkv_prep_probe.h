@@ -78,6 +78,32 @@ int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t store_polic
                           int32_t lanes_per_block, int32_t depth, void *dst, const void *src, int64_t bytes,
                           uint32_t key, void *stream);
 
+/* The MXFP8 operator's memory access pattern with no arithmetic, for
+ * measuring how close that operator runs to what its own loads and stores
+ * allow: the same grid and workgroups (one per row, rows padded to 128), the
+ * same non-temporal 16-byte loads and stores, per group of 64 chunks a
+ * 16-byte gamma load before that group's 8-byte code stores and 4-byte
+ * swizzled scale words, and zero words for the padding rows.  x, residual and
+ * residual_out are [m][hidden] 16-bit elements and gamma [hidden] 16-bit
+ * elements (16-byte aligned), codes [m][hidden] bytes (8-byte aligned),
+ * scales the 128x4 swizzled layout of qkv_prep_mxfp8.h (4-byte aligned,
+ * qkv_prep_mxfp8_scale_bytes(m, hidden) bytes).  hidden a multiple of 512
+ * from 512 to 16384 whose group count hidden / 512 is even or at most 15.
+ * With w the four 32-bit words of a 16-byte chunk of x (of x XOR residual
+ * with bit 0) and y those of the same chunk of gamma, streams:
+ *   bit 0 (1)  reads residual, writes residual_out = x XOR residual;
+ *   bit 1 (2)  writes the codes, chunk c's 8 bytes = {w0^w1^y0^e, w2^w3^y1};
+ *   bit 2 (4)  writes the scale word of every 4 chunks (columns 4j..4j+3 of
+ *              the row) = w0^w3^y3^e of its first chunk, and zero words in
+ *              the padding rows;
+ *   bit 3 (8)  adds the operator's LDS barrier, after which e = word 0 of
+ *              the row's first chunk (e = 0 without it).
+ * At least one of bits 0-2; gamma may be NULL without bits 1-2, residual and
+ * residual_out without bit 0.  m == 0 is a no-op after the checks. */
+int qkv_prep_probe_mxfp8_pattern(const void *x, const void *residual, const void *gamma, void *residual_out,
+                                 void *codes, void *scales, int64_t m, int32_t hidden, int32_t streams,
+                                 void *stream);
+
 /* The operator's fp32 conversions on n values of `in`:
  * e4m3_out[i] = the E4M3 code of in[i] (OCP e4m3fn, round to nearest even;
  * defined for |in[i]| <= 448, the range the operator converts) and

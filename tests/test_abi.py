@@ -379,6 +379,37 @@ def test_probes_reject_bad_arguments_without_launching():
     ]
     for a in bad:
         assert st(*a, 0, None) == qp.ERR_INVALID_ARG, a
+    mx = lib.qkv_prep_probe_mxfp8_pattern
+    X, Rs, Gm, Ro, Cd, Sc = 1 << 20, 2 << 20, 6 << 20, 3 << 20, 4 << 20, 5 << 20
+    assert mx(X, Rs, Gm, Ro, Cd, Sc, 0, 7168, 15, None) == qp.OK             # no rows
+    assert mx(X, None, Gm, None, Cd, None, 0, 512, 2, None) == qp.OK         # codes only
+    assert mx(X, None, Gm, None, None, Sc + 4, 0, 16384, 12, None) == qp.OK  # scales + barrier
+    assert mx(X, Rs, None, Ro, None, None, 0, 1024, 9, None) == qp.OK        # no gamma without codes/scales
+    for a in [
+        (X, Rs, Gm, Ro, Cd, Sc, 0, 7168, 0),          # no stream
+        (X, Rs, Gm, Ro, Cd, Sc, 0, 7168, 8),          # a barrier alone stores nothing
+        (X, Rs, Gm, Ro, Cd, Sc, 0, 7168, 16),
+        (X, Rs, Gm, Ro, Cd, Sc, -1, 7168, 15),
+        (X, Rs, Gm, Ro, Cd, Sc, 0, 7040, 15),         # hidden a multiple of 512
+        (X, Rs, Gm, Ro, Cd, Sc, 0, 0, 15),
+        (X, Rs, Gm, Ro, Cd, Sc, 0, 16896, 15),        # above 16384
+        (X, Rs, Gm, Ro, Cd, Sc, 0, 512 * 17, 15),     # 17 groups: odd above 15
+        (None, Rs, Gm, Ro, Cd, Sc, 0, 7168, 15),
+        (X + 8, Rs, Gm, Ro, Cd, Sc, 0, 7168, 15),
+        (X, None, Gm, Ro, Cd, Sc, 0, 7168, 1),
+        (X, Rs, Gm, None, Cd, Sc, 0, 7168, 1),
+        (X, Rs + 8, Gm, Ro, Cd, Sc, 0, 7168, 1),
+        (X, Rs, Gm, Ro + 8, Cd, Sc, 0, 7168, 1),
+        (X, Rs, Gm, Ro, None, Sc, 0, 7168, 2),
+        (X, Rs, Gm, Ro, Cd + 4, Sc, 0, 7168, 2),
+        (X, Rs, Gm, Ro, Cd, None, 0, 7168, 4),
+        (X, Rs, Gm, Ro, Cd, Sc + 2, 0, 7168, 4),
+        (X, Rs, None, Ro, Cd, Sc, 0, 7168, 2),        # codes need gamma
+        (X, Rs, None, Ro, Cd, Sc, 0, 7168, 4),        # scales need gamma
+        (X, Rs, Gm + 8, Ro, Cd, Sc, 0, 7168, 6),
+        (X, Rs, Gm, Ro, Cd, Sc, (1 << 32) // 448, 7168, 15),   # 2^32 work-items
+    ]:
+        assert mx(*a, None) == qp.ERR_INVALID_ARG, a
     conv = lib.qkv_prep_probe_convert
     assert conv(None, 0, None, None, 2, None) == qp.OK
     assert conv(None, 4, None, None, 2, None) == qp.ERR_INVALID_ARG            # NULL input

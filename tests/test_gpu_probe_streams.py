@@ -170,3 +170,67 @@ def test_streams_with_several_chunks_per_lane(chunks):
         probe.qkv_prep_probe_stream(probe.READ, NT, 0, 0, lanes, depth, sink.data_ptr(), planted.data_ptr(),
                                     nbytes, key, stream())
         assert sink.tolist() == [key, 77, 77, 77], "read with a match " + what
+
+
+# ------------------------------------------------------------ MXFP8 pattern
+
+MX_SHAPES = ((1, 512), (130, 1536), (200, 7168), (129, 16384))   # 1536: three groups, one per wavefront
+MX_STREAMS = (15, 7, 1, 2, 4, 3, 6, 13, 10)
+
+
+@pytest.mark.parametrize("m,hidden", MX_SHAPES)
+def test_mxfp8_pattern_probe_writes_what_its_header_states(m, hidden):
+    import oracle
+    g = torch.Generator(device=DEV).manual_seed(m + hidden)
+    x = torch.randint(-(1 << 31), 1 << 31, (m, hidden // 2), dtype=torch.int64, device=DEV, generator=g)
+    x = x.to(torch.int32)
+    r = torch.randint(-(1 << 31), 1 << 31, (m, hidden // 2), dtype=torch.int64, device=DEV,
+                      generator=g).to(torch.int32)
+    gamma = torch.randint(-(1 << 31), 1 << 31, (hidden // 2,), dtype=torch.int64, device=DEV,
+                          generator=g).to(torch.int32)
+    gw = gamma.cpu().numpy().view(np.uint32).reshape(hidden // 8, 4)
+    nscale = probe_scale_bytes(m, hidden)
+    pad_cols = hidden // 32
+    # Scale positions: word j of row `row` covers columns 4j..4j+3; the oracle's
+    # swizzle gives each column's byte.
+    rows_padded = (m + 127) // 128 * 128
+    where = np.array([[oracle.mxfp8_scale_offset(row, col, pad_cols) for col in range(pad_cols)]
+                      for row in range(rows_padded)], dtype=np.int64)
+    xw = x.cpu().numpy().view(np.uint32).reshape(m, hidden // 8, 4)
+    rw = r.cpu().numpy().view(np.uint32).reshape(m, hidden // 8, 4)
+    for streams in MX_STREAMS:
+        what = "m=%d hidden=%d streams=%d" % (m, hidden, streams)
+        res, cod, sca, bar = (streams & 1, streams & 2, streams & 4, streams & 8)
+        ro = guarded(m * hidden * 2, 700 + streams)
+        cd = guarded(m * hidden, 800 + streams)
+        sc = guarded(nscale, 900 + streams)
+        before = [t.clone() for t in (ro, cd, sc)]
+        probe.qkv_prep_probe_mxfp8_pattern(x.data_ptr(), r.data_ptr(), gamma.data_ptr(), ro[GUARD:].data_ptr(),
+                                           cd[GUARD:].data_ptr(), sc[GUARD:].data_ptr(), m, hidden, streams,
+                                           stream())
+        torch.cuda.synchronize()
+        w = xw ^ rw if res else xw
+        e = w[:, 0, 0][:, None] if bar else np.zeros((m, 1), np.uint32)
+        for buf, old, n, on, name in ((ro, before[0], m * hidden * 2, res, "residual_out"),
+                                      (cd, before[1], m * hidden, cod, "codes"),
+                                      (sc, before[2], nscale, sca, "scales")):
+            check_guards(buf, old, n, "%s %s" % (name, what))
+            if not on:
+                assert torch.equal(buf, old), "%s written without its stream (%s)" % (name, what)
+        if res:
+            got = ro[GUARD:GUARD + m * hidden * 2].cpu().numpy().view(np.uint32).reshape(m, hidden // 8, 4)
+            assert np.array_equal(got, w), "residual_out " + what
+        if cod:
+            got = cd[GUARD:GUARD + m * hidden].cpu().numpy().view(np.uint32).reshape(m, hidden // 8, 2)
+            assert np.array_equal(got[:, :, 0], w[:, :, 0] ^ w[:, :, 1] ^ gw[None, :, 0] ^ e), "codes word 0 " + what
+            assert np.array_equal(got[:, :, 1], w[:, :, 2] ^ w[:, :, 3] ^ gw[None, :, 1]), "codes word 1 " + what
+        if sca:
+            got = sc[GUARD:GUARD + nscale].cpu().numpy()
+            word = (w[:, 0::16, 0] ^ w[:, 0::16, 3] ^ gw[None, 0::16, 3] ^ e).astype(np.uint32)   # [m, cols / 4]
+            want = np.zeros((rows_padded, pad_cols), np.uint8)
+            want[:m] = word.view(np.uint8).reshape(m, pad_cols)                   # little-endian bytes
+            assert np.array_equal(got[where], want), "scales " + what
+
+
+def probe_scale_bytes(m, hidden):
+    return (m + 127) // 128 * 128 * (hidden // 32)
