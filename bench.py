@@ -512,14 +512,24 @@ def warm_chip(torch, probe, seconds=0.5, nbytes=2 << 30):
     del buf
 
 
-def sweep_workload(W, name, size):
+def sweep_workload(W, name, size, block_size=0):
     """A named workload, or for size "TxH" a decode-like one of that size:
     positions uniform in [0, 131072), random distinct slots of a cache twice
-    the token count."""
+    the token count.  block_size > 0 re-cuts the cache into blocks of that
+    many slots, keeping its slot count (the slot recipe follows the new
+    blocks)."""
+    import dataclasses
     if not size:
-        return W.WORKLOADS[name]
-    T, H = (int(v) for v in size.lower().split("x"))
-    return W.custom(T, H, seed=11 + T + H, max_position=131072)
+        w = W.WORKLOADS[name]
+    else:
+        T, H = (int(v) for v in size.lower().split("x"))
+        w = W.custom(T, H, seed=11 + T + H, max_position=131072)
+    if block_size and block_size != w.block_size:
+        slots = w.num_blocks * w.block_size
+        if slots % block_size:
+            raise ValueError("the cache's %d slots do not split into blocks of %d" % (slots, block_size))
+        w = dataclasses.replace(w, block_size=block_size, num_blocks=slots // block_size)
+    return w
 
 
 def parse_shapes(text):
@@ -534,7 +544,7 @@ def parse_shapes(text):
     return out
 
 
-def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3, only=None):
+def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3, only=None, block_size=0):
     """Every forced launch shape of the operator on one workload (rows per
     wavefront 1/2/4 x wavefronts per workgroup 1/2/4/8 x kv tokens per
     wavefront 1/2/4), plus both conversion paths at the heuristic's shape, or
@@ -544,7 +554,7 @@ def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3, only=None
     this measures only their speed, so the heuristic's choice can be
     re-checked on any machine."""
     from fp8_kv_cache_amd import probe
-    w = sweep_workload(W, name, size)
+    w = sweep_workload(W, name, size, block_size)
     name = w.name
     inp = W.make_inputs(w, device="cuda")
     valid = int(((inp["slot_mapping"] >= 0) & (inp["slot_mapping"] < w.num_blocks * w.block_size)).sum())
@@ -576,6 +586,7 @@ def sweep_shapes(torch, W, qp, name, size=None, launches=30, rounds=3, only=None
     del inp, args, ops, launches_of
     torch.cuda.empty_cache()
     res = {"mode": "sweep", "workload": "%s %dx%d" % (name, w.num_tokens, w.num_heads),
+           "cache": "%d blocks x %d slots" % (w.num_blocks, w.block_size),
            "bytes_per_launch": nbytes, "launches": launches, "rounds": rounds,
            "heuristic": {"rows_per_wave": heur.rows_per_wave, "waves_per_block": heur.waves_per_block,
                          "kv_per_wave": heur.kv_per_wave, "convert": heur.convert},
@@ -791,6 +802,9 @@ def main():
     ap.add_argument("--sizes", default="",
                     help="sweep mode: comma-separated TxH sizes (decode-like inputs) instead of --workload; "
                          "streams mode: comma-separated buffer sizes in MiB (default 512,2048)")
+    ap.add_argument("--block-sizes", default="",
+                    help="sweep mode: comma-separated cache block sizes (slots per block), each timed with "
+                         "the workload's slot count kept; default the workload's own")
     ap.add_argument("--shapes", default="",
                     help="sweep mode: only these shapes, as rows_per_wave:waves_per_block:kv_per_wave,...")
     args = ap.parse_args()
@@ -826,8 +840,10 @@ def main():
     if args.mode == "sweep":
         results = []
         for size in (args.sizes.split(",") if args.sizes else [None]):
-            results.append(sweep_shapes(torch, W, qp, args.workload, size, only=parse_shapes(args.shapes)))
-            print(json.dumps(results[-1]), flush=True)
+            for bs in ([int(v) for v in args.block_sizes.split(",")] if args.block_sizes else [0]):
+                results.append(sweep_shapes(torch, W, qp, args.workload, size, only=parse_shapes(args.shapes),
+                                            block_size=bs))
+                print(json.dumps(results[-1]), flush=True)
         if len(results) > 1:
             print(json.dumps(sweep_summary(results)), flush=True)
         return

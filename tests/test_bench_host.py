@@ -107,3 +107,19 @@ def test_sweep_reports_the_heuristic_against_the_fastest_shape():
     assert s["max_heuristic_over_best"] == r["heuristic_over_best"]
     assert s["mean_heuristic_over_best"] == round(r["heuristic_over_best"] / 2, 4)
     assert bench.sweep_summary([r3]) == {"mode": "sweep_summary", "sizes": 0}
+
+
+def test_sweep_block_sizes_keep_the_slot_count():
+    from fp8_kv_cache_amd import workloads as W
+    for name in ("prefill", "decode", "long"):
+        base = W.WORKLOADS[name]
+        for bs in (16, 64, 256):
+            w = bench.sweep_workload(W, name, None, bs)
+            assert w.block_size == bs and w.num_blocks * bs == base.num_blocks * base.block_size
+            assert (w.num_tokens, w.num_heads, w.slots, w.positions) == \
+                (base.num_tokens, base.num_heads, base.slots, base.positions)
+    assert bench.sweep_workload(W, "prefill", None, 0) == W.WORKLOADS["prefill"]
+    with pytest.raises(ValueError):
+        bench.sweep_workload(W, "tiny", None, 512)            # 256 slots do not split into 512
+    w = bench.sweep_workload(W, "prefill", "1000x8", 16)
+    assert w.block_size == 16 and w.num_tokens == 1000
