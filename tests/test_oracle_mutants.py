@@ -115,6 +115,10 @@ MUTANTS = [
      "data[ORC_NOPE_DIM + 2 * j] = (uint8_t)(h >> 8);\n        data[ORC_NOPE_DIM + 2 * j + 1] = (uint8_t)(h & 0xff);"),
     ("quantized from the wrong block", "scale[b] = orc_quant_block(y + b * ORC_QBLOCK, data + b * ORC_QBLOCK);",
      "scale[b] = orc_quant_block(y + (b ^ 1) * ORC_QBLOCK, data + b * ORC_QBLOCK);"),
+    ("kv codes from bf16-rounded values", "codes[j] = orc_f32_to_e4m3(y[j] * inv_scale);",
+     "codes[j] = orc_f32_to_e4m3(orc_bf16_to_f32(orc_f32_to_bf16(y[j])) * inv_scale);"),
+    ("kv amax from bf16-rounded values", "amax = fmaxf(amax, fabsf(y[j]));",
+     "amax = fmaxf(amax, fabsf(orc_bf16_to_f32(orc_f32_to_bf16(y[j]))));"),
     ("bf16 store unrotated", "insert_bf16_slot(z, cache, slot_mapping[t]);", "insert_bf16_slot(y, cache, slot_mapping[t]);"),
     ("gather exponent bias", "(int)scale[j / ORC_QBLOCK] - 127", "(int)scale[j / ORC_QBLOCK] - 128"),
     ("mxfp8 byte of a power of two bumped", "while (b > 0 && a <= ldexp(1.0, b - 1 - 127))  /* the least such b, not below 0 */\n        b -= 1;",
