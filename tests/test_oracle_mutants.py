@@ -119,6 +119,32 @@ MUTANTS = [
      "codes[j] = orc_f32_to_e4m3(orc_bf16_to_f32(orc_f32_to_bf16(y[j])) * inv_scale);"),
     ("kv amax from bf16-rounded values", "amax = fmaxf(amax, fabsf(y[j]));",
      "amax = fmaxf(amax, fabsf(orc_bf16_to_f32(orc_f32_to_bf16(y[j]))));"),
+    ("rope table row of position + 1", "const float *cs = cos_sin + positions[t] * 64;",
+     "const float *cs = cos_sin + ((positions[t] + 1) % max_position) * 64;"),
+    ("q weight ignored", "orc_row(q_in + row, q_w, eps, cs, y, z, NULL);", "orc_row(q_in + row, NULL, eps, cs, y, z, NULL);"),
+    ("q takes the kv weight", "orc_row(q_in + row, q_w, eps, cs, y, z, NULL);",
+     "orc_row(q_in + row, kv_w, eps, cs, y, z, NULL);"),
+    ("kv weight ignored", "orc_row(kv + t * ORC_HEAD_DIM, kv_w, eps, cs, y, z, NULL);",
+     "orc_row(kv + t * ORC_HEAD_DIM, NULL, eps, cs, y, z, NULL);"),
+    ("kv row of the next token", "orc_row(kv + t * ORC_HEAD_DIM, kv_w, eps, cs, y, z, NULL);",
+     "orc_row(kv + ((t + 1) % num_tokens) * ORC_HEAD_DIM, kv_w, eps, cs, y, z, NULL);"),
+    ("inverse root in double", "    float r = sqrtf(v);\n    return 1.0f / r;", "    return (float)(1.0 / sqrt((double)v));"),
+    ("eps doubled", "float v = mean_sq + eps;", "float v = mean_sq + 2.0f * eps;"),
+    ("mean over 511", "float mean_sq = sum_sq / 512.0f;", "float mean_sq = sum_sq / 511.0f;"),
+    ("e4m3 ties away from zero", "double q = nearbyint((2.0 * f - 1.0) * 8.0);", "double q = round((2.0 * f - 1.0) * 8.0);"),
+    ("e4m3 subnormal ties away from zero", "double m = nearbyint(a * 512.0);", "double m = round(a * 512.0);"),
+    ("only slot -1 skips", "if (slot < 0 || block_size <= 0 || slot >= num_blocks * (int64_t)block_size)",
+     "if (slot == -1 || block_size <= 0 || slot >= num_blocks * (int64_t)block_size)"),
+    ("scale records reversed", "scale[b] = orc_quant_block(y + b * ORC_QBLOCK, data + b * ORC_QBLOCK);",
+     "scale[ORC_NQBLOCK - 1 - b] = orc_quant_block(y + b * ORC_QBLOCK, data + b * ORC_QBLOCK);"),
+    ("q output unrotated", "q_out[row + j] = orc_f32_to_bf16(z[j]);", "q_out[row + j] = orc_f32_to_bf16(y[j]);"),
+    ("kv rope bytes unrotated", "uint16_t h = orc_f32_to_bf16(z[ORC_NOPE_DIM + j]);\n        data[ORC_NOPE_DIM + 2 * j]",
+     "uint16_t h = orc_f32_to_bf16(y[ORC_NOPE_DIM + j]);\n        data[ORC_NOPE_DIM + 2 * j]"),
+    ("bf16 store at the fp8 slot stride", "uint8_t *data = cache + slot * 1024;", "uint8_t *data = cache + slot * 584;"),
+    ("gather rope from the nope bytes",
+     "(uint16_t)(data[ORC_NOPE_DIM + 2 * j] | (data[ORC_NOPE_DIM + 2 * j + 1] << 8)));",
+     "(uint16_t)(data[2 * j] | (data[2 * j + 1] << 8)));"),
+    ("gather scale of the next block", "(int)scale[j / ORC_QBLOCK] - 127", "(int)scale[(j / ORC_QBLOCK + 1) % 7] - 127"),
     ("bf16 store unrotated", "insert_bf16_slot(z, cache, slot_mapping[t]);", "insert_bf16_slot(y, cache, slot_mapping[t]);"),
     ("gather exponent bias", "(int)scale[j / ORC_QBLOCK] - 127", "(int)scale[j / ORC_QBLOCK] - 128"),
     ("mxfp8 byte of a power of two bumped", "while (b > 0 && a <= ldexp(1.0, b - 1 - 127))  /* the least such b, not below 0 */\n        b -= 1;",
