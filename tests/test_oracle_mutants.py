@@ -163,6 +163,25 @@ MUTANTS = [
     ("mxfp8 odd element dropped", "if (nc % 2)\n            c[half] = c[nc - 1];", "if (nc % 2)\n            c[half] = 0.0f;"),
     ("mxfp8 residual ignored", "float sum = orc_bf16_to_f32(xr[j]) + orc_bf16_to_f32(residual[r * hidden + j]);",
      "float sum = orc_bf16_to_f32(xr[j]);"),
+    ("mxfp8 eps outside the root", "float inv = 1.0f / sqrtf(mean_sq + eps);", "float inv = 1.0f / (sqrtf(mean_sq) + eps);"),
+    ("mxfp8 norm scales the binary32 residual sum", "float t = orc_bf16_to_f32(pre[j]) * inv;",
+     "float t = (residual ? orc_bf16_to_f32(xr[j]) + orc_bf16_to_f32(residual[r * hidden + j])\n"
+     "                                 : orc_bf16_to_f32(pre[j])) * inv;"),
+    ("mxfp8 weight before inv",
+     "float t = orc_bf16_to_f32(pre[j]) * inv;\n            normed[j] = orc_bf16_to_f32(orc_f32_to_bf16(t * g1));",
+     "float t = orc_bf16_to_f32(pre[j]) * g1;\n            normed[j] = orc_bf16_to_f32(orc_f32_to_bf16(t * inv));"),
+    ("mxfp8 residual output from x", "                residual_out[r * hidden + j] = pre[j];",
+     "                residual_out[r * hidden + j] = xr[j];"),
+    ("mxfp8 mean over the padded width", "float mean_sq = f32_div(s, (float)hidden);",
+     "float mean_sq = f32_div(s, (float)((hidden + 511) / 512 * 512));"),
+    ("mxfp8 clamp at 240", "v = fminf(fmaxf(v, -448.0f), 448.0f);", "v = fminf(fmaxf(v, -240.0f), 240.0f);"),
+    ("mxfp8 column interleave", "return col % 4 + (col / 4) * 512 +", "return (col / 4) % 4 + (col % 4) * 512 + (col / 16) * 2048 +"),
+    ("mxfp8 tile stride of 64 columns", "(row / 128) * 128 * padded_cols;", "(row / 128) * 64 * padded_cols;"),
+    ("mxfp8 amax over 31 elements",
+     "for (int k = 0; k < 32; ++k)\n                amax = fmaxf(amax, fabsf(normed[32 * b + k]));",
+     "for (int k = 0; k < 31; ++k)\n                amax = fmaxf(amax, fabsf(normed[32 * b + k]));"),
+    ("mxfp8 scale byte one column over", "scale_out[orc_mxfp8_scale_offset(r, b, padded_cols)] = (uint8_t)byte;",
+     "scale_out[orc_mxfp8_scale_offset(r, (b + 1) % cols, padded_cols)] = (uint8_t)byte;"),
     ("mxfp8 block of 16", "uint32_t byte = orc_ue8m0_ceil_byte(amax * inv448);",
      "uint32_t byte = orc_ue8m0_ceil_byte(fmaxf(amax, 0.0f) * inv448 * ((b & 1) ? 1.0f : 1.0f) + 0.0f * normed[0]);\n            amax = 0.0f; for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(normed[32 * b + k]));\n            byte = orc_ue8m0_ceil_byte(amax * inv448);"),
 ]

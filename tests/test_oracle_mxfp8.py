@@ -216,3 +216,118 @@ def test_odd_carry_tree_equals_the_zero_padded_tree():
         a = oracle.lib().orc_sum_squares_n(np.ascontiguousarray(x).ctypes.data, n)
         b = oracle.lib().orc_sum_squares_n(np.ascontiguousarray(padded).ctypes.data, width)
         assert np.float32(a).view(np.uint32) == np.float32(b).view(np.uint32), n
+
+
+# ------------------------------------------------------------- exact arithmetic
+#
+# tests/mx_exact.py evaluates readings M1-M6 in exact rational arithmetic with
+# one rounding per stated step, independently of the oracle.  The oracle must
+# match it code for code and byte for byte; the cases below are chosen so that
+# the alternative readings it can also evaluate (eps outside the root, the norm
+# reading the binary32 sum instead of its bf16 rounding, the Gemma weight
+# applied before inv) give different codes.
+
+from fractions import Fraction  # noqa: E402
+
+import mx_exact as X  # noqa: E402
+
+
+def _bits(vals):
+    """bf16 bit patterns of values that are bf16 numbers (checked)."""
+    f = np.array([float(v) for v in vals], np.float32)
+    b = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), f)
+    return b
+
+
+def _oracle_row(x, gamma, eps, residual=None):
+    hidden = len(x)
+    codes, scales, _ = oracle.mxfp8_norm_quant(_bits(x)[None, :], _bits(gamma), eps,
+                                               residual=None if residual is None else _bits(residual)[None, :])
+    pc = hidden // 32
+    return [int(c) for c in codes[0]], [int(scales[oracle.mxfp8_scale_offset(0, c, pc)]) for c in range(pc)]
+
+
+def test_exact_helper_known_values():
+    assert X.sqrt_rn32(Fraction(9)) == 3
+    assert np.float32(float(X.sqrt_rn32(Fraction(2)))).view(np.uint32) == 0x3FB504F3
+    assert X.sqrt_rn32(Fraction(1, 4)) == Fraction(1, 2)
+    assert X.bf16(1 + Fraction(1, 256)) == 1                      # tie to the even significand
+    assert X.bf16(1 + Fraction(3, 256)) == 1 + Fraction(1, 64)
+    assert X.rn32(Fraction(1, 3)) == Fraction(11184811, 2 ** 25)
+    assert [X.e4m3(v) for v in (448, 304, 288, Fraction(1, 512), Fraction(3, 1024), Fraction(1, 1024), -1)] == \
+        [0x7E, 0x7A, 0x79, 0x01, 0x02, 0x00, 0xB8]
+    assert X.scale_byte(Fraction(1, 256)) == 119 and X.scale_byte(Fraction(1, 256) * (1 + Fraction(1, 2 ** 23))) == 120
+    assert X.scale_byte(0) == 0 and X.scale_byte(Fraction(1, 2 ** 140)) == 0
+
+
+def test_eps_inside_the_root():
+    # x = 2 everywhere, gamma = 0, eps = 5: S = 128 * 4, mean 4, RN(4 + 5) = 9,
+    # root 3, inv = RN(1/3), t = RN(2 * inv) = 0.666666686..., whose bf16 is
+    # 0.66796875: v = RN(0.66796875 * RN(1/448)) lies in (2^-10, 2^-9], byte
+    # 118, inverse 2^9, 342 -> 352, code 0x7b.  With eps outside the root:
+    # inv = RN(1/7), n = bf16(2/7) = 0.28515625, byte 117, 292 -> 288, code 0x79.
+    x, g = [2] * 128, [0] * 128
+    codes, bytes_ = _oracle_row(x, g, 5.0)
+    assert codes == [0x7B] * 128 and bytes_ == [118] * 4
+    assert (codes, bytes_) == X.row(x, g, 5.0)
+    assert X.row(x, g, 5.0, eps_outside=True) == ([0x79] * 128, [117] * 4)
+
+
+def _residual_case(seed, hidden=128, k=8):
+    # k non-zero elements (integers 1..3) with residuals of +-1 or 3 / 256, so
+    # that x + residual is not always a bf16 number and the sum of squares stays
+    # exact in binary32; weights in steps of 1/64.
+    rng = np.random.default_rng(seed)
+    x = [Fraction(0)] * hidden
+    r = [Fraction(0)] * hidden
+    for j in rng.choice(hidden, k, replace=False):
+        x[j] = Fraction(int(rng.integers(1, 4)))
+        r[j] = Fraction(int(rng.choice([-3, -1, 1, 3])), 256)
+    g = [Fraction(int(v), 64) for v in rng.integers(-16, 17, hidden)]
+    return x, r, g
+
+
+def test_norm_reads_the_bf16_residual_sum():
+    # Seeds where the readings part: at 12 the binary32 sum read in both the
+    # sum of squares and the scaling moves block 2's byte (119 -> 120); at 40
+    # it moves block 2's byte (122 -> 121) also when only the scaling reads it.
+    x, r, g = _residual_case(12)
+    got = _oracle_row(x, g, 0.0, residual=r)
+    assert got == X.row(x, g, 0.0, residual=r)
+    alt = X.row(x, g, 0.0, residual=r, fp32_sum=True)
+    assert got[1][2] == 119 and alt[1][2] == 120
+    x, r, g = _residual_case(40)
+    got = _oracle_row(x, g, 0.0, residual=r)
+    assert got == X.row(x, g, 0.0, residual=r)
+    assert got[1][2] == 122
+    for alt in (X.row(x, g, 0.0, residual=r, fp32_sum=True), X.row(x, g, 0.0, residual=r, fp32_scaled=True)):
+        assert alt[1][2] == 121 and alt[0] != got[0]
+
+
+def test_gemma_weight_applied_after_inv():
+    # x = 7 everywhere at eps = 0: inv = RN(1/7) and RN(7 * inv) = 1, so n is
+    # the bf16 of (gamma + 1); with the weight first, RN(RN(7 * (gamma + 1)) * inv)
+    # moves some of them by an ulp, and at this seed one across an E4M3 midpoint.
+    rng = np.random.default_rng(0)
+    g = [X.bf16(Fraction(int(v), 512)) for v in rng.integers(-200, 201, 128)]
+    x = [7] * 128
+    got = _oracle_row(x, g, 0.0)
+    assert got == X.row(x, g, 0.0)
+    assert X.row(x, g, 0.0, weight_first=True)[0] != got[0]
+
+
+@pytest.mark.parametrize("hidden,with_residual,eps", [(128, False, 0.0), (512, True, 1e-6), (1536, True, 0.0),
+                                                     (7168, False, 1e-6)])
+def test_dyadic_rows_code_for_code(hidden, with_residual, eps):
+    # Quarter-integer inputs keep every sum of squares exact (and every
+    # residual sum a bf16 number), so the whole row is fixed by the readings.
+    rng = np.random.default_rng(hidden)
+    x = [Fraction(int(v), 4) for v in rng.integers(-16, 17, hidden)]
+    x = [v if v != 0 else Fraction(1, 4) for v in x]
+    r = [Fraction(int(v), 4) for v in rng.integers(-8, 9, hidden)] if with_residual else None
+    if r is not None:
+        r = [b if a + b != 0 else b + Fraction(1, 4) for a, b in zip(x, r)]
+    g = [X.bf16(Fraction(int(v), 256)) for v in rng.integers(-60, 61, hidden)]
+    eps32 = float(np.float32(eps))
+    assert _oracle_row(x, g, eps32, residual=r) == X.row(x, g, Fraction(eps32), residual=r)
