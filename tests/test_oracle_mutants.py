@@ -145,6 +145,11 @@ MUTANTS = [
      "(uint16_t)(data[ORC_NOPE_DIM + 2 * j] | (data[ORC_NOPE_DIM + 2 * j + 1] << 8)));",
      "(uint16_t)(data[2 * j] | (data[2 * j + 1] << 8)));"),
     ("gather scale of the next block", "(int)scale[j / ORC_QBLOCK] - 127", "(int)scale[(j / ORC_QBLOCK + 1) % 7] - 127"),
+    ("cos/sin table interleaved", "float c = cs[i];\n        float sn = cs[ORC_NPAIR + i];",
+     "float c = cs[2 * i];\n        float sn = cs[2 * i + 1];"),
+    ("rope dims weighted after the rotation",
+     "        y[j] = w ? t * orc_bf16_to_f32(w[j]) : t;\n        z[j] = y[j];",
+     "        y[j] = (w && j < ORC_NOPE_DIM) ? t * orc_bf16_to_f32(w[j]) : t;\n        z[j] = y[j];"),
     ("bf16 store unrotated", "insert_bf16_slot(z, cache, slot_mapping[t]);", "insert_bf16_slot(y, cache, slot_mapping[t]);"),
     ("gather exponent bias", "(int)scale[j / ORC_QBLOCK] - 127", "(int)scale[j / ORC_QBLOCK] - 128"),
     ("mxfp8 byte of a power of two bumped", "while (b > 0 && a <= ldexp(1.0, b - 1 - 127))  /* the least such b, not below 0 */\n        b -= 1;",
