@@ -133,3 +133,40 @@ def test_mxfp8_partial_group_decides_the_sum_order():
     wc, ws, _ = oracle.mxfp8_norm_quant(W.as_u16(x), W.as_u16(gamma), 1e-6)
     assert np.array_equal(codes.cpu().numpy(), wc)
     assert np.array_equal(scales.cpu().numpy(), ws)
+
+
+def _reading_cases():
+    """The CPU pins' rows that decide a reading (tests/test_oracle_mxfp8.py):
+    eps inside the root, the norm reading the bf16 residual sum (two seeds),
+    the Gemma weight applied after inv.  Returns (name, x, residual, gamma,
+    eps) with bf16 bit patterns."""
+    from fractions import Fraction
+    import test_oracle_mxfp8 as T
+    import mx_exact as X
+    cases = [("eps inside the root", T._bits([2] * 128), None, T._bits([0] * 128), 5.0)]
+    for seed in (12, 40):
+        x, r, g = T._residual_case(seed)
+        cases.append(("bf16 residual sum, seed %d" % seed, T._bits(x), T._bits(r), T._bits(g), 0.0))
+    rng = np.random.default_rng(0)
+    g = [X.bf16(Fraction(int(v), 512)) for v in rng.integers(-200, 201, 128)]
+    cases.append(("weight after inv", T._bits([7] * 128), None, T._bits(g), 0.0))
+    return cases
+
+
+def test_mxfp8_rows_that_decide_a_reading():
+    # The kernel takes the same side of each reading as the oracle, on the rows
+    # where the alternatives give other codes.
+    for name, x, r, g, eps in _reading_cases():
+        print("case mxfp8 reading: %s" % name, flush=True)
+        hidden = x.size
+        xt = torch.from_numpy(x.view(np.int16).reshape(1, hidden)).view(torch.bfloat16).to(DEV)
+        gt = torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).to(DEV)
+        rt = None if r is None else torch.from_numpy(r.view(np.int16).reshape(1, hidden)).view(torch.bfloat16).to(DEV)
+        scales = torch.full((qp.qkv_prep_mxfp8_scale_bytes(1, hidden),), 0xEE, dtype=torch.uint8, device=DEV)
+        codes = torch.full((1, hidden), 0xEE, dtype=torch.uint8, device=DEV)
+        qp.mxfp8_norm_quant(xt, gt, eps, residual=rt, quant_out=codes, scale_out=scales)
+        torch.cuda.synchronize()
+        want_codes, want_scales, _ = oracle.mxfp8_norm_quant(x.reshape(1, hidden), g, eps,
+                                                            residual=None if r is None else r.reshape(1, hidden))
+        assert np.array_equal(codes.cpu().numpy(), want_codes), name
+        assert np.array_equal(scales.cpu().numpy(), want_scales), name
