@@ -25,6 +25,15 @@ struct MxArgs {
     float eps;
 };
 
+// The byte of scale column `col` of row `row` in the 128x4 swizzled layout
+// (rows in tiles of 128, each tile padded_cols * 128 bytes: column group
+// col/4 takes 512 bytes, row r of the tile sits at (r % 32) * 16 + (r / 32) * 4
+// in it, and the 4 columns of the group are consecutive bytes).
+__host__ __device__ __forceinline__ int64_t mx_swizzled_offset(int64_t row, int64_t col, int64_t padded_cols)
+{
+    return (col & 3) + (col >> 2) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (row >> 7) * 128 * padded_cols;
+}
+
 // Rows of up to kMxMaxGroups groups of 512 values (hidden <= 16384).
 constexpr int kMxMaxGroups = 32;
 

@@ -23,11 +23,6 @@ namespace {
 
 using namespace dev;
 
-__device__ __forceinline__ int64_t swizzled_offset(int64_t row, int64_t col, int64_t padded_cols)
-{
-    return (col & 3) + (col >> 2) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (row >> 7) * 128 * padded_cols;
-}
-
 __device__ __forceinline__ uint32_t max4(uint32_t v)
 {
     v = max(v, dpp_u32<kDppXor1>(v));
@@ -55,7 +50,7 @@ __global__ __launch_bounds__(1024) void mxfp8_kernel(MxArgs a)
         // Padding rows of the last 128-row tile: zero scale bytes, one aligned
         // word of 4 columns per lane.
         for (int c = threadIdx.x * 4; c < a.padded_cols; c += blockDim.x * 4)
-            *reinterpret_cast<uint32_t *>(a.scale_out + swizzled_offset(row, c, a.padded_cols)) = 0u;
+            *reinterpret_cast<uint32_t *>(a.scale_out + mx_swizzled_offset(row, c, a.padded_cols)) = 0u;
         return;
     }
     const int64_t rbase = row * a.hidden;
@@ -157,7 +152,7 @@ __global__ __launch_bounds__(1024) void mxfp8_kernel(MxArgs a)
         if (in_row(chunk)) {
             store_sys2(a.quant_out + rbase, (uint32_t)a.hidden, (uint32_t)chunk * 8u, codes);
             if ((lane & 15) == 0)
-                *reinterpret_cast<uint32_t *>(a.scale_out + swizzled_offset(row, chunk >> 2, a.padded_cols)) = word;
+                *reinterpret_cast<uint32_t *>(a.scale_out + mx_swizzled_offset(row, chunk >> 2, a.padded_cols)) = word;
         }
     }
 }

@@ -234,13 +234,6 @@ struct MxPattern {
     int32_t padded_cols;
 };
 
-// The scale byte of (row, col) in the 128x4 swizzled layout (the MXFP8
-// operator's output format): 128-row tiles of padded_cols columns.
-__device__ __forceinline__ int64_t mx_swizzled(int64_t row, int64_t col, int64_t padded_cols)
-{
-    return (col & 3) + (col >> 2) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (row >> 7) * 128 * padded_cols;
-}
-
 template <int G, bool RES, bool CODES, bool SCALES, bool BARRIER>
 __global__ __launch_bounds__(1024) void mxfp8_pattern(MxPattern a)
 {
@@ -251,7 +244,7 @@ __global__ __launch_bounds__(1024) void mxfp8_pattern(MxPattern a)
     if (row >= a.m) {
         if constexpr (SCALES)
             for (int c = threadIdx.x * 4; c < a.padded_cols; c += blockDim.x * 4)
-                *reinterpret_cast<uint32_t *>(a.scales + mx_swizzled(row, c, a.padded_cols)) = 0u;
+                *reinterpret_cast<uint32_t *>(a.scales + qkvp::mx_swizzled_offset(row, c, a.padded_cols)) = 0u;
         return;
     }
     const int64_t chunks_per_row = a.hidden / 8;
@@ -287,7 +280,7 @@ __global__ __launch_bounds__(1024) void mxfp8_pattern(MxPattern a)
                                       u32x2{p[j][0] ^ p[j][1] ^ gm[0] ^ extra, p[j][2] ^ p[j][3] ^ gm[1]});
             if constexpr (SCALES) {
                 if ((lane & 15) == 0)
-                    *reinterpret_cast<uint32_t *>(a.scales + mx_swizzled(row, chunk >> 2, a.padded_cols)) =
+                    *reinterpret_cast<uint32_t *>(a.scales + qkvp::mx_swizzled_offset(row, chunk >> 2, a.padded_cols)) =
                         p[j][0] ^ p[j][3] ^ gm[3] ^ extra;
             }
         }
