@@ -478,3 +478,88 @@ def test_probe_update_increments_every_chunk_once():
         want = host.reshape(-1, 4).copy()
         want[:, 0] += np.uint32(1)
         assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------- readings R3 and R4
+
+def _bf16_tensor(u16, shape):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16).reshape(shape)).view(torch.bfloat16).to(DEV)
+
+
+def _one_row(x16, w16, eps, cs):
+    """One token, one head: q row x16 with q weight w16, the same row and
+    weight for kv, position 0 of the table cs, slot 0 of a poisoned
+    one-block cache.  Returns (GPU q, GPU cache, oracle q, oracle cache)."""
+    from fp8_kv_cache_amd.qkv_prep import QkvPrep
+    q = _bf16_tensor(x16, (1, 1, 512))
+    kv = _bf16_tensor(x16, (1, 512))
+    w = _bf16_tensor(w16, (512,))
+    pos = torch.zeros(1, dtype=torch.int64, device=DEV)
+    slots = torch.zeros(1, dtype=torch.int64, device=DEV)
+    table = torch.from_numpy(cs).to(DEV)
+    cache = torch.full((1, 64 * 584), 0x5A, dtype=torch.uint8, device=DEV)
+    want_cache = cache.cpu().numpy().copy()
+    QkvPrep(1, block_size=64, eps=eps)(q, kv, w, w, pos, table, slots, cache)
+    torch.cuda.synchronize()
+    want_q = oracle.qkv_prep(x16.reshape(1, 1, 512), x16.reshape(1, 512), w16, w16, np.zeros(1, np.int64), cs,
+                             np.zeros(1, np.int64), want_cache, 1, 64, eps)
+    return W.as_u16(q), cache.cpu().numpy(), want_q, want_cache
+
+
+def test_rows_where_the_readings_part_in_bf16():
+    # The CPU pins fix the oracle to readings R3 (y = RN(RN(x*inv)*w)) and R4
+    # (a' = RN(fma(a, c, -RN(b*s))), b' = RN(fma(a, s, RN(b*c)))) with cases
+    # whose fp32 intermediates differ; these two rows are ones where the
+    # alternatives also change a stored bf16 value, so the kernel's bits show
+    # which reading it takes.
+    from fractions import Fraction
+    import mx_exact as X
+
+    def bf16(v):
+        return oracle.f32_to_bf16(np.asarray(v, np.float32))
+
+    # R3: row 249 of seed 1000's normal rows, weights 1 + 0.1 N(0, 1), eps 1e-6,
+    # the identity rotation: at dim 425, RN(RN(x*w)*inv) and RN(x*RN(inv*w))
+    # both round to another bf16 than the stated order.
+    rng = np.random.default_rng(1000)
+    x = bf16(rng.standard_normal((256, 512)))[249]
+    w = bf16(1.0 + 0.1 * rng.standard_normal(512))
+    cs = W.rope_table(8)
+    note("case R3 row (seed 1000, row 249)")
+    got_q, got_cache, want_q, want_cache = _one_row(x, w, 1e-6, cs)
+    assert np.array_equal(got_q.reshape(-1), want_q.reshape(-1))
+    assert np.array_equal(got_cache, want_cache)
+    _, _, _, inv = oracle.rows(x.reshape(1, 512), w, 1e-6, cs[:1])
+    xf, wf, iv = (float(oracle.bf16_to_f32(x)[425]), float(oracle.bf16_to_f32(w)[425]), float(inv[0]))
+    stated = X.rn32(Fraction(X.rn32(Fraction(xf) * Fraction(iv))) * Fraction(wf))
+    others = (X.rn32(Fraction(X.rn32(Fraction(xf) * Fraction(wf))) * Fraction(iv)),
+              X.rn32(Fraction(xf) * Fraction(X.rn32(Fraction(iv) * Fraction(wf)))))
+    assert all(X.bf16(o) != X.bf16(stated) for o in others)
+    assert got_q.reshape(-1)[425] == int(bf16([float(stated)])[0])
+
+    # R4: a row of ones at eps = 0 (inv = 1, y = w) with the pairs set by the
+    # weight; table row 0 is the identity except pairs 0 and 1, which take
+    # float32 cos 7 and sin 7.  Pair 0 decides the first output, pair 1 the
+    # second: both alternatives (two roundings; the fma on the other product)
+    # give another bf16.
+    c = float(np.uint32(0x3F40FFBD).view(np.float32))
+    s = float(np.uint32(0x3F283046).view(np.float32))
+    wv = np.ones(512, np.float32)
+    wv[448:452] = (-0.90234375, -0.96875, -1.7734375, 1.4921875)
+    w = bf16(wv)
+    cs = np.zeros((8, 64), np.float32)
+    cs[:, :32] = 1.0
+    cs[0, 0] = cs[0, 1] = c
+    cs[0, 32] = cs[0, 33] = s
+    note("case R4 pairs at cos 7, sin 7")
+    got_q, got_cache, want_q, want_cache = _one_row(bf16(np.ones(512)), w, 0.0, cs)
+    assert np.array_equal(got_q.reshape(-1), want_q.reshape(-1))
+    assert np.array_equal(got_cache, want_cache)
+    C, S = Fraction(c), Fraction(s)
+    a, b = Fraction(-0.90234375), Fraction(-0.96875)
+    first = [X.rn32(a * C - X.rn32(b * S)), X.rn32(X.rn32(a * C) - X.rn32(b * S)), X.rn32(-b * S + X.rn32(a * C))]
+    a, b = Fraction(-1.7734375), Fraction(1.4921875)
+    second = [X.rn32(a * S + X.rn32(b * C)), X.rn32(X.rn32(a * S) + X.rn32(b * C)), X.rn32(b * C + X.rn32(a * S))]
+    for vals, dim in ((first, 448), (second, 451)):
+        assert X.bf16(vals[0]) != X.bf16(vals[1]) and X.bf16(vals[0]) != X.bf16(vals[2])
+        assert got_q.reshape(-1)[dim] == int(bf16([float(vals[0])])[0])
