@@ -123,3 +123,18 @@ def test_sweep_block_sizes_keep_the_slot_count():
         bench.sweep_workload(W, "tiny", None, 512)            # 256 slots do not split into 512
     w = bench.sweep_workload(W, "prefill", "1000x8", 16)
     assert w.block_size == 16 and w.num_tokens == 1000
+
+
+def test_streams_table_holds_only_combinations_the_probe_accepts():
+    # With zero bytes the probe checks every argument and launches nothing.
+    from fp8_kv_cache_amd import probe
+    lib = probe.library()
+    table = bench.stream_table(probe)
+    assert len({row[0] for row in table}) == len(table)
+    for label, kind, lp, sp, sleep, lanes, depth in table:
+        src = None if kind in (probe.WRITE, probe.UPDATE) else 1 << 30
+        assert lib.qkv_prep_probe_stream(kind, lp, sp, sleep, lanes, depth, 1 << 20, src, 0, 0, None) == 0, label
+    # the MXFP8 pattern's stream sets, with every buffer given
+    for streams in (1 | 2 | 4 | 8, 1 | 2 | 4, 1 | 2 | 8, 1 | 4 | 8, 1 | 8):
+        assert lib.qkv_prep_probe_mxfp8_pattern(1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 6 << 20, 0, 7168,
+                                                streams, None) == 0
