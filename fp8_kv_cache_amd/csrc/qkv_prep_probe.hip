@@ -1,10 +1,11 @@
 // The measurement and verification probes of libqkv_prep_probe.so (see
 // include/qkv_prep_probe.h): policy-selectable read, write, copy and in-place
 // update streams, two of which (a copy and an in-place update at their fastest
-// settings) serve as bandwidth ceilings, and the operators' own number-format
-// code run on arrays so that tests can compare it with a reference on every
-// input pattern.
-// None of this is part of the operators; it is built into its own library.
+// settings) serve as bandwidth ceilings; the MXFP8 operator's memory access
+// pattern without its arithmetic; and the operators' own number-format code
+// run on arrays so that tests can compare it with a reference on every input
+// pattern.  None of this is part of the operators; it is built into its own
+// library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,12 +18,13 @@ namespace {
 using qkvp::dev::u32x2;
 using qkvp::dev::u32x4;
 
-// Policy-selectable streams (qkv_prep_probe_stream): one 16-byte access per
-// lane, blockDim.x lanes per workgroup, every access through a buffer
-// descriptor whose base is the workgroup's first chunk, so any combination of
-// the cache-policy bits can be put on the loads and on the stores.  These are
-// the streams behind the read / write / copy / update rates and the
-// cache-policy comparison quoted in the kernels' comments.
+// Policy-selectable streams (qkv_prep_probe_stream): 16-byte accesses, one or
+// several per lane, blockDim.x lanes per workgroup, every access through a
+// buffer descriptor whose base is the workgroup's first chunk, so any
+// combination of the cache-policy bits can be put on the loads and on the
+// stores.  These are the streams behind the read / write / copy / update rates,
+// the cache-policy comparison and the rows-in-flight comparison quoted in the
+// kernels' comments.
 constexpr int kSc0 = 1, kNt = 2, kSc1 = 16;
 enum StreamKind { kRead = 0, kWrite = 1, kCopy = 2, kUpdate = 3 };
 
