@@ -672,6 +672,16 @@ def stream_table(probe):
     ]
 
 
+def stream_bytes(size):
+    """A streams-mode buffer size: MiB, or KiB with a trailing k ("146k"),
+    rounded down to whole 16-byte chunks."""
+    size = size.strip().lower()
+    n = int(size[:-1]) << 10 if size.endswith("k") else int(size) << 20
+    if n < 16:
+        raise ValueError("a stream needs at least one 16-byte chunk: %r" % size)
+    return n // 16 * 16
+
+
 def sweep_streams(torch, probe, nbytes, launches=20, rounds=4):
     """Every stream of stream_table over `nbytes`-byte buffers: the region
     time of `launches` back-to-back launches, best of `rounds` interleaved
@@ -801,7 +811,8 @@ def main():
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--sizes", default="",
                     help="sweep mode: comma-separated TxH sizes (decode-like inputs) instead of --workload; "
-                         "streams mode: comma-separated buffer sizes in MiB (default 512,2048)")
+                         "streams mode: comma-separated buffer sizes in MiB, or KiB with a k suffix "
+                         "(default 512,2048)")
     ap.add_argument("--block-sizes", default="",
                     help="sweep mode: comma-separated cache block sizes (slots per block), each timed with "
                          "the workload's slot count kept; default the workload's own")
@@ -834,8 +845,8 @@ def main():
             print(json.dumps(mxfp8_pattern(torch, probe, qp, m, h)), flush=True)
         return
     if args.mode == "streams":
-        for mib in (args.sizes or "512,2048").split(","):
-            print(json.dumps(sweep_streams(torch, probe, int(mib) << 20)), flush=True)
+        for size in (args.sizes or "512,2048").split(","):
+            print(json.dumps(sweep_streams(torch, probe, stream_bytes(size))), flush=True)
         return
     if args.mode == "sweep":
         results = []

@@ -138,3 +138,11 @@ def test_streams_table_holds_only_combinations_the_probe_accepts():
     for streams in (1 | 2 | 4 | 8, 1 | 2 | 4, 1 | 2 | 8, 1 | 4 | 8, 1 | 8):
         assert lib.qkv_prep_probe_mxfp8_pattern(1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 6 << 20, 0, 7168,
                                                 streams, None) == 0
+
+
+def test_stream_sizes():
+    assert bench.stream_bytes("512") == 512 << 20
+    assert bench.stream_bytes("146k") == 146 << 10
+    assert bench.stream_bytes(" 1K ") == 1024
+    with pytest.raises(ValueError):
+        bench.stream_bytes("0k")
