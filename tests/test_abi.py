@@ -564,3 +564,20 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     res = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "libqkv_prep.so is not built" in res.stdout
+
+
+def test_public_headers_compile_as_c99_and_cpp(tmp_path):
+    # Every public header, alone and together, from plain C (C99, pedantic,
+    # warnings as errors) and from C++11: a C consumer needs nothing else.
+    import shutil
+    import subprocess
+    headers = sorted({os.path.basename(h) for h in HEADERS + [PROBE_HEADER]})
+    src = tmp_path / "hdr.c"
+    src.write_text("".join('#include "%s"\n' % h for h in headers) + "int main(void) { return 0; }\n")
+    for cc, std, lang in (("gcc", "-std=c99", "c"), ("g++", "-std=c++11", "c++")):
+        if shutil.which(cc) is None:
+            pytest.skip("%s not available" % cc)
+        res = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                              os.path.join(ROOT, "include"), "-x", lang, str(src), "-o", str(tmp_path / "hdr")],
+                             capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr
