@@ -630,45 +630,48 @@ def sweep_summary(results):
 
 def stream_table(probe):
     """The streams timed by --mode streams: (label, kind, load policy, store
-    policy, sleep, lanes per workgroup, chunks per lane).  Reads, writes,
+    policy, sleep, lanes per workgroup, chunks per lane, XCD-contiguous order).  Reads, writes,
     copies and in-place updates with the cache-policy bits the kernels choose
     between, the pause before the store that an in-place update was once
     thought to need, the workgroup sizes of the copy and the update, and
     several chunks per lane with all their loads issued first (with 64 lanes,
     several consecutive 1 KiB rows per wavefront: the "several tokens' loads
-    in flight" shape)."""
+    in flight" shape), and the copy and the update with each XCD streaming one
+    contiguous eighth of the buffer."""
     R, Wr, C, U = probe.READ, probe.WRITE, probe.COPY, probe.UPDATE
     NT, SC1, SC0 = probe.NT, probe.SC1, probe.SC0
     return [
-        ("read plain", R, 0, 0, 0, 256, 1),
-        ("read nt", R, NT, 0, 0, 256, 1),
-        ("read nt sc1", R, NT | SC1, 0, 0, 256, 1),
-        ("write plain", Wr, 0, 0, 0, 256, 1),
-        ("write nt", Wr, 0, NT, 0, 256, 1),
-        ("write sc1", Wr, 0, SC1, 0, 256, 1),
-        ("write nt sc1", Wr, 0, NT | SC1, 0, 256, 1),
-        ("write sc0 nt sc1", Wr, 0, SC0 | NT | SC1, 0, 256, 1),
-        ("copy plain -> plain", C, 0, 0, 0, 256, 1),
-        ("copy nt -> nt", C, NT, NT, 0, 256, 1),
-        ("copy nt -> nt sc1", C, NT, NT | SC1, 0, 256, 1),
-        ("copy nt sc1 -> nt sc1", C, NT | SC1, NT | SC1, 0, 256, 1),
-        ("copy nt -> nt sc1, sleep", C, NT, NT | SC1, 1, 256, 1),
-        ("copy nt -> nt sc1, 64 lanes", C, NT, NT | SC1, 0, 64, 1),
-        ("copy nt -> nt sc1, 1024 lanes", C, NT, NT | SC1, 0, 1024, 1),
-        ("copy nt -> nt sc1, 4 chunks per lane", C, NT, NT | SC1, 0, 256, 4),
-        ("copy nt -> nt sc1, 16 chunks per lane", C, NT, NT | SC1, 0, 256, 16),
-        ("update nt -> nt", U, NT, NT, 0, 64, 1),
-        ("update nt -> nt, sleep", U, NT, NT, 1, 64, 1),
-        ("update nt -> nt sc1", U, NT, NT | SC1, 0, 64, 1),
-        ("update nt -> nt sc1, sleep", U, NT, NT | SC1, 1, 64, 1),
-        ("update plain -> plain, sleep", U, 0, 0, 1, 64, 1),
-        ("update nt -> nt sc1, sleep, 256 lanes", U, NT, NT | SC1, 1, 256, 1),
-        ("update nt -> nt sc1, 2 rows per wavefront", U, NT, NT | SC1, 0, 64, 2),
-        ("update nt -> nt sc1, 4 rows per wavefront", U, NT, NT | SC1, 0, 64, 4),
-        ("update nt -> nt sc1, 8 rows per wavefront", U, NT, NT | SC1, 0, 64, 8),
-        ("update nt -> nt sc1, 16 rows per wavefront", U, NT, NT | SC1, 0, 64, 16),
-        ("read nt, 4 chunks per lane", R, NT, 0, 0, 256, 4),
-        ("write nt sc1, 4 chunks per lane", Wr, 0, NT | SC1, 0, 256, 4),
+        ("read plain", R, 0, 0, 0, 256, 1, 0),
+        ("read nt", R, NT, 0, 0, 256, 1, 0),
+        ("read nt sc1", R, NT | SC1, 0, 0, 256, 1, 0),
+        ("write plain", Wr, 0, 0, 0, 256, 1, 0),
+        ("write nt", Wr, 0, NT, 0, 256, 1, 0),
+        ("write sc1", Wr, 0, SC1, 0, 256, 1, 0),
+        ("write nt sc1", Wr, 0, NT | SC1, 0, 256, 1, 0),
+        ("write sc0 nt sc1", Wr, 0, SC0 | NT | SC1, 0, 256, 1, 0),
+        ("copy plain -> plain", C, 0, 0, 0, 256, 1, 0),
+        ("copy nt -> nt", C, NT, NT, 0, 256, 1, 0),
+        ("copy nt -> nt sc1", C, NT, NT | SC1, 0, 256, 1, 0),
+        ("copy nt sc1 -> nt sc1", C, NT | SC1, NT | SC1, 0, 256, 1, 0),
+        ("copy nt -> nt sc1, sleep", C, NT, NT | SC1, 1, 256, 1, 0),
+        ("copy nt -> nt sc1, 64 lanes", C, NT, NT | SC1, 0, 64, 1, 0),
+        ("copy nt -> nt sc1, 1024 lanes", C, NT, NT | SC1, 0, 1024, 1, 0),
+        ("copy nt -> nt sc1, 4 chunks per lane", C, NT, NT | SC1, 0, 256, 4, 0),
+        ("copy nt -> nt sc1, 16 chunks per lane", C, NT, NT | SC1, 0, 256, 16, 0),
+        ("update nt -> nt", U, NT, NT, 0, 64, 1, 0),
+        ("update nt -> nt, sleep", U, NT, NT, 1, 64, 1, 0),
+        ("update nt -> nt sc1", U, NT, NT | SC1, 0, 64, 1, 0),
+        ("update nt -> nt sc1, sleep", U, NT, NT | SC1, 1, 64, 1, 0),
+        ("update plain -> plain, sleep", U, 0, 0, 1, 64, 1, 0),
+        ("update nt -> nt sc1, sleep, 256 lanes", U, NT, NT | SC1, 1, 256, 1, 0),
+        ("update nt -> nt sc1, 2 rows per wavefront", U, NT, NT | SC1, 0, 64, 2, 0),
+        ("update nt -> nt sc1, 4 rows per wavefront", U, NT, NT | SC1, 0, 64, 4, 0),
+        ("update nt -> nt sc1, 8 rows per wavefront", U, NT, NT | SC1, 0, 64, 8, 0),
+        ("update nt -> nt sc1, 16 rows per wavefront", U, NT, NT | SC1, 0, 64, 16, 0),
+        ("read nt, 4 chunks per lane", R, NT, 0, 0, 256, 4, 0),
+        ("write nt sc1, 4 chunks per lane", Wr, 0, NT | SC1, 0, 256, 4, 0),
+        ("copy nt -> nt sc1, 64 lanes, XCD-contiguous", C, NT, NT | SC1, 0, 64, 1, 1),
+        ("update nt -> nt sc1, XCD-contiguous", U, NT, NT | SC1, 0, 64, 1, 1),
     ]
 
 
@@ -695,14 +698,15 @@ def sweep_streams(torch, probe, nbytes, launches=20, rounds=4):
     key = 0x9E3779B9
     stream = torch.cuda.current_stream().cuda_stream
 
-    def launcher(kind, lp, sp, sleep, lanes, depth):
+    def launcher(kind, lp, sp, sleep, lanes, depth, xcd):
         if kind == probe.READ:
             d, s_ = sink.data_ptr(), src.data_ptr()
         elif kind == probe.COPY:
             d, s_ = dst.data_ptr(), src.data_ptr()
         else:
             d, s_ = dst.data_ptr(), None
-        return lambda: probe.qkv_prep_probe_stream(kind, lp, sp, sleep, lanes, depth, d, s_, nbytes, key, stream)
+        return lambda: probe.qkv_prep_probe_stream(kind, lp, sp, sleep, lanes, depth, xcd, d, s_, nbytes, key,
+                                                   stream)
 
     fns = [launcher(*row[1:]) for row in table]
     warm_chip(torch, probe)
@@ -717,10 +721,11 @@ def sweep_streams(torch, probe, nbytes, launches=20, rounds=4):
     if int(sink[0].item()) != 0:
         raise RuntimeError("read stream sink was written: the source did not hold zeros")
     rows = []
-    for (label, kind, lp, sp, sleep, lanes, depth), t in zip(table, best):
+    for (label, kind, lp, sp, sleep, lanes, depth, xcd), t in zip(table, best):
         traffic = nbytes * (2 if kind in (probe.COPY, probe.UPDATE) else 1)
         rows.append({"stream": label, "kind": kind, "load_policy": lp, "store_policy": sp, "sleep": sleep,
-                     "lanes": lanes, "depth": depth, "us": round(t * 1e6, 2), "gbps": round(traffic / t / 1e9, 1)})
+                     "lanes": lanes, "depth": depth, "xcd_order": xcd, "us": round(t * 1e6, 2),
+                     "gbps": round(traffic / t / 1e9, 1)})
     del src, dst, sink
     torch.cuda.empty_cache()
     return {"mode": "streams", "bytes": nbytes, "launches": launches, "rounds": rounds, "streams": rows}

@@ -55,10 +55,18 @@ __device__ __forceinline__ void store_policy(u32x4 *base, uint32_t bytes, uint32
 // each in-range chunk's four words with `key` and writing the key to the sink
 // word dst[0] on a match.
 template <int KIND, int LP, int SP, bool SLEEP, int DEPTH>
-__device__ __forceinline__ void stream_body(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
+__device__ __forceinline__ void stream_body(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key,
+                                            uint32_t xcd_chunk)
 {
+    // Workgroups go to the 8 XCDs round-robin (workgroup b to XCD b % 8).
+    // With xcd_chunk > 0 (a grid of 8 * xcd_chunk workgroups), workgroup b
+    // takes range (b % 8) * xcd_chunk + b / 8, so each XCD streams one
+    // contiguous eighth; workgroups past the end exit before any access.
+    const uint32_t b = xcd_chunk ? (blockIdx.x & 7u) * xcd_chunk + (blockIdx.x >> 3) : blockIdx.x;
     const int64_t per = (int64_t)blockDim.x * DEPTH;
-    const int64_t first = (int64_t)blockIdx.x * per;
+    const int64_t first = (int64_t)b * per;
+    if (first >= n)
+        return;
     const int64_t left = n - first;
     const uint32_t span = (uint32_t)(left < per ? left : per) * 16u;
     uint32_t off[DEPTH];
@@ -99,9 +107,10 @@ __device__ __forceinline__ void stream_body(u32x4 *dst, const u32x4 *src, int64_
 }
 
 template <int KIND, int LP, int SP, bool SLEEP, int DEPTH>
-__global__ __launch_bounds__(1024) void policy_stream(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
+__global__ __launch_bounds__(1024) void policy_stream(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key,
+                                                     uint32_t xcd_chunk)
 {
-    stream_body<KIND, LP, SP, SLEEP, DEPTH>(dst, src, n, key);
+    stream_body<KIND, LP, SP, SLEEP, DEPTH>(dst, src, n, key, xcd_chunk);
 }
 
 // The two ceilings are the policy streams at their fastest settings in the
@@ -115,12 +124,12 @@ constexpr int kCeilingLanes = 64;
 
 __global__ __launch_bounds__(kCeilingLanes) void stream_copy(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
 {
-    stream_body<kCopy, kNt, kNt | kSc1, false, 1>(dst, src, n, key);
+    stream_body<kCopy, kNt, kNt | kSc1, false, 1>(dst, src, n, key, 0u);
 }
 
 __global__ __launch_bounds__(kCeilingLanes) void stream_update(u32x4 *dst, const u32x4 *src, int64_t n, uint32_t key)
 {
-    stream_body<kUpdate, kNt, kNt | kSc1, false, 1>(dst, src, n, key);
+    stream_body<kUpdate, kNt, kNt | kSc1, false, 1>(dst, src, n, key, 0u);
 }
 
 struct StreamLaunch {
@@ -130,13 +139,14 @@ struct StreamLaunch {
     const u32x4 *src;
     int64_t n;
     uint32_t key;
+    uint32_t xcd_chunk;
 };
 
 template <int KIND, int LP, int SP, bool SLEEP, int DEPTH = 1>
 bool launch_stream(const StreamLaunch &L)
 {
     hipLaunchKernelGGL((policy_stream<KIND, LP, SP, SLEEP, DEPTH>), L.grid, L.block, 0, L.stream, L.dst, L.src,
-                       L.n, L.key);
+                       L.n, L.key, L.xcd_chunk);
     return true;
 }
 
@@ -428,8 +438,8 @@ extern "C" int qkv_prep_probe_ue8m0(const float *in, int64_t n, void *op_byte_ou
 }
 
 extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t store_policy, int32_t sleep,
-                                     int32_t lanes_per_block, int32_t depth, void *dst, const void *src,
-                                     int64_t bytes, uint32_t key, void *stream)
+                                     int32_t lanes_per_block, int32_t depth, int32_t xcd_order, void *dst,
+                                     const void *src, int64_t bytes, uint32_t key, void *stream)
 {
     const uintptr_t pd = reinterpret_cast<uintptr_t>(dst), ps = reinterpret_cast<uintptr_t>(src);
     const bool reads = kind == kRead || kind == kCopy || kind == kUpdate;
@@ -447,6 +457,8 @@ extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t 
         return 1;
     if (depth != 1 && depth != 2 && depth != 4 && depth != 8 && depth != 16)
         return 1;
+    if (xcd_order != 0 && xcd_order != 1)
+        return 1;
     if (depth > 1 && (sleep || load_policy != (reads ? kNt : 0) || store_policy != (writes ? (kNt | kSc1) : 0)))
         return 1;
     // dst: the sink word of a read (4-byte aligned), else the written range
@@ -461,10 +473,13 @@ extern "C" int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t 
     const int64_t n = bytes / 16;
     const int64_t per = (int64_t)lanes_per_block * depth;
     const int64_t blocks = (n + per - 1) / per;
-    if (blocks >= ((int64_t)1 << 31))
+    const int64_t chunk = xcd_order ? (blocks + 7) / 8 : 0;
+    const int64_t grid = xcd_order ? 8 * chunk : blocks;
+    if (grid >= ((int64_t)1 << 31))
         return 1;
     StreamLaunch L;
-    L.grid = dim3((uint32_t)blocks);
+    L.grid = dim3((uint32_t)grid);
+    L.xcd_chunk = (uint32_t)chunk;
     L.block = dim3((uint32_t)lanes_per_block);
     L.stream = static_cast<hipStream_t>(stream);
     L.dst = static_cast<u32x4 *>(dst);

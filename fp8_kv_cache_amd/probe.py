@@ -32,7 +32,7 @@ def _load():
     L.qkv_prep_probe_copy.argtypes = [vp, vp, i64, vp]
     L.qkv_prep_probe_update.argtypes = [vp, i64, vp]
     i32 = ctypes.c_int32
-    L.qkv_prep_probe_stream.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, ctypes.c_uint32, vp]
+    L.qkv_prep_probe_stream.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, i64, ctypes.c_uint32, vp]
     L.qkv_prep_probe_mxfp8_pattern.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, vp]
     L.qkv_prep_probe_convert.argtypes = [vp, i64, vp, vp, ctypes.c_int32, vp]
     L.qkv_prep_probe_ue8m0.argtypes = [vp, i64, vp, vp, vp, vp]
@@ -64,10 +64,11 @@ def qkv_prep_probe_update(buf_ptr: int, nbytes: int, stream=None) -> None:
 
 
 def qkv_prep_probe_stream(kind: int, load_policy: int, store_policy: int, sleep: int, lanes_per_block: int,
-                          depth: int, dst_ptr, src_ptr, nbytes: int, key: int = 0, stream=None) -> None:
+                          depth: int, xcd_order: int, dst_ptr, src_ptr, nbytes: int, key: int = 0,
+                          stream=None) -> None:
     """A policy-selectable read, write, copy or in-place update stream."""
-    _check(_lib.qkv_prep_probe_stream(kind, load_policy, store_policy, sleep, lanes_per_block, depth, dst_ptr,
-                                      src_ptr, nbytes, key, stream), "qkv_prep_probe_stream")
+    _check(_lib.qkv_prep_probe_stream(kind, load_policy, store_policy, sleep, lanes_per_block, depth, xcd_order,
+                                      dst_ptr, src_ptr, nbytes, key, stream), "qkv_prep_probe_stream")
 
 
 def qkv_prep_probe_mxfp8_pattern(x_ptr, residual_ptr, gamma_ptr, residual_out_ptr, codes_ptr, scales_ptr, m: int,

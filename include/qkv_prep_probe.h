@@ -69,14 +69,18 @@ int qkv_prep_probe_update(void *buf, int64_t bytes, void *stream);
  * make must be 0.  sleep = 1 (copy and update only) pauses each wavefront for
  * about 128 cycles between its loads' arrival and its stores; else 0.  With
  * depth > 1 the policies must be NT loads and NT|SC1 stores, and sleep 0.
+ * xcd_order = 0 takes the workgroups' ranges in dispatch order (consecutive
+ * workgroups, which the hardware deals round-robin over the 8 XCDs, take
+ * consecutive ranges); xcd_order = 1 gives each XCD one contiguous eighth of
+ * the buffer instead (the grid is padded to a multiple of 8 workgroups).
  * Written and read ranges 16-byte aligned.  Traffic: `bytes` for a read or a
  * write, 2 * bytes for a copy or an update.  bytes == 0 is a no-op after the
  * checks. */
 enum { QKV_PREP_PROBE_READ = 0, QKV_PREP_PROBE_WRITE = 1, QKV_PREP_PROBE_COPY = 2, QKV_PREP_PROBE_UPDATE = 3 };
 enum { QKV_PREP_PROBE_SC0 = 1, QKV_PREP_PROBE_NT = 2, QKV_PREP_PROBE_SC1 = 16 };
 int qkv_prep_probe_stream(int32_t kind, int32_t load_policy, int32_t store_policy, int32_t sleep,
-                          int32_t lanes_per_block, int32_t depth, void *dst, const void *src, int64_t bytes,
-                          uint32_t key, void *stream);
+                          int32_t lanes_per_block, int32_t depth, int32_t xcd_order, void *dst, const void *src,
+                          int64_t bytes, uint32_t key, void *stream);
 
 /* The MXFP8 operator's memory access pattern with no arithmetic, for
  * measuring how close that operator runs to what its own loads and stores

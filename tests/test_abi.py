@@ -329,56 +329,62 @@ def test_probes_reject_bad_arguments_without_launching():
     R, Wr, C, U = probe.READ, probe.WRITE, probe.COPY, probe.UPDATE
     NT, SC1, SC0 = probe.NT, probe.SC1, probe.SC0
     # Good arguments with nothing to do return OK without launching.
-    assert st(R, NT, 0, 0, 256, 1, A, B, 0, 0, None) == qp.OK
-    assert st(Wr, 0, NT | SC1, 0, 64, 1, A, None, 0, 0, None) == qp.OK
-    assert st(C, NT, NT | SC1, 1, 1024, 1, A, B, 0, 0, None) == qp.OK
-    assert st(U, NT, SC0 | NT | SC1, 1, 64, 1, A, None, 0, 0, None) == qp.OK
-    assert st(R, 0, 0, 0, 256, 1, A + 4, B, 0, 0, None) == qp.OK        # a read's sink is a word
+    assert st(R, NT, 0, 0, 256, 1, 0, A, B, 0, 0, None) == qp.OK
+    assert st(Wr, 0, NT | SC1, 0, 64, 1, 0, A, None, 0, 0, None) == qp.OK
+    assert st(C, NT, NT | SC1, 1, 1024, 1, 0, A, B, 0, 0, None) == qp.OK
+    assert st(U, NT, SC0 | NT | SC1, 1, 64, 1, 0, A, None, 0, 0, None) == qp.OK
+    assert st(R, 0, 0, 0, 256, 1, 0, A + 4, B, 0, 0, None) == qp.OK        # a read's sink is a word
     for depth in (2, 4, 8, 16):
-        assert st(R, NT, 0, 0, 64, depth, A, B, 0, 0, None) == qp.OK
-        assert st(Wr, 0, NT | SC1, 0, 64, depth, A, None, 0, 0, None) == qp.OK
-        assert st(C, NT, NT | SC1, 0, 64, depth, A, B, 0, 0, None) == qp.OK
-        assert st(U, NT, NT | SC1, 0, 1024, depth, A, None, 0, 0, None) == qp.OK
+        assert st(R, NT, 0, 0, 64, depth, 0, A, B, 0, 0, None) == qp.OK
+        assert st(Wr, 0, NT | SC1, 0, 64, depth, 0, A, None, 0, 0, None) == qp.OK
+        assert st(C, NT, NT | SC1, 0, 64, depth, 0, A, B, 0, 0, None) == qp.OK
+        assert st(U, NT, NT | SC1, 0, 1024, depth, 0, A, None, 0, 0, None) == qp.OK
     bad = [
-        (4, NT, 0, 0, 256, 1, A, B, 16),            # no such kind
-        (-1, NT, 0, 0, 256, 1, A, B, 16),
-        (R, NT, 0, 0, 256, 1, A, B, 15),            # not whole chunks
-        (R, NT, 0, 0, 256, 1, A, B, -16),
-        (R, NT, 0, 0, 32, 1, A, B, 16),             # lanes per block
-        (R, NT, 0, 0, 2048, 1, A, B, 16),
-        (R, NT, 0, 0, 96, 1, A, B, 16),
-        (R, SC1, 0, 0, 256, 1, A, B, 16),           # load policy outside the accepted set
-        (R, SC0 | NT, 0, 0, 256, 1, A, B, 16),
-        (R, NT, NT, 0, 256, 1, A, B, 16),           # a read makes no store
-        (Wr, NT, NT, 0, 256, 1, A, None, 16),       # a write makes no load
-        (Wr, 0, SC0, 0, 256, 1, A, None, 16),       # store policy outside the accepted set
-        (Wr, 0, NT | SC0, 0, 256, 1, A, None, 16),
-        (R, NT, 0, 1, 256, 1, A, B, 16),            # sleep only in a copy or an update
-        (Wr, 0, NT, 1, 256, 1, A, None, 16),
-        (C, NT, NT, 2, 256, 1, A, B, 16),           # sleep is 0 or 1
-        (R, NT, 0, 0, 256, 1, None, B, 16),         # NULL sink
-        (R, NT, 0, 0, 256, 1, A + 2, B, 16),        # misaligned sink
-        (R, NT, 0, 0, 256, 1, A, None, 16),         # NULL source
-        (R, NT, 0, 0, 256, 1, A, B + 8, 16),        # misaligned source
-        (Wr, 0, NT, 0, 256, 1, A + 4, None, 16),    # misaligned destination
-        (Wr, 0, NT, 0, 256, 1, A, B, 16),           # a write takes no source
-        (U, NT, NT, 0, 256, 1, A, B, 16),           # an update takes no source
-        (C, NT, NT, 0, 256, 1, A, A + 16, 32),      # overlapping copy
-        (C, NT, NT, 0, 256, 1, A + 16, A, 32),
-        (C, NT, NT, 0, 256, 1, A, None, 16),
-        (Wr, 0, NT, 0, 64, 1, A, None, (1 << 31) * 64 * 16),  # 2^31 workgroups
-        (Wr, 0, NT | SC1, 0, 64, 16, A, None, (1 << 31) * 64 * 16 * 16),
-        (R, NT, 0, 0, 256, 3, A, B, 16),         # depth 1, 2, 4, 8 or 16
-        (R, NT, 0, 0, 256, 32, A, B, 16),
-        (R, NT, 0, 0, 256, 0, A, B, 16),
-        (R, NT | SC1, 0, 0, 256, 2, A, B, 16),   # depth > 1: nt loads, nt sc1 stores, no pause
-        (Wr, 0, NT, 0, 256, 4, A, None, 16),
-        (C, NT, NT, 0, 256, 8, A, B, 16),
-        (C, 0, NT | SC1, 0, 256, 8, A, B, 16),
-        (U, NT, NT | SC1, 1, 256, 2, A, None, 16),
+        (4, NT, 0, 0, 256, 1, 0, A, B, 16),            # no such kind
+        (-1, NT, 0, 0, 256, 1, 0, A, B, 16),
+        (R, NT, 0, 0, 256, 1, 0, A, B, 15),            # not whole chunks
+        (R, NT, 0, 0, 256, 1, 0, A, B, -16),
+        (R, NT, 0, 0, 32, 1, 0, A, B, 16),             # lanes per block
+        (R, NT, 0, 0, 2048, 1, 0, A, B, 16),
+        (R, NT, 0, 0, 96, 1, 0, A, B, 16),
+        (R, SC1, 0, 0, 256, 1, 0, A, B, 16),           # load policy outside the accepted set
+        (R, SC0 | NT, 0, 0, 256, 1, 0, A, B, 16),
+        (R, NT, NT, 0, 256, 1, 0, A, B, 16),           # a read makes no store
+        (Wr, NT, NT, 0, 256, 1, 0, A, None, 16),       # a write makes no load
+        (Wr, 0, SC0, 0, 256, 1, 0, A, None, 16),       # store policy outside the accepted set
+        (Wr, 0, NT | SC0, 0, 256, 1, 0, A, None, 16),
+        (R, NT, 0, 1, 256, 1, 0, A, B, 16),            # sleep only in a copy or an update
+        (Wr, 0, NT, 1, 256, 1, 0, A, None, 16),
+        (C, NT, NT, 2, 256, 1, 0, A, B, 16),           # sleep is 0 or 1
+        (R, NT, 0, 0, 256, 1, 0, None, B, 16),         # NULL sink
+        (R, NT, 0, 0, 256, 1, 0, A + 2, B, 16),        # misaligned sink
+        (R, NT, 0, 0, 256, 1, 0, A, None, 16),         # NULL source
+        (R, NT, 0, 0, 256, 1, 0, A, B + 8, 16),        # misaligned source
+        (Wr, 0, NT, 0, 256, 1, 0, A + 4, None, 16),    # misaligned destination
+        (Wr, 0, NT, 0, 256, 1, 0, A, B, 16),           # a write takes no source
+        (U, NT, NT, 0, 256, 1, 0, A, B, 16),           # an update takes no source
+        (C, NT, NT, 0, 256, 1, 0, A, A + 16, 32),      # overlapping copy
+        (C, NT, NT, 0, 256, 1, 0, A + 16, A, 32),
+        (C, NT, NT, 0, 256, 1, 0, A, None, 16),
+        (Wr, 0, NT, 0, 64, 1, 0, A, None, (1 << 31) * 64 * 16),  # 2^31 workgroups
+        (Wr, 0, NT | SC1, 0, 64, 16, 0, A, None, (1 << 31) * 64 * 16 * 16),
+        (R, NT, 0, 0, 256, 3, 0, A, B, 16),         # depth 1, 2, 4, 8 or 16
+        (R, NT, 0, 0, 256, 32, 0, A, B, 16),
+        (R, NT, 0, 0, 256, 0, 0, A, B, 16),
+        (R, NT | SC1, 0, 0, 256, 2, 0, A, B, 16),   # depth > 1: nt loads, nt sc1 stores, no pause
+        (Wr, 0, NT, 0, 256, 4, 0, A, None, 16),
+        (C, NT, NT, 0, 256, 8, 0, A, B, 16),
+        (C, 0, NT | SC1, 0, 256, 8, 0, A, B, 16),
+        (U, NT, NT | SC1, 1, 256, 2, 0, A, None, 16),
     ]
     for a in bad:
         assert st(*a, 0, None) == qp.ERR_INVALID_ARG, a
+    for xcd in (0, 1):
+        assert st(C, NT, NT | SC1, 0, 64, 1, xcd, A, B, 0, 0, None) == qp.OK
+    for xcd in (-1, 2):
+        assert st(C, NT, NT | SC1, 0, 64, 1, xcd, A, B, 16, 0, None) == qp.ERR_INVALID_ARG
+    # the padded grid must stay below 2^31 workgroups too
+    assert st(Wr, 0, NT, 0, 64, 1, 1, A, None, ((1 << 31) - 7) * 64 * 16, 0, None) == qp.ERR_INVALID_ARG
     mx = lib.qkv_prep_probe_mxfp8_pattern
     X, Rs, Gm, Ro, Cd, Sc = 1 << 20, 2 << 20, 6 << 20, 3 << 20, 4 << 20, 5 << 20
     assert mx(X, Rs, Gm, Ro, Cd, Sc, 0, 7168, 15, None) == qp.OK             # no rows

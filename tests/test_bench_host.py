@@ -131,9 +131,9 @@ def test_streams_table_holds_only_combinations_the_probe_accepts():
     lib = probe.library()
     table = bench.stream_table(probe)
     assert len({row[0] for row in table}) == len(table)
-    for label, kind, lp, sp, sleep, lanes, depth in table:
+    for label, kind, lp, sp, sleep, lanes, depth, xcd in table:
         src = None if kind in (probe.WRITE, probe.UPDATE) else 1 << 30
-        assert lib.qkv_prep_probe_stream(kind, lp, sp, sleep, lanes, depth, 1 << 20, src, 0, 0, None) == 0, label
+        assert lib.qkv_prep_probe_stream(kind, lp, sp, sleep, lanes, depth, xcd, 1 << 20, src, 0, 0, None) == 0, label
     # the MXFP8 pattern's stream sets, with every buffer given
     for streams in (1 | 2 | 4 | 8, 1 | 2 | 4, 1 | 2 | 8, 1 | 4 | 8, 1 | 8):
         assert lib.qkv_prep_probe_mxfp8_pattern(1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 6 << 20, 0, 7168,

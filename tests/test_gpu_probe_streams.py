@@ -48,7 +48,7 @@ def test_write_stream_pattern_every_policy(chunks):
     for n, (sp, lanes) in enumerate(itertools.product(STORES, LANES)):
         buf = guarded(nbytes, 100 + n)
         before = buf.clone()
-        probe.qkv_prep_probe_stream(probe.WRITE, 0, sp, 0, lanes, 1, buf[GUARD:].data_ptr(), None, nbytes, key,
+        probe.qkv_prep_probe_stream(probe.WRITE, 0, sp, 0, lanes, 1, 0, buf[GUARD:].data_ptr(), None, nbytes, key,
                                     stream())
         what = "write chunks=%d store=%d lanes=%d" % (chunks, sp, lanes)
         check_guards(buf, before, nbytes, what)
@@ -66,7 +66,7 @@ def test_copy_stream_every_policy(chunks):
             continue
         buf = guarded(nbytes, 200 + n)
         before = buf.clone()
-        probe.qkv_prep_probe_stream(probe.COPY, lp, sp, sleep, lanes, 1, buf[GUARD:].data_ptr(), src.data_ptr(),
+        probe.qkv_prep_probe_stream(probe.COPY, lp, sp, sleep, lanes, 1, 0, buf[GUARD:].data_ptr(), src.data_ptr(),
                                     nbytes, 0, stream())
         what = "copy chunks=%d load=%d store=%d sleep=%d lanes=%d" % (chunks, lp, sp, sleep, lanes)
         check_guards(buf, before, nbytes, what)
@@ -83,7 +83,7 @@ def test_update_stream_every_policy(chunks):
         words = buf[GUARD:GUARD + nbytes].view(torch.int32).view(chunks, 4)
         words[::5, 0] = -1                         # 0xFFFFFFFF wraps to 0
         before = buf.clone()
-        probe.qkv_prep_probe_stream(probe.UPDATE, lp, sp, sleep, lanes, 1, buf[GUARD:].data_ptr(), None, nbytes, 0,
+        probe.qkv_prep_probe_stream(probe.UPDATE, lp, sp, sleep, lanes, 1, 0, buf[GUARD:].data_ptr(), None, nbytes, 0,
                                     stream())
         what = "update chunks=%d load=%d store=%d sleep=%d lanes=%d" % (chunks, lp, sp, sleep, lanes)
         check_guards(buf, before, nbytes, what)
@@ -105,14 +105,14 @@ def test_read_stream_writes_the_key_only_on_a_match(chunks):
     src[x == key, 0] ^= 1
     for lp, lanes in itertools.product(LOADS, LANES):
         sink = torch.full((4,), 77, dtype=torch.int32, device=DEV)
-        probe.qkv_prep_probe_stream(probe.READ, lp, 0, 0, lanes, 1, sink.data_ptr(), src.data_ptr(), nbytes, key,
+        probe.qkv_prep_probe_stream(probe.READ, lp, 0, 0, lanes, 1, 0, sink.data_ptr(), src.data_ptr(), nbytes, key,
                                     stream())
         assert sink.tolist() == [77] * 4, "read without a match wrote the sink (load=%d lanes=%d)" % (lp, lanes)
     planted = src.clone()
     planted[-1, 3] = planted[-1, 0] ^ planted[-1, 1] ^ planted[-1, 2] ^ key
     for lp, lanes in itertools.product(LOADS, LANES):
         sink = torch.full((4,), 77, dtype=torch.int32, device=DEV)
-        probe.qkv_prep_probe_stream(probe.READ, lp, 0, 0, lanes, 1, sink.data_ptr(), planted.data_ptr(), nbytes,
+        probe.qkv_prep_probe_stream(probe.READ, lp, 0, 0, lanes, 1, 0, sink.data_ptr(), planted.data_ptr(), nbytes,
                                     key, stream())
         assert sink.tolist() == [key, 77, 77, 77], "read with a match (load=%d lanes=%d)" % (lp, lanes)
 
@@ -121,9 +121,11 @@ DEPTHS = (2, 4, 8, 16)
 
 
 @pytest.mark.parametrize("chunks", CHUNKS)
-def test_streams_with_several_chunks_per_lane(chunks):
-    """depth > 1: every lane takes `depth` chunks, the workgroup's range is
-    lanes * depth chunks, and the last workgroup is ragged."""
+def test_streams_by_chunks_per_lane_and_xcd_order(chunks):
+    """Every lane takes `depth` chunks, the workgroup's range is lanes * depth
+    chunks and the last workgroup is ragged; with the XCD-contiguous order the
+    ranges are dealt to the workgroups in another order and the grid is padded
+    to a multiple of 8 workgroups."""
     nbytes = chunks * 16
     key = 0x5EED5EED
     g = torch.Generator(device=DEV).manual_seed(1000 + chunks)
@@ -134,11 +136,11 @@ def test_streams_with_several_chunks_per_lane(chunks):
     want_write = np.stack([(i & 0xFFFFFFFF).astype(np.uint32), (i >> np.uint64(32)).astype(np.uint32),
                            np.full(chunks, key, np.uint32), np.full(chunks, ~np.uint32(key), np.uint32)], axis=1)
     NT, NTS = probe.NT, probe.NT | probe.SC1
-    for n, (depth, lanes) in enumerate(itertools.product(DEPTHS, (64, 256, 1024))):
-        what = "chunks=%d depth=%d lanes=%d" % (chunks, depth, lanes)
+    for n, (depth, lanes, XCD) in enumerate(itertools.product((1,) + DEPTHS, (64, 256, 1024), (0, 1))):
+        what = "chunks=%d depth=%d lanes=%d xcd_order=%d" % (chunks, depth, lanes, XCD)
         buf = guarded(nbytes, 400 + n)
         before = buf.clone()
-        probe.qkv_prep_probe_stream(probe.WRITE, 0, NTS, 0, lanes, depth, buf[GUARD:].data_ptr(), None, nbytes,
+        probe.qkv_prep_probe_stream(probe.WRITE, 0, NTS, 0, lanes, depth, XCD, buf[GUARD:].data_ptr(), None, nbytes,
                                     key, stream())
         check_guards(buf, before, nbytes, "write " + what)
         got = buf[GUARD:GUARD + nbytes].cpu().numpy().view(np.uint32).reshape(chunks, 4)
@@ -146,14 +148,14 @@ def test_streams_with_several_chunks_per_lane(chunks):
 
         buf = guarded(nbytes, 500 + n)
         before = buf.clone()
-        probe.qkv_prep_probe_stream(probe.COPY, NT, NTS, 0, lanes, depth, buf[GUARD:].data_ptr(), src.data_ptr(),
+        probe.qkv_prep_probe_stream(probe.COPY, NT, NTS, 0, lanes, depth, XCD, buf[GUARD:].data_ptr(), src.data_ptr(),
                                     nbytes, 0, stream())
         check_guards(buf, before, nbytes, "copy " + what)
         assert torch.equal(buf[GUARD:GUARD + nbytes].view(torch.int32).view(chunks, 4), src), "copy " + what
 
         buf = guarded(nbytes, 600 + n)
         before = buf.clone()
-        probe.qkv_prep_probe_stream(probe.UPDATE, NT, NTS, 0, lanes, depth, buf[GUARD:].data_ptr(), None, nbytes,
+        probe.qkv_prep_probe_stream(probe.UPDATE, NT, NTS, 0, lanes, depth, XCD, buf[GUARD:].data_ptr(), None, nbytes,
                                     0, stream())
         check_guards(buf, before, nbytes, "update " + what)
         old = before[GUARD:GUARD + nbytes].cpu().numpy().view(np.uint32).reshape(chunks, 4)
@@ -162,12 +164,12 @@ def test_streams_with_several_chunks_per_lane(chunks):
         assert np.array_equal(got[:, 1:], old[:, 1:]), "update " + what
 
         sink = torch.full((4,), 77, dtype=torch.int32, device=DEV)
-        probe.qkv_prep_probe_stream(probe.READ, NT, 0, 0, lanes, depth, sink.data_ptr(), src.data_ptr(), nbytes,
+        probe.qkv_prep_probe_stream(probe.READ, NT, 0, 0, lanes, depth, XCD, sink.data_ptr(), src.data_ptr(), nbytes,
                                     key, stream())
         assert sink.tolist() == [77] * 4, "read without a match " + what
         planted = src.clone()
         planted[-1, 3] = planted[-1, 0] ^ planted[-1, 1] ^ planted[-1, 2] ^ key
-        probe.qkv_prep_probe_stream(probe.READ, NT, 0, 0, lanes, depth, sink.data_ptr(), planted.data_ptr(),
+        probe.qkv_prep_probe_stream(probe.READ, NT, 0, 0, lanes, depth, XCD, sink.data_ptr(), planted.data_ptr(),
                                     nbytes, key, stream())
         assert sink.tolist() == [key, 77, 77, 77], "read with a match " + what
 
