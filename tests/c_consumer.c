@@ -1,5 +1,5 @@
 /* A C99 consumer of the library: no Python, no torch.  It includes only the
- * public header and the HIP runtime's C API, allocates device memory, runs
+ * public headers and the HIP runtime's C API, allocates device memory, runs
  * qkv_prep_run and qkv_prep_gather on a small ragged case (37 tokens x 12
  * heads, 16-slot blocks, skipped and out-of-range slots, a poisoned cache) and
  * compares q, the whole cache and the gathered rows with the oracle's C
@@ -7,8 +7,11 @@
  * for byte.  Then it captures the same two calls into a HIP graph on a stream
  * of its own and replays the graph three times over freshly uploaded inputs,
  * each replay compared the same way: the calls allocate nothing and issue no
- * memset, so a C caller can capture them.  Exit status 0 = bit-exact; the
- * last line printed says which part differed otherwise. */
+ * memset, so a C caller can capture them.  Last, qkv_prep_mxfp8_norm_quant on
+ * 130 rows of hidden 640 (a ragged 128-row tile and a partial 512-group) with
+ * the residual in and out: codes, the whole poisoned scale buffer and the
+ * residual output against the oracle.  Exit status 0 = bit-exact; the last
+ * line printed says which part differed otherwise. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -17,6 +20,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "qkv_prep.h"
+#include "qkv_prep_mxfp8.h"
 
 /* The oracle (oracle/qkv_oracle.c). */
 int orc_qkv_prep(int64_t num_tokens, int32_t num_heads, const uint16_t *q_in, uint16_t *q_out,
@@ -25,6 +29,9 @@ int orc_qkv_prep(int64_t num_tokens, int32_t num_heads, const uint16_t *q_in, ui
                  int64_t num_blocks, int32_t block_size, float eps, int nthreads);
 void orc_gather_dequant(const uint8_t *cache, int64_t num_blocks, int32_t block_size, const int64_t *slots,
                         int64_t n, float *out);
+int orc_mxfp8_norm_quant(int64_t m, int64_t hidden, const uint16_t *x, const uint16_t *residual,
+                         uint16_t *residual_out, const uint16_t *gamma, float eps, uint8_t *quant_out,
+                         uint8_t *scale_out);
 
 enum { T = 37, H = 12, B = 16, NB = 5, P = 1000, D = 512 };
 
@@ -52,6 +59,81 @@ static uint16_t rand_bf16(void)
             return 2;                                                                    \
         }                                                                                \
     } while (0)
+
+/* The MXFP8 operator from C: 0 = bit-exact, 1 = a part differs, 2 = a call failed. */
+enum { MXM = 130, MXH = 640 };
+
+static int run_mxfp8(void)
+{
+    static uint16_t x[MXM * MXH], r[MXM * MXH], gamma[MXH], res_out[MXM * MXH], res_ref[MXM * MXH];
+    static uint8_t codes[MXM * MXH], codes_ref[MXM * MXH];
+    const int64_t ns = qkv_prep_mxfp8_scale_bytes(MXM, MXH);
+    size_t i;
+    if (ns <= 0) {
+        printf("qkv_prep_mxfp8_scale_bytes failed\n");
+        return 2;
+    }
+    uint8_t *scales = (uint8_t *)malloc((size_t)ns), *scales_ref = (uint8_t *)malloc((size_t)ns);
+    if (!scales || !scales_ref)
+        return 2;
+    for (i = 0; i < MXM * MXH; ++i) {
+        x[i] = rand_bf16();
+        r[i] = rand_bf16();
+    }
+    for (i = 0; i < MXH; ++i)
+        gamma[i] = (uint16_t)(rand_bf16() & 0xbfff);      /* |gamma| < 2 */
+    void *dx, *dr, *dg, *dres, *dcodes, *dscales;
+    CHECK_HIP(hipMalloc(&dx, sizeof(x)));
+    CHECK_HIP(hipMalloc(&dr, sizeof(r)));
+    CHECK_HIP(hipMalloc(&dg, sizeof(gamma)));
+    CHECK_HIP(hipMalloc(&dres, sizeof(res_out)));
+    CHECK_HIP(hipMalloc(&dcodes, sizeof(codes)));
+    CHECK_HIP(hipMalloc(&dscales, (size_t)ns));
+    CHECK_HIP(hipMemcpy(dx, x, sizeof(x), hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dr, r, sizeof(r), hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dg, gamma, sizeof(gamma), hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemset(dscales, 0xee, (size_t)ns));     /* poison: every byte must be written */
+    CHECK_HIP(hipMemset(dcodes, 0xee, sizeof(codes)));
+    qkv_prep_mxfp8_args a;
+    memset(&a, 0, sizeof(a));
+    a.x = dx;
+    a.residual = dr;
+    a.residual_out = dres;
+    a.gamma = dg;
+    a.quant_out = dcodes;
+    a.scale_out = dscales;
+    a.m = MXM;
+    a.hidden = MXH;
+    a.eps = 1e-6f;
+    const int rc = qkv_prep_mxfp8_norm_quant(&a, 0, NULL);
+    if (rc != QKV_PREP_OK) {
+        printf("qkv_prep_mxfp8_norm_quant: %s\n", qkv_prep_strerror(rc));
+        return 2;
+    }
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_HIP(hipMemcpy(codes, dcodes, sizeof(codes), hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(scales, dscales, (size_t)ns, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(res_out, dres, sizeof(res_out), hipMemcpyDeviceToHost));
+    if (orc_mxfp8_norm_quant(MXM, MXH, x, r, res_ref, gamma, 1e-6f, codes_ref, scales_ref) != 0) {
+        printf("oracle rejected the MXFP8 case\n");
+        return 2;
+    }
+    int bad = 0;
+    if (memcmp(codes, codes_ref, sizeof(codes)) != 0) {
+        printf("mxfp8: codes differ\n");
+        bad = 1;
+    } else if (memcmp(scales, scales_ref, (size_t)ns) != 0) {
+        printf("mxfp8: scale bytes differ\n");
+        bad = 1;
+    } else if (memcmp(res_out, res_ref, sizeof(res_out)) != 0) {
+        printf("mxfp8: residual output differs\n");
+        bad = 1;
+    }
+    hipFree(dx); hipFree(dr); hipFree(dg); hipFree(dres); hipFree(dcodes); hipFree(dscales);
+    free(scales);
+    free(scales_ref);
+    return bad;
+}
 
 /* Nonzero (after printing which part) when a result differs from the oracle. */
 static int compare(const char *what, const void *q_out, const void *q_ref, size_t qn, const void *cache_out,
@@ -213,7 +295,10 @@ int main(void)
     qkv_prep_destroy(h);
     hipFree(dq); hipFree(dkv); hipFree(dqw); hipFree(dkvw); hipFree(dpos);
     hipFree(dcs); hipFree(dslots); hipFree(dcache); hipFree(drows);
-    printf("c consumer: q, cache and gathered rows bit-exact, eager and 3 graph replays (%d tokens x %d heads)\n",
-           T, H);
+    const int mx = run_mxfp8();
+    if (mx != 0)
+        return mx;
+    printf("c consumer: q, cache and gathered rows bit-exact, eager and 3 graph replays (%d tokens x %d heads); "
+           "MXFP8 codes, scales and residual bit-exact (%d x %d)\n", T, H, MXM, MXH);
     return 0;
 }
